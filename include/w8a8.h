@@ -1,0 +1,208 @@
+/*
+ * w8a8.h — C ABI of libw8a8.so, the W8A8 quantized-verification hot path
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The method (Quasar, arXiv 2603.01399, "Quasar: Quantized Self-Speculative
+ * Acceleration for Rapid Inference via Memory-Efficient Verification"):
+ * a drafter proposes a block of tokens and the target model checks the
+ * whole block in one forward pass; Quasar runs that verification pass with
+ * a W8A8 copy of the target — weights smoothed and quantized to INT8
+ * offline, activations scaled by the smoothing factor and quantized to
+ * INT8 at run time, an INT8 product accumulated in INT32, and a dequant
+ * back to high precision before acceptance reads the logits.  Sources, cited
+ * by page and section below:
+ *   [de] gist.science German summary, "Technische Zusammenfassung";
+ *   [it] gist.science Italian summary, "Sommario tecnico";
+ *   [fr] gist.science French summary, "Résumé technique";
+ *   [zh] shd-paper.top Chinese summary and its English abstract;
+ *   [ja] gist.science Japanese summary, "技術的サマリー".
+ *
+ * Conventions for every call:
+ *   - Tensor arguments are DEVICE pointers owned by the caller; the library
+ *     never frees or keeps them.  Tensors are dense and row-major (last
+ *     dimension contiguous).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Calls enqueue kernels on it and return without synchronizing; results
+ *     are valid once the caller synchronizes the stream.  No call allocates
+ *     device or host memory, and none keeps state between calls, so calls
+ *     are thread-safe; calls that share a workspace must be ordered on one
+ *     stream.
+ *   - Arguments are validated on the host before anything is enqueued; a
+ *     rejected call enqueues nothing.  Device data is not validated: inputs
+ *     must be finite (non-finite values give unspecified but in-range
+ *     results, never an out-of-bounds access).
+ *   - Nothing throws across the ABI.  A non-zero status names the failure;
+ *     w8a8_last_error() returns a message for the calling thread's most
+ *     recent failure.
+ *   - Sizes are int64_t; M == 0, N == 0 or B == 0 makes the call a no-op
+ *     that returns W8A8_OK (its pointers may then be NULL).  K == 0 is a
+ *     valid empty contraction (zero products, zero scales).
+ */
+#ifndef W8A8_H
+#define W8A8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t w8a8_status;
+
+#define W8A8_OK              0  /* success */
+#define W8A8_ERR_INVALID_ARG 1  /* NULL pointer, bad size, misalignment, K out of range */
+#define W8A8_ERR_UNSUPPORTED 2  /* valid request this build does not handle */
+#define W8A8_ERR_WORKSPACE   3  /* workspace NULL or smaller than the query says */
+#define W8A8_ERR_HIP         4  /* the HIP runtime reported an error at launch */
+
+/* Largest K for which |sum_k qx*qw| <= 127*127*K fits an int32 accumulator. */
+#define W8A8_MAX_K 133144
+
+/* ABI version of this header; w8a8_abi_version() returns the library's. */
+#define W8A8_ABI_VERSION 1
+
+int32_t     w8a8_abi_version(void);
+
+/* Static text for a status code; never NULL. */
+const char* w8a8_status_string(w8a8_status status);
+
+/* Message describing the calling thread's most recent failure ("" if none).
+ * The pointer stays valid until the thread's next call into the library. */
+const char* w8a8_last_error(void);
+
+/*
+ * Per-token dynamic activation quantization, BF16 -> INT8.
+ *
+ * Pages: activations arrive in BF16, are scaled by the per-channel smoothing
+ * factor s and converted to INT8 at run time ([ja] §2.2 item 3; [de] §2
+ * "Online-Prozess"; [it] §2 pipeline "Inferenza Online"); the quantization
+ * is symmetric and uniform ([it] §2 "Componenti Tecnici" 1).
+ * Computes, for each row m (one token):
+ *   x'[k]      = fp32(x[m][k]) * smooth[k]      (smooth == NULL: x' = fp32(x))
+ *   amax       = max_k |x'[k]|
+ *   x_scale[m] = amax / 127                     (correctly rounded fp32)
+ *   inv        = 127 / amax                     (0 when amax == 0)
+ *   xq[m][k]   = 0 if x'[k] == 0, else clamp(round_half_even(x'[k] * inv), -127, 127)
+ * Every fp32 operation is a single correctly rounded operation; no fused
+ * multiply-add.
+ *
+ * x_bf16   [M][K] bf16 bit patterns, 16-byte aligned.
+ * smooth   [K] fp32, positive and finite, 16-byte aligned; or NULL.
+ * xq       [M][K] int8 output, 16-byte aligned.
+ * x_scale  [M] fp32 output.
+ * Requires 0 <= K <= W8A8_MAX_K and K % 16 == 0.
+ */
+w8a8_status w8a8_quantize_act(const uint16_t* x_bf16, const float* smooth,
+                              int64_t M, int64_t K,
+                              int8_t* xq, float* x_scale, void* stream);
+
+/*
+ * Offline per-output-channel weight quantization, FP32 -> INT8.
+ *
+ * Pages: the weights are smoothed and quantized to INT8 ahead of inference
+ * and kept in device memory ([ja] §2.2 item 2; [it] §2 pipeline
+ * "Preparazione Offline"); smoothing divides the weights by s per input
+ * channel, Y = (W diag(s)^-1)(diag(s) X) ([ja] §2.2 item 1).
+ * Computes, for each output channel n (a row of W):
+ *   w'[k]      = w[n][k] / smooth[k]            (smooth == NULL: w' = w)
+ *   then the same rule as w8a8_quantize_act, giving wq[n][k] and w_scale[n].
+ *
+ * w        [N][K] fp32 (nn.Linear order: K contiguous), 16-byte aligned.
+ * smooth   [K] fp32, positive and finite, 16-byte aligned; or NULL.
+ * wq       [N][K] int8 output, 16-byte aligned.
+ * w_scale  [N] fp32 output.
+ * Requires 0 <= K <= W8A8_MAX_K and K % 16 == 0.
+ */
+w8a8_status w8a8_quantize_weight(const float* w, const float* smooth,
+                                 int64_t N, int64_t K,
+                                 int8_t* wq, float* w_scale, void* stream);
+
+/*
+ * One W8A8 linear: INT8 x INT8 product with INT32 accumulation, then the
+ * dequant epilogue.
+ *
+ * Pages: the product runs on INT8 matrix units and accumulates in INT32;
+ * the result is dequantized to BF16 before the nonlinear layers ([ja] §2.2
+ * item 3; [de] §2 "Online-Prozess" and "De-Quantisierung"; [it] §2 pipeline
+ * "Calcolo" / "Dequantizzazione").
+ * Computes, for m < M, n < N:
+ *   acc[m][n]    = sum_k xq[m][k] * wq[n][k]                  (exact int32)
+ *   y_f32[m][n]  = fp32(fp32(fp32(acc) * x_scale[m]) * w_scale[n])
+ *   y_bf16[m][n] = bf16 round-half-even of y_f32[m][n]
+ *
+ * xq       [M][K] int8 (from w8a8_quantize_act), 16-byte aligned.
+ * x_scale  [M] fp32.
+ * wq       [N][K] int8 (from w8a8_quantize_weight), 16-byte aligned.
+ * w_scale  [N] fp32.
+ * y_bf16   [M][N] bf16 output, or NULL.
+ * y_f32    [M][N] fp32 output, or NULL (the LM head's logits).
+ * acc      [M][N] int32 output, or NULL.   At least one output is non-NULL.
+ * workspace / workspace_bytes: device scratch of at least
+ *          w8a8_linear_workspace_bytes(M, N, K) bytes (NULL allowed when that
+ *          is 0).  The workspace must be zero-filled before its first use;
+ *          every completed call leaves it zero-filled again.  Calls that share
+ *          a workspace must not overlap in time.
+ * Requires 0 <= K <= W8A8_MAX_K, K % 16 == 0; any N (ragged tails are
+ * handled); any M (M <= 16 takes the skinny kernel, larger M the batched one).
+ */
+size_t      w8a8_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
+w8a8_status w8a8_linear(const int8_t* xq, const float* x_scale,
+                        const int8_t* wq, const float* w_scale,
+                        int64_t M, int64_t N, int64_t K,
+                        uint16_t* y_bf16, float* y_f32, int32_t* acc,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * LM-head argmax and greedy acceptance of a draft block.
+ *
+ * Pages: the target verifies the drafted block in one pass and the
+ * acceptance reads the dequantized, high-precision logits ([ja] §2.2
+ * item 4; [it] §2 "Campionamento di rifiuto"); correct drafts are accepted
+ * together and decoding restarts at the first wrong one ([fr] lay summary);
+ * evaluation is greedy, T = 0 ([ja] §4).
+ * Row b*(G+1)+i of `logits` is the target's prediction after position i of
+ * sequence b.  Computes:
+ *   argmax[r]      = lowest n with logits[r][n] == max_j logits[r][j]
+ *   accept_len[b]  = number of leading i < G with draft[b][i] == argmax[b*(G+1)+i]
+ *   next_token[b]  = argmax[b*(G+1) + accept_len[b]]
+ * (tokens emitted by the step: accept_len + 1).  Draft ids outside [0, V)
+ * never match.
+ *
+ * logits     [B*(G+1)][V] fp32, 16-byte aligned.
+ * draft      [B][G] int32 (may be NULL when G == 0).
+ * argmax     [B*(G+1)] int32 output, or NULL.
+ * accept_len [B] int32 output;  next_token [B] int32 output.
+ * workspace: at least w8a8_verify_accept_workspace_bytes(B, G, V) bytes.
+ * Requires 0 <= G <= W8A8_MAX_DRAFT and 1 <= V < 2^31.
+ */
+#define W8A8_MAX_DRAFT 255
+size_t      w8a8_verify_accept_workspace_bytes(int64_t B, int64_t G, int64_t V);
+w8a8_status w8a8_verify_accept(const float* logits, int64_t V,
+                               const int32_t* draft, int64_t B, int64_t G,
+                               int32_t* argmax, int32_t* accept_len,
+                               int32_t* next_token,
+                               void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/*
+ * The BF16 verifier's linear at the same shapes, as the weight-traffic
+ * reference (BF16 weights move twice the bytes of INT8 ones: [zh] abstract;
+ * [de] §3 item 4, latency M*2B/BW against M*1B/BW).
+ * Computes y_f32[m][n] = sum_k x[m][k] * w[n][k] with bf16 operands and
+ * fp32 accumulation (summation order unspecified), y_bf16 = its bf16
+ * round-half-even.
+ *
+ * x_bf16 [M][K] and w_bf16 [N][K] bf16 bit patterns, 16-byte aligned.
+ * y_bf16 [M][N] and/or y_f32 [M][N] outputs (at least one non-NULL).
+ * Requires 0 <= K, K % 16 == 0, M <= 16.
+ */
+w8a8_status w8a8_bf16_linear(const uint16_t* x_bf16, const uint16_t* w_bf16,
+                             int64_t M, int64_t N, int64_t K,
+                             uint16_t* y_bf16, float* y_f32, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W8A8_H */

@@ -1,0 +1,130 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/w8a8.h declares, and rejects bad arguments on the host before
+anything is enqueued (no call here reaches a kernel launch)."""
+import ctypes
+
+import pytest
+
+from w8a8_quantized_verification_amd import _lib
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIP = 0, 1, 2, 3, 4
+A16 = 0x10000  # fake, 16-byte aligned addresses: validation never dereferences them
+A16b = 0x20000
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.lib()
+
+
+def test_exports_every_declared_function(lib):
+    names = _lib.header_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.SIGNATURES), "binding signatures out of sync with the header"
+
+
+def test_version_and_status_strings(lib):
+    assert lib.w8a8_abi_version() == 1
+    for s in (OK, INVALID, UNSUPPORTED, WORKSPACE, HIP, 99):
+        assert lib.w8a8_status_string(s)
+
+
+def q_act(lib, x=A16, smooth=None, M=5, K=4096, xq=A16b, xs=A16):
+    return lib.w8a8_quantize_act(x, smooth, M, K, xq, xs, None)
+
+
+def test_quantize_act_validation(lib):
+    assert q_act(lib, xs=None) == INVALID
+    assert q_act(lib, x=None) == INVALID
+    assert q_act(lib, K=17) == INVALID
+    assert q_act(lib, K=-16) == INVALID
+    assert q_act(lib, M=-1) == INVALID
+    assert q_act(lib, K=133144 + 16) == INVALID
+    assert q_act(lib, x=A16 + 2) == INVALID          # misaligned input
+    assert q_act(lib, smooth=A16 + 4) == INVALID     # misaligned smoothing vector
+    assert q_act(lib, K=24) == INVALID
+    assert b"K must be a multiple of 16" in lib.w8a8_last_error()
+    # empty problem: a no-op that needs no pointers
+    assert q_act(lib, x=None, M=0, xq=None, xs=None) == OK
+    assert lib.w8a8_last_error() == b""
+
+
+def test_quantize_weight_validation(lib):
+    f = lib.w8a8_quantize_weight
+    assert f(A16, None, 10, 4096, A16b, None, None) == INVALID
+    assert f(A16 + 8, None, 10, 4096, A16b, A16, None) == INVALID
+    assert f(None, None, 0, 4096, None, None, None) == OK
+
+
+def lin(lib, xq=A16, xs=A16, wq=A16b, ws=A16, M=5, N=4096, K=4096, yb=A16, yf=None, acc=None,
+        work=None, wbytes=0):
+    return lib.w8a8_linear(xq, xs, wq, ws, M, N, K, yb, yf, acc, work, wbytes, None)
+
+
+def test_linear_validation(lib):
+    assert lin(lib, yb=None) == INVALID                 # no output requested
+    assert lin(lib, K=4100) == INVALID
+    assert lin(lib, K=133144 + 16) == INVALID
+    assert lin(lib, xq=A16 + 1) == INVALID
+    assert lin(lib, wq=A16 + 8) == INVALID
+    assert lin(lib, yf=A16 + 2) == INVALID
+    assert lin(lib, N=-3) == INVALID
+    assert lin(lib, M=0, xq=None, xs=None, wq=None, ws=None, yb=None) == OK
+    assert lin(lib, N=0) == OK
+
+
+def test_linear_workspace(lib):
+    # small-N shapes split K across workgroups and need scratch; the LM head does not
+    need = lib.w8a8_linear_workspace_bytes(5, 1024, 4096)
+    assert need >= 5 * 1024 * 4
+    assert lib.w8a8_linear_workspace_bytes(5, 151936, 4096) == 0
+    assert lib.w8a8_linear_workspace_bytes(0, 1024, 4096) == 0
+    assert lin(lib, N=1024, work=None) == WORKSPACE
+    assert lin(lib, N=1024, work=A16, wbytes=need - 1) == WORKSPACE
+    assert lin(lib, N=1024, work=A16 + 16, wbytes=need) == INVALID  # workspace alignment
+
+
+def va(lib, logits=A16, V=151936, draft=A16, B=1, G=4, am=None, al=A16, nt=A16b, work=A16,
+       wbytes=None):
+    if wbytes is None:
+        wbytes = lib.w8a8_verify_accept_workspace_bytes(B, G, V)
+    return lib.w8a8_verify_accept(logits, V, draft, B, G, am, al, nt, work, wbytes, None)
+
+
+def test_verify_accept_validation(lib):
+    assert lib.w8a8_verify_accept_workspace_bytes(1, 4, 151936) > 0
+    assert va(lib, G=256) == INVALID
+    assert va(lib, G=-1) == INVALID
+    assert va(lib, V=0) == INVALID
+    assert va(lib, draft=None) == INVALID
+    assert va(lib, al=None) == INVALID
+    assert va(lib, logits=A16 + 2) == INVALID
+    assert va(lib, work=None) == WORKSPACE
+    assert va(lib, wbytes=8) == WORKSPACE
+    assert va(lib, B=0, logits=None, draft=None, al=None, nt=None, work=None) == OK
+
+
+def test_bf16_linear_validation(lib):
+    f = lib.w8a8_bf16_linear
+    assert f(A16, A16b, 17, 512, 256, A16, None, None) == UNSUPPORTED
+    assert f(A16, A16b, 5, 512, 250, A16, None, None) == INVALID
+    assert f(A16, A16b, 5, 512, 256, None, None, None) == INVALID
+    assert f(A16 + 2, A16b, 5, 512, 256, A16, None, None) == INVALID
+    assert f(None, None, 0, 512, 256, None, None, None) == OK
+
+
+def test_last_error_is_per_call(lib):
+    assert q_act(lib, K=24) == INVALID
+    assert lib.w8a8_last_error()
+    assert q_act(lib, M=0) == OK
+    assert lib.w8a8_last_error() == b""
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    import w8a8_quantized_verification_amd as w
+    x = torch.zeros(5, 256, dtype=torch.bfloat16)
+    with pytest.raises(TypeError, match="ROCm device"):
+        w.quantize_act(x)

@@ -1,0 +1,14 @@
+"""MI355X-native W8A8 quantized-verification hot path.
+
+The kernels live in libw8a8.so (HIP for gfx950, C ABI in include/w8a8.h);
+this package is its thin torch-tensor binding.  Build the library with
+``python -m w8a8_quantized_verification_amd.build``.
+"""
+from .api import (W8A8Error, Workspace, bf16_linear, linear, linear_workspace_bytes,
+                  quantize_act, quantize_weight, verify_accept,
+                  verify_accept_workspace_bytes)
+
+__all__ = [
+    "W8A8Error", "Workspace", "bf16_linear", "linear", "linear_workspace_bytes",
+    "quantize_act", "quantize_weight", "verify_accept", "verify_accept_workspace_bytes",
+]

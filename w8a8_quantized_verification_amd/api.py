@@ -1,0 +1,178 @@
+"""Python binding of libw8a8.so on torch tensors.
+
+Every function checks dtype, device, contiguity and shape, then passes raw
+device pointers and torch's current HIP stream to the C ABI (include/w8a8.h);
+all arithmetic happens in the library's kernels.  Outputs are allocated with
+torch unless passed in.  Tensors must live on a ROCm device: there is no CPU
+path.
+"""
+from __future__ import annotations
+
+import torch
+
+from ._lib import W8A8Error, check, lib
+
+__all__ = [
+    "W8A8Error", "quantize_act", "quantize_weight", "linear", "linear_workspace_bytes",
+    "verify_accept", "verify_accept_workspace_bytes", "bf16_linear", "Workspace",
+]
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype, ndim: int, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise TypeError(f"{name} must be on a ROCm device (got {t.device}); there is no CPU path")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must be {ndim}-D (got shape {tuple(t.shape)})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _out(t, shape, dtype, device, name):
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    _need(t, name, dtype, len(shape), device)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    return t
+
+
+class Workspace:
+    """Per-device zero-filled scratch for w8a8_linear's split-K partials and
+    verify_accept's chunk results.  Calls that use it must run in order on
+    one stream (the default use)."""
+
+    def __init__(self):
+        self._buf = {}
+
+    def get(self, nbytes: int, device: torch.device) -> torch.Tensor | None:
+        if nbytes == 0:
+            return None
+        key = device.index if device.index is not None else torch.cuda.current_device()
+        b = self._buf.get(key)
+        if b is None or b.numel() < nbytes:
+            b = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+            self._buf[key] = b
+        return b
+
+
+_default_ws = Workspace()
+
+
+def quantize_act(x: torch.Tensor, smooth: torch.Tensor | None = None, *, xq=None, x_scale=None):
+    """Per-token symmetric int8 quantization of bf16 ``x[M][K]``; returns
+    ``(xq int8[M][K], x_scale float32[M])``."""
+    _need(x, "x", torch.bfloat16, 2)
+    M, K = x.shape
+    if smooth is not None:
+        _need(smooth, "smooth", torch.float32, 1, x.device)
+    xq = _out(xq, (M, K), torch.int8, x.device, "xq")
+    x_scale = _out(x_scale, (M,), torch.float32, x.device, "x_scale")
+    check(lib().w8a8_quantize_act(_ptr(x), _ptr(smooth), M, K, _ptr(xq), _ptr(x_scale),
+                                  _stream(x.device)))
+    return xq, x_scale
+
+
+def quantize_weight(w: torch.Tensor, smooth: torch.Tensor | None = None, *, wq=None, w_scale=None):
+    """Per-output-channel symmetric int8 quantization of fp32 ``w[N][K]``;
+    returns ``(wq int8[N][K], w_scale float32[N])``."""
+    _need(w, "w", torch.float32, 2)
+    N, K = w.shape
+    if smooth is not None:
+        _need(smooth, "smooth", torch.float32, 1, w.device)
+    wq = _out(wq, (N, K), torch.int8, w.device, "wq")
+    w_scale = _out(w_scale, (N,), torch.float32, w.device, "w_scale")
+    check(lib().w8a8_quantize_weight(_ptr(w), _ptr(smooth), N, K, _ptr(wq), _ptr(w_scale),
+                                     _stream(w.device)))
+    return wq, w_scale
+
+
+def linear_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(lib().w8a8_linear_workspace_bytes(M, N, K))
+
+
+def linear(xq, x_scale, wq, w_scale, *, want_bf16=True, want_f32=False, want_acc=False,
+           y_bf16=None, y_f32=None, acc=None, workspace: Workspace | None = None):
+    """One W8A8 linear.  Returns ``(y_bf16, y_f32, acc)``, each None unless
+    requested (``want_*``) or passed in."""
+    _need(xq, "xq", torch.int8, 2)
+    dev = xq.device
+    _need(x_scale, "x_scale", torch.float32, 1, dev)
+    _need(wq, "wq", torch.int8, 2, dev)
+    _need(w_scale, "w_scale", torch.float32, 1, dev)
+    M, K = xq.shape
+    N, K2 = wq.shape
+    if K2 != K or x_scale.shape[0] != M or w_scale.shape[0] != N:
+        raise ValueError("shape mismatch between xq[M][K], x_scale[M], wq[N][K], w_scale[N]")
+    if want_bf16 or y_bf16 is not None:
+        y_bf16 = _out(y_bf16, (M, N), torch.bfloat16, dev, "y_bf16")
+    if want_f32 or y_f32 is not None:
+        y_f32 = _out(y_f32, (M, N), torch.float32, dev, "y_f32")
+    if want_acc or acc is not None:
+        acc = _out(acc, (M, N), torch.int32, dev, "acc")
+    need = linear_workspace_bytes(M, N, K)
+    ws = (workspace or _default_ws).get(need, dev)
+    check(lib().w8a8_linear(_ptr(xq), _ptr(x_scale), _ptr(wq), _ptr(w_scale), M, N, K,
+                            _ptr(y_bf16), _ptr(y_f32), _ptr(acc), _ptr(ws),
+                            0 if ws is None else ws.numel(), _stream(dev)))
+    return y_bf16, y_f32, acc
+
+
+def verify_accept_workspace_bytes(B: int, G: int, V: int) -> int:
+    return int(lib().w8a8_verify_accept_workspace_bytes(B, G, V))
+
+
+def verify_accept(logits, draft, *, want_argmax=True, argmax=None, accept_len=None,
+                  next_token=None, workspace: Workspace | None = None):
+    """Argmax of every row of fp32 ``logits[B*(G+1)][V]`` and greedy
+    acceptance of int32 ``draft[B][G]``.  Returns ``(argmax or None,
+    accept_len, next_token)``."""
+    _need(logits, "logits", torch.float32, 2)
+    dev = logits.device
+    _need(draft, "draft", torch.int32, 2, dev)
+    B, G = draft.shape
+    R, V = logits.shape
+    if R != B * (G + 1):
+        raise ValueError(f"logits must have B*(G+1) = {B * (G + 1)} rows (got {R})")
+    if want_argmax or argmax is not None:
+        argmax = _out(argmax, (R,), torch.int32, dev, "argmax")
+    accept_len = _out(accept_len, (B,), torch.int32, dev, "accept_len")
+    next_token = _out(next_token, (B,), torch.int32, dev, "next_token")
+    need = verify_accept_workspace_bytes(B, G, V)
+    ws = (workspace or _default_ws).get(need, dev)
+    check(lib().w8a8_verify_accept(_ptr(logits), V, _ptr(draft), B, G, _ptr(argmax),
+                                   _ptr(accept_len), _ptr(next_token), _ptr(ws),
+                                   0 if ws is None else ws.numel(), _stream(dev)))
+    return argmax, accept_len, next_token
+
+
+def bf16_linear(x, w, *, want_bf16=True, want_f32=False, y_bf16=None, y_f32=None):
+    """The bf16 reference linear ``x[M][K] @ w[N][K]^T`` (M <= 16), fp32
+    accumulation.  Returns ``(y_bf16, y_f32)``."""
+    _need(x, "x", torch.bfloat16, 2)
+    dev = x.device
+    _need(w, "w", torch.bfloat16, 2, dev)
+    M, K = x.shape
+    N, K2 = w.shape
+    if K2 != K:
+        raise ValueError("x and w must share K")
+    if want_bf16 or y_bf16 is not None:
+        y_bf16 = _out(y_bf16, (M, N), torch.bfloat16, dev, "y_bf16")
+    if want_f32 or y_f32 is not None:
+        y_f32 = _out(y_f32, (M, N), torch.float32, dev, "y_f32")
+    check(lib().w8a8_bf16_linear(_ptr(x), _ptr(w), M, N, K, _ptr(y_bf16), _ptr(y_f32),
+                                 _stream(dev)))
+    return y_bf16, y_f32

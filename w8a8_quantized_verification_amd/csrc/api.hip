@@ -1,0 +1,166 @@
+// C ABI of libw8a8.so: argument validation, workspace checks, error
+// reporting, and dispatch to the kernel launchers.  Declarations and the
+// contract of each call are in include/w8a8.h.
+#include "../../include/w8a8.h"
+
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "common.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+w8a8_status fail(w8a8_status s, const char* fn, const char* what) {
+  g_last_error = std::string(fn) + ": " + what;
+  return s;
+}
+
+w8a8_status hip_status(hipError_t e, const char* fn) {
+  if (e == hipSuccess) return W8A8_OK;
+  g_last_error = std::string(fn) + ": HIP error: " + hipGetErrorString(e);
+  return W8A8_ERR_HIP;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr int64_t kMaxRows = int64_t(1) << 30;    // token rows / output channels
+constexpr int64_t kMaxVocab = (int64_t(1) << 31) - 1;
+
+// Common checks on an [R][K] quantization problem.
+w8a8_status check_rows_k(const char* fn, int64_t R, int64_t K) {
+  if (R < 0 || R > kMaxRows) return fail(W8A8_ERR_INVALID_ARG, fn, "row count out of range");
+  if (K < 0 || K > W8A8_MAX_K) return fail(W8A8_ERR_INVALID_ARG, fn, "K out of range [0, 133144]");
+  if (K % 16 != 0) return fail(W8A8_ERR_INVALID_ARG, fn, "K must be a multiple of 16");
+  return W8A8_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t w8a8_abi_version(void) { return W8A8_ABI_VERSION; }
+
+const char* w8a8_status_string(w8a8_status s) {
+  switch (s) {
+    case W8A8_OK: return "ok";
+    case W8A8_ERR_INVALID_ARG: return "invalid argument";
+    case W8A8_ERR_UNSUPPORTED: return "unsupported";
+    case W8A8_ERR_WORKSPACE: return "workspace missing or too small";
+    case W8A8_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* w8a8_last_error(void) { return g_last_error.c_str(); }
+
+w8a8_status w8a8_quantize_act(const uint16_t* x_bf16, const float* smooth, int64_t M, int64_t K,
+                              int8_t* xq, float* x_scale, void* stream) {
+  static const char* fn = "w8a8_quantize_act";
+  g_last_error.clear();
+  if (w8a8_status s = check_rows_k(fn, M, K)) return s;
+  if (M == 0) return W8A8_OK;
+  if (!x_scale) return fail(W8A8_ERR_INVALID_ARG, fn, "x_scale is NULL");
+  if (K > 0 && (!x_bf16 || !xq)) return fail(W8A8_ERR_INVALID_ARG, fn, "x_bf16 or xq is NULL");
+  if (!aligned(x_bf16, 16) || !aligned(xq, 16) || !aligned(smooth, 16) || !aligned(x_scale, 4))
+    return fail(W8A8_ERR_INVALID_ARG, fn, "pointer misaligned (16 bytes for tensors, 4 for scales)");
+  return hip_status(w8a8_launch_quantize_rows(x_bf16, true, smooth, false, M, K, xq, x_scale,
+                                              reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
+w8a8_status w8a8_quantize_weight(const float* w, const float* smooth, int64_t N, int64_t K,
+                                 int8_t* wq, float* w_scale, void* stream) {
+  static const char* fn = "w8a8_quantize_weight";
+  g_last_error.clear();
+  if (w8a8_status s = check_rows_k(fn, N, K)) return s;
+  if (N == 0) return W8A8_OK;
+  if (!w_scale) return fail(W8A8_ERR_INVALID_ARG, fn, "w_scale is NULL");
+  if (K > 0 && (!w || !wq)) return fail(W8A8_ERR_INVALID_ARG, fn, "w or wq is NULL");
+  if (!aligned(w, 16) || !aligned(wq, 16) || !aligned(smooth, 16) || !aligned(w_scale, 4))
+    return fail(W8A8_ERR_INVALID_ARG, fn, "pointer misaligned (16 bytes for tensors, 4 for scales)");
+  return hip_status(w8a8_launch_quantize_rows(w, false, smooth, true, N, K, wq, w_scale,
+                                              reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
+size_t w8a8_linear_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || M > kMaxRows || N > kMaxRows || K < 0 || K > W8A8_MAX_K) return 0;
+  return w8a8_gemm_workspace_bytes(M, N, K);
+}
+
+w8a8_status w8a8_linear(const int8_t* xq, const float* x_scale, const int8_t* wq,
+                        const float* w_scale, int64_t M, int64_t N, int64_t K, uint16_t* y_bf16,
+                        float* y_f32, int32_t* acc, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  static const char* fn = "w8a8_linear";
+  g_last_error.clear();
+  if (w8a8_status s = check_rows_k(fn, M, K)) return s;
+  if (N < 0 || N > kMaxRows) return fail(W8A8_ERR_INVALID_ARG, fn, "N out of range");
+  if (M == 0 || N == 0) return W8A8_OK;
+  if (!y_bf16 && !y_f32 && !acc) return fail(W8A8_ERR_INVALID_ARG, fn, "all outputs are NULL");
+  if (!x_scale || !w_scale) return fail(W8A8_ERR_INVALID_ARG, fn, "x_scale or w_scale is NULL");
+  if (K > 0 && (!xq || !wq)) return fail(W8A8_ERR_INVALID_ARG, fn, "xq or wq is NULL");
+  if (!aligned(xq, 16) || !aligned(wq, 16))
+    return fail(W8A8_ERR_INVALID_ARG, fn, "xq and wq must be 16-byte aligned");
+  if (!aligned(x_scale, 4) || !aligned(w_scale, 4) || !aligned(y_bf16, 2) || !aligned(y_f32, 4) ||
+      !aligned(acc, 4))
+    return fail(W8A8_ERR_INVALID_ARG, fn, "scale or output pointer misaligned");
+  const size_t need = w8a8_gemm_workspace_bytes(M, N, K);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(W8A8_ERR_WORKSPACE, fn, "workspace NULL or smaller than w8a8_linear_workspace_bytes()");
+  if (need > 0 && !aligned(workspace, 256))
+    return fail(W8A8_ERR_INVALID_ARG, fn, "workspace must be 256-byte aligned");
+  return hip_status(w8a8_launch_gemm(xq, x_scale, wq, w_scale, M, N, K, y_bf16, y_f32, acc,
+                                     workspace, reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
+size_t w8a8_verify_accept_workspace_bytes(int64_t B, int64_t G, int64_t V) {
+  if (B <= 0 || G < 0 || G > W8A8_MAX_DRAFT || V <= 0 || V > kMaxVocab || B > kMaxRows) return 0;
+  return w8a8_argmax_workspace_bytes(B * (G + 1), V);
+}
+
+w8a8_status w8a8_verify_accept(const float* logits, int64_t V, const int32_t* draft, int64_t B,
+                               int64_t G, int32_t* argmax, int32_t* accept_len,
+                               int32_t* next_token, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  static const char* fn = "w8a8_verify_accept";
+  g_last_error.clear();
+  if (B < 0 || B > kMaxRows) return fail(W8A8_ERR_INVALID_ARG, fn, "B out of range");
+  if (G < 0 || G > W8A8_MAX_DRAFT) return fail(W8A8_ERR_INVALID_ARG, fn, "G out of range [0, 255]");
+  if (B == 0) return W8A8_OK;
+  if (V < 1 || V > kMaxVocab) return fail(W8A8_ERR_INVALID_ARG, fn, "V out of range [1, 2^31)");
+  if ((B * (G + 1)) * ((V + 4095) / 4096) > kMaxVocab)
+    return fail(W8A8_ERR_INVALID_ARG, fn, "too many logits rows for one launch");
+  if (!logits || !accept_len || !next_token || (G > 0 && !draft))
+    return fail(W8A8_ERR_INVALID_ARG, fn, "required pointer is NULL");
+  if (!aligned(logits, 4) || !aligned(draft, 4) || !aligned(argmax, 4) ||
+      !aligned(accept_len, 4) || !aligned(next_token, 4))
+    return fail(W8A8_ERR_INVALID_ARG, fn, "pointer misaligned (4 bytes)");
+  const size_t need = w8a8_argmax_workspace_bytes(B * (G + 1), V);
+  if (!workspace || workspace_bytes < need)
+    return fail(W8A8_ERR_WORKSPACE, fn, "workspace NULL or smaller than w8a8_verify_accept_workspace_bytes()");
+  if (!aligned(workspace, 256)) return fail(W8A8_ERR_INVALID_ARG, fn, "workspace must be 256-byte aligned");
+  return hip_status(w8a8_launch_verify_accept(logits, V, draft, B, G, argmax, accept_len,
+                                              next_token, workspace,
+                                              reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
+w8a8_status w8a8_bf16_linear(const uint16_t* x_bf16, const uint16_t* w_bf16, int64_t M, int64_t N,
+                             int64_t K, uint16_t* y_bf16, float* y_f32, void* stream) {
+  static const char* fn = "w8a8_bf16_linear";
+  g_last_error.clear();
+  if (M < 0 || N < 0 || N > kMaxRows) return fail(W8A8_ERR_INVALID_ARG, fn, "M or N out of range");
+  if (M > 16) return fail(W8A8_ERR_UNSUPPORTED, fn, "the bf16 reference handles M <= 16");
+  if (K < 0 || K > (int64_t(1) << 24) || K % 16 != 0)
+    return fail(W8A8_ERR_INVALID_ARG, fn, "K must be a multiple of 16 in [0, 2^24]");
+  if (M == 0 || N == 0) return W8A8_OK;
+  if (!y_bf16 && !y_f32) return fail(W8A8_ERR_INVALID_ARG, fn, "all outputs are NULL");
+  if (K > 0 && (!x_bf16 || !w_bf16)) return fail(W8A8_ERR_INVALID_ARG, fn, "x_bf16 or w_bf16 is NULL");
+  if (!aligned(x_bf16, 16) || !aligned(w_bf16, 16) || !aligned(y_bf16, 2) || !aligned(y_f32, 4))
+    return fail(W8A8_ERR_INVALID_ARG, fn, "pointer misaligned");
+  return hip_status(w8a8_launch_bf16_gemm(x_bf16, w_bf16, M, N, K, y_bf16, y_f32,
+                                          reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,69 @@
+// Internal helpers shared by the HIP kernels of libw8a8.so (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace w8a8 {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// fp32 -> bf16 bit pattern, round to nearest with ties to even; NaN stays a
+// quiet NaN with its sign.
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// Maximum over the 64 lanes of a wave (every lane receives it).
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
+// (value, index) maximum with the lowest index on equal values, over a wave.
+__device__ __forceinline__ void wave_argmax(float& v, int& idx) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    float ov = __shfl_xor(v, off, kWave);
+    int oi = __shfl_xor(idx, off, kWave);
+    if (ov > v || (ov == v && oi < idx)) { v = ov; idx = oi; }
+  }
+}
+
+}  // namespace w8a8
+
+// ---------------------------------------------------------------------------
+// Launchers (host functions defined next to their kernels).  Arguments are
+// validated by the C-ABI layer before these are called.  Each returns
+// hipSuccess or the launch error.
+// ---------------------------------------------------------------------------
+hipError_t w8a8_launch_quantize_rows(const void* in, bool in_is_bf16, const float* smooth,
+                                     bool smooth_divides, int64_t R, int64_t K,
+                                     int8_t* q, float* scale, hipStream_t stream);
+
+size_t w8a8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t w8a8_launch_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq,
+                            const float* w_scale, int64_t M, int64_t N, int64_t K,
+                            uint16_t* y_bf16, float* y_f32, int32_t* acc,
+                            void* workspace, hipStream_t stream);
+
+size_t w8a8_argmax_workspace_bytes(int64_t R, int64_t V);
+hipError_t w8a8_launch_verify_accept(const float* logits, int64_t V, const int32_t* draft,
+                                     int64_t B, int64_t G, int32_t* argmax,
+                                     int32_t* accept_len, int32_t* next_token,
+                                     void* workspace, hipStream_t stream);
+
+hipError_t w8a8_launch_bf16_gemm(const uint16_t* x, const uint16_t* w, int64_t M, int64_t N,
+                                 int64_t K, uint16_t* y_bf16, float* y_f32, hipStream_t stream);
