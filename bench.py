@@ -2,20 +2,21 @@
 """Benchmark of the W8A8 verify hot path on one MI355X.
 
 Headline workload: LM-head verification at M = 5 (4 drafts + 1) — hidden
-4096, vocabulary 151936 (Qwen3-8B shapes), int8 per-channel weights, one
-verify step = quantize_act -> w8a8_linear (fp32 logits) -> verify_accept
-(argmax over the vocabulary + greedy acceptance of the 4 drafts).  It is the
-only M = 5 workload that runs every step of the path.  Two copies of the
-622 MB int8 LM head alternate between steps so that no step finds its
-weights in the 256 MB Infinity Cache.
+4096, vocabulary 151936 (Qwen3-8B shapes), int8 per-output-channel weights
+in the tiled layout, one verify step = quantize_act -> w8a8_linear (fp32
+logits) -> verify_accept (argmax over the vocabulary + greedy acceptance of
+the 4 drafts).  It is the M = 5 workload that runs every step of the path.
+Two copies of the 622 MB int8 LM head alternate between steps so that no
+step finds its weights in the 256 MB Infinity Cache.
 
-Printed: one JSON line with verified tokens/s (value), the roofline of the
-dominant kernel (the LM-head GEMM: algorithmic bytes per launch over its
-HIP-event-timed average duration, against 8 TB/s), the CPU oracle timed on
-this host on a bounded sample, and secondary figures (per-linear GB/s of
-the Qwen3-8B decoder-layer linears at M = 5 with weights rotated past the
-cache, the in-build bf16 GEMM at the LM-head shape as the two-times-traffic
-reference).
+Printed: one JSON line with verified tokens/s (value; eager launches, K
+timed steps between synchronizations), the roofline of the dominant kernel
+(the LM-head GEMM: algorithmic bytes per launch over its HIP-event-timed
+average duration, against 8 TB/s), the CPU oracle timed on this host on a
+bounded sample, and secondary figures: the same step replayed as a HIP
+graph, the Qwen3-8B decoder-layer linears at M = 5 (graph-replayed, weights
+rotated past the cache), the row-major weight layout, and the in-build bf16
+GEMM at the LM-head shape as the two-times-traffic reference.
 
     python bench.py [--steps 200] [--warmup 20] [--no-cpu-baseline] [--no-extra]
     python bench.py --pmc-probe     # a short fixed run for rocprofv3 --pmc
@@ -43,15 +44,16 @@ def parse_args():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-steps", type=int, default=3)
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--no-extra", action="store_true")
     p.add_argument("--pmc-probe", action="store_true")
     return p.parse_args()
 
 
-def lm_head_bytes(M, N, K):
-    # int8 weight + fp32 scales + int8 activations + fp32 per-token scales + fp32 logits
-    return N * K + 4 * N + M * K + 4 * M + 4 * M * N
+def lm_head_bytes(M, N, K, logits=True):
+    # int8 weight + fp32 scales + int8 activations + fp32 per-token scales
+    # (+ fp32 logits when written)
+    return N * K + 4 * N + M * K + 4 * M + (4 * M * N if logits else 0)
 
 
 def linear_bytes(M, N, K):
@@ -83,17 +85,47 @@ def read_traffic():
         return None
 
 
-def make_int8_weight(N, K, seed, device):
+def make_weight(N, K, seed, device, tiled=True, with_bf16=False):
+    """Random-init N(0, 0.02) fp32 weight drawn on the device, quantized to
+    int8 per output channel by the library."""
     import torch
     import w8a8_quantized_verification_amd as w8
     g = torch.Generator(device=device)
     g.manual_seed(seed)
     w = torch.randn(N, K, generator=g, device=device, dtype=torch.float32)
     w.mul_(0.02)
-    wq, ws = w8.quantize_weight(w)
-    wb = w.to(torch.bfloat16)
+    wq, ws = w8.quantize_weight(w, tiled=tiled)
+    wb = w.to(torch.bfloat16) if with_bf16 else None
     del w
     return wq, ws, wb
+
+
+def graph_time(fns, replays=20):
+    """Capture the callables into one HIP graph; return the mean replay time
+    in seconds (one replay runs every callable once, in order)."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for f in fns:
+            f()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for f in fns:
+            f()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / replays / 1e3
 
 
 def main():
@@ -117,7 +149,7 @@ def main():
     torch.cuda.set_device(dev)
 
     M, K, V, G, B = 5, 4096, synth.QWEN3_VOCAB, 4, 1
-    copies = [make_int8_weight(V, K, 1000 + i, dev) for i in range(2)]
+    copies = [make_weight(V, K, 1000 + i, dev, tiled=True) for i in range(2)]
     n_x = 8
     xs_host = [synth.activations_bf16(synth.W_LM_HEAD, M, K, index=i) for i in range(n_x)]
     x_dev = [torch.from_numpy(x.view(np.int16).copy()).view(torch.bfloat16).to(dev) for x in xs_host]
@@ -131,13 +163,23 @@ def main():
     wsp = w8.Workspace()
 
     def step(i, ev=None):
+        """One verify step: quantize the 5 hidden rows, then the LM-head
+        linear with the argmax's first pass fused into its epilogue, then
+        greedy acceptance (the logits themselves are not written)."""
         w8.quantize_act(x_dev[i % n_x], xq=xq, x_scale=xsc)
         wq, ws, _ = copies[i % 2]
         if ev is not None:
             ev[0].record()
-        w8.linear(xq, xsc, wq, ws, want_bf16=False, y_f32=logits, workspace=wsp)
+        w8.lm_head_argmax(xq, xsc, wq, ws, workspace=wsp)
         if ev is not None:
             ev[1].record()
+        w8.accept_from_keys(draft, argmax=am, accept_len=al, next_token=nt, workspace=wsp)
+
+    def step_separate(i):
+        """The same step through the three separate calls, fp32 logits written."""
+        w8.quantize_act(x_dev[i % n_x], xq=xq, x_scale=xsc)
+        wq, ws, _ = copies[i % 2]
+        w8.linear(xq, xsc, wq, ws, want_bf16=False, y_f32=logits, workspace=wsp)
         w8.verify_accept(logits, draft, argmax=am, accept_len=al, next_token=nt, workspace=wsp)
 
     if args.pmc_probe:
@@ -150,7 +192,8 @@ def main():
             step(i)
         torch.cuda.synchronize()
         print(json.dumps({"pmc_probe": "done", "copy_bytes": 1 << 30,
-                          "gemm_algorithmic_bytes": lm_head_bytes(M, V, K)}), flush=True)
+                          "gemm_algorithmic_bytes": lm_head_bytes(M, V, K, logits=False)
+                          + 8 * M * ((V + 31) // 32)}), flush=True)
         return
 
     for i in range(args.warmup):
@@ -173,7 +216,10 @@ def main():
     gemm_avg_s = float(np.mean(gemm_ms)) / 1e3
     ms_per_step = total_ms / args.steps
     tok_s = M * args.steps / (total_ms / 1e3)
-    bytes_launch = lm_head_bytes(M, V, K)
+    # the fused kernel reads the weights, scales and activations; its only
+    # writes are the atomic folds of the row maxima (8 bytes per row per
+    # 32-channel workgroup)
+    bytes_launch = lm_head_bytes(M, V, K, logits=False) + 8 * M * ((V + 31) // 32)
     achieved = bytes_launch / gemm_avg_s / 1e9
     traffic = read_traffic()
 
@@ -189,14 +235,18 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "int8",
-        "data": "synthetic (seeded N(0,1) bf16 activations, N(0,0.02) weights quantized to int8 on the GPU)",
+        "data": "synthetic (seeded N(0,1) bf16 activations; N(0,0.02) weights drawn on the GPU, "
+                "quantized to int8 by the library)",
         "config": {"workload": "lm_head_verify_m5", "M": M, "K": K, "V": V, "B": B, "G": G,
-                   "weights": "int8 per-output-channel, 2 rotating copies of 622 MB",
-                   "step": "quantize_act + w8a8_linear(fp32 logits) + verify_accept"},
+                   "weights": "int8 per-output-channel, tiled layout, 2 rotating copies of 622 MB",
+                   "step": "quantize_act + lm_head_argmax (LM-head W8A8 linear with the "
+                           "argmax folded into its epilogue) + accept_from_keys (greedy "
+                           "acceptance)",
+                   "launch": "eager, one stream"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": "gemm_w8a8_skinny (LM head)",
+                     "kernel": "gemm_w8a8_skinny<2,4,8,tiled,argmax> (LM head 4096->151936, M=5)",
                      "algorithmic_bytes_per_launch": bytes_launch,
                      "avg_launch_us": round(gemm_avg_s * 1e6, 3)},
         "gemm_gbs": round(achieved, 1),
@@ -205,17 +255,27 @@ def main():
     }
 
     if not args.no_extra:
-        out["extra"] = extra_measurements(dev, copies, x_dev, xq, xsc, wsp)
+        extra = {}
+        # the whole step as one HIP graph (two steps per graph: both weight copies)
+        t_graph = graph_time([lambda: step(0), lambda: step(1)], replays=50) / 2
+        extra["graph_step"] = {"ms_per_step": round(t_graph * 1e3, 5),
+                               "verified_tokens_per_s": round(M / t_graph, 1)}
+        t_sep = graph_time([lambda: step_separate(0), lambda: step_separate(1)], replays=50) / 2
+        extra["graph_step_separate_calls"] = {"ms_per_step": round(t_sep * 1e3, 5),
+                                              "verified_tokens_per_s": round(M / t_sep, 1)}
+        extra.update(extra_measurements(dev, copies, x_dev, xq, xsc, wsp))
+        out["extra"] = extra
 
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(copies[0], xs_host, synth.draft_ids(synth.W_LM_HEAD, B, G, V),
-                                           args.cpu_steps, M)
+        out["cpu_baseline"] = cpu_baseline(dev, xs_host, synth.draft_ids(synth.W_LM_HEAD, B, G, V),
+                                           args.cpu_seconds, M)
     print(json.dumps(out), flush=True)
 
 
 def extra_measurements(dev, copies, x_dev, xq, xsc, wsp):
     """Secondary figures: Qwen3-8B decoder-layer linears at M=5 (8 rotating
-    copies of the layer), and the bf16 reference GEMM at the LM-head shape."""
+    copies of each weight, graph-replayed), the row-major layout and the
+    bf16 reference GEMM at the LM-head shape."""
     import numpy as np
     import torch
 
@@ -224,82 +284,85 @@ def extra_measurements(dev, copies, x_dev, xq, xsc, wsp):
 
     M = 5
     res = {}
-    reps = 40
     nc = 8
     layer = []
     for li, lin in enumerate(synth.QWEN3_8B_LAYER):
-        ws_list = [make_int8_weight(lin.N, lin.K, 2000 + 10 * li + c, dev)[:2] for c in range(nc)]
+        wl = [make_weight(lin.N, lin.K, 2000 + 10 * li + c, dev)[:2] for c in range(nc)]
         x = torch.from_numpy(synth.activations_bf16(synth.W_LAYER_M5, M, lin.K, outliers=True)
                              .view(np.int16).copy()).view(torch.bfloat16).to(dev)
         lxq, lxs = w8.quantize_act(x)
         y = torch.empty(M, lin.N, dtype=torch.bfloat16, device=dev)
-        for i in range(nc):
-            w8.linear(lxq, lxs, *ws_list[i % nc], y_bf16=y, workspace=wsp)
+        fns = [(lambda c=c: w8.linear(lxq, lxs, *wl[c], y_bf16=y, workspace=wsp)) for c in range(nc)]
+        t = graph_time(fns, replays=20) / nc
+        b = linear_bytes(M, lin.N, lin.K)
+        layer.append({"name": lin.name, "N": lin.N, "K": lin.K, "us": round(t * 1e6, 2),
+                      "GBs": round(b / t / 1e9, 1)})
+        del wl
+    tot_b = sum(linear_bytes(M, l.N, l.K) for l in synth.QWEN3_8B_LAYER)
+    tot_t = sum(e["us"] for e in layer) / 1e6
+    res["qwen3_8b_layer_linears_m5"] = {"per_linear": layer, "sum_us": round(tot_t * 1e6, 2),
+                                        "aggregate_GBs": round(tot_b / tot_t / 1e9, 1),
+                                        "aggregate_frac": round(tot_b / tot_t / 1e9 / HBM_PEAK_GBS, 4),
+                                        "timing": "HIP graph of 8 launches over 8 weight copies"}
+
+    K, V = 4096, synth.QWEN3_VOCAB
+    lg = torch.empty(M, V, dtype=torch.float32, device=dev)
+
+    def ev_time(fn, reps=20):
+        for i in range(4):
+            fn(i)
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(reps)]
         torch.cuda.synchronize()
         for i in range(reps):
             ev[i][0].record()
-            w8.linear(lxq, lxs, *ws_list[i % nc], y_bf16=y, workspace=wsp)
+            fn(i)
             ev[i][1].record()
         torch.cuda.synchronize()
-        t = float(np.median([a.elapsed_time(b) for a, b in ev])) / 1e3
-        b = linear_bytes(M, lin.N, lin.K)
-        layer.append({"name": lin.name, "N": lin.N, "K": lin.K, "us": round(t * 1e6, 2),
-                      "GBs": round(b / t / 1e9, 1)})
-        del ws_list
-    tot_b = sum(linear_bytes(M, l.N, l.K) for l in synth.QWEN3_8B_LAYER)
-    tot_t = sum(e["us"] for e in layer) / 1e6
-    res["qwen3_8b_layer_linears_m5"] = {"per_linear": layer, "sum_us": round(tot_t * 1e6, 2),
-                                        "aggregate_GBs": round(tot_b / tot_t / 1e9, 1),
-                                        "aggregate_frac": round(tot_b / tot_t / 1e9 / HBM_PEAK_GBS, 4)}
+        return float(np.mean([a.elapsed_time(b) for a, b in ev])) / 1e3
+
+    # row-major weight layout at the LM-head shape
+    rm = [make_weight(V, K, 1000 + i, dev, tiled=False, with_bf16=True) for i in range(2)]
+    t_rm = ev_time(lambda i: w8.linear(xq, xsc, rm[i % 2][0], rm[i % 2][1], want_bf16=False,
+                                       y_f32=lg, workspace=wsp))
+    t_tl = ev_time(lambda i: w8.linear(xq, xsc, copies[i % 2][0], copies[i % 2][1],
+                                       want_bf16=False, y_f32=lg, workspace=wsp))
+    b = lm_head_bytes(M, V, K)
+    res["lm_head_layouts_m5"] = {"tiled_us": round(t_tl * 1e6, 2),
+                                 "tiled_GBs": round(b / t_tl / 1e9, 1),
+                                 "row_major_us": round(t_rm * 1e6, 2),
+                                 "row_major_GBs": round(b / t_rm / 1e9, 1)}
     # bf16 reference at the LM-head shape (two-times weight traffic)
-    K, V = 4096, synth.QWEN3_VOCAB
-    xb = x_dev[0]
-    yf = torch.empty(M, V, dtype=torch.float32, device=dev)
-    for i in range(4):
-        w8.bf16_linear(xb, copies[i % 2][2], want_bf16=False, y_f32=yf)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
-    torch.cuda.synchronize()
-    for i in range(20):
-        ev[i][0].record()
-        w8.bf16_linear(xb, copies[i % 2][2], want_bf16=False, y_f32=yf)
-        ev[i][1].record()
-    torch.cuda.synchronize()
-    tb = float(np.mean([a.elapsed_time(b) for a, b in ev])) / 1e3
+    t_bf = ev_time(lambda i: w8.bf16_linear(x_dev[0], rm[i % 2][2], want_bf16=False, y_f32=lg))
     bb = 2 * V * K + 2 * M * K + 4 * M * V
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
-    lg = torch.empty(M, V, dtype=torch.float32, device=dev)
-    for i in range(20):
-        ev[i][0].record()
-        w8.linear(xq, xsc, copies[i % 2][0], copies[i % 2][1], want_bf16=False, y_f32=lg, workspace=wsp)
-        ev[i][1].record()
-    torch.cuda.synchronize()
-    ti = float(np.mean([a.elapsed_time(b) for a, b in ev])) / 1e3
-    res["bf16_reference_lm_head_m5"] = {"us": round(tb * 1e6, 2), "GBs": round(bb / tb / 1e9, 1),
-                                        "w8a8_us": round(ti * 1e6, 2),
-                                        "time_ratio_bf16_over_w8a8": round(tb / ti, 3)}
+    res["bf16_reference_lm_head_m5"] = {"us": round(t_bf * 1e6, 2), "GBs": round(bb / t_bf / 1e9, 1),
+                                        "w8a8_tiled_us": round(t_tl * 1e6, 2),
+                                        "time_ratio_bf16_over_w8a8": round(t_bf / t_tl, 3)}
+    del rm
     return res
 
 
-def cpu_baseline(copy0, xs_host, draft, steps, M):
+def cpu_baseline(dev, xs_host, draft, seconds, M):
     """The oracle's verify step on this host's cores, on a bounded sample:
-    ``steps`` LM-head steps with the same int8 weights (copied to the host)."""
-    import numpy as np
-
+    whole LM-head steps (M=5, K=4096, V=151936) until ``seconds`` have
+    passed (at least 2, at most 100), with int8 weights made by the library
+    (row-major) and copied to the host."""
     import oracle
-    wq = copy0[0].cpu().numpy()
-    ws = copy0[1].cpu().numpy()
+    wq, ws, _ = make_weight(151936, 4096, 1000, dev, tiled=False)
+    wq = wq.cpu().numpy()
+    ws = ws.cpu().numpy()
     try:
         from threadpoolctl import threadpool_info
         blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         blas = os.cpu_count() or 1
     t0 = time.perf_counter()
-    for i in range(steps):
-        xq, xs = oracle.quantize_act(xs_host[i % len(xs_host)])
+    steps = 0
+    while steps < 100 and (steps < 2 or time.perf_counter() - t0 < seconds):
+        xq, xs = oracle.quantize_act(xs_host[steps % len(xs_host)])
         _, y32, _ = oracle.w8a8_linear(xq, xs, wq, ws)
         oracle.verify_accept(y32, draft)
+        steps += 1
     dt = time.perf_counter() - t0
     return {"value": round(M * steps / dt, 3), "unit": "verified tokens/s", "cores": int(blas),
             "kind": "oracle",

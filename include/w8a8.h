@@ -119,6 +119,33 @@ w8a8_status w8a8_quantize_weight(const float* w, const float* smooth,
                                  int8_t* wq, float* w_scale, void* stream);
 
 /*
+ * Tiled weight layout (the layout the W8A8 linear streams fastest).
+ *
+ * The INT8 weights live in device memory for the life of the verifier
+ * ([ja] §2.2 item 2), so their layout is chosen for the kernel: for each
+ * tile of 16 output channels and each 64-wide k step, the 1 KiB that one
+ * int8 MFMA consumes is stored contiguously in lane order.  With
+ * steps = ceil(K/64), element (n, k) of the row-major [N][K] matrix is at
+ * byte
+ *   ((n/16 * steps + k/64) * 64 + (n%16 + 16*((k%64)/16))) * 16 + k%16
+ * and every other byte (rows n >= N of the last tile, k >= K) is zero.
+ * Size: w8a8_tiled_weight_bytes(N, K) = ceil(N/16)*16 * ceil(K/64)*64.
+ *
+ * w8a8_quantize_weight_tiled: same arithmetic and arguments as
+ *   w8a8_quantize_weight, writing the codes in the tiled layout (wq_tiled,
+ *   16-byte aligned, w8a8_tiled_weight_bytes(N, K) bytes, every byte
+ *   written).
+ * w8a8_tile_weight: rearranges row-major int8 wq [N][K] into the tiled
+ *   layout (no arithmetic).  Requires K % 16 == 0, 16-byte aligned pointers.
+ */
+size_t      w8a8_tiled_weight_bytes(int64_t N, int64_t K);
+w8a8_status w8a8_quantize_weight_tiled(const float* w, const float* smooth,
+                                       int64_t N, int64_t K,
+                                       int8_t* wq_tiled, float* w_scale, void* stream);
+w8a8_status w8a8_tile_weight(const int8_t* wq, int64_t N, int64_t K,
+                             int8_t* wq_tiled, void* stream);
+
+/*
  * One W8A8 linear: INT8 x INT8 product with INT32 accumulation, then the
  * dequant epilogue.
  *
@@ -154,6 +181,17 @@ w8a8_status w8a8_linear(const int8_t* xq, const float* x_scale,
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * w8a8_linear_tiled: w8a8_linear with the weights in the tiled layout
+ * (wq_tiled from w8a8_quantize_weight_tiled or w8a8_tile_weight for the
+ * same N and K).  Same results bit for bit; same workspace rule.
+ */
+w8a8_status w8a8_linear_tiled(const int8_t* xq, const float* x_scale,
+                              const int8_t* wq_tiled, const float* w_scale,
+                              int64_t M, int64_t N, int64_t K,
+                              uint16_t* y_bf16, float* y_f32, int32_t* acc,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * LM-head argmax and greedy acceptance of a draft block.
  *
  * Pages: the target verifies the drafted block in one pass and the
@@ -169,7 +207,7 @@ w8a8_status w8a8_linear(const int8_t* xq, const float* x_scale,
  * (tokens emitted by the step: accept_len + 1).  Draft ids outside [0, V)
  * never match.
  *
- * logits     [B*(G+1)][V] fp32, 16-byte aligned.
+ * logits     [B*(G+1)][V] fp32, 4-byte aligned.
  * draft      [B][G] int32 (may be NULL when G == 0).
  * argmax     [B*(G+1)] int32 output, or NULL.
  * accept_len [B] int32 output;  next_token [B] int32 output.
@@ -184,6 +222,49 @@ w8a8_status w8a8_verify_accept(const float* logits, int64_t V,
                                int32_t* next_token,
                                void* workspace, size_t workspace_bytes,
                                void* stream);
+
+/*
+ * The LM-head verification in two kernels: the LM-head W8A8 linear (tiled
+ * weights) whose epilogue also folds each row's maximum (value, lowest
+ * index) into 64-bit keys (64 per row) with device-scope atomic max, then a
+ * tiny acceptance kernel that reads, combines and resets the keys.  Same results, bit
+ * for bit, as w8a8_linear_tiled(..., y_f32 = logits) followed by
+ * w8a8_verify_accept; it saves the separate pass over the logits (and their
+ * write, when logits == NULL).
+ * xq [B*(G+1)][K], x_scale [B*(G+1)]: the quantized hidden states of the
+ *    verified rows (row b*(G+1)+i as in w8a8_verify_accept).
+ * wq_tiled / w_scale: the LM head [V][K] in the tiled layout and its scales.
+ * logits [B*(G+1)][V] fp32 output, or NULL; argmax [B*(G+1)] output or NULL;
+ * accept_len, next_token [B] outputs.  draft [B][G].
+ * workspace: w8a8_lm_head_verify_workspace_bytes(B, G, V, K) bytes (16 KiB
+ *    per verified row), 256-byte aligned.  It must be zero-filled before its
+ *    first use; every completed call leaves it zero-filled again.  Calls that
+ *    share a workspace must not overlap in time.
+ * Requires 0 <= G <= W8A8_MAX_DRAFT, 1 <= V <= 2^30, K as for w8a8_linear.
+ */
+size_t      w8a8_lm_head_verify_workspace_bytes(int64_t B, int64_t G, int64_t V, int64_t K);
+
+/* The two phases of w8a8_lm_head_verify, for callers that schedule (or time)
+ * them apart.  w8a8_lm_head_argmax runs the LM-head linear for M = B*(G+1)
+ * rows and folds the row maxima into the workspace keys; a following
+ * w8a8_accept_from_keys on the same stream and workspace reads and resets
+ * the keys and accepts the drafts.  Arguments as for w8a8_lm_head_verify. */
+w8a8_status w8a8_lm_head_argmax(const int8_t* xq, const float* x_scale,
+                                const int8_t* wq_tiled, const float* w_scale,
+                                int64_t M, int64_t V, int64_t K, float* logits,
+                                void* workspace, size_t workspace_bytes, void* stream);
+w8a8_status w8a8_accept_from_keys(void* workspace, size_t workspace_bytes,
+                                  const int32_t* draft, int64_t B, int64_t G,
+                                  int32_t* argmax, int32_t* accept_len,
+                                  int32_t* next_token, void* stream);
+
+w8a8_status w8a8_lm_head_verify(const int8_t* xq, const float* x_scale,
+                                const int8_t* wq_tiled, const float* w_scale,
+                                int64_t V, int64_t K,
+                                const int32_t* draft, int64_t B, int64_t G,
+                                float* logits, int32_t* argmax,
+                                int32_t* accept_len, int32_t* next_token,
+                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * The BF16 verifier's linear at the same shapes, as the weight-traffic

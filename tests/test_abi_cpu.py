@@ -76,14 +76,23 @@ def test_linear_validation(lib):
 
 
 def test_linear_workspace(lib):
-    # small-N shapes split K across workgroups and need scratch; the LM head does not
-    need = lib.w8a8_linear_workspace_bytes(5, 1024, 4096)
-    assert need >= 5 * 1024 * 4
+    # an output of one 16-channel tile splits K across workgroups and needs
+    # scratch; the LM head and the layer shapes do not
+    need = lib.w8a8_linear_workspace_bytes(5, 16, 25600)
+    assert need >= 5 * 16 * 4
     assert lib.w8a8_linear_workspace_bytes(5, 151936, 4096) == 0
-    assert lib.w8a8_linear_workspace_bytes(0, 1024, 4096) == 0
-    assert lin(lib, N=1024, work=None) == WORKSPACE
-    assert lin(lib, N=1024, work=A16, wbytes=need - 1) == WORKSPACE
-    assert lin(lib, N=1024, work=A16 + 16, wbytes=need) == INVALID  # workspace alignment
+    assert lib.w8a8_linear_workspace_bytes(5, 1024, 4096) == 0
+    assert lib.w8a8_linear_workspace_bytes(0, 16, 25600) == 0
+    assert lin(lib, N=16, K=25600, work=None) == WORKSPACE
+    assert lin(lib, N=16, K=25600, work=A16, wbytes=need - 1) == WORKSPACE
+    assert lin(lib, N=16, K=25600, work=A16 + 16, wbytes=need) == INVALID  # alignment
+
+
+def test_linear_workspace_follows_split_override(lib, monkeypatch):
+    monkeypatch.setenv("W8A8_SPLITK", "4")
+    assert lib.w8a8_linear_workspace_bytes(5, 1024, 4096) >= 5 * 1024 * 4
+    monkeypatch.delenv("W8A8_SPLITK")
+    assert lib.w8a8_linear_workspace_bytes(5, 1024, 4096) == 0
 
 
 def va(lib, logits=A16, V=151936, draft=A16, B=1, G=4, am=None, al=A16, nt=A16b, work=A16,

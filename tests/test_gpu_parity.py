@@ -107,14 +107,24 @@ def test_quantize_weight(N, K, smooth):
 # w8a8_linear
 # --------------------------------------------------------------------------
 
-def run_linear_case(M, N, K, seed, outliers=True):
+def untile(t: np.ndarray, N: int, K: int) -> np.ndarray:
+    """Row-major [N][K] view of a tiled weight buffer [N/16][K/64][64][16]:
+    lane l of (tile, step) holds channel 16*tile + l%16 and k = 64*step +
+    16*(l//16) .. +15 (the layout stated in include/w8a8.h)."""
+    tiles, steps = t.shape[0], t.shape[1]
+    a = t.reshape(tiles, steps, 4, 16, 16)          # tile, step, k-group, channel, byte
+    a = a.transpose(0, 3, 1, 2, 4)                  # tile, channel, step, k-group, byte
+    return a.reshape(tiles * 16, steps * 64)[:N, :K]
+
+
+def run_linear_case(M, N, K, seed, outliers=True, tiled=False):
     bits = synth.activations_bf16(seed, M, K, outliers=outliers and K > 0)
     w = synth.weights_f32(seed, N, K)
     xq_ref, xs_ref = oracle.quantize_act(bits)
     wq_ref, ws_ref = oracle.quantize_weight(w)
     acc_ref, y32_ref, y_ref = oracle.w8a8_linear(xq_ref, xs_ref, wq_ref, ws_ref)
     xq, xs = w8.quantize_act(dev_bf16(bits))
-    wq, ws = w8.quantize_weight(dev(w))
+    wq, ws = w8.quantize_weight(dev(w), tiled=tiled)
     yb, yf, acc = w8.linear(xq, xs, wq, ws, want_bf16=True, want_f32=True, want_acc=True)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(host(acc), acc_ref)
@@ -142,18 +152,69 @@ LINEAR_CASES = [
 ]
 
 
+@pytest.mark.parametrize("tiled", [False, True])
 @pytest.mark.parametrize("M,N,K", LINEAR_CASES)
-def test_linear(M, N, K):
-    announce(f"linear M={M} N={N} K={K}")
-    run_linear_case(M, N, K, seed=200 + M + N % 97 + K % 89)
+def test_linear(M, N, K, tiled):
+    announce(f"linear M={M} N={N} K={K} tiled={tiled}")
+    run_linear_case(M, N, K, seed=200 + M + N % 97 + K % 89, tiled=tiled)
 
 
-def test_linear_outputs_subsets_and_workspace_reuse():
+@pytest.mark.parametrize("N,K", [(512, 256), (1000, 4096), (17, 25600), (33, 80), (5, 16)])
+@pytest.mark.parametrize("smooth", [False, True])
+def test_quantize_weight_tiled(N, K, smooth):
+    """Tiled codes equal the oracle's row-major codes after un-tiling, every
+    padding byte is zero, and tiling the row-major codes gives the same bytes."""
+    announce(f"quantize_weight tiled N={N} K={K} smooth={smooth}")
+    w = synth.weights_f32(104, N, K)
+    s = synth.smoothing_vector(104, K) if smooth else None
+    sd = None if s is None else dev(s)
+    wt, ws = w8.quantize_weight(dev(w), sd, tiled=True)
+    wr, _ = w8.quantize_weight(dev(w), sd)
+    wt2 = w8.tile_weight(wr)
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.quantize_weight(w, smooth=s)
+    t = host(wt)
+    assert t.shape == w8.tiled_shape(N, K)
+    np.testing.assert_array_equal(untile(t, N, K), q_ref)
+    np.testing.assert_array_equal(host(ws).view(np.uint32), s_ref.view(np.uint32))
+    full = untile(t, t.shape[0] * 16, t.shape[1] * 64)
+    pad = np.ones(full.shape, dtype=bool)
+    pad[:N, :K] = False
+    assert np.all(full[pad] == 0)
+    np.testing.assert_array_equal(host(wt2), t)
+
+
+@pytest.fixture
+def forced_split(monkeypatch):
+    """Force the cross-workgroup split-K path (a tuning override that must
+    not change any result)."""
+    monkeypatch.setenv("W8A8_SPLITK", "8")
+    monkeypatch.setenv("W8A8_WAVES", "4")
+    yield
+
+
+@pytest.mark.parametrize("M,N,K", [(5, 1024, 4096), (8, 1000, 5120), (16, 17, 25600), (33, 96, 2048)])
+@pytest.mark.parametrize("tiled", [False, True])
+def test_linear_forced_split_k(M, N, K, tiled, forced_split):
+    announce(f"linear forced split-K M={M} N={N} K={K} tiled={tiled}")
+    assert w8.linear_workspace_bytes(M, N, K) > 0
+    run_linear_case(M, N, K, seed=310 + N % 13, tiled=tiled)
+
+
+def test_linear_narrow_output_splits_by_default():
+    """An output of a single 16-channel tile with a long K takes the split-K
+    path without any override."""
+    announce("linear narrow output default split")
+    assert w8.linear_workspace_bytes(5, 16, 25600) > 0
+    run_linear_case(5, 16, 25600, seed=320, tiled=True)
+
+
+def test_linear_outputs_subsets_and_workspace_reuse(forced_split):
     """Each output alone matches; repeated split-K calls on one workspace stay
     exact (the workspace is left zero-filled after every call)."""
     announce("linear output subsets + split-K workspace reuse")
     M, N, K = 5, 1024, 4096
-    xq, xs, wq, ws = run_linear_case(M, N, K, seed=301)
+    xq, xs, wq, ws = run_linear_case(M, N, K, seed=301, tiled=True)
     assert w8.linear_workspace_bytes(M, N, K) > 0
     ref_b, ref_f, ref_a = (host(t) for t in w8.linear(xq, xs, wq, ws, want_bf16=True,
                                                          want_f32=True, want_acc=True))
@@ -187,7 +248,7 @@ def test_linear_batched_m288_sampled():
     """Batched verification, M = 32 x (8+1) = 288 on the q shape: the full
     int32 result against the oracle."""
     announce("linear M=288 q shape")
-    run_linear_case(288, 4096, 4096, seed=302)
+    run_linear_case(288, 4096, 4096, seed=302, tiled=True)
 
 
 # --------------------------------------------------------------------------
@@ -285,3 +346,133 @@ def test_tiny_verify_step_end_to_end():
     np.testing.assert_array_equal(host(am), am_r)
     np.testing.assert_array_equal(host(al), al_r)
     np.testing.assert_array_equal(host(nt), nt_r)
+
+
+# --------------------------------------------------------------------------
+# the step captured in a HIP graph (the benchmark replays it this way)
+# --------------------------------------------------------------------------
+
+def test_graph_replay_matches_eager(forced_split):
+    """A verify step (quantize_act, a split-K linear, the LM-head-style linear
+    and verify_accept) captured once in a HIP graph: every replay, with eager
+    work and synchronizations between replays, equals the eager result."""
+    announce("graph replay of a verify step")
+    M, K, Nmid, V, G = 5, 4096, 1024, 4099, 4
+    bits = synth.activations_bf16(600, M, K)
+    w1 = synth.weights_f32(600, Nmid, K)
+    w2 = synth.weights_f32(601, V, K)
+    x = dev_bf16(bits)
+    wq1, ws1 = w8.quantize_weight(dev(w1), tiled=True)
+    wq2, ws2 = w8.quantize_weight(dev(w2), tiled=True)
+    draft = dev(synth.draft_ids(600, 1, G, V))
+    assert w8.linear_workspace_bytes(M, Nmid, K) > 0  # the split-K path is in the graph
+    ws = w8.Workspace()
+    xq = torch.empty(M, K, dtype=torch.int8, device="cuda:0")
+    xs = torch.empty(M, dtype=torch.float32, device="cuda:0")
+    mid = torch.empty(M, Nmid, dtype=torch.int32, device="cuda:0")
+    lg = torch.empty(M, V, dtype=torch.float32, device="cuda:0")
+    am = torch.empty(M, dtype=torch.int32, device="cuda:0")
+    al = torch.empty(1, dtype=torch.int32, device="cuda:0")
+    nt = torch.empty(1, dtype=torch.int32, device="cuda:0")
+
+    am2 = torch.empty(M, dtype=torch.int32, device="cuda:0")
+    al2 = torch.empty(1, dtype=torch.int32, device="cuda:0")
+    nt2 = torch.empty(1, dtype=torch.int32, device="cuda:0")
+
+    def step():
+        w8.quantize_act(x, xq=xq, x_scale=xs)
+        w8.linear(xq, xs, wq1, ws1, want_bf16=False, acc=mid, workspace=ws)
+        w8.linear(xq, xs, wq2, ws2, want_bf16=False, y_f32=lg, workspace=ws)
+        w8.verify_accept(lg, draft, argmax=am, accept_len=al, next_token=nt, workspace=ws)
+        w8.lm_head_verify(xq, xs, wq2, ws2, draft, argmax=am2, accept_len=al2, next_token=nt2,
+                          workspace=ws)
+
+    outs = (xq, xs, mid, lg, am, al, nt, am2, al2, nt2)
+    step()
+    torch.cuda.synchronize()
+    ref = [host(t) for t in outs]
+    np.testing.assert_array_equal(ref[7], ref[4])
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for r in range(5):
+        for t in outs:
+            t.zero_()
+        scratch = torch.randn(1 << 20, device="cuda:0").sum()  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [host(t) for t in outs]
+        for a, b in zip(got, ref):
+            np.testing.assert_array_equal(a, b, err_msg=f"replay {r}")
+        del scratch
+
+
+# --------------------------------------------------------------------------
+# fused LM-head verification
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("B,G,V,K", [(1, 4, 512, 256), (1, 4, 151936, 4096), (32, 8, 4099, 1024),
+                                     (1, 7, 5000, 5120), (3, 0, 1000, 256), (2, 3, 17, 64),
+                                     (1, 15, 40000, 2048)])
+def test_lm_head_verify(B, G, V, K):
+    """Fused LM-head linear + argmax + acceptance against the oracle and
+    against the separate linear -> verify_accept path."""
+    announce(f"lm_head_verify B={B} G={G} V={V} K={K}")
+    R = B * (G + 1)
+    bits = synth.activations_bf16(700, R, K)
+    w = synth.weights_f32(700, V, K)
+    xq_r, xs_r = oracle.quantize_act(bits)
+    wq_r, ws_r = oracle.quantize_weight(w)
+    _, y32_r, _ = oracle.w8a8_linear(xq_r, xs_r, wq_r, ws_r)
+    am_r = oracle.argmax_rows(y32_r).reshape(B, G + 1)
+    draft = synth.draft_ids(700, B, G, V)
+    for b in range(B):                       # spread the accepted lengths
+        p = b % (G + 1)
+        draft[b, :p] = am_r[b, :p]
+    am_r, al_r, nt_r = oracle.verify_accept(y32_r, draft)
+    xq, xs = w8.quantize_act(dev_bf16(bits))
+    wt, ws = w8.quantize_weight(dev(w), tiled=True)
+    d = dev(draft)
+    lg, am, al, nt = w8.lm_head_verify(xq, xs, wt, ws, d, want_logits=True)
+    _, am2, al2, nt2 = w8.lm_head_verify(xq, xs, wt, ws, d)          # no logits written
+    _, yf, _ = w8.linear(xq, xs, wt, ws, want_bf16=False, want_f32=True)
+    am3, al3, nt3 = w8.verify_accept(yf, d)
+    lg4 = w8.lm_head_argmax(xq, xs, wt, ws, logits=torch.empty_like(yf))   # the two phases
+    am4, al4, nt4 = w8.accept_from_keys(d)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(lg).view(np.uint32), y32_r.view(np.uint32))
+    np.testing.assert_array_equal(host(lg4).view(np.uint32), y32_r.view(np.uint32))
+    for a, l, n in ((am, al, nt), (am2, al2, nt2), (am3, al3, nt3), (am4, al4, nt4)):
+        np.testing.assert_array_equal(host(a), am_r)
+        np.testing.assert_array_equal(host(l), al_r)
+        np.testing.assert_array_equal(host(n), nt_r)
+
+
+def test_lm_head_verify_ties_across_workgroups():
+    """Equal maxima in columns owned by different workgroups (and inside one
+    16-column tile): the lowest index wins."""
+    announce("lm_head_verify ties")
+    M, K, V = 5, 64, 4096
+    hot = {0: [100, 3000], 1: [5, 7], 2: [4095, 2048, 64], 3: [0, 4095], 4: [31, 32, 33]}
+    # row r reads only k = r, where exactly its hot columns hold a weight
+    xq = torch.zeros(M, K, dtype=torch.int8, device="cuda:0")
+    wq = torch.zeros(V, K, dtype=torch.int8, device="cuda:0")
+    for r, cols in hot.items():
+        xq[r, r] = 1
+        for c in cols:
+            wq[c, r] = 3
+    xs = torch.ones(M, dtype=torch.float32, device="cuda:0")
+    ws = torch.ones(V, dtype=torch.float32, device="cuda:0")
+    wt = w8.tile_weight(wq)
+    draft = torch.tensor([[100, 5, 64, 0]], dtype=torch.int32, device="cuda:0")
+    _, am, al, nt = w8.lm_head_verify(xq, xs, wt, ws, draft)
+    torch.cuda.synchronize()
+    assert host(am).tolist() == [100, 5, 64, 0, 31]
+    assert int(host(al)[0]) == 4 and int(host(nt)[0]) == 31

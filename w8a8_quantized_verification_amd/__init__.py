@@ -5,10 +5,12 @@ this package is its thin torch-tensor binding.  Build the library with
 ``python -m w8a8_quantized_verification_amd.build``.
 """
 from .api import (W8A8Error, Workspace, bf16_linear, linear, linear_workspace_bytes,
-                  quantize_act, quantize_weight, verify_accept,
+                  accept_from_keys, lm_head_argmax, lm_head_verify, quantize_act, quantize_weight, tile_weight, tiled_shape, verify_accept,
                   verify_accept_workspace_bytes)
 
 __all__ = [
-    "W8A8Error", "Workspace", "bf16_linear", "linear", "linear_workspace_bytes",
-    "quantize_act", "quantize_weight", "verify_accept", "verify_accept_workspace_bytes",
+    "W8A8Error", "Workspace", "accept_from_keys", "bf16_linear", "linear", "linear_workspace_bytes",
+    "lm_head_argmax", "lm_head_verify",
+    "quantize_act", "quantize_weight", "tile_weight", "tiled_shape", "verify_accept",
+    "verify_accept_workspace_bytes",
 ]

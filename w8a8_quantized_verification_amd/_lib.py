@@ -28,10 +28,19 @@ SIGNATURES = {
     "w8a8_last_error": (_c.c_char_p, []),
     "w8a8_quantize_act": (_i32, [_vp, _vp, _i64, _i64, _vp, _vp, _vp]),
     "w8a8_quantize_weight": (_i32, [_vp, _vp, _i64, _i64, _vp, _vp, _vp]),
+    "w8a8_tiled_weight_bytes": (_sz, [_i64, _i64]),
+    "w8a8_quantize_weight_tiled": (_i32, [_vp, _vp, _i64, _i64, _vp, _vp, _vp]),
+    "w8a8_tile_weight": (_i32, [_vp, _i64, _i64, _vp, _vp]),
     "w8a8_linear_workspace_bytes": (_sz, [_i64, _i64, _i64]),
+    "w8a8_linear_tiled": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
     "w8a8_linear": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
     "w8a8_verify_accept_workspace_bytes": (_sz, [_i64, _i64, _i64]),
     "w8a8_verify_accept": (_i32, [_vp, _i64, _vp, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "w8a8_lm_head_verify_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64]),
+    "w8a8_lm_head_verify": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _vp,
+                                   _vp, _vp, _sz, _vp]),
+    "w8a8_lm_head_argmax": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _sz, _vp]),
+    "w8a8_accept_from_keys": (_i32, [_vp, _sz, _vp, _i64, _i64, _vp, _vp, _vp, _vp]),
     "w8a8_bf16_linear": (_i32, [_vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp]),
 }
 

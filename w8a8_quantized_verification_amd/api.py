@@ -13,8 +13,10 @@ import torch
 from ._lib import W8A8Error, check, lib
 
 __all__ = [
-    "W8A8Error", "quantize_act", "quantize_weight", "linear", "linear_workspace_bytes",
-    "verify_accept", "verify_accept_workspace_bytes", "bf16_linear", "Workspace",
+    "W8A8Error", "quantize_act", "quantize_weight", "tile_weight", "tiled_shape", "linear",
+    "linear_workspace_bytes",
+    "verify_accept", "verify_accept_workspace_bytes", "lm_head_verify", "lm_head_argmax",
+    "accept_from_keys", "bf16_linear", "Workspace",
 ]
 
 
@@ -51,17 +53,21 @@ def _out(t, shape, dtype, device, name):
 
 
 class Workspace:
-    """Per-device zero-filled scratch for w8a8_linear's split-K partials and
-    verify_accept's chunk results.  Calls that use it must run in order on
-    one stream (the default use)."""
+    """Per-device scratch buffers, two per device: a "zeroed" one (allocated
+    zero-filled) for the calls that need zeros on entry and leave zeros
+    behind — w8a8_linear's split-K partials and lm_head_verify's argmax keys
+    — and a "verify" one for verify_accept's per-chunk results, which it
+    overwrites and leaves non-zero.  Calls that use one Workspace must run
+    in order on one stream (the default use)."""
 
     def __init__(self):
         self._buf = {}
 
-    def get(self, nbytes: int, device: torch.device) -> torch.Tensor | None:
+    def get(self, nbytes: int, device: torch.device, use: str) -> torch.Tensor | None:
         if nbytes == 0:
             return None
-        key = device.index if device.index is not None else torch.cuda.current_device()
+        idx = device.index if device.index is not None else torch.cuda.current_device()
+        key = (idx, use)
         b = self._buf.get(key)
         if b is None or b.numel() < nbytes:
             b = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
@@ -86,18 +92,36 @@ def quantize_act(x: torch.Tensor, smooth: torch.Tensor | None = None, *, xq=None
     return xq, x_scale
 
 
-def quantize_weight(w: torch.Tensor, smooth: torch.Tensor | None = None, *, wq=None, w_scale=None):
+def tiled_shape(N: int, K: int) -> tuple:
+    """Shape of the tiled weight layout as an int8 tensor: [ceil(N/16),
+    ceil(K/64), 64 lanes, 16 bytes] (see include/w8a8.h)."""
+    return ((N + 15) // 16, (K + 63) // 64, 64, 16)
+
+
+def quantize_weight(w: torch.Tensor, smooth: torch.Tensor | None = None, *, tiled: bool = False,
+                    wq=None, w_scale=None):
     """Per-output-channel symmetric int8 quantization of fp32 ``w[N][K]``;
-    returns ``(wq int8[N][K], w_scale float32[N])``."""
+    returns ``(wq, w_scale float32[N])`` with ``wq`` int8 ``[N][K]`` or, with
+    ``tiled=True``, in the tiled layout (shape :func:`tiled_shape`)."""
     _need(w, "w", torch.float32, 2)
     N, K = w.shape
     if smooth is not None:
         _need(smooth, "smooth", torch.float32, 1, w.device)
-    wq = _out(wq, (N, K), torch.int8, w.device, "wq")
+    shape = tiled_shape(N, K) if tiled else (N, K)
+    wq = _out(wq, shape, torch.int8, w.device, "wq")
     w_scale = _out(w_scale, (N,), torch.float32, w.device, "w_scale")
-    check(lib().w8a8_quantize_weight(_ptr(w), _ptr(smooth), N, K, _ptr(wq), _ptr(w_scale),
-                                     _stream(w.device)))
+    f = lib().w8a8_quantize_weight_tiled if tiled else lib().w8a8_quantize_weight
+    check(f(_ptr(w), _ptr(smooth), N, K, _ptr(wq), _ptr(w_scale), _stream(w.device)))
     return wq, w_scale
+
+
+def tile_weight(wq: torch.Tensor, *, out=None) -> torch.Tensor:
+    """Rearrange row-major int8 ``wq[N][K]`` into the tiled layout."""
+    _need(wq, "wq", torch.int8, 2)
+    N, K = wq.shape
+    out = _out(out, tiled_shape(N, K), torch.int8, wq.device, "out")
+    check(lib().w8a8_tile_weight(_ptr(wq), N, K, _ptr(out), _stream(wq.device)))
+    return out
 
 
 def linear_workspace_bytes(M: int, N: int, K: int) -> int:
@@ -106,17 +130,24 @@ def linear_workspace_bytes(M: int, N: int, K: int) -> int:
 
 def linear(xq, x_scale, wq, w_scale, *, want_bf16=True, want_f32=False, want_acc=False,
            y_bf16=None, y_f32=None, acc=None, workspace: Workspace | None = None):
-    """One W8A8 linear.  Returns ``(y_bf16, y_f32, acc)``, each None unless
-    requested (``want_*``) or passed in."""
+    """One W8A8 linear.  ``wq`` is int8 ``[N][K]`` or the tiled layout (4-D,
+    shape :func:`tiled_shape`).  Returns ``(y_bf16, y_f32, acc)``, each None
+    unless requested (``want_*``) or passed in."""
     _need(xq, "xq", torch.int8, 2)
     dev = xq.device
     _need(x_scale, "x_scale", torch.float32, 1, dev)
-    _need(wq, "wq", torch.int8, 2, dev)
     _need(w_scale, "w_scale", torch.float32, 1, dev)
     M, K = xq.shape
-    N, K2 = wq.shape
-    if K2 != K or x_scale.shape[0] != M or w_scale.shape[0] != N:
-        raise ValueError("shape mismatch between xq[M][K], x_scale[M], wq[N][K], w_scale[N]")
+    N = w_scale.shape[0]
+    tiled = isinstance(wq, torch.Tensor) and wq.dim() == 4
+    _need(wq, "wq", torch.int8, 4 if tiled else 2, dev)
+    if tiled:
+        if tuple(wq.shape) != tiled_shape(N, K):
+            raise ValueError(f"tiled wq must have shape {tiled_shape(N, K)} (got {tuple(wq.shape)})")
+    elif tuple(wq.shape) != (N, K):
+        raise ValueError("shape mismatch between xq[M][K], wq[N][K], w_scale[N]")
+    if x_scale.shape[0] != M:
+        raise ValueError("x_scale must have M entries")
     if want_bf16 or y_bf16 is not None:
         y_bf16 = _out(y_bf16, (M, N), torch.bfloat16, dev, "y_bf16")
     if want_f32 or y_f32 is not None:
@@ -124,10 +155,11 @@ def linear(xq, x_scale, wq, w_scale, *, want_bf16=True, want_f32=False, want_acc
     if want_acc or acc is not None:
         acc = _out(acc, (M, N), torch.int32, dev, "acc")
     need = linear_workspace_bytes(M, N, K)
-    ws = (workspace or _default_ws).get(need, dev)
-    check(lib().w8a8_linear(_ptr(xq), _ptr(x_scale), _ptr(wq), _ptr(w_scale), M, N, K,
-                            _ptr(y_bf16), _ptr(y_f32), _ptr(acc), _ptr(ws),
-                            0 if ws is None else ws.numel(), _stream(dev)))
+    ws = (workspace or _default_ws).get(need, dev, use="zeroed")
+    f = lib().w8a8_linear_tiled if tiled else lib().w8a8_linear
+    check(f(_ptr(xq), _ptr(x_scale), _ptr(wq), _ptr(w_scale), M, N, K,
+            _ptr(y_bf16), _ptr(y_f32), _ptr(acc), _ptr(ws),
+            0 if ws is None else ws.numel(), _stream(dev)))
     return y_bf16, y_f32, acc
 
 
@@ -152,10 +184,89 @@ def verify_accept(logits, draft, *, want_argmax=True, argmax=None, accept_len=No
     accept_len = _out(accept_len, (B,), torch.int32, dev, "accept_len")
     next_token = _out(next_token, (B,), torch.int32, dev, "next_token")
     need = verify_accept_workspace_bytes(B, G, V)
-    ws = (workspace or _default_ws).get(need, dev)
+    ws = (workspace or _default_ws).get(need, dev, use="verify")
     check(lib().w8a8_verify_accept(_ptr(logits), V, _ptr(draft), B, G, _ptr(argmax),
                                    _ptr(accept_len), _ptr(next_token), _ptr(ws),
                                    0 if ws is None else ws.numel(), _stream(dev)))
+    return argmax, accept_len, next_token
+
+
+def lm_head_verify(xq, x_scale, wq_tiled, w_scale, draft, *, want_logits=False,
+                   want_argmax=True, logits=None, argmax=None, accept_len=None, next_token=None,
+                   workspace: Workspace | None = None):
+    """LM-head W8A8 linear with the argmax's first pass fused into its
+    epilogue, then greedy acceptance.  ``xq[B*(G+1)][K]``, tiled ``wq_tiled``
+    for ``[V][K]``, ``draft[B][G]``.  Returns ``(logits or None, argmax or
+    None, accept_len, next_token)``."""
+    _need(xq, "xq", torch.int8, 2)
+    dev = xq.device
+    _need(x_scale, "x_scale", torch.float32, 1, dev)
+    _need(w_scale, "w_scale", torch.float32, 1, dev)
+    _need(draft, "draft", torch.int32, 2, dev)
+    R, K = xq.shape
+    V = w_scale.shape[0]
+    B, G = draft.shape
+    if R != B * (G + 1) or x_scale.shape[0] != R:
+        raise ValueError(f"xq and x_scale must have B*(G+1) = {B * (G + 1)} rows")
+    _need(wq_tiled, "wq_tiled", torch.int8, 4, dev)
+    if tuple(wq_tiled.shape) != tiled_shape(V, K):
+        raise ValueError(f"wq_tiled must have shape {tiled_shape(V, K)}")
+    if want_logits or logits is not None:
+        logits = _out(logits, (R, V), torch.float32, dev, "logits")
+    if want_argmax or argmax is not None:
+        argmax = _out(argmax, (R,), torch.int32, dev, "argmax")
+    accept_len = _out(accept_len, (B,), torch.int32, dev, "accept_len")
+    next_token = _out(next_token, (B,), torch.int32, dev, "next_token")
+    need = int(lib().w8a8_lm_head_verify_workspace_bytes(B, G, V, K))
+    ws = (workspace or _default_ws).get(need, dev, use="zeroed")
+    check(lib().w8a8_lm_head_verify(_ptr(xq), _ptr(x_scale), _ptr(wq_tiled), _ptr(w_scale), V, K,
+                                    _ptr(draft), B, G, _ptr(logits), _ptr(argmax),
+                                    _ptr(accept_len), _ptr(next_token), _ptr(ws),
+                                    0 if ws is None else ws.numel(), _stream(dev)))
+    return logits, argmax, accept_len, next_token
+
+
+def lm_head_argmax(xq, x_scale, wq_tiled, w_scale, *, logits=None,
+                   workspace: Workspace | None = None):
+    """Phase 1 of :func:`lm_head_verify`: the LM-head linear with the row
+    maxima folded into the workspace keys (and the logits written if
+    ``logits`` is given)."""
+    _need(xq, "xq", torch.int8, 2)
+    dev = xq.device
+    _need(x_scale, "x_scale", torch.float32, 1, dev)
+    _need(w_scale, "w_scale", torch.float32, 1, dev)
+    M, K = xq.shape
+    V = w_scale.shape[0]
+    _need(wq_tiled, "wq_tiled", torch.int8, 4, dev)
+    if tuple(wq_tiled.shape) != tiled_shape(V, K):
+        raise ValueError(f"wq_tiled must have shape {tiled_shape(V, K)}")
+    if logits is not None:
+        logits = _out(logits, (M, V), torch.float32, dev, "logits")
+    ws = (workspace or _default_ws).get(int(lib().w8a8_lm_head_verify_workspace_bytes(M, 0, V, K)),
+                                        dev, use="zeroed")
+    check(lib().w8a8_lm_head_argmax(_ptr(xq), _ptr(x_scale), _ptr(wq_tiled), _ptr(w_scale), M, V,
+                                    K, _ptr(logits), _ptr(ws), 0 if ws is None else ws.numel(),
+                                    _stream(dev)))
+    return logits
+
+
+def accept_from_keys(draft, *, want_argmax=True, argmax=None, accept_len=None, next_token=None,
+                     workspace: Workspace | None = None):
+    """Phase 2 of :func:`lm_head_verify`: read and reset the keys a preceding
+    :func:`lm_head_argmax` left in the same workspace, then accept."""
+    _need(draft, "draft", torch.int32, 2)
+    dev = draft.device
+    B, G = draft.shape
+    R = B * (G + 1)
+    if want_argmax or argmax is not None:
+        argmax = _out(argmax, (R,), torch.int32, dev, "argmax")
+    accept_len = _out(accept_len, (B,), torch.int32, dev, "accept_len")
+    next_token = _out(next_token, (B,), torch.int32, dev, "next_token")
+    ws = (workspace or _default_ws).get(int(lib().w8a8_lm_head_verify_workspace_bytes(R, 0, 1, 0)),
+                                        dev, use="zeroed")
+    check(lib().w8a8_accept_from_keys(_ptr(ws), 0 if ws is None else ws.numel(), _ptr(draft), B, G,
+                                      _ptr(argmax), _ptr(accept_len), _ptr(next_token),
+                                      _stream(dev)))
     return argmax, accept_len, next_token
 
 

@@ -66,13 +66,13 @@ w8a8_status w8a8_quantize_act(const uint16_t* x_bf16, const float* smooth, int64
   if (K > 0 && (!x_bf16 || !xq)) return fail(W8A8_ERR_INVALID_ARG, fn, "x_bf16 or xq is NULL");
   if (!aligned(x_bf16, 16) || !aligned(xq, 16) || !aligned(smooth, 16) || !aligned(x_scale, 4))
     return fail(W8A8_ERR_INVALID_ARG, fn, "pointer misaligned (16 bytes for tensors, 4 for scales)");
-  return hip_status(w8a8_launch_quantize_rows(x_bf16, true, smooth, false, M, K, xq, x_scale,
-                                              reinterpret_cast<hipStream_t>(stream)), fn);
+  return hip_status(w8a8_launch_quantize_rows(x_bf16, true, smooth, false, M, K, false, xq,
+                                              x_scale, reinterpret_cast<hipStream_t>(stream)), fn);
 }
 
-w8a8_status w8a8_quantize_weight(const float* w, const float* smooth, int64_t N, int64_t K,
-                                 int8_t* wq, float* w_scale, void* stream) {
-  static const char* fn = "w8a8_quantize_weight";
+static w8a8_status quantize_weight_common(const char* fn, const float* w, const float* smooth,
+                                          int64_t N, int64_t K, bool tiled, int8_t* wq,
+                                          float* w_scale, void* stream) {
   g_last_error.clear();
   if (w8a8_status s = check_rows_k(fn, N, K)) return s;
   if (N == 0) return W8A8_OK;
@@ -80,20 +80,52 @@ w8a8_status w8a8_quantize_weight(const float* w, const float* smooth, int64_t N,
   if (K > 0 && (!w || !wq)) return fail(W8A8_ERR_INVALID_ARG, fn, "w or wq is NULL");
   if (!aligned(w, 16) || !aligned(wq, 16) || !aligned(smooth, 16) || !aligned(w_scale, 4))
     return fail(W8A8_ERR_INVALID_ARG, fn, "pointer misaligned (16 bytes for tensors, 4 for scales)");
-  return hip_status(w8a8_launch_quantize_rows(w, false, smooth, true, N, K, wq, w_scale,
+  return hip_status(w8a8_launch_quantize_rows(w, false, smooth, true, N, K, tiled, wq, w_scale,
                                               reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
+w8a8_status w8a8_quantize_weight(const float* w, const float* smooth, int64_t N, int64_t K,
+                                 int8_t* wq, float* w_scale, void* stream) {
+  return quantize_weight_common("w8a8_quantize_weight", w, smooth, N, K, false, wq, w_scale,
+                                stream);
+}
+
+size_t w8a8_tiled_weight_bytes(int64_t N, int64_t K) {
+  if (N <= 0 || K <= 0 || N > kMaxRows || K > W8A8_MAX_K) return 0;
+  return w8a8_tiled_weight_bytes_impl(N, K);
+}
+
+w8a8_status w8a8_quantize_weight_tiled(const float* w, const float* smooth, int64_t N, int64_t K,
+                                       int8_t* wq_tiled, float* w_scale, void* stream) {
+  return quantize_weight_common("w8a8_quantize_weight_tiled", w, smooth, N, K, true, wq_tiled,
+                                w_scale, stream);
+}
+
+w8a8_status w8a8_tile_weight(const int8_t* wq, int64_t N, int64_t K, int8_t* wq_tiled,
+                             void* stream) {
+  static const char* fn = "w8a8_tile_weight";
+  g_last_error.clear();
+  if (w8a8_status s = check_rows_k(fn, N, K)) return s;
+  if (N == 0 || K == 0) return W8A8_OK;
+  if (!wq || !wq_tiled) return fail(W8A8_ERR_INVALID_ARG, fn, "wq or wq_tiled is NULL");
+  if (!aligned(wq, 16) || !aligned(wq_tiled, 16))
+    return fail(W8A8_ERR_INVALID_ARG, fn, "wq and wq_tiled must be 16-byte aligned");
+  return hip_status(w8a8_launch_tile_weight(wq, N, K, wq_tiled,
+                                            reinterpret_cast<hipStream_t>(stream)), fn);
 }
 
 size_t w8a8_linear_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0 || M > kMaxRows || N > kMaxRows || K < 0 || K > W8A8_MAX_K) return 0;
-  return w8a8_gemm_workspace_bytes(M, N, K);
+  const size_t a = w8a8_gemm_workspace_bytes(M, N, K, false);
+  const size_t b = w8a8_gemm_workspace_bytes(M, N, K, true);
+  return a > b ? a : b;
 }
 
-w8a8_status w8a8_linear(const int8_t* xq, const float* x_scale, const int8_t* wq,
-                        const float* w_scale, int64_t M, int64_t N, int64_t K, uint16_t* y_bf16,
-                        float* y_f32, int32_t* acc, void* workspace, size_t workspace_bytes,
-                        void* stream) {
-  static const char* fn = "w8a8_linear";
+static w8a8_status linear_common(const char* fn, const int8_t* xq, const float* x_scale,
+                                 const int8_t* wq, const float* w_scale, int64_t M, int64_t N,
+                                 int64_t K, bool tiled, uint16_t* y_bf16, float* y_f32,
+                                 int32_t* acc, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
   g_last_error.clear();
   if (w8a8_status s = check_rows_k(fn, M, K)) return s;
   if (N < 0 || N > kMaxRows) return fail(W8A8_ERR_INVALID_ARG, fn, "N out of range");
@@ -106,13 +138,29 @@ w8a8_status w8a8_linear(const int8_t* xq, const float* x_scale, const int8_t* wq
   if (!aligned(x_scale, 4) || !aligned(w_scale, 4) || !aligned(y_bf16, 2) || !aligned(y_f32, 4) ||
       !aligned(acc, 4))
     return fail(W8A8_ERR_INVALID_ARG, fn, "scale or output pointer misaligned");
-  const size_t need = w8a8_gemm_workspace_bytes(M, N, K);
+  const size_t need = w8a8_gemm_workspace_bytes(M, N, K, tiled);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(W8A8_ERR_WORKSPACE, fn, "workspace NULL or smaller than w8a8_linear_workspace_bytes()");
   if (need > 0 && !aligned(workspace, 256))
     return fail(W8A8_ERR_INVALID_ARG, fn, "workspace must be 256-byte aligned");
-  return hip_status(w8a8_launch_gemm(xq, x_scale, wq, w_scale, M, N, K, y_bf16, y_f32, acc,
+  return hip_status(w8a8_launch_gemm(xq, x_scale, wq, w_scale, M, N, K, tiled, y_bf16, y_f32, acc,
                                      workspace, reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
+w8a8_status w8a8_linear(const int8_t* xq, const float* x_scale, const int8_t* wq,
+                        const float* w_scale, int64_t M, int64_t N, int64_t K, uint16_t* y_bf16,
+                        float* y_f32, int32_t* acc, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  return linear_common("w8a8_linear", xq, x_scale, wq, w_scale, M, N, K, false, y_bf16, y_f32,
+                       acc, workspace, workspace_bytes, stream);
+}
+
+w8a8_status w8a8_linear_tiled(const int8_t* xq, const float* x_scale, const int8_t* wq_tiled,
+                              const float* w_scale, int64_t M, int64_t N, int64_t K,
+                              uint16_t* y_bf16, float* y_f32, int32_t* acc, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  return linear_common("w8a8_linear_tiled", xq, x_scale, wq_tiled, w_scale, M, N, K, true, y_bf16,
+                       y_f32, acc, workspace, workspace_bytes, stream);
 }
 
 size_t w8a8_verify_accept_workspace_bytes(int64_t B, int64_t G, int64_t V) {
@@ -144,6 +192,96 @@ w8a8_status w8a8_verify_accept(const float* logits, int64_t V, const int32_t* dr
   return hip_status(w8a8_launch_verify_accept(logits, V, draft, B, G, argmax, accept_len,
                                               next_token, workspace,
                                               reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
+size_t w8a8_lm_head_verify_workspace_bytes(int64_t B, int64_t G, int64_t V, int64_t K) {
+  if (B <= 0 || G < 0 || G > W8A8_MAX_DRAFT || V <= 0 || V > kMaxRows || B > kMaxRows ||
+      K < 0 || K > W8A8_MAX_K)
+    return 0;
+  return w8a8_lm_head_workspace_bytes(B * (G + 1));
+}
+
+static w8a8_status check_lm_head(const char* fn, const int8_t* xq, const float* x_scale,
+                                 const int8_t* wq_tiled, const float* w_scale, int64_t M,
+                                 int64_t V, int64_t K, const float* logits, const void* keys,
+                                 size_t keys_bytes) {
+  if (w8a8_status s = check_rows_k(fn, M, K)) return s;
+  if (M == 0) return W8A8_OK;
+  if (V < 1 || V > kMaxRows) return fail(W8A8_ERR_INVALID_ARG, fn, "V out of range [1, 2^30]");
+  if (!x_scale || !w_scale || (K > 0 && (!xq || !wq_tiled)))
+    return fail(W8A8_ERR_INVALID_ARG, fn, "required pointer is NULL");
+  if (!aligned(xq, 16) || !aligned(wq_tiled, 16))
+    return fail(W8A8_ERR_INVALID_ARG, fn, "xq and wq_tiled must be 16-byte aligned");
+  if (!aligned(x_scale, 4) || !aligned(w_scale, 4) || !aligned(logits, 4))
+    return fail(W8A8_ERR_INVALID_ARG, fn, "pointer misaligned (4 bytes)");
+  if (!keys || keys_bytes < w8a8_lm_head_workspace_bytes(M))
+    return fail(W8A8_ERR_WORKSPACE, fn, "workspace NULL or smaller than w8a8_lm_head_verify_workspace_bytes()");
+  if (!aligned(keys, 256)) return fail(W8A8_ERR_INVALID_ARG, fn, "workspace must be 256-byte aligned");
+  return W8A8_OK;
+}
+
+static w8a8_status check_accept_keys(const char* fn, const int32_t* draft, int64_t B, int64_t G,
+                                     const int32_t* argmax, const int32_t* accept_len,
+                                     const int32_t* next_token) {
+  if (B < 0 || B > kMaxRows) return fail(W8A8_ERR_INVALID_ARG, fn, "B out of range");
+  if (G < 0 || G > W8A8_MAX_DRAFT) return fail(W8A8_ERR_INVALID_ARG, fn, "G out of range [0, 255]");
+  if (B == 0) return W8A8_OK;
+  if (!accept_len || !next_token || (G > 0 && !draft))
+    return fail(W8A8_ERR_INVALID_ARG, fn, "required pointer is NULL");
+  if (!aligned(draft, 4) || !aligned(argmax, 4) || !aligned(accept_len, 4) || !aligned(next_token, 4))
+    return fail(W8A8_ERR_INVALID_ARG, fn, "pointer misaligned (4 bytes)");
+  return W8A8_OK;
+}
+
+w8a8_status w8a8_lm_head_argmax(const int8_t* xq, const float* x_scale, const int8_t* wq_tiled,
+                                const float* w_scale, int64_t M, int64_t V, int64_t K,
+                                float* logits, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  static const char* fn = "w8a8_lm_head_argmax";
+  g_last_error.clear();
+  if (w8a8_status s = check_lm_head(fn, xq, x_scale, wq_tiled, w_scale, M, V, K, logits,
+                                    workspace, workspace_bytes))
+    return s;
+  if (M == 0) return W8A8_OK;
+  return hip_status(w8a8_launch_lm_head_argmax(xq, x_scale, wq_tiled, w_scale, M, V, K, logits,
+                                               workspace, reinterpret_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+w8a8_status w8a8_accept_from_keys(void* workspace, size_t workspace_bytes, const int32_t* draft,
+                                  int64_t B, int64_t G, int32_t* argmax, int32_t* accept_len,
+                                  int32_t* next_token, void* stream) {
+  static const char* fn = "w8a8_accept_from_keys";
+  g_last_error.clear();
+  if (w8a8_status s = check_accept_keys(fn, draft, B, G, argmax, accept_len, next_token)) return s;
+  if (B == 0) return W8A8_OK;
+  if (!workspace || workspace_bytes < w8a8_lm_head_workspace_bytes(B * (G + 1)))
+    return fail(W8A8_ERR_WORKSPACE, fn, "workspace NULL or smaller than w8a8_lm_head_verify_workspace_bytes()");
+  if (!aligned(workspace, 256)) return fail(W8A8_ERR_INVALID_ARG, fn, "workspace must be 256-byte aligned");
+  return hip_status(w8a8_launch_accept_from_keys(workspace, draft, B, G, argmax, accept_len,
+                                                 next_token, reinterpret_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+w8a8_status w8a8_lm_head_verify(const int8_t* xq, const float* x_scale, const int8_t* wq_tiled,
+                                const float* w_scale, int64_t V, int64_t K, const int32_t* draft,
+                                int64_t B, int64_t G, float* logits, int32_t* argmax,
+                                int32_t* accept_len, int32_t* next_token, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  static const char* fn = "w8a8_lm_head_verify";
+  g_last_error.clear();
+  if (w8a8_status s = check_accept_keys(fn, draft, B, G, argmax, accept_len, next_token)) return s;
+  if (B == 0) return W8A8_OK;
+  if (w8a8_status s = check_lm_head(fn, xq, x_scale, wq_tiled, w_scale, B * (G + 1), V, K, logits,
+                                    workspace, workspace_bytes))
+    return s;
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (w8a8_status s = hip_status(w8a8_launch_lm_head_argmax(xq, x_scale, wq_tiled, w_scale,
+                                                            B * (G + 1), V, K, logits, workspace,
+                                                            st), fn))
+    return s;
+  return hip_status(w8a8_launch_accept_from_keys(workspace, draft, B, G, argmax, accept_len,
+                                                 next_token, st), fn);
 }
 
 w8a8_status w8a8_bf16_linear(const uint16_t* x_bf16, const uint16_t* w_bf16, int64_t M, int64_t N,

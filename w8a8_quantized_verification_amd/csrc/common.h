@@ -50,12 +50,23 @@ __device__ __forceinline__ void wave_argmax(float& v, int& idx) {
 // hipSuccess or the launch error.
 // ---------------------------------------------------------------------------
 hipError_t w8a8_launch_quantize_rows(const void* in, bool in_is_bf16, const float* smooth,
-                                     bool smooth_divides, int64_t R, int64_t K,
+                                     bool smooth_divides, int64_t R, int64_t K, bool tiled,
                                      int8_t* q, float* scale, hipStream_t stream);
+size_t w8a8_tiled_weight_bytes_impl(int64_t N, int64_t K);
+hipError_t w8a8_launch_tile_weight(const int8_t* wq, int64_t N, int64_t K, int8_t* out,
+                                   hipStream_t stream);
 
-size_t w8a8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+size_t w8a8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, bool tiled);
+size_t w8a8_lm_head_workspace_bytes(int64_t M);
+hipError_t w8a8_launch_lm_head_argmax(const int8_t* xq, const float* x_scale,
+                                      const int8_t* wq_tiled, const float* w_scale, int64_t M,
+                                      int64_t V, int64_t K, float* logits, void* keys,
+                                      hipStream_t stream);
+hipError_t w8a8_launch_accept_from_keys(void* keys, const int32_t* draft, int64_t B, int64_t G,
+                                        int32_t* argmax, int32_t* accept_len, int32_t* next_token,
+                                        hipStream_t stream);
 hipError_t w8a8_launch_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq,
-                            const float* w_scale, int64_t M, int64_t N, int64_t K,
+                            const float* w_scale, int64_t M, int64_t N, int64_t K, bool tiled,
                             uint16_t* y_bf16, float* y_f32, int32_t* acc,
                             void* workspace, hipStream_t stream);
 
@@ -64,6 +75,15 @@ hipError_t w8a8_launch_verify_accept(const float* logits, int64_t V, const int32
                                      int64_t B, int64_t G, int32_t* argmax,
                                      int32_t* accept_len, int32_t* next_token,
                                      void* workspace, hipStream_t stream);
+
+// parts: [B*(G+1)][nparts] 8-byte (float maximum bits, lowest index) pairs
+hipError_t w8a8_launch_accept(const void* parts, int nparts, const int32_t* draft, int64_t B,
+                              int64_t G, int32_t* argmax, int32_t* accept_len,
+                              int32_t* next_token, hipStream_t stream);
+
+hipError_t w8a8_launch_accept_keys(unsigned long long* keys, int subkeys, int key_stride,
+                                   const int32_t* draft, int64_t B, int64_t G, int32_t* argmax,
+                                   int32_t* accept_len, int32_t* next_token, hipStream_t stream);
 
 hipError_t w8a8_launch_bf16_gemm(const uint16_t* x, const uint16_t* w, int64_t M, int64_t N,
                                  int64_t K, uint16_t* y_bf16, float* y_f32, hipStream_t stream);

@@ -23,16 +23,29 @@
 // B inside the instruction is right whatever order the hardware sums the
 // 64 products in — and int32 sums are exact in any order.
 //
+// Two weight layouts:
+//  * row-major [N][K]: one B load touches 16 rows x 64 bytes;
+//  * tiled (see w8a8_quantize_weight_tiled): for each tile of 16 output
+//    channels and each 64-wide k step, the 1 KiB the MFMA consumes is stored
+//    contiguously in lane order, so every B load is one fully coalesced 1 KiB
+//    read.  Tiles are zero-padded to 16 rows and K to a multiple of 64.
+// Tiled weight loads are non-temporal (streamed once, kept out of the
+// caches); that measured faster for the contiguous tiled stream and not for
+// the row-major pattern, which keeps ordinary loads.
+//
 // Work split: a workgroup owns TN tiles of 16 output channels and one
-// k-range; its WAVES waves split that k-range, issue U steps of 16-byte
-// loads (U*(TN+1) loads in flight per lane) before their MFMAs, and reduce
-// their partial tiles through LDS.  When the output has too few tiles to
-// fill the 256 CUs, the k-range is also split across SPLIT workgroups
-// (grid.y); those add their int32 partials into a workspace with atomics
-// (exact, order-free) and the last one to arrive, found with a per-tile
-// counter, applies the epilogue and zeroes the workspace tile and counter
-// behind it.  Token rows beyond 16 are handled by grid.z blocks of 16 rows.
+// k-range; its WAVES waves share the k steps of that range, issue U steps of
+// loads before their MFMAs, and reduce their partial tiles through LDS.
+// When the output is too narrow to occupy the chip (a few dozen tiles), the
+// k-range is also split across SPLIT workgroups (grid.y): they add their
+// int32 partials into a workspace with atomics (exact, order-free) and the
+// last one to arrive, found with a per-tile counter, applies the epilogue
+// and zeroes the workspace tile and counter behind it.  Token rows beyond 16
+// are handled by grid.z blocks of 16 rows.
 #include "common.h"
+
+#include <climits>
+#include <cstdlib>
 
 namespace w8a8 {
 
@@ -42,6 +55,8 @@ struct GemmArgs {
   const int8_t* wq;
   const float* ws;
   int M, N, K;
+  int steps;    // ceil(K / 64)
+  int tiles16;  // ceil(N / 16): 16-channel tiles in the tiled weight layout
   int split;
   int tiles;  // number of workgroup column tiles (grid.x)
   uint16_t* y_bf16;
@@ -49,21 +64,45 @@ struct GemmArgs {
   int32_t* acc;
   int32_t* part;    // [M][N] int32 split-K workspace (zero between calls)
   uint32_t* count;  // [grid.z][tiles] arrival counters (zero between calls)
+  unsigned long long* keys;  // fused argmax: packed (value, index) sub-keys, see
+                             // kArgmaxSubkeys (zero before the call), or null
 };
 
-__device__ __forceinline__ void epilogue_store(const GemmArgs& g, int m, int n, int32_t a) {
+// Fused-argmax keys: row m keeps kArgmaxSubkeys running maxima; workgroup w
+// folds into sub-key w % kArgmaxSubkeys, at keys[(m * kArgmaxSubkeys + s) *
+// kArgmaxKeyStride].  Spreading the folds over 64 addresses 256 bytes apart
+// keeps same-address atomics (which serialize) to a few dozen per key.
+constexpr int kArgmaxSubkeys = 64;
+constexpr int kArgmaxKeyStride = 32;  // in 8-byte words: 256 bytes
+
+// Pack (value, index) into a 64-bit key whose unsigned order is "larger value
+// first, then lower index": the value's bits mapped to an order-preserving
+// unsigned (negatives complemented, positives with the sign bit set; -0 made
+// +0 first so that it ties with +0), the index complemented.  Key 0 means
+// "empty".
+__device__ __forceinline__ unsigned long long argmax_key(float v, int idx) {
+  uint32_t u = __float_as_uint(v == 0.0f ? 0.0f : v);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((unsigned long long)u << 32) | (unsigned long long)(~(uint32_t)idx);
+}
+
+__device__ __forceinline__ float epilogue_store(const GemmArgs& g, int m, int n, int32_t a) {
   const float y = (static_cast<float>(a) * g.xs[m]) * g.ws[n];
   const size_t o = (size_t)m * (size_t)g.N + (size_t)n;
   if (g.y_f32) g.y_f32[o] = y;
   if (g.y_bf16) g.y_bf16[o] = f32_to_bf16_rne(y);
   if (g.acc) g.acc[o] = a;
+  return y;
 }
 
 __device__ __forceinline__ v4i load16(const int8_t* p) {
   return *reinterpret_cast<const v4i*>(p);
 }
+__device__ __forceinline__ v4i load16_stream(const int8_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const v4i*>(p));
+}
 
-template <int TN, int WAVES, int U>
+template <int TN, int WAVES, int U, bool kTiled, bool kArgmax>
 __global__ __launch_bounds__(WAVES * kWave) void gemm_w8a8_skinny(GemmArgs g) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
@@ -73,13 +112,23 @@ __global__ __launch_bounds__(WAVES * kWave) void gemm_w8a8_skinny(GemmArgs g) {
   const int m_base = blockIdx.z * 16;
   const int n0 = tile * 16 * TN;
   const int K = g.K;
-  const int steps = (K + 63) >> 6;
+  const int steps = g.steps;
 
-  // this workgroup's k-steps [g0, g1), then this wave's [s0, s1)
+  // this workgroup's k steps [g0, g1).  Tiled weights: the waves take them
+  // round-robin (s = g0 + wave + WAVES*j), so the workgroup sweeps adjacent
+  // KiB blocks.  Row-major weights: each wave takes a contiguous share
+  // (s = sw + j), so each of its loads continues the same 16 rows.
   const int g0 = (int)(((int64_t)steps * blockIdx.y) / g.split);
   const int g1 = (int)(((int64_t)steps * (blockIdx.y + 1)) / g.split);
-  const int s0 = g0 + (int)(((int64_t)(g1 - g0) * wave) / WAVES);
-  const int s1 = g0 + (int)(((int64_t)(g1 - g0) * (wave + 1)) / WAVES);
+  int J, sw;
+  constexpr int kStride = kTiled ? WAVES : 1;
+  if constexpr (kTiled) {
+    J = (g1 - g0 > wave) ? (g1 - g0 - wave + WAVES - 1) / WAVES : 0;
+    sw = g0 + wave;
+  } else {
+    sw = g0 + (int)(((int64_t)(g1 - g0) * wave) / WAVES);
+    J = g0 + (int)(((int64_t)(g1 - g0) * (wave + 1)) / WAVES) - sw;
+  }
 
   const int m_a = m_base + col;
   const bool a_ok = m_a < g.M;
@@ -88,26 +137,38 @@ __global__ __launch_bounds__(WAVES * kWave) void gemm_w8a8_skinny(GemmArgs g) {
   bool b_ok[TN];
 #pragma unroll
   for (int t = 0; t < TN; ++t) {
-    const int n = n0 + 16 * t + col;
-    b_ok[t] = n < g.N;
-    b_ptr[t] = g.wq + (size_t)(b_ok[t] ? n : 0) * (size_t)K + grp * 16;
+    if constexpr (kTiled) {
+      const int t16 = tile * TN + t;
+      b_ok[t] = t16 < g.tiles16;
+      b_ptr[t] = g.wq + ((size_t)(b_ok[t] ? t16 : 0) * (size_t)steps << 10) + (lane << 4);
+    } else {
+      const int n = n0 + 16 * t + col;
+      b_ok[t] = n < g.N;
+      b_ptr[t] = g.wq + (size_t)(b_ok[t] ? n : 0) * (size_t)K + grp * 16;
+    }
   }
+  // byte offset of k step s inside a B stream
+  auto b_off = [](int s) -> size_t { return kTiled ? ((size_t)s << 10) : (size_t)s * 64; };
 
   v4i acc[TN];
 #pragma unroll
   for (int t = 0; t < TN; ++t) acc[t] = v4i{0, 0, 0, 0};
 
   const v4i zero = v4i{0, 0, 0, 0};
-  int s = s0;
-  for (; s + U <= s1; s += U) {
+  int j = 0;
+  for (; j + U <= J; j += U) {
     v4i a[U], b[U][TN];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int k = (s + u) * 64;
+      const int s = sw + kStride * (j + u);
+      const int k = s * 64;
       const bool kin = k + grp * 16 < K;
       a[u] = (a_ok && kin) ? load16(a_ptr + k) : zero;
 #pragma unroll
-      for (int t = 0; t < TN; ++t) b[u][t] = (b_ok[t] && kin) ? load16(b_ptr[t] + k) : zero;
+      for (int t = 0; t < TN; ++t) {
+        if constexpr (kTiled) b[u][t] = (TN == 1 || b_ok[t]) ? load16_stream(b_ptr[t] + b_off(s)) : zero;
+        else b[u][t] = (b_ok[t] && kin) ? load16(b_ptr[t] + b_off(s)) : zero;
+      }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
@@ -115,13 +176,16 @@ __global__ __launch_bounds__(WAVES * kWave) void gemm_w8a8_skinny(GemmArgs g) {
       for (int t = 0; t < TN; ++t)
         acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[u], b[u][t], acc[t], 0, 0, 0);
   }
-  for (; s < s1; ++s) {
+  for (; j < J; ++j) {
+    const int s = sw + kStride * j;
     const int k = s * 64;
     const bool kin = k + grp * 16 < K;
     const v4i a = (a_ok && kin) ? load16(a_ptr + k) : zero;
 #pragma unroll
     for (int t = 0; t < TN; ++t) {
-      const v4i b = (b_ok[t] && kin) ? load16(b_ptr[t] + k) : zero;
+      v4i b;
+      if constexpr (kTiled) b = (TN == 1 || b_ok[t]) ? load16_stream(b_ptr[t] + b_off(s)) : zero;
+      else b = (b_ok[t] && kin) ? load16(b_ptr[t] + b_off(s)) : zero;
       acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[t], 0, 0, 0);
     }
   }
@@ -143,6 +207,8 @@ __global__ __launch_bounds__(WAVES * kWave) void gemm_w8a8_skinny(GemmArgs g) {
 
   // wave 0 holds the workgroup's partial tile: rows 4*grp + r, column col.
   if (g.split == 1) {
+    float bv[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    int bi[4] = {INT_MAX, INT_MAX, INT_MAX, INT_MAX};
 #pragma unroll
     for (int t = 0; t < TN; ++t) {
       const int n = n0 + 16 * t + col;
@@ -150,12 +216,45 @@ __global__ __launch_bounds__(WAVES * kWave) void gemm_w8a8_skinny(GemmArgs g) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = m_base + 4 * grp + r;
-        if (m < g.M) epilogue_store(g, m, n, acc[t][r]);
+        if (m < g.M) {
+          const float y = epilogue_store(g, m, n, acc[t][r]);
+          if constexpr (kArgmax) {
+            if (y > bv[r]) { bv[r] = y; bi[r] = n; }  // t ascending: first maximum kept
+          }
+        }
+      }
+    }
+    if constexpr (kArgmax) {
+      // fused LM-head argmax: (max, lowest index) of each row over this
+      // workgroup's columns, reduced over the 16 lanes that share the row
+      // group (lane bits 0..3), then folded into one of the row's sub-keys
+      // with one device-scope atomic max (performed at the coherence point,
+      // so the acceptance kernel that follows sees every workgroup's fold)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) {
+          const float ov = __shfl_xor(bv[r], off, kWave);
+          const int oi = __shfl_xor(bi[r], off, kWave);
+          if (ov > bv[r] || (ov == bv[r] && oi < bi[r])) { bv[r] = ov; bi[r] = oi; }
+        }
+        const int m = m_base + 4 * grp + r;
+        if (col == 0 && m < g.M) {
+          const size_t sub = (size_t)m * kArgmaxSubkeys + (tile % kArgmaxSubkeys);
+          __hip_atomic_fetch_max(&g.keys[sub * kArgmaxKeyStride], argmax_key(bv[r], bi[r]),
+                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
       }
     }
     return;
   }
 
+  // Split-K handoff.  Every exchange goes through device-scope atomic
+  // read-modify-writes, which the hardware performs at one coherence point
+  // per address, so no cache write-back or invalidate (an agent-scope fence)
+  // is needed: the wave waits for its partial adds to complete (vmcnt(0))
+  // before lane 0 adds to the arrival counter, and the last arriver reads the
+  // totals with atomic exchanges issued after its counter add returned.
 #pragma unroll
   for (int t = 0; t < TN; ++t) {
     const int n = n0 + 16 * t + col;
@@ -163,16 +262,21 @@ __global__ __launch_bounds__(WAVES * kWave) void gemm_w8a8_skinny(GemmArgs g) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int m = m_base + 4 * grp + r;
-      if (m < g.M) atomicAdd(&g.part[(size_t)m * g.N + n], acc[t][r]);
+      if (m < g.M)
+        __hip_atomic_fetch_add(&g.part[(size_t)m * g.N + n], acc[t][r], __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  __threadfence();
+  // wait until this wave's adds have returned before counting the arrival
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   uint32_t* counter = &g.count[(size_t)blockIdx.z * g.tiles + tile];
   uint32_t old = 0;
-  if (lane == 0) old = atomicAdd(counter, 1u);
+  if (lane == 0)
+    old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   old = __shfl(old, 0, kWave);
   if (old != (uint32_t)(g.split - 1)) return;
-  __threadfence();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 #pragma unroll
   for (int t = 0; t < TN; ++t) {
     const int n = n0 + 16 * t + col;
@@ -181,69 +285,157 @@ __global__ __launch_bounds__(WAVES * kWave) void gemm_w8a8_skinny(GemmArgs g) {
     for (int r = 0; r < 4; ++r) {
       const int m = m_base + 4 * grp + r;
       if (m < g.M) {
-        const int32_t total = atomicExch(&g.part[(size_t)m * g.N + n], 0);
+        const int32_t total = __hip_atomic_exchange(&g.part[(size_t)m * g.N + n], 0,
+                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         epilogue_store(g, m, n, total);
       }
     }
   }
-  if (lane == 0) atomicExch(counter, 0u);
+  if (lane == 0)
+    __hip_atomic_exchange(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Launch shape: (tiles, split, mblocks) workgroups of WAVES waves.
+// Launch shape: (tiles, split, mblocks) workgroups of `waves` waves, each
+// owning tn 16-channel tiles.
 struct SkinnyPlan {
-  int tiles, split, mblocks;
+  int tiles, split, mblocks, waves, tn;
 };
 
-constexpr int kTN = 1;
-constexpr int kWaves = 4;
 constexpr int kUnroll = 8;
-constexpr int kTargetWorkgroups = 1024;  // 4 per CU on 256 CUs
+constexpr int kSplitBelowTiles = 32;  // split k across workgroups only below this
 
-static SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K) {
+// Tuning overrides (results do not depend on them: int32 sums are exact in
+// any order): W8A8_SPLITK forces the cross-workgroup split, W8A8_WAVES the
+// waves per workgroup (4, 8 or 16).  Read on every call.
+static int env_int(const char* name) {
+  const char* v = getenv(name);
+  return v ? atoi(v) : 0;
+}
+
+// Measured on MI355X at M=5 over the Qwen3-8B shapes (N = 1024..12288, K =
+// 4096/12288) and the LM head: 4 waves per workgroup once there are >= 512
+// column tiles, 8 below; splitting k across workgroups never paid (its
+// atomic handoff costs more than the extra parallelism), so it is kept for
+// outputs too narrow to occupy more than a few dozen CUs.
+static SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, bool tiled, bool no_split = false) {
   SkinnyPlan p;
-  p.tiles = (int)((N + 16 * kTN - 1) / (16 * kTN));
+  const int64_t tiles16 = (N + 15) / 16;
   p.mblocks = (int)((M + 15) / 16);
+  // two tiles per workgroup halve the activation loads per weight byte; it
+  // pays on the tiled layout once there are enough tiles to go round
+  p.tn = (tiled && tiles16 * p.mblocks >= 2048) ? 2 : 1;
+  const int fn = env_int("W8A8_TN");
+  if (fn == 1 || fn == 2) p.tn = fn;
+  p.tiles = (int)((tiles16 + p.tn - 1) / p.tn);
   const int64_t steps = (K + 63) / 64;
+  const int64_t wgs = (int64_t)p.tiles * p.mblocks;
+  p.waves = wgs >= 512 ? 4 : (wgs >= kSplitBelowTiles ? 8 : 16);
   p.split = 1;
-  while ((int64_t)p.tiles * p.mblocks * p.split < kTargetWorkgroups &&
-         steps / ((int64_t)p.split * 2 * kWaves) >= 2)
+  while (!no_split && wgs * p.split < kSplitBelowTiles &&
+         steps / ((int64_t)p.split * 2 * p.waves) >= 2)
     p.split *= 2;
+  const int fw = env_int("W8A8_WAVES");
+  if (fw == 4 || fw == 8 || fw == 16) p.waves = fw;
+  const int fs = env_int("W8A8_SPLITK");
+  if (!no_split && fs >= 1 && fs <= 64 && fs <= steps) p.split = fs;
   return p;
 }
 
 }  // namespace w8a8
 
-size_t w8a8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+size_t w8a8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, bool tiled) {
   using namespace w8a8;
   if (M <= 0 || N <= 0) return 0;
-  const SkinnyPlan p = plan_skinny(M, N, K);
+  const SkinnyPlan p = plan_skinny(M, N, K, tiled);
   if (p.split == 1) return 0;
   const size_t part = (size_t)M * (size_t)N * sizeof(int32_t);
   const size_t part_aligned = (part + 255) & ~(size_t)255;
   return part_aligned + (size_t)p.tiles * p.mblocks * sizeof(uint32_t);
 }
 
-hipError_t w8a8_launch_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq,
-                            const float* w_scale, int64_t M, int64_t N, int64_t K,
-                            uint16_t* y_bf16, float* y_f32, int32_t* acc,
-                            void* workspace, hipStream_t stream) {
+static hipError_t launch_plan(const w8a8::SkinnyPlan& p, const w8a8::GemmArgs& g, bool tiled,
+                              bool argmax, hipStream_t stream) {
   using namespace w8a8;
-  if (M == 0 || N == 0) return hipSuccess;
-  const SkinnyPlan p = plan_skinny(M, N, K);
-  GemmArgs g;
+  const dim3 grid((unsigned)p.tiles, (unsigned)p.split, (unsigned)p.mblocks);
+#define W8A8_GEMM(TN, W, TL, AM)                                                            \
+  hipLaunchKernelGGL((gemm_w8a8_skinny<TN, W, kUnroll, TL, AM>), grid, dim3(W * kWave), 0, \
+                     stream, g)
+#define W8A8_GEMM_W(TN, TL, AM)                   \
+  do {                                            \
+    if (p.waves == 4) W8A8_GEMM(TN, 4, TL, AM);   \
+    else if (p.waves == 8) W8A8_GEMM(TN, 8, TL, AM); \
+    else W8A8_GEMM(TN, 16, TL, AM);               \
+  } while (0)
+  if (argmax) {
+    if (p.tn == 2) W8A8_GEMM_W(2, true, true);
+    else W8A8_GEMM_W(1, true, true);
+  } else if (tiled) {
+    if (p.tn == 2) W8A8_GEMM_W(2, true, false);
+    else W8A8_GEMM_W(1, true, false);
+  } else {
+    W8A8_GEMM_W(1, false, false);
+  }
+#undef W8A8_GEMM_W
+#undef W8A8_GEMM
+  return hipGetLastError();
+}
+
+static w8a8::GemmArgs make_args(const w8a8::SkinnyPlan& p, const int8_t* xq, const float* x_scale,
+                                const int8_t* wq, const float* w_scale, int64_t M, int64_t N,
+                                int64_t K, uint16_t* y_bf16, float* y_f32, int32_t* acc) {
+  w8a8::GemmArgs g{};
   g.xq = xq; g.xs = x_scale; g.wq = wq; g.ws = w_scale;
   g.M = (int)M; g.N = (int)N; g.K = (int)K;
+  g.steps = (int)((K + 63) / 64);
+  g.tiles16 = (int)((N + 15) / 16);
   g.split = p.split; g.tiles = p.tiles;
   g.y_bf16 = y_bf16; g.y_f32 = y_f32; g.acc = acc;
-  g.part = nullptr; g.count = nullptr;
+  return g;
+}
+
+hipError_t w8a8_launch_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq,
+                            const float* w_scale, int64_t M, int64_t N, int64_t K, bool tiled,
+                            uint16_t* y_bf16, float* y_f32, int32_t* acc, void* workspace,
+                            hipStream_t stream) {
+  using namespace w8a8;
+  if (M == 0 || N == 0) return hipSuccess;
+  const SkinnyPlan p = plan_skinny(M, N, K, tiled);
+  GemmArgs g = make_args(p, xq, x_scale, wq, w_scale, M, N, K, y_bf16, y_f32, acc);
   if (p.split > 1) {
     const size_t part = (size_t)M * (size_t)N * sizeof(int32_t);
     g.part = reinterpret_cast<int32_t*>(workspace);
     g.count = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(workspace) +
                                           ((part + 255) & ~(size_t)255));
   }
-  const dim3 grid((unsigned)p.tiles, (unsigned)p.split, (unsigned)p.mblocks);
-  const dim3 block(kWaves * kWave);
-  hipLaunchKernelGGL((gemm_w8a8_skinny<kTN, kWaves, kUnroll>), grid, block, 0, stream, g);
-  return hipGetLastError();
+  return launch_plan(p, g, tiled, false, stream);
+}
+
+// LM head with the argmax fused into the epilogue: every workgroup folds
+// its per-row maxima into one of each row's sub-keys; the acceptance kernel
+// reads the sub-keys, resets them to zero and accepts the draft.
+size_t w8a8_lm_head_workspace_bytes(int64_t M) {
+  using namespace w8a8;
+  if (M <= 0) return 0;
+  return (size_t)M * kArgmaxSubkeys * kArgmaxKeyStride * sizeof(unsigned long long);
+}
+
+hipError_t w8a8_launch_lm_head_argmax(const int8_t* xq, const float* x_scale,
+                                      const int8_t* wq_tiled, const float* w_scale, int64_t M,
+                                      int64_t V, int64_t K, float* logits, void* keys,
+                                      hipStream_t stream) {
+  using namespace w8a8;
+  if (M == 0) return hipSuccess;
+  const SkinnyPlan p = plan_skinny(M, V, K, true, true);
+  GemmArgs g = make_args(p, xq, x_scale, wq_tiled, w_scale, M, V, K, nullptr, logits, nullptr);
+  g.keys = reinterpret_cast<unsigned long long*>(keys);
+  return launch_plan(p, g, true, true, stream);
+}
+
+hipError_t w8a8_launch_accept_from_keys(void* keys, const int32_t* draft, int64_t B, int64_t G,
+                                        int32_t* argmax, int32_t* accept_len, int32_t* next_token,
+                                        hipStream_t stream) {
+  using namespace w8a8;
+  return w8a8_launch_accept_keys(reinterpret_cast<unsigned long long*>(keys), kArgmaxSubkeys,
+                                 kArgmaxKeyStride, draft, B, G, argmax, accept_len, next_token,
+                                 stream);
 }

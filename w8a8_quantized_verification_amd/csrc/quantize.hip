@@ -15,13 +15,26 @@
 // One workgroup of 256 threads (4 waves) per row.  Each thread handles
 // groups of 8 consecutive elements with 16-byte loads (bf16: one load; fp32:
 // two); the row maximum is a wave reduction followed by a 4-entry LDS
-// reduction; the second pass re-reads the row (an L2 hit) and writes 8 int8
-// codes per store.
+// reduction; the second pass takes the first 4 groups per thread (rows of up
+// to 8192 elements) from registers, re-reads the rest (an L2 hit), and writes
+// 8 int8 codes per store.
+//
+// Weights can also be written in the tiled layout the W8A8 linear streams
+// (one contiguous KiB per 16 channels x 64 k): element (n, k) goes to byte
+//   ((n/16 * steps + k/64) * 64 + (n%16 + 16*((k%64)/16))) * 16 + k%16,
+// steps = ceil(K/64); the grid then covers whole 16-row tiles and every
+// padding byte (rows >= N, k >= K) is written as zero.
 #include "common.h"
 
 namespace w8a8 {
 
 constexpr int kQuantThreads = 256;
+constexpr int kCache = 4;  // groups of 8 elements kept in registers between the passes
+
+__host__ __device__ __forceinline__ size_t tiled_offset(int64_t n, int64_t k, int64_t steps) {
+  return ((((size_t)(n >> 4) * (size_t)steps + (size_t)(k >> 6)) << 6) +
+          (size_t)((n & 15) | (((k >> 4) & 3) << 4))) * 16 + (size_t)(k & 15);
+}
 
 template <bool kBf16In, bool kSmooth, bool kDivide>
 __device__ __forceinline__ void load8(const void* __restrict__ in_row, const float* __restrict__ smooth,
@@ -50,18 +63,41 @@ __device__ __forceinline__ void load8(const void* __restrict__ in_row, const flo
   }
 }
 
-template <bool kBf16In, bool kSmooth, bool kDivide>
+// Rows [0, R) are real; with kTiled the grid also covers the padding rows of
+// the last 16-row tile and the k range is padded to a multiple of 64.
+template <bool kBf16In, bool kSmooth, bool kDivide, bool kTiled>
 __global__ __launch_bounds__(kQuantThreads) void quantize_rows_kernel(
-    const void* __restrict__ in, const float* __restrict__ smooth, int64_t K,
+    const void* __restrict__ in, const float* __restrict__ smooth, int64_t R, int64_t K,
     int8_t* __restrict__ q, float* __restrict__ scale) {
   __shared__ float red[kQuantThreads / kWave];
   const int64_t row = blockIdx.x;
   const int tid = threadIdx.x;
+  const int64_t steps = (K + 63) >> 6;
+  const int64_t k_end = kTiled ? steps * 64 : K;
+
+  if (kTiled && row >= R) {  // padding row of the last tile: zeros
+    for (int64_t k = (int64_t)tid * 8; k < k_end; k += kQuantThreads * 8)
+      *reinterpret_cast<uint2*>(q + tiled_offset(row, k, steps)) = make_uint2(0u, 0u);
+    return;
+  }
+
   const size_t elt = kBf16In ? sizeof(uint16_t) : sizeof(float);
   const void* in_row = reinterpret_cast<const char*>(in) + (size_t)row * (size_t)K * elt;
+  constexpr int64_t kStride = kQuantThreads * 8;
 
+  // pass 1: row maximum; the first kCache groups of 8 stay in registers
+  float cache[kCache][8];
   float amax = 0.0f;
-  for (int64_t k = (int64_t)tid * 8; k < K; k += kQuantThreads * 8) {
+#pragma unroll
+  for (int c = 0; c < kCache; ++c) {
+    const int64_t k = (int64_t)tid * 8 + c * kStride;
+    if (k < K) {
+      load8<kBf16In, kSmooth, kDivide>(in_row, smooth, k, cache[c]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(cache[c][i]));
+    }
+  }
+  for (int64_t k = (int64_t)tid * 8 + kCache * kStride; k < K; k += kStride) {
     float v[8];
     load8<kBf16In, kSmooth, kDivide>(in_row, smooth, k, v);
 #pragma unroll
@@ -76,41 +112,91 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_rows_kernel(
   const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
   if (tid == 0) scale[row] = amax > 0.0f ? s : 0.0f;
 
-  int8_t* q_row = q + (size_t)row * (size_t)K;
-  for (int64_t k = (int64_t)tid * 8; k < K; k += kQuantThreads * 8) {
-    float v[8];
-    load8<kBf16In, kSmooth, kDivide>(in_row, smooth, k, v);
+  // pass 2: codes (cached groups from registers, the rest re-read)
+  auto emit = [&](int64_t k, const float v[8], bool real) {
     uint32_t packed[2] = {0u, 0u};
+    if (real) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float r = __builtin_rintf(v[i] * inv);
-      r = fminf(fmaxf(r, -127.0f), 127.0f);
-      const int qi = (v[i] == 0.0f) ? 0 : (int)r;
-      packed[i >> 2] |= ((uint32_t)(qi & 0xff)) << (8 * (i & 3));
+      for (int i = 0; i < 8; ++i) {
+        float r = __builtin_rintf(v[i] * inv);
+        r = fminf(fmaxf(r, -127.0f), 127.0f);
+        const int qi = (v[i] == 0.0f) ? 0 : (int)r;
+        packed[i >> 2] |= ((uint32_t)(qi & 0xff)) << (8 * (i & 3));
+      }
     }
-    *reinterpret_cast<uint2*>(q_row + k) = make_uint2(packed[0], packed[1]);
+    const size_t o = kTiled ? tiled_offset(row, k, steps) : (size_t)row * (size_t)K + (size_t)k;
+    *reinterpret_cast<uint2*>(q + o) = make_uint2(packed[0], packed[1]);
+  };
+#pragma unroll
+  for (int c = 0; c < kCache; ++c) {
+    const int64_t k = (int64_t)tid * 8 + c * kStride;
+    if (k < k_end) emit(k, cache[c], k < K);
   }
+  for (int64_t k = (int64_t)tid * 8 + kCache * kStride; k < k_end; k += kStride) {
+    float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (k < K) load8<kBf16In, kSmooth, kDivide>(in_row, smooth, k, v);
+    emit(k, v, k < K);
+  }
+}
+
+// Row-major int8 [N][K] -> tiled layout: one thread per 16-byte chunk of the
+// tiled buffer, in tiled order (coalesced writes), zeros for padding.
+__global__ __launch_bounds__(256) void tile_weight_kernel(const int8_t* __restrict__ wq, int64_t N,
+                                                          int64_t K, int64_t steps, int64_t chunks,
+                                                          int8_t* __restrict__ out) {
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= chunks) return;
+  const int64_t t = c / (steps * 64);
+  const int64_t rem = c - t * steps * 64;
+  const int64_t s = rem >> 6;
+  const int l = (int)(rem & 63);
+  const int64_t n = t * 16 + (l & 15);
+  const int64_t k = s * 64 + (int64_t)(l >> 4) * 16;
+  uint4 v = make_uint4(0u, 0u, 0u, 0u);
+  if (n < N && k < K) v = *reinterpret_cast<const uint4*>(wq + (size_t)n * (size_t)K + (size_t)k);
+  *reinterpret_cast<uint4*>(out + (size_t)c * 16) = v;
 }
 
 }  // namespace w8a8
 
+size_t w8a8_tiled_weight_bytes_impl(int64_t N, int64_t K) {
+  return (size_t)((N + 15) / 16) * 16 * (size_t)((K + 63) / 64) * 64;
+}
+
 hipError_t w8a8_launch_quantize_rows(const void* in, bool in_is_bf16, const float* smooth,
-                                     bool smooth_divides, int64_t R, int64_t K,
+                                     bool smooth_divides, int64_t R, int64_t K, bool tiled,
                                      int8_t* q, float* scale, hipStream_t stream) {
   using namespace w8a8;
   if (R == 0) return hipSuccess;
-  const dim3 grid((unsigned)R), block(kQuantThreads);
-#define W8A8_QLAUNCH(BF, SM, DIV) \
-  hipLaunchKernelGGL((quantize_rows_kernel<BF, SM, DIV>), grid, block, 0, stream, in, smooth, K, q, scale)
+  const int64_t grid_rows = tiled ? (R + 15) / 16 * 16 : R;
+  const dim3 grid((unsigned)grid_rows), block(kQuantThreads);
+#define W8A8_QLAUNCH(BF, SM, DIV, TL) \
+  hipLaunchKernelGGL((quantize_rows_kernel<BF, SM, DIV, TL>), grid, block, 0, stream, in, smooth, R, K, q, scale)
   if (in_is_bf16) {
-    if (!smooth) W8A8_QLAUNCH(true, false, false);
-    else if (smooth_divides) W8A8_QLAUNCH(true, true, true);
-    else W8A8_QLAUNCH(true, true, false);
+    // activations: row-major output only
+    if (!smooth) W8A8_QLAUNCH(true, false, false, false);
+    else W8A8_QLAUNCH(true, true, false, false);
+  } else if (!tiled) {
+    if (!smooth) W8A8_QLAUNCH(false, false, false, false);
+    else if (smooth_divides) W8A8_QLAUNCH(false, true, true, false);
+    else W8A8_QLAUNCH(false, true, false, false);
   } else {
-    if (!smooth) W8A8_QLAUNCH(false, false, false);
-    else if (smooth_divides) W8A8_QLAUNCH(false, true, true);
-    else W8A8_QLAUNCH(false, true, false);
+    if (!smooth) W8A8_QLAUNCH(false, false, false, true);
+    else if (smooth_divides) W8A8_QLAUNCH(false, true, true, true);
+    else W8A8_QLAUNCH(false, true, false, true);
   }
 #undef W8A8_QLAUNCH
+  return hipGetLastError();
+}
+
+hipError_t w8a8_launch_tile_weight(const int8_t* wq, int64_t N, int64_t K, int8_t* out,
+                                   hipStream_t stream) {
+  using namespace w8a8;
+  if (N == 0) return hipSuccess;
+  const int64_t steps = (K + 63) / 64;
+  const int64_t chunks = (N + 15) / 16 * steps * 64;
+  if (chunks == 0) return hipSuccess;
+  hipLaunchKernelGGL(tile_weight_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0,
+                     stream, wq, N, K, steps, chunks, out);
   return hipGetLastError();
 }
