@@ -47,6 +47,11 @@ def parse_args():
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--no-extra", action="store_true")
     p.add_argument("--pmc-probe", action="store_true")
+    p.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="turn two rocprofv3 --pmc runs of --pmc-probe into the traffic summary")
+    p.add_argument("--ingest-trace", metavar="TRACE_DIR",
+                   help="turn a rocprofv3 --kernel-trace --stats csv run into a summary")
+    p.add_argument("--command", default="", help="the command that produced the ingested run")
     return p.parse_args()
 
 
@@ -128,8 +133,88 @@ def graph_time(fns, replays=20):
     return e0.elapsed_time(e1) / replays / 1e3
 
 
+def _csv_rows(d, suffix):
+    import csv
+    import glob
+    files = sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True))
+    if not files:
+        raise SystemExit(f"no *{suffix} under {d}")
+    rows = []
+    for f in files:
+        rows.extend(csv.DictReader(open(f)))
+    return rows
+
+
+GEMM_KERNEL = "gemm_w8a8_skinny<2, 4, 8, true, true>"
+COPY_KERNEL_HINT = "copy"
+
+
+def ingest_pmc(fetch_dir, write_dir, command):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the LM-head GEMM, each
+    scaled by what the same counter reads for the 1 GiB copy of the probe."""
+    import numpy as np
+    out = {}
+    for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = [r for r in _csv_rows(d, "counter_collection.csv") if r["Counter_Name"] == name]
+        gemm = [float(r["Counter_Value"]) for r in rows if GEMM_KERNEL in r["Kernel_Name"]]
+        copy = [float(r["Counter_Value"]) for r in rows
+                if COPY_KERNEL_HINT in r["Kernel_Name"].lower() and GEMM_KERNEL not in r["Kernel_Name"]]
+        if not gemm or not copy:
+            raise SystemExit(f"{name}: no GEMM or copy dispatch found in {d}")
+        kib_copy = max(copy)          # the 1 GiB copy: its largest dispatch
+        factor = (1 << 30) / (kib_copy * 1024.0)
+        kib = float(np.median(gemm))
+        out[name] = (kib, kib_copy, factor, kib * 1024.0 * factor)
+    M, K, V = 5, 4096, 151936
+    alg = lm_head_bytes(M, V, K, logits=False) + 8 * M * ((V + 31) // 32)
+    total = out["FETCH_SIZE"][3] + out["WRITE_SIZE"][3]
+    lines = [
+        "# HBM traffic of the LM-head W8A8 GEMM (M=5, K=4096, V=151936, tiled int8, fused argmax)",
+        f"# kernel: {GEMM_KERNEL}",
+        f"# commands: {command}",
+        "# counters are KiB per dispatch (median over the probe's 8 GEMM dispatches); each is",
+        "# scaled by (2^30 bytes) / (the same counter on the probe's 1 GiB copy dispatch)",
+    ]
+    for name, (kib, kib_copy, factor, b) in out.items():
+        lines.append(f"{name.lower()}_kib_per_dispatch: {kib:.1f}")
+        lines.append(f"{name.lower()}_copy_kib: {kib_copy:.1f}")
+        lines.append(f"{name.lower()}_scale: {factor:.5f}")
+        lines.append(f"{name.lower()}_bytes_per_launch: {b:.0f}")
+    lines += [f"hbm_bytes_per_launch: {total:.0f}",
+              f"algorithmic_bytes_per_launch: {alg}",
+              f"traffic_over_algorithmic: {total / alg:.4f}",
+              f"kernel_source_sha: {file_sha(GEMM_SRC)}"]
+    os.makedirs(os.path.dirname(PMC_FILE), exist_ok=True)
+    with open(PMC_FILE, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def ingest_trace(trace_dir, command, out_path):
+    """Short text summary of a rocprofv3 --kernel-trace --stats csv run."""
+    rows = _csv_rows(trace_dir, "kernel_stats.csv")
+    lines = ["# rocprofv3 kernel statistics", f"# command: {command}",
+             f"{'avg_us':>10} {'min_us':>10} {'max_us':>10} {'calls':>6}  kernel"]
+    for r in rows:
+        n = r["Name"]
+        if len(n) > 110:
+            n = n[:107] + "..."
+        lines.append(f"{float(r['AverageNs']) / 1e3:10.2f} {float(r['MinNs']) / 1e3:10.2f} "
+                     f"{float(r['MaxNs']) / 1e3:10.2f} {int(r['Calls']):6d}  {n}")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     args = parse_args()
+    if args.ingest_pmc:
+        ingest_pmc(args.ingest_pmc[0], args.ingest_pmc[1], args.command)
+        return
+    if args.ingest_trace:
+        ingest_trace(args.ingest_trace, args.command,
+                     os.path.join(ROOT, "profiles", "lm_head_verify_m5_kernel_trace.txt"))
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
