@@ -193,7 +193,7 @@ def forced_split(monkeypatch):
     yield
 
 
-@pytest.mark.parametrize("M,N,K", [(5, 1024, 4096), (8, 1000, 5120), (16, 17, 25600), (33, 96, 2048)])
+@pytest.mark.parametrize("M,N,K", [(5, 1024, 4096), (8, 1000, 5120), (16, 17, 25600), (16, 96, 2048)])
 @pytest.mark.parametrize("tiled", [False, True])
 def test_linear_forced_split_k(M, N, K, tiled, forced_split):
     announce(f"linear forced split-K M={M} N={N} K={K} tiled={tiled}")
@@ -244,11 +244,21 @@ def test_linear_extreme_accumulators():
     assert np.all(a[:, 0::2] == -16129 * K) and np.all(a[:, 1::2] == 16129 * K)
 
 
-def test_linear_batched_m288_sampled():
-    """Batched verification, M = 32 x (8+1) = 288 on the q shape: the full
-    int32 result against the oracle."""
-    announce("linear M=288 q shape")
-    run_linear_case(288, 4096, 4096, seed=302, tiled=True)
+@pytest.mark.parametrize("N,K", [(4096, 4096), (1024, 4096), (12288, 4096), (4096, 12288)])
+@pytest.mark.parametrize("tiled", [True, False])
+def test_linear_batched_m288(N, K, tiled):
+    """Batched verification, M = 32 x (8+1) = 288, on every Qwen3-8B layer
+    shape: the full int32, fp32 and bf16 results against the oracle."""
+    announce(f"linear M=288 N={N} K={K} tiled={tiled}")
+    run_linear_case(288, N, K, seed=302 + N % 7, tiled=tiled)
+
+
+@pytest.mark.parametrize("M,N,K", [(17, 65, 80), (96, 64, 64), (97, 4099, 1040), (200, 130, 16),
+                                   (513, 300, 2048)])
+def test_linear_batched_ragged(M, N, K):
+    """Row tiles of 96 with ragged last tiles in M, N and K (tiled layout)."""
+    announce(f"linear batched ragged M={M} N={N} K={K}")
+    run_linear_case(M, N, K, seed=330 + M, tiled=True)
 
 
 # --------------------------------------------------------------------------

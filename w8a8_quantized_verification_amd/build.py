@@ -20,7 +20,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libw8a8.so")
 
-SOURCES = ["api.hip", "quantize.hip", "gemm_w8a8.hip", "argmax_accept.hip", "gemm_bf16.hip"]
+SOURCES = ["api.hip", "quantize.hip", "gemm_w8a8.hip", "gemm_w8a8_batched.hip", "argmax_accept.hip",
+           "gemm_bf16.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

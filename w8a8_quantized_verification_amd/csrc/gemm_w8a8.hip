@@ -40,8 +40,8 @@
 // k-range is also split across SPLIT workgroups (grid.y): they add their
 // int32 partials into a workspace with atomics (exact, order-free) and the
 // last one to arrive, found with a per-tile counter, applies the epilogue
-// and zeroes the workspace tile and counter behind it.  Token rows beyond 16
-// are handled by grid.z blocks of 16 rows.
+// and zeroes the workspace tile and counter behind it.  More than 16 token
+// rows go to the batched kernel (gemm_w8a8_batched.hip).
 #include "common.h"
 
 #include <climits>
@@ -302,6 +302,7 @@ struct SkinnyPlan {
 };
 
 constexpr int kUnroll = 8;
+constexpr int64_t kSkinnyMaxRows = 16;  // more token rows go to the batched kernel
 constexpr int kSplitBelowTiles = 32;  // split k across workgroups only below this
 
 // Tuning overrides (results do not depend on them: int32 sums are exact in
@@ -346,6 +347,7 @@ static SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, bool tiled, bool 
 size_t w8a8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, bool tiled) {
   using namespace w8a8;
   if (M <= 0 || N <= 0) return 0;
+  if (M > kSkinnyMaxRows) return w8a8_gemm_batched_workspace_bytes(M, N, K);
   const SkinnyPlan p = plan_skinny(M, N, K, tiled);
   if (p.split == 1) return 0;
   const size_t part = (size_t)M * (size_t)N * sizeof(int32_t);
@@ -399,6 +401,11 @@ hipError_t w8a8_launch_gemm(const int8_t* xq, const float* x_scale, const int8_t
                             hipStream_t stream) {
   using namespace w8a8;
   if (M == 0 || N == 0) return hipSuccess;
+  if (M > kSkinnyMaxRows)
+    return w8a8_launch_gemm_batched(xq, x_scale, wq, w_scale, M, N, K, tiled, y_bf16, y_f32, acc,
+                                    nullptr, 0, 0,
+                                    w8a8_gemm_batched_workspace_bytes(M, N, K) ? workspace : nullptr,
+                                    stream);
   const SkinnyPlan p = plan_skinny(M, N, K, tiled);
   GemmArgs g = make_args(p, xq, x_scale, wq, w_scale, M, N, K, y_bf16, y_f32, acc);
   if (p.split > 1) {
@@ -425,6 +432,9 @@ hipError_t w8a8_launch_lm_head_argmax(const int8_t* xq, const float* x_scale,
                                       hipStream_t stream) {
   using namespace w8a8;
   if (M == 0) return hipSuccess;
+  if (M > kSkinnyMaxRows)
+    return w8a8_launch_gemm_batched(xq, x_scale, wq_tiled, w_scale, M, V, K, true, nullptr, logits,
+                                    nullptr, keys, kArgmaxSubkeys, kArgmaxKeyStride, nullptr, stream);
   const SkinnyPlan p = plan_skinny(M, V, K, true, true);
   GemmArgs g = make_args(p, xq, x_scale, wq_tiled, w_scale, M, V, K, nullptr, logits, nullptr);
   g.keys = reinterpret_cast<unsigned long long*>(keys);
