@@ -46,6 +46,8 @@ def parse_args():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--no-extra", action="store_true")
+    p.add_argument("--no-stack", action="store_true",
+                   help="skip the Qwen3-32B-shaped stack (96 GB of device memory)")
     p.add_argument("--pmc-probe", action="store_true")
     p.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="turn two rocprofv3 --pmc runs of --pmc-probe into the traffic summary")
@@ -90,15 +92,14 @@ def read_traffic():
         return None
 
 
-def make_weight(N, K, seed, device, tiled=True, with_bf16=False):
-    """Random-init N(0, 0.02) fp32 weight drawn on the device, quantized to
-    int8 per output channel by the library."""
+def make_weight(N, K, workload, index, device, tiled=True, with_bf16=False):
+    """Random-init N(0, 0.02) fp32 weight drawn on the device (seeded by
+    workload and index), quantized to int8 per output channel by the library;
+    optionally also its bf16 copy."""
     import torch
+    import synth
     import w8a8_quantized_verification_amd as w8
-    g = torch.Generator(device=device)
-    g.manual_seed(seed)
-    w = torch.randn(N, K, generator=g, device=device, dtype=torch.float32)
-    w.mul_(0.02)
+    w = synth.weights_device(workload, index, N, K, device)
     wq, ws = w8.quantize_weight(w, tiled=tiled)
     wb = w.to(torch.bfloat16) if with_bf16 else None
     del w
@@ -234,7 +235,7 @@ def main():
     torch.cuda.set_device(dev)
 
     M, K, V, G, B = 5, 4096, synth.QWEN3_VOCAB, 4, 1
-    copies = [make_weight(V, K, 1000 + i, dev, tiled=True) for i in range(2)]
+    copies = [make_weight(V, K, synth.W_LM_HEAD, 1000 + i, dev, tiled=True) for i in range(2)]
     n_x = 8
     xs_host = [synth.activations_bf16(synth.W_LM_HEAD, M, K, index=i) for i in range(n_x)]
     x_dev = [torch.from_numpy(x.view(np.int16).copy()).view(torch.bfloat16).to(dev) for x in xs_host]
@@ -349,6 +350,8 @@ def main():
         extra["graph_step_separate_calls"] = {"ms_per_step": round(t_sep * 1e3, 5),
                                               "verified_tokens_per_s": round(M / t_sep, 1)}
         extra.update(extra_measurements(dev, copies, x_dev, xq, xsc, wsp))
+        if not args.no_stack:
+            extra["qwen3_32b_stack_m8"] = stack32b_measurement(dev, wsp)
         out["extra"] = extra
 
     if not args.no_cpu_baseline:
@@ -372,7 +375,8 @@ def extra_measurements(dev, copies, x_dev, xq, xsc, wsp):
     nc = 8
     layer = []
     for li, lin in enumerate(synth.QWEN3_8B_LAYER):
-        wl = [make_weight(lin.N, lin.K, 2000 + 10 * li + c, dev)[:2] for c in range(nc)]
+        wl = [make_weight(lin.N, lin.K, synth.W_LAYER_M5, 2000 + 10 * li + c, dev)[:2]
+              for c in range(nc)]
         x = torch.from_numpy(synth.activations_bf16(synth.W_LAYER_M5, M, lin.K, outliers=True)
                              .view(np.int16).copy()).view(torch.bfloat16).to(dev)
         lxq, lxs = w8.quantize_act(x)
@@ -407,7 +411,8 @@ def extra_measurements(dev, copies, x_dev, xq, xsc, wsp):
         return float(np.mean([a.elapsed_time(b) for a, b in ev])) / 1e3
 
     # row-major weight layout at the LM-head shape
-    rm = [make_weight(V, K, 1000 + i, dev, tiled=False, with_bf16=True) for i in range(2)]
+    rm = [make_weight(V, K, synth.W_LM_HEAD, 1000 + i, dev, tiled=False, with_bf16=True)
+          for i in range(2)]
     t_rm = ev_time(lambda i: w8.linear(xq, xsc, rm[i % 2][0], rm[i % 2][1], want_bf16=False,
                                        y_f32=lg, workspace=wsp))
     t_tl = ev_time(lambda i: w8.linear(xq, xsc, copies[i % 2][0], copies[i % 2][1],
@@ -427,15 +432,110 @@ def extra_measurements(dev, copies, x_dev, xq, xsc, wsp):
     return res
 
 
+def stack32b_measurement(dev, wsp, replays=10):
+    """The Qwen3-32B-shaped linear stack at M = 8 (7 drafts + 1): 64 layers
+    of q/k/v/o/gate/up/down plus the LM head 5120 -> 151936, int8 weights
+    (32 GB, tiled layout) drawn on the device, and the matching bf16 stack
+    (64 GB) run through the in-build bf16 GEMM as the two-times-traffic
+    reference.  One step: per layer, quantize_act of its four distinct
+    inputs (q/k/v share one, gate/up share one) and the seven linears; then
+    quantize_act, the LM head with the argmax folded in, and greedy
+    acceptance (bf16: the LM head's fp32 logits, then verify_accept).  The
+    stack never fits the 256 MB Infinity Cache, so no rotation is needed.
+    Each step is one HIP graph replay; the layer inputs are seeded synthetic
+    activations (no decoder-layer glue between the linears)."""
+    import numpy as np
+    import torch
+
+    import synth
+    import w8a8_quantized_verification_amd as w8
+
+    M, G = 8, 7
+    L = synth.QWEN3_32B_LAYERS
+    lins = synth.QWEN3_32B_LAYER
+    head = synth.QWEN3_32B_LM_HEAD
+    t0 = time.perf_counter()
+    wts = []
+    for layer in range(L):
+        wts.append([make_weight(lin.N, lin.K, synth.W_STACK32B, synth.stack_tensor_index(layer, li),
+                                dev, tiled=True, with_bf16=True) for li, lin in enumerate(lins)])
+    lm = make_weight(head.N, head.K, synth.W_STACK32B, synth.stack_tensor_index(L, 0), dev,
+                     tiled=True, with_bf16=True)
+    torch.cuda.synchronize()
+    print(f"[bench] 32B stack drawn and quantized on the device "
+          f"({time.perf_counter() - t0:.1f} s)", file=sys.stderr, flush=True)
+
+    def act(K, index, layer):
+        b = synth.activations_bf16(synth.W_STACK32B, M, K, index=index, outliers=True, layer=layer)
+        return torch.from_numpy(b.view(np.int16).copy()).view(torch.bfloat16).to(dev)
+
+    # the four inputs of each layer: attention (K=5120), o (8192), mlp (5120), down (25600)
+    in_k = (lins[0].K, lins[3].K, lins[4].K, lins[6].K)
+    users = ((0, 1, 2), (3,), (4, 5), (6,))
+    xs = [[act(k, 10_000 + 4 * layer + j, layer) for j, k in enumerate(in_k)] for layer in range(L)]
+    x_lm = act(head.K, 20_000, L)
+    xq = {k: torch.empty(M, k, dtype=torch.int8, device=dev) for k in set(in_k) | {head.K}}
+    xsc = torch.empty(M, dtype=torch.float32, device=dev)
+    ys = [torch.empty(M, lin.N, dtype=torch.bfloat16, device=dev) for lin in lins]
+    draft = torch.from_numpy(synth.draft_ids(synth.W_STACK32B, 1, G, head.N)).to(dev)
+    am = torch.empty(M, dtype=torch.int32, device=dev)
+    al = torch.empty(1, dtype=torch.int32, device=dev)
+    nt = torch.empty(1, dtype=torch.int32, device=dev)
+    logits = torch.empty(M, head.N, dtype=torch.float32, device=dev)
+
+    def w8a8_step():
+        for layer in range(L):
+            for j, k in enumerate(in_k):
+                w8.quantize_act(xs[layer][j], xq=xq[k], x_scale=xsc)
+                for li in users[j]:
+                    wq, ws, _ = wts[layer][li]
+                    w8.linear(xq[k], xsc, wq, ws, y_bf16=ys[li], workspace=wsp)
+        w8.quantize_act(x_lm, xq=xq[head.K], x_scale=xsc)
+        w8.lm_head_argmax(xq[head.K], xsc, lm[0], lm[1], workspace=wsp)
+        w8.accept_from_keys(draft, argmax=am, accept_len=al, next_token=nt, workspace=wsp)
+
+    def bf16_step():
+        for layer in range(L):
+            for j in range(4):
+                for li in users[j]:
+                    w8.bf16_linear(xs[layer][j], wts[layer][li][2], y_bf16=ys[li])
+        w8.bf16_linear(x_lm, lm[2], want_bf16=False, y_f32=logits)
+        w8.verify_accept(logits, draft, argmax=am, accept_len=al, next_token=nt, workspace=wsp)
+
+    t_w8 = graph_time([w8a8_step], replays=replays)
+    t_bf = graph_time([bf16_step], replays=replays)
+    w8_bytes = L * sum(linear_bytes(M, lin.N, lin.K) for lin in lins) + \
+        L * sum(M * k + 4 * M for k in in_k) + lm_head_bytes(M, head.N, head.K, logits=False)
+    bf_bytes = L * sum(2 * lin.N * lin.K + 2 * M * lin.K + 2 * M * lin.N for lin in lins) + \
+        2 * head.N * head.K + 2 * M * head.K + 4 * M * head.N
+    weight_bytes = L * sum(lin.N * lin.K for lin in lins) + head.N * head.K
+    res = {"M": M, "G": G, "layers": L, "int8_weight_bytes": weight_bytes,
+           "w8a8_ms_per_step": round(t_w8 * 1e3, 4),
+           "w8a8_verified_tokens_per_s": round(M / t_w8, 1),
+           "w8a8_GBs": round(w8_bytes / t_w8 / 1e9, 1),
+           "w8a8_frac_of_peak": round(w8_bytes / t_w8 / 1e9 / HBM_PEAK_GBS, 4),
+           "bf16_ms_per_step": round(t_bf * 1e3, 4),
+           "bf16_verified_tokens_per_s": round(M / t_bf, 1),
+           "bf16_GBs": round(bf_bytes / t_bf / 1e9, 1),
+           "time_ratio_bf16_over_w8a8": round(t_bf / t_w8, 3),
+           "timing": f"HIP graph of one whole step, mean of {replays} replays",
+           "launches_per_step": L * (4 + 7) + 3}
+    del wts, lm
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(dev, xs_host, draft, seconds, M):
     """The oracle's verify step on this host's cores, on a bounded sample:
     whole LM-head steps (M=5, K=4096, V=151936) until ``seconds`` have
-    passed (at least 2, at most 100), with int8 weights made by the library
-    (row-major) and copied to the host."""
+    passed (at least 2, at most 100).  The oracle quantizes the weights
+    itself (untimed) from a host copy of the same fp32 draw the GPU copy 0
+    was made from."""
+    import synth
     import oracle
-    wq, ws, _ = make_weight(151936, 4096, 1000, dev, tiled=False)
-    wq = wq.cpu().numpy()
-    ws = ws.cpu().numpy()
+    w = synth.weights_device(synth.W_LM_HEAD, 1000, 151936, 4096, dev).cpu().numpy()
+    wq, ws = oracle.quantize_weight(w)
+    del w
     try:
         from threadpoolctl import threadpool_info
         blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])

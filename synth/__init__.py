@@ -119,6 +119,19 @@ def weight_rows_f32(workload: int, N: int, K: int, rows: np.ndarray,
     return out
 
 
+def weights_device(workload: int, tensor_index: int, N: int, K: int, device,
+                   std: float = 0.02) -> torch.Tensor:
+    """fp32 ``[N][K]`` ~ N(0, std) drawn on a GPU with torch's device
+    generator seeded from (workload, tensor_index).  Used where the host
+    generator is too slow (tens of GB of weights); the values differ from
+    :func:`weights_f32`.  A consumer on the host takes a copy of this tensor."""
+    g = torch.Generator(device=device)
+    g.manual_seed(int(workload) * 1_000_003 + int(tensor_index))
+    w = torch.randn(N, K, generator=g, device=device, dtype=torch.float32)
+    w.mul_(std)
+    return w
+
+
 def draft_ids(workload: int, B: int, G: int, V: int, index: int = 0) -> np.ndarray:
     """Uniform draft ids ``int32[B][G]`` in [0, V)."""
     return rng(workload, T_DRAFT, index).integers(0, V, size=(B, G)).astype(np.int32)
@@ -173,6 +186,13 @@ QWEN3_32B_LAYER = (
 )
 QWEN3_32B_LM_HEAD = Linear("lm_head", 5120, QWEN3_VOCAB)
 QWEN3_32B_LAYERS = 64
+
+
+def stack_tensor_index(layer: int, linear: int) -> int:
+    """Weight tensor id of linear ``linear`` (0..6, in QWEN3_32B_LAYER order)
+    of ``layer`` in the 32B stack; the LM head is ``layer = QWEN3_32B_LAYERS``,
+    ``linear = 0``."""
+    return layer * 8 + linear
 
 # workload ids (the first element of every seed)
 W_TINY = 1        # M=5, K=256, N=512, B=1, G=4
