@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "W8A8 verify GEMM HBM GB/s (% of peak) + verified tokens/s at M=5"
 HBM_PEAK_GBS = 8000.0
+INT8_PEAK_TOPS = 5000.0   # dense int8 MFMA, MI355X
 PMC_FILE = os.path.join(ROOT, "profiles", "gemm_w8a8_lm_head_m5_traffic.txt")
 GEMM_SRC = os.path.join(ROOT, "w8a8_quantized_verification_amd", "csrc", "gemm_w8a8.hip")
 
@@ -49,6 +50,10 @@ def parse_args():
     p.add_argument("--no-stack", action="store_true",
                    help="skip the Qwen3-32B-shaped stack (96 GB of device memory)")
     p.add_argument("--pmc-probe", action="store_true")
+    p.add_argument("--pmc-probe-batched", action="store_true",
+                   help="short fixed run of the 288-row linears for rocprofv3 --pmc")
+    p.add_argument("--ingest-pmc-batched", nargs="+", metavar="DIR",
+                   help="rocprofv3 --pmc output dirs of --pmc-probe-batched runs")
     p.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="turn two rocprofv3 --pmc runs of --pmc-probe into the traffic summary")
     p.add_argument("--ingest-trace", metavar="TRACE_DIR",
@@ -207,10 +212,103 @@ def ingest_trace(trace_dir, command, out_path):
     print("\n".join(lines))
 
 
+BATCHED_SHAPES = ("q", "gate", "down")   # probe order; 4 dispatches each
+BATCHED_PMC_FILE = os.path.join(ROOT, "profiles", "gemm_w8a8_batched_m288_counters.txt")
+BATCHED_SRC = os.path.join(ROOT, "w8a8_quantized_verification_amd", "csrc", "gemm_w8a8_batched.hip")
+
+
+def pmc_probe_batched(dev):
+    """A plain 1 GiB copy (the traffic calibration), then 4 launches of each
+    288-row Qwen3-8B linear in BATCHED_SHAPES, alternating 2 weight copies."""
+    import numpy as np
+    import torch
+
+    import synth
+    import w8a8_quantized_verification_amd as w8
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    del src, dst
+    M = 288
+    for name in BATCHED_SHAPES:
+        lin = next(l for l in synth.QWEN3_8B_LAYER if l.name == name)
+        wl = [make_weight(lin.N, lin.K, synth.W_BATCHED, 7000 + c, dev)[:2] for c in range(2)]
+        x = torch.from_numpy(synth.activations_bf16(synth.W_BATCHED, M, lin.K, outliers=True)
+                             .view(np.int16).copy()).view(torch.bfloat16).to(dev)
+        xq, xs = w8.quantize_act(x)
+        y = torch.empty(M, lin.N, dtype=torch.bfloat16, device=dev)
+        for i in range(4):
+            w8.linear(xq, xs, *wl[i % 2], y_bf16=y)
+        torch.cuda.synchronize()
+        del wl
+    print(json.dumps({"pmc_probe_batched": "done", "shapes": BATCHED_SHAPES}), flush=True)
+
+
+def ingest_pmc_batched(dirs, command):
+    """Per-shape medians of the counters found in the --pmc-probe-batched runs:
+    HBM bytes (FETCH_SIZE/WRITE_SIZE, scaled by the 1 GiB copy as for the
+    LM-head GEMM) against the algorithmic bytes, and MfmaUtil (rocprofv3's
+    derived MFMA-busy percentage) beside the utilisation implied by the
+    kernel durations."""
+    import numpy as np
+
+    import synth
+    M = 288
+    per = {n: {} for n in BATCHED_SHAPES}
+    kname = ""
+    for d in dirs:
+        rows = _csv_rows(d, "counter_collection.csv")
+        for cname in sorted({r["Counter_Name"] for r in rows}):
+            rr = [r for r in rows if r["Counter_Name"] == cname]
+            gem = sorted([r for r in rr if "gemm_w8a8_batched" in r["Kernel_Name"]],
+                         key=lambda r: int(r["Dispatch_Id"]))
+            if len(gem) != 4 * len(BATCHED_SHAPES):
+                raise SystemExit(f"{d}: {cname}: expected {4 * len(BATCHED_SHAPES)} batched "
+                                 f"dispatches, found {len(gem)}")
+            kname = gem[0]["Kernel_Name"]
+            scale = 1.0
+            if cname in ("FETCH_SIZE", "WRITE_SIZE"):
+                copy = [float(r["Counter_Value"]) for r in rr if "copy" in r["Kernel_Name"].lower()]
+                scale = (1 << 30) / (max(copy) * 1024.0) * 1024.0   # KiB -> calibrated bytes
+            for i, n in enumerate(BATCHED_SHAPES):
+                vals = [float(r["Counter_Value"]) * scale for r in gem[4 * i:4 * i + 4]]
+                durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e9
+                        for r in gem[4 * i:4 * i + 4]]
+                per[n][cname] = float(np.median(vals))
+                per[n].setdefault("dur_s", []).extend(durs)
+    lines = ["# Counters of the batched W8A8 GEMM at M=288 (Qwen3-8B linears, tiled int8 weights)",
+             f"# kernel: {kname[:120]}",
+             f"# commands: {command}",
+             "# per shape: medians over 4 dispatches.  FETCH_SIZE/WRITE_SIZE in bytes, calibrated",
+             "# by the probe's 1 GiB copy.  MfmaUtil = 100*sum(SQ_VALU_MFMA_BUSY_CYCLES) /",
+             "# (max(GRBM_GUI_ACTIVE)*SIMD_NUM).  implied_mfma_pct = 2*M*N*K / duration / 5.0 POPS,",
+             "# with the duration taken from the same dispatches under the counter run"]
+    for n in BATCHED_SHAPES:
+        lin = next(l for l in synth.QWEN3_8B_LAYER if l.name == n)
+        alg = linear_bytes(M, lin.N, lin.K)
+        e = per[n]
+        dur = float(np.median(e.pop("dur_s")))
+        lines.append(f"[{n}] N={lin.N} K={lin.K}")
+        lines.append(f"  duration_us_under_counters: {dur * 1e6:.2f}")
+        lines.append(f"  implied_mfma_pct: {100 * 2 * M * lin.N * lin.K / dur / 5.0e15:.2f}")
+        for k, v in sorted(e.items()):
+            lines.append(f"  {k}: {v:.1f}")
+        if "FETCH_SIZE" in e and "WRITE_SIZE" in e:
+            lines.append(f"  algorithmic_bytes: {alg}")
+            lines.append(f"  hbm_over_algorithmic: {(e['FETCH_SIZE'] + e['WRITE_SIZE']) / alg:.3f}")
+    lines.append(f"kernel_source_sha: {file_sha(BATCHED_SRC)}")
+    with open(BATCHED_PMC_FILE, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     args = parse_args()
     if args.ingest_pmc:
         ingest_pmc(args.ingest_pmc[0], args.ingest_pmc[1], args.command)
+        return
+    if args.ingest_pmc_batched:
+        ingest_pmc_batched(args.ingest_pmc_batched, args.command)
         return
     if args.ingest_trace:
         ingest_trace(args.ingest_trace, args.command,
@@ -268,6 +366,9 @@ def main():
         w8.linear(xq, xsc, wq, ws, want_bf16=False, y_f32=logits, workspace=wsp)
         w8.verify_accept(logits, draft, argmax=am, accept_len=al, next_token=nt, workspace=wsp)
 
+    if args.pmc_probe_batched:
+        pmc_probe_batched(dev)
+        return
     if args.pmc_probe:
         # fixed short run for counter collection: a plain 1 GiB copy (the
         # calibration kernel) then 8 LM-head steps
@@ -360,6 +461,50 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+def rotation_copies(N, K):
+    """Distinct weight copies a graph cycles through so that the weights of
+    one pass (>= 600 MB) cannot sit in the 256 MB Infinity Cache."""
+    return int(min(128, max(8, -(-600_000_000 // (N * K)))))
+
+
+def layer_measurement(dev, wsp, M, workload):
+    """The Qwen3-8B decoder-layer linears at M rows: each linear graph-replayed
+    over enough distinct weight copies to defeat the Infinity Cache; GB/s of
+    the algorithmic bytes and int8 TOPS (2*M*N*K) against the 5.0 POPS dense
+    int8 MFMA peak."""
+    import numpy as np
+    import torch
+
+    import synth
+    import w8a8_quantized_verification_amd as w8
+
+    layer = []
+    for li, lin in enumerate(synth.QWEN3_8B_LAYER):
+        nc = rotation_copies(lin.N, lin.K)
+        wl = [make_weight(lin.N, lin.K, workload, 2000 + 200 * li + c, dev)[:2] for c in range(nc)]
+        x = torch.from_numpy(synth.activations_bf16(workload, M, lin.K, outliers=True)
+                             .view(np.int16).copy()).view(torch.bfloat16).to(dev)
+        lxq, lxs = w8.quantize_act(x)
+        y = torch.empty(M, lin.N, dtype=torch.bfloat16, device=dev)
+        fns = [(lambda c=c: w8.linear(lxq, lxs, *wl[c], y_bf16=y, workspace=wsp)) for c in range(nc)]
+        t = graph_time(fns, replays=10) / nc
+        b = linear_bytes(M, lin.N, lin.K)
+        tops = 2 * M * lin.N * lin.K / t / 1e12
+        layer.append({"name": lin.name, "N": lin.N, "K": lin.K, "copies": nc,
+                      "us": round(t * 1e6, 2), "GBs": round(b / t / 1e9, 1),
+                      "TOPS": round(tops, 1), "mfma_frac": round(tops / INT8_PEAK_TOPS, 4)})
+        del wl
+    tot_b = sum(linear_bytes(M, l.N, l.K) for l in synth.QWEN3_8B_LAYER)
+    tot_ops = sum(2 * M * l.N * l.K for l in synth.QWEN3_8B_LAYER)
+    tot_t = sum(e["us"] for e in layer) / 1e6
+    return {"M": M, "per_linear": layer, "sum_us": round(tot_t * 1e6, 2),
+            "aggregate_GBs": round(tot_b / tot_t / 1e9, 1),
+            "aggregate_frac": round(tot_b / tot_t / 1e9 / HBM_PEAK_GBS, 4),
+            "aggregate_TOPS": round(tot_ops / tot_t / 1e12, 1),
+            "aggregate_mfma_frac": round(tot_ops / tot_t / 1e12 / INT8_PEAK_TOPS, 4),
+            "timing": "HIP graph over the rotating weight copies, mean of 10 replays"}
+
+
 def extra_measurements(dev, copies, x_dev, xq, xsc, wsp):
     """Secondary figures: Qwen3-8B decoder-layer linears at M=5 (8 rotating
     copies of each weight, graph-replayed), the row-major layout and the
@@ -372,27 +517,8 @@ def extra_measurements(dev, copies, x_dev, xq, xsc, wsp):
 
     M = 5
     res = {}
-    nc = 8
-    layer = []
-    for li, lin in enumerate(synth.QWEN3_8B_LAYER):
-        wl = [make_weight(lin.N, lin.K, synth.W_LAYER_M5, 2000 + 10 * li + c, dev)[:2]
-              for c in range(nc)]
-        x = torch.from_numpy(synth.activations_bf16(synth.W_LAYER_M5, M, lin.K, outliers=True)
-                             .view(np.int16).copy()).view(torch.bfloat16).to(dev)
-        lxq, lxs = w8.quantize_act(x)
-        y = torch.empty(M, lin.N, dtype=torch.bfloat16, device=dev)
-        fns = [(lambda c=c: w8.linear(lxq, lxs, *wl[c], y_bf16=y, workspace=wsp)) for c in range(nc)]
-        t = graph_time(fns, replays=20) / nc
-        b = linear_bytes(M, lin.N, lin.K)
-        layer.append({"name": lin.name, "N": lin.N, "K": lin.K, "us": round(t * 1e6, 2),
-                      "GBs": round(b / t / 1e9, 1)})
-        del wl
-    tot_b = sum(linear_bytes(M, l.N, l.K) for l in synth.QWEN3_8B_LAYER)
-    tot_t = sum(e["us"] for e in layer) / 1e6
-    res["qwen3_8b_layer_linears_m5"] = {"per_linear": layer, "sum_us": round(tot_t * 1e6, 2),
-                                        "aggregate_GBs": round(tot_b / tot_t / 1e9, 1),
-                                        "aggregate_frac": round(tot_b / tot_t / 1e9 / HBM_PEAK_GBS, 4),
-                                        "timing": "HIP graph of 8 launches over 8 weight copies"}
+    res["qwen3_8b_layer_linears_m5"] = layer_measurement(dev, wsp, M, synth.W_LAYER_M5)
+    res["qwen3_8b_layer_linears_m288"] = layer_measurement(dev, wsp, 288, synth.W_BATCHED)
 
     K, V = 4096, synth.QWEN3_VOCAB
     lg = torch.empty(M, V, dtype=torch.float32, device=dev)

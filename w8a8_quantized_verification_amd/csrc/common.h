@@ -57,13 +57,10 @@ hipError_t w8a8_launch_tile_weight(const int8_t* wq, int64_t N, int64_t K, int8_
                                    hipStream_t stream);
 
 size_t w8a8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, bool tiled);
-size_t w8a8_gemm_batched_workspace_bytes(int64_t M, int64_t N, int64_t K);
-// workspace == nullptr: no split-K (one k range per tile)
 hipError_t w8a8_launch_gemm_batched(const int8_t* xq, const float* x_scale, const int8_t* wq,
                                     const float* w_scale, int64_t M, int64_t N, int64_t K,
                                     bool tiled, uint16_t* y_bf16, float* y_f32, int32_t* acc,
-                                    void* keys, int subkeys, int key_stride, void* workspace,
-                                    hipStream_t stream);
+                                    void* keys, int subkeys, int key_stride, hipStream_t stream);
 size_t w8a8_lm_head_workspace_bytes(int64_t M);
 hipError_t w8a8_launch_lm_head_argmax(const int8_t* xq, const float* x_scale,
                                       const int8_t* wq_tiled, const float* w_scale, int64_t M,

@@ -347,7 +347,7 @@ static SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, bool tiled, bool 
 size_t w8a8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, bool tiled) {
   using namespace w8a8;
   if (M <= 0 || N <= 0) return 0;
-  if (M > kSkinnyMaxRows) return w8a8_gemm_batched_workspace_bytes(M, N, K);
+  if (M > kSkinnyMaxRows) return 0;  // the batched kernel needs none
   const SkinnyPlan p = plan_skinny(M, N, K, tiled);
   if (p.split == 1) return 0;
   const size_t part = (size_t)M * (size_t)N * sizeof(int32_t);
@@ -403,9 +403,7 @@ hipError_t w8a8_launch_gemm(const int8_t* xq, const float* x_scale, const int8_t
   if (M == 0 || N == 0) return hipSuccess;
   if (M > kSkinnyMaxRows)
     return w8a8_launch_gemm_batched(xq, x_scale, wq, w_scale, M, N, K, tiled, y_bf16, y_f32, acc,
-                                    nullptr, 0, 0,
-                                    w8a8_gemm_batched_workspace_bytes(M, N, K) ? workspace : nullptr,
-                                    stream);
+                                    nullptr, 0, 0, stream);
   const SkinnyPlan p = plan_skinny(M, N, K, tiled);
   GemmArgs g = make_args(p, xq, x_scale, wq, w_scale, M, N, K, y_bf16, y_f32, acc);
   if (p.split > 1) {
@@ -434,7 +432,7 @@ hipError_t w8a8_launch_lm_head_argmax(const int8_t* xq, const float* x_scale,
   if (M == 0) return hipSuccess;
   if (M > kSkinnyMaxRows)
     return w8a8_launch_gemm_batched(xq, x_scale, wq_tiled, w_scale, M, V, K, true, nullptr, logits,
-                                    nullptr, keys, kArgmaxSubkeys, kArgmaxKeyStride, nullptr, stream);
+                                    nullptr, keys, kArgmaxSubkeys, kArgmaxKeyStride, stream);
   const SkinnyPlan p = plan_skinny(M, V, K, true, true);
   GemmArgs g = make_args(p, xq, x_scale, wq_tiled, w_scale, M, V, K, nullptr, logits, nullptr);
   g.keys = reinterpret_cast<unsigned long long*>(keys);
