@@ -16,6 +16,9 @@ the pages by eye:
 * the exact int8 x int8 -> int32 product (``gemm.int8_gemm``);
 * the dequant epilogue to fp32 and bf16 (``gemm.dequant``);
 * LM-head argmax and greedy acceptance (``accept``);
+* stochastic verification at temperature T > 0: softmax of the dequantized
+  logits, acceptance of each draft with its probability, residual or bonus
+  sampling by inverse CDF (``sample``);
 * the bf16 reference layer and the weight-traffic closed forms
   (``reference``).
 
@@ -40,6 +43,7 @@ from .bf16 import bf16_to_f32, f32_to_bf16
 from .quant import quantize_rows, quantize_act, quantize_weight
 from .gemm import int8_gemm, dequant, w8a8_linear, INT32_MAX_K
 from .accept import argmax_rows, greedy_accept, verify_accept
+from .sample import exp_f32, fixed_weights, verify_sample
 from .reference import (bf16_reference_logits, w8a8_linear_bytes,
                         bf16_linear_bytes, weight_bytes_int8, weight_bytes_bf16)
 
@@ -48,5 +52,5 @@ __all__ = [
     "quantize_weight", "int8_gemm", "dequant", "w8a8_linear", "INT32_MAX_K",
     "argmax_rows", "greedy_accept", "verify_accept", "bf16_reference_logits",
     "w8a8_linear_bytes", "bf16_linear_bytes", "weight_bytes_int8",
-    "weight_bytes_bf16",
+    "weight_bytes_bf16", "exp_f32", "fixed_weights", "verify_sample",
 ]
