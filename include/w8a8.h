@@ -267,6 +267,69 @@ w8a8_status w8a8_lm_head_verify(const int8_t* xq, const float* x_scale,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Stochastic verification at temperature T > 0: speculative sampling of a
+ * block of single-token drafts on the fp32 dequantized logits.
+ *
+ * Pages: the logits are restored to high precision before softmax and the
+ * rejection-sampling test, so the lossless guarantee of speculative decoding
+ * holds ([de] §2 "De-Quantisierung"; [it] §2 item 3; [fr] §2
+ * "Échantillonnage de rejet"; [ja] §2.2 item 4); T = 0 .. 1 ([de] §3,
+ * [ja] §4).  The drafter's distribution at each position is taken to be a
+ * point mass on its draft (N-gram or greedy self-drafting).  With rows laid
+ * out as in w8a8_verify_accept, for each sequence b:
+ *   p_i = softmax(logits[b*(G+1)+i] / T), in the exact fixed-point form
+ *         below;
+ *   positions i = 0..G-1 in order: accept draft[b][i] with probability
+ *         p_i(draft), decided by u_accept[b][i]; stop at the first rejection;
+ *   accept_len[b] = n, the number accepted;
+ *   next_token[b] ~ p_n with draft[b][n] removed and renormalised when
+ *         n < G, else ~ p_G; decided by u_sample[b].
+ * Exact form (every step one IEEE fp32 operation, no contraction):
+ *   m = max_j y_j; x_j = max(fp32(fp32(y_j - m) * fp32(1/T)), -32);
+ *   e_j = exp_f32(x_j): k = rint(x*log2e), r = (x - k*ln2_hi) - k*ln2_lo,
+ *         degree-7 Taylor polynomial in Horner form at r, times 2^k;
+ *   W_j = floor(e_j * 2^40) (uint64), Z = sum_j W_j (exact);
+ *   accept iff u_accept * Z < W(draft) * 2^32 (exact integer compare);
+ *   next_token = first j whose inclusive prefix sum of W (draft removed)
+ *         exceeds floor(u_sample * Z' / 2^64), Z' the total.
+ * Draft ids outside [0, V) have weight 0: never accepted, nothing removed.
+ * The same inputs give the same outputs on any device.
+ *
+ * logits     [B*(G+1)][V] fp32, finite, 4-byte aligned.
+ * draft      [B][G] int32; u_accept [B][G] uint32 (both may be NULL when
+ *            G == 0); u_sample [B] uint64, 8-byte aligned: uniform random
+ *            words drawn by the caller.
+ * accept_len [B], next_token [B] int32 outputs.
+ * temperature: finite, > 0, with 1/T finite in fp32.
+ * workspace: at least w8a8_verify_sample_workspace_bytes(B, G, V) bytes,
+ *            256-byte aligned; no initial contents needed.
+ * Requires 1 <= V <= W8A8_MAX_SAMPLE_VOCAB (sums of W stay below 2^63) and
+ * 0 <= G <= W8A8_MAX_DRAFT.
+ */
+#define W8A8_MAX_SAMPLE_VOCAB (1 << 23)
+size_t      w8a8_verify_sample_workspace_bytes(int64_t B, int64_t G, int64_t V);
+w8a8_status w8a8_verify_sample(const float* logits, int64_t V,
+                               const int32_t* draft, int64_t B, int64_t G,
+                               float temperature, const uint32_t* u_accept,
+                               const uint64_t* u_sample,
+                               int32_t* accept_len, int32_t* next_token,
+                               void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/*
+ * The fixed-point softmax numerators W_j of w8a8_verify_sample for every
+ * element of R rows: weights[r][j] = W_j of row r at temperature T (the
+ * same kernels and values the sampler uses).
+ * logits [R][V] fp32; weights [R][V] uint64 output, 8-byte aligned;
+ * workspace: at least w8a8_sample_weights_workspace_bytes(R, V) bytes.
+ */
+size_t      w8a8_sample_weights_workspace_bytes(int64_t R, int64_t V);
+w8a8_status w8a8_sample_weights(const float* logits, int64_t R, int64_t V,
+                                float temperature, uint64_t* weights,
+                                void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/*
  * The BF16 verifier's linear at the same shapes, as the weight-traffic
  * reference (BF16 weights move twice the bytes of INT8 ones: [zh] abstract;
  * [de] §3 item 4, latency M*2B/BW against M*1B/BW).

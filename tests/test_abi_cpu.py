@@ -115,6 +115,38 @@ def test_verify_accept_validation(lib):
     assert va(lib, B=0, logits=None, draft=None, al=None, nt=None, work=None) == OK
 
 
+def vs(lib, logits=A16, V=151936, draft=A16, B=1, G=4, T=1.0, ua=A16, us=A16, al=A16, nt=A16,
+       work=A16, wbytes=None):
+    if wbytes is None:
+        wbytes = lib.w8a8_verify_sample_workspace_bytes(B, G, V)
+    return lib.w8a8_verify_sample(logits, V, draft, B, G, T, ua, us, al, nt, work, wbytes, None)
+
+
+def test_verify_sample_validation(lib):
+    assert lib.w8a8_verify_sample_workspace_bytes(1, 4, 151936) > 0
+    assert lib.w8a8_verify_sample_workspace_bytes(1, 4, (1 << 23) + 1) == 0
+    for bad_t in (0.0, -1.0, float("inf"), float("nan"), 1e-40):
+        assert vs(lib, T=bad_t) == INVALID
+    assert vs(lib, V=(1 << 23) + 1, wbytes=1 << 30) == INVALID
+    assert vs(lib, G=256) == INVALID
+    assert vs(lib, ua=None) == INVALID
+    assert vs(lib, us=None) == INVALID
+    assert vs(lib, us=A16 + 4) == INVALID
+    assert vs(lib, nt=None) == INVALID
+    assert vs(lib, work=None) == WORKSPACE
+    assert vs(lib, wbytes=8) == WORKSPACE
+    assert vs(lib, work=A16 + 16) == INVALID
+    assert vs(lib, B=0, logits=None, draft=None, ua=None, us=None, al=None, nt=None,
+              work=None) == OK
+    f = lib.w8a8_sample_weights
+    need = lib.w8a8_sample_weights_workspace_bytes(3, 1000)
+    assert need > 0
+    assert f(A16, 3, 1000, 1.0, A16 + 4, A16, need, None) == INVALID
+    assert f(A16, 3, 1000, 0.0, A16, A16, need, None) == INVALID
+    assert f(A16, 3, 1000, 1.0, A16, A16, 8, None) == WORKSPACE
+    assert f(None, 0, 1000, 1.0, None, None, 0, None) == OK
+
+
 def test_bf16_linear_validation(lib):
     f = lib.w8a8_bf16_linear
     assert f(A16, A16b, 17, 512, 256, A16, None, None) == UNSUPPORTED

@@ -4,13 +4,15 @@ The kernels live in libw8a8.so (HIP for gfx950, C ABI in include/w8a8.h);
 this package is its thin torch-tensor binding.  Build the library with
 ``python -m w8a8_quantized_verification_amd.build``.
 """
-from .api import (W8A8Error, Workspace, bf16_linear, linear, linear_workspace_bytes,
-                  accept_from_keys, lm_head_argmax, lm_head_verify, quantize_act, quantize_weight, tile_weight, tiled_shape, verify_accept,
-                  verify_accept_workspace_bytes)
+from .api import (W8A8Error, Workspace, accept_from_keys, bf16_linear, linear,
+                  linear_workspace_bytes, lm_head_argmax, lm_head_verify, quantize_act,
+                  quantize_weight, sample_weights, tile_weight, tiled_shape, verify_accept,
+                  verify_accept_workspace_bytes, verify_sample, verify_sample_workspace_bytes)
 
 __all__ = [
     "W8A8Error", "Workspace", "accept_from_keys", "bf16_linear", "linear", "linear_workspace_bytes",
     "lm_head_argmax", "lm_head_verify",
     "quantize_act", "quantize_weight", "tile_weight", "tiled_shape", "verify_accept",
-    "verify_accept_workspace_bytes",
+    "verify_accept_workspace_bytes", "verify_sample", "verify_sample_workspace_bytes",
+    "sample_weights",
 ]

@@ -16,7 +16,8 @@ __all__ = [
     "W8A8Error", "quantize_act", "quantize_weight", "tile_weight", "tiled_shape", "linear",
     "linear_workspace_bytes",
     "verify_accept", "verify_accept_workspace_bytes", "lm_head_verify", "lm_head_argmax",
-    "accept_from_keys", "bf16_linear", "Workspace",
+    "accept_from_keys", "bf16_linear", "Workspace", "verify_sample",
+    "verify_sample_workspace_bytes", "sample_weights",
 ]
 
 
@@ -287,3 +288,63 @@ def bf16_linear(x, w, *, want_bf16=True, want_f32=False, y_bf16=None, y_f32=None
     check(lib().w8a8_bf16_linear(_ptr(x), _ptr(w), M, N, K, _ptr(y_bf16), _ptr(y_f32),
                                  _stream(dev)))
     return y_bf16, y_f32
+
+
+def _need_bits(t, name, dtypes, ndim, device):
+    """A tensor of random words: any of the given dtypes (same bits), on
+    ``device``, contiguous, ``ndim`` dimensions."""
+    if not isinstance(t, torch.Tensor) or t.dtype not in dtypes:
+        raise TypeError(f"{name} must be a tensor of dtype {' or '.join(map(str, dtypes))}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+    if t.dim() != ndim or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {ndim}-D tensor")
+
+
+def verify_sample_workspace_bytes(B: int, G: int, V: int) -> int:
+    return int(lib().w8a8_verify_sample_workspace_bytes(B, G, V))
+
+
+def verify_sample(logits, draft, temperature: float, u_accept, u_sample, *, accept_len=None,
+                  next_token=None, workspace: Workspace | None = None):
+    """Stochastic verification at temperature ``T > 0`` of int32
+    ``draft[B][G]`` on fp32 ``logits[B*(G+1)][V]``: each draft is accepted
+    with its softmax probability (decided by the uint32 words
+    ``u_accept[B][G]``), the next token is drawn from the residual or the
+    bonus row (decided by the uint64 words ``u_sample[B]``).  int32/int64
+    tensors holding the same bits are accepted for the random words.
+    Returns ``(accept_len, next_token)``."""
+    _need(logits, "logits", torch.float32, 2)
+    dev = logits.device
+    _need(draft, "draft", torch.int32, 2, dev)
+    B, G = draft.shape
+    R, V = logits.shape
+    if R != B * (G + 1):
+        raise ValueError(f"logits must have B*(G+1) = {B * (G + 1)} rows (got {R})")
+    _need_bits(u_accept, "u_accept", (torch.uint32, torch.int32), 2, dev)
+    _need_bits(u_sample, "u_sample", (torch.uint64, torch.int64), 1, dev)
+    if tuple(u_accept.shape) != (B, G) or tuple(u_sample.shape) != (B,):
+        raise ValueError("u_accept must be [B][G] and u_sample [B]")
+    accept_len = _out(accept_len, (B,), torch.int32, dev, "accept_len")
+    next_token = _out(next_token, (B,), torch.int32, dev, "next_token")
+    need = verify_sample_workspace_bytes(B, G, V)
+    ws = (workspace or _default_ws).get(need, dev, use="verify")
+    check(lib().w8a8_verify_sample(_ptr(logits), V, _ptr(draft), B, G, float(temperature),
+                                   _ptr(u_accept), _ptr(u_sample), _ptr(accept_len),
+                                   _ptr(next_token), _ptr(ws), 0 if ws is None else ws.numel(),
+                                   _stream(dev)))
+    return accept_len, next_token
+
+
+def sample_weights(logits, temperature: float, *, weights=None, workspace: Workspace | None = None):
+    """The fixed-point softmax numerators (uint64 bits in an int64 tensor
+    ``[R][V]``) that :func:`verify_sample` draws from."""
+    _need(logits, "logits", torch.float32, 2)
+    dev = logits.device
+    R, V = logits.shape
+    weights = _out(weights, (R, V), torch.int64, dev, "weights")
+    need = int(lib().w8a8_sample_weights_workspace_bytes(R, V))
+    ws = (workspace or _default_ws).get(need, dev, use="verify")
+    check(lib().w8a8_sample_weights(_ptr(logits), R, V, float(temperature), _ptr(weights),
+                                    _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev)))
+    return weights

@@ -3,6 +3,7 @@
 // contract of each call are in include/w8a8.h.
 #include "../../include/w8a8.h"
 
+#include <cmath>
 #include <cstdio>
 #include <cstring>
 #include <string>
@@ -299,6 +300,82 @@ w8a8_status w8a8_bf16_linear(const uint16_t* x_bf16, const uint16_t* w_bf16, int
     return fail(W8A8_ERR_INVALID_ARG, fn, "pointer misaligned");
   return hip_status(w8a8_launch_bf16_gemm(x_bf16, w_bf16, M, N, K, y_bf16, y_f32,
                                           reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
+
+// ---- stochastic verification (T > 0) ----
+
+static w8a8_status check_sample_common(const char* fn, const float* logits, int64_t R, int64_t V,
+                                       float temperature, float* inv_t) {
+  if (V < 1 || V > W8A8_MAX_SAMPLE_VOCAB)
+    return fail(W8A8_ERR_INVALID_ARG, fn, "V out of range [1, 2^23]");
+  if (R * ((V + 2047) / 2048) > INT32_MAX)
+    return fail(W8A8_ERR_INVALID_ARG, fn, "too many logits rows for one launch");
+  if (!(std::isfinite(temperature) && temperature > 0.0f))
+    return fail(W8A8_ERR_INVALID_ARG, fn, "temperature must be finite and > 0");
+  const float inv = 1.0f / temperature;   // one correctly rounded fp32 division
+  if (!std::isfinite(inv)) return fail(W8A8_ERR_INVALID_ARG, fn, "1/temperature overflows fp32");
+  if (!logits) return fail(W8A8_ERR_INVALID_ARG, fn, "required pointer is NULL");
+  if (!aligned(logits, 4)) return fail(W8A8_ERR_INVALID_ARG, fn, "pointer misaligned (4 bytes)");
+  *inv_t = inv;
+  return W8A8_OK;
+}
+
+size_t w8a8_sample_weights_workspace_bytes(int64_t R, int64_t V) {
+  if (R <= 0 || R > kMaxRows || V <= 0 || V > W8A8_MAX_SAMPLE_VOCAB) return 0;
+  return w8a8_sample_workspace_bytes_impl(R, V);
+}
+
+w8a8_status w8a8_sample_weights(const float* logits, int64_t R, int64_t V, float temperature,
+                                uint64_t* weights, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  static const char* fn = "w8a8_sample_weights";
+  g_last_error.clear();
+  if (R < 0 || R > kMaxRows) return fail(W8A8_ERR_INVALID_ARG, fn, "R out of range");
+  if (R == 0) return W8A8_OK;
+  float inv_t = 0.0f;
+  if (w8a8_status st = check_sample_common(fn, logits, R, V, temperature, &inv_t)) return st;
+  if (!weights) return fail(W8A8_ERR_INVALID_ARG, fn, "required pointer is NULL");
+  if (!aligned(weights, 8)) return fail(W8A8_ERR_INVALID_ARG, fn, "weights must be 8-byte aligned");
+  if (!workspace || workspace_bytes < w8a8_sample_workspace_bytes_impl(R, V))
+    return fail(W8A8_ERR_WORKSPACE, fn, "workspace NULL or smaller than w8a8_sample_weights_workspace_bytes()");
+  if (!aligned(workspace, 256)) return fail(W8A8_ERR_INVALID_ARG, fn, "workspace must be 256-byte aligned");
+  return hip_status(w8a8_launch_sample_weights(logits, R, V, inv_t, weights, workspace,
+                                               reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
+size_t w8a8_verify_sample_workspace_bytes(int64_t B, int64_t G, int64_t V) {
+  if (B <= 0 || B > kMaxRows || G < 0 || G > W8A8_MAX_DRAFT || V <= 0 ||
+      V > W8A8_MAX_SAMPLE_VOCAB)
+    return 0;
+  return w8a8_sample_workspace_bytes_impl(B * (G + 1), V);
+}
+
+w8a8_status w8a8_verify_sample(const float* logits, int64_t V, const int32_t* draft, int64_t B,
+                               int64_t G, float temperature, const uint32_t* u_accept,
+                               const uint64_t* u_sample, int32_t* accept_len,
+                               int32_t* next_token, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  static const char* fn = "w8a8_verify_sample";
+  g_last_error.clear();
+  if (B < 0 || B > kMaxRows) return fail(W8A8_ERR_INVALID_ARG, fn, "B out of range");
+  if (G < 0 || G > W8A8_MAX_DRAFT) return fail(W8A8_ERR_INVALID_ARG, fn, "G out of range [0, 255]");
+  if (B == 0) return W8A8_OK;
+  float inv_t = 0.0f;
+  if (w8a8_status st = check_sample_common(fn, logits, B * (G + 1), V, temperature, &inv_t))
+    return st;
+  if (!u_sample || !accept_len || !next_token || (G > 0 && (!draft || !u_accept)))
+    return fail(W8A8_ERR_INVALID_ARG, fn, "required pointer is NULL");
+  if (!aligned(draft, 4) || !aligned(u_accept, 4) || !aligned(accept_len, 4) ||
+      !aligned(next_token, 4))
+    return fail(W8A8_ERR_INVALID_ARG, fn, "pointer misaligned (4 bytes)");
+  if (!aligned(u_sample, 8)) return fail(W8A8_ERR_INVALID_ARG, fn, "u_sample must be 8-byte aligned");
+  if (!workspace || workspace_bytes < w8a8_sample_workspace_bytes_impl(B * (G + 1), V))
+    return fail(W8A8_ERR_WORKSPACE, fn, "workspace NULL or smaller than w8a8_verify_sample_workspace_bytes()");
+  if (!aligned(workspace, 256)) return fail(W8A8_ERR_INVALID_ARG, fn, "workspace must be 256-byte aligned");
+  return hip_status(w8a8_launch_verify_sample(logits, V, draft, B, G, inv_t, u_accept, u_sample,
+                                              accept_len, next_token, workspace,
+                                              reinterpret_cast<hipStream_t>(stream)), fn);
 }
 
 }  // extern "C"

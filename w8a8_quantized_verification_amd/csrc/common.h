@@ -91,3 +91,11 @@ hipError_t w8a8_launch_accept_keys(unsigned long long* keys, int subkeys, int ke
 
 hipError_t w8a8_launch_bf16_gemm(const uint16_t* x, const uint16_t* w, int64_t M, int64_t N,
                                  int64_t K, uint16_t* y_bf16, float* y_f32, hipStream_t stream);
+
+size_t w8a8_sample_workspace_bytes_impl(int64_t R, int64_t V);
+hipError_t w8a8_launch_sample_weights(const float* logits, int64_t R, int64_t V, float inv_t,
+                                      uint64_t* weights, void* workspace, hipStream_t stream);
+hipError_t w8a8_launch_verify_sample(const float* logits, int64_t V, const int32_t* draft,
+                                     int64_t B, int64_t G, float inv_t, const uint32_t* u_accept,
+                                     const uint64_t* u_sample, int32_t* accept_len,
+                                     int32_t* next_token, void* workspace, hipStream_t stream);
