@@ -3,23 +3,27 @@
 
 Headline workload: LM-head verification at M = 5 (4 drafts + 1) — hidden
 4096, vocabulary 151936 (Qwen3-8B shapes), int8 per-output-channel weights
-in the tiled layout, one verify step = quantize_act -> w8a8_linear (fp32
-logits) -> verify_accept (argmax over the vocabulary + greedy acceptance of
-the 4 drafts).  It is the M = 5 workload that runs every step of the path.
-Two copies of the 622 MB int8 LM head alternate between steps so that no
-step finds its weights in the 256 MB Infinity Cache.
+in the tiled layout.  One verify step = quantize_act -> lm_head_argmax (the
+LM-head W8A8 linear with the row argmax folded into its epilogue) ->
+accept_from_keys (greedy acceptance of the 4 drafts).  Two copies of the
+622 MB int8 LM head alternate between steps so that no step finds its
+weights in the 256 MB Infinity Cache.
 
 Printed: one JSON line with verified tokens/s (value; eager launches, K
 timed steps between synchronizations), the roofline of the dominant kernel
 (the LM-head GEMM: algorithmic bytes per launch over its HIP-event-timed
-average duration, against 8 TB/s), the CPU oracle timed on this host on a
-bounded sample, and secondary figures: the same step replayed as a HIP
-graph, the Qwen3-8B decoder-layer linears at M = 5 (graph-replayed, weights
-rotated past the cache), the row-major weight layout, and the in-build bf16
-GEMM at the LM-head shape as the two-times-traffic reference.
+average duration, against 8 TB/s; HBM traffic from the committed rocprofv3
+counters), the CPU oracle timed on this host on a bounded sample, and
+secondary figures ("extra"): the step as a HIP graph and through the
+separate calls; the Qwen3-8B decoder-layer linears at M = 5 and M = 288
+(TOPS and MFMA fraction); the row-major weight layout; the in-build bf16
+GEMM at the LM-head shape (two-times-traffic reference); stochastic
+verification at T = 1; the Qwen3-32B-shaped stack at M = 8 (int8 and bf16).
 
     python bench.py [--steps 200] [--warmup 20] [--no-cpu-baseline] [--no-extra]
-    python bench.py --pmc-probe     # a short fixed run for rocprofv3 --pmc
+                    [--no-stack]
+    python bench.py --pmc-probe           # short fixed runs for rocprofv3 --pmc
+    python bench.py --pmc-probe-batched
 """
 from __future__ import annotations
 
@@ -555,6 +559,34 @@ def extra_measurements(dev, copies, x_dev, xq, xsc, wsp):
                                         "w8a8_tiled_us": round(t_tl * 1e6, 2),
                                         "time_ratio_bf16_over_w8a8": round(t_bf / t_tl, 3)}
     del rm
+
+    # stochastic verification at T = 1 on the same LM head: quantize_act ->
+    # linear (fp32 logits) -> verify_sample, and verify_sample alone
+    G, B = M - 1, 1
+    r = synth.rng(synth.W_LM_HEAD, 40, 0)
+    ua = torch.from_numpy(r.integers(0, 1 << 32, size=(B, G), dtype=np.uint64)
+                          .astype(np.uint32).view(np.int32)).to(dev)
+    us = torch.from_numpy(r.integers(0, 1 << 64, size=B, dtype=np.uint64).view(np.int64)).to(dev)
+    draft = torch.from_numpy(synth.draft_ids(synth.W_LM_HEAD, B, G, V)).to(dev)
+    al = torch.empty(B, dtype=torch.int32, device=dev)
+    nt = torch.empty(B, dtype=torch.int32, device=dev)
+
+    def stoch_step(i):
+        w8.quantize_act(x_dev[i % len(x_dev)], xq=xq, x_scale=xsc)
+        w8.linear(xq, xsc, copies[i % 2][0], copies[i % 2][1], want_bf16=False, y_f32=lg,
+                  workspace=wsp)
+        w8.verify_sample(lg, draft, 1.0, ua, us, accept_len=al, next_token=nt, workspace=wsp)
+
+    t_st = graph_time([lambda: stoch_step(0), lambda: stoch_step(1)], replays=50) / 2
+    t_vs = graph_time([lambda: w8.verify_sample(lg, draft, 1.0, ua, us, accept_len=al,
+                                                next_token=nt, workspace=wsp)] * 8,
+                      replays=50) / 8
+    res["stochastic_step_m5_t1"] = {
+        "ms_per_step": round(t_st * 1e3, 5), "verified_tokens_per_s": round(M / t_st, 1),
+        "verify_sample_us": round(t_vs * 1e6, 2),
+        "verify_sample_logit_GBs": round(4 * M * V / t_vs / 1e9, 1),
+        "step": "quantize_act + LM-head linear (fp32 logits) + verify_sample (T=1)",
+        "timing": "HIP graph, 2 weight copies alternating; verify_sample alone: 8 launches"}
     return res
 
 
@@ -563,13 +595,18 @@ def stack32b_measurement(dev, wsp, replays=10):
     of q/k/v/o/gate/up/down plus the LM head 5120 -> 151936, int8 weights
     (32 GB, tiled layout) drawn on the device, and the matching bf16 stack
     (64 GB) run through the in-build bf16 GEMM as the two-times-traffic
-    reference.  One step: per layer, quantize_act of its four distinct
-    inputs (q/k/v share one, gate/up share one) and the seven linears; then
+    reference.  q/k/v and gate/up are stored fused: each layer holds one
+    [q;k;v] and one [gate;up] weight (their output channels stacked; per-
+    channel quantization makes the codes and scales those of the separate
+    matrices), so one launch covers each group.  One step: per layer,
+    quantize_act of its four distinct inputs and its linears; then
     quantize_act, the LM head with the argmax folded in, and greedy
     acceptance (bf16: the LM head's fp32 logits, then verify_accept).  The
     stack never fits the 256 MB Infinity Cache, so no rotation is needed.
     Each step is one HIP graph replay; the layer inputs are seeded synthetic
-    activations (no decoder-layer glue between the linears)."""
+    activations (no decoder-layer glue between the linears).  The same step
+    is also timed with the seven linears launched separately (views into
+    the fused weights)."""
     import numpy as np
     import torch
 
@@ -580,11 +617,19 @@ def stack32b_measurement(dev, wsp, replays=10):
     L = synth.QWEN3_32B_LAYERS
     lins = synth.QWEN3_32B_LAYER
     head = synth.QWEN3_32B_LM_HEAD
+    groups = ((0, 1, 2), (3,), (4, 5), (6,))   # [q;k;v], o, [gate;up], down
     t0 = time.perf_counter()
-    wts = []
+    wts = []     # per layer, per group: (wq tiled, w_scale, w bf16)
     for layer in range(L):
-        wts.append([make_weight(lin.N, lin.K, synth.W_STACK32B, synth.stack_tensor_index(layer, li),
-                                dev, tiled=True, with_bf16=True) for li, lin in enumerate(lins)])
+        row = []
+        for grp in groups:
+            w = torch.cat([synth.weights_device(synth.W_STACK32B,
+                                                synth.stack_tensor_index(layer, li),
+                                                lins[li].N, lins[li].K, dev) for li in grp])
+            wq, ws = w8.quantize_weight(w, tiled=True)
+            row.append((wq, ws, w.to(torch.bfloat16)))
+            del w
+        wts.append(row)
     lm = make_weight(head.N, head.K, synth.W_STACK32B, synth.stack_tensor_index(L, 0), dev,
                      tiled=True, with_bf16=True)
     torch.cuda.synchronize()
@@ -595,40 +640,65 @@ def stack32b_measurement(dev, wsp, replays=10):
         b = synth.activations_bf16(synth.W_STACK32B, M, K, index=index, outliers=True, layer=layer)
         return torch.from_numpy(b.view(np.int16).copy()).view(torch.bfloat16).to(dev)
 
-    # the four inputs of each layer: attention (K=5120), o (8192), mlp (5120), down (25600)
-    in_k = (lins[0].K, lins[3].K, lins[4].K, lins[6].K)
-    users = ((0, 1, 2), (3,), (4, 5), (6,))
+    in_k = tuple(lins[g[0]].K for g in groups)
     xs = [[act(k, 10_000 + 4 * layer + j, layer) for j, k in enumerate(in_k)] for layer in range(L)]
     x_lm = act(head.K, 20_000, L)
     xq = {k: torch.empty(M, k, dtype=torch.int8, device=dev) for k in set(in_k) | {head.K}}
     xsc = torch.empty(M, dtype=torch.float32, device=dev)
-    ys = [torch.empty(M, lin.N, dtype=torch.bfloat16, device=dev) for lin in lins]
+    ys = [torch.empty(M, sum(lins[li].N for li in g), dtype=torch.bfloat16, device=dev)
+          for g in groups]
     draft = torch.from_numpy(synth.draft_ids(synth.W_STACK32B, 1, G, head.N)).to(dev)
     am = torch.empty(M, dtype=torch.int32, device=dev)
     al = torch.empty(1, dtype=torch.int32, device=dev)
     nt = torch.empty(1, dtype=torch.int32, device=dev)
     logits = torch.empty(M, head.N, dtype=torch.float32, device=dev)
 
-    def w8a8_step():
-        for layer in range(L):
-            for j, k in enumerate(in_k):
-                w8.quantize_act(xs[layer][j], xq=xq[k], x_scale=xsc)
-                for li in users[j]:
-                    wq, ws, _ = wts[layer][li]
-                    w8.linear(xq[k], xsc, wq, ws, y_bf16=ys[li], workspace=wsp)
+    # the separate linears: row ranges of the fused weights (whole 16-row tiles)
+    parts = []
+    for layer in range(L):
+        pl = []
+        for j, grp in enumerate(groups):
+            wq, ws, _ = wts[layer][j]
+            n0 = 0
+            for li in grp:
+                n = lins[li].N
+                pl.append((wq[n0 // 16:(n0 + n) // 16], ws[n0:n0 + n]))
+                n0 += n
+        parts.append(pl)
+    ysep = [torch.empty(M, lin.N, dtype=torch.bfloat16, device=dev) for lin in lins]
+
+    def head_step():
         w8.quantize_act(x_lm, xq=xq[head.K], x_scale=xsc)
         w8.lm_head_argmax(xq[head.K], xsc, lm[0], lm[1], workspace=wsp)
         w8.accept_from_keys(draft, argmax=am, accept_len=al, next_token=nt, workspace=wsp)
 
+    def w8a8_step():
+        for layer in range(L):
+            for j, k in enumerate(in_k):
+                w8.quantize_act(xs[layer][j], xq=xq[k], x_scale=xsc)
+                wq, ws, _ = wts[layer][j]
+                w8.linear(xq[k], xsc, wq, ws, y_bf16=ys[j], workspace=wsp)
+        head_step()
+
+    def w8a8_step_separate():
+        for layer in range(L):
+            pl = iter(parts[layer])
+            for j, k in enumerate(in_k):
+                w8.quantize_act(xs[layer][j], xq=xq[k], x_scale=xsc)
+                for li in groups[j]:
+                    wq, ws = next(pl)
+                    w8.linear(xq[k], xsc, wq, ws, y_bf16=ysep[li], workspace=wsp)
+        head_step()
+
     def bf16_step():
         for layer in range(L):
             for j in range(4):
-                for li in users[j]:
-                    w8.bf16_linear(xs[layer][j], wts[layer][li][2], y_bf16=ys[li])
+                w8.bf16_linear(xs[layer][j], wts[layer][j][2], y_bf16=ys[j])
         w8.bf16_linear(x_lm, lm[2], want_bf16=False, y_f32=logits)
         w8.verify_accept(logits, draft, argmax=am, accept_len=al, next_token=nt, workspace=wsp)
 
     t_w8 = graph_time([w8a8_step], replays=replays)
+    t_sep = graph_time([w8a8_step_separate], replays=replays)
     t_bf = graph_time([bf16_step], replays=replays)
     w8_bytes = L * sum(linear_bytes(M, lin.N, lin.K) for lin in lins) + \
         L * sum(M * k + 4 * M for k in in_k) + lm_head_bytes(M, head.N, head.K, logits=False)
@@ -640,13 +710,15 @@ def stack32b_measurement(dev, wsp, replays=10):
            "w8a8_verified_tokens_per_s": round(M / t_w8, 1),
            "w8a8_GBs": round(w8_bytes / t_w8 / 1e9, 1),
            "w8a8_frac_of_peak": round(w8_bytes / t_w8 / 1e9 / HBM_PEAK_GBS, 4),
+           "w8a8_separate_linears_ms_per_step": round(t_sep * 1e3, 4),
            "bf16_ms_per_step": round(t_bf * 1e3, 4),
            "bf16_verified_tokens_per_s": round(M / t_bf, 1),
            "bf16_GBs": round(bf_bytes / t_bf / 1e9, 1),
            "time_ratio_bf16_over_w8a8": round(t_bf / t_w8, 3),
            "timing": f"HIP graph of one whole step, mean of {replays} replays",
-           "launches_per_step": L * (4 + 7) + 3}
-    del wts, lm
+           "launches_per_step": L * 8 + 3,
+           "weights": "q/k/v and gate/up fused per layer (one launch each)"}
+    del wts, lm, parts
     torch.cuda.empty_cache()
     return res
 

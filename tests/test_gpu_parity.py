@@ -38,6 +38,7 @@ def assert_bf16_tolerance(y_bits, y32_oracle):
 # --------------------------------------------------------------------------
 
 ACT_SHAPES = [(5, 256), (5, 4096), (5, 12288), (8, 25600), (288, 4096), (7, 16), (1, 2064),
+              (3, 8208), (2, 131072),
               (3, 0), (0, 64)]
 
 
@@ -76,7 +77,7 @@ def test_quantize_act_degenerate_rows():
     assert list(q_ref[5, :8]) == [127, 0, 2, 2, -2, -2, 64, -64]
 
 
-@pytest.mark.parametrize("M,K", [(5, 4096), (288, 1024)])
+@pytest.mark.parametrize("M,K", [(5, 4096), (288, 1024), (8, 25600)])
 def test_quantize_act_smoothing(M, K):
     announce(f"quantize_act smoothing M={M} K={K}")
     bits = synth.activations_bf16(102, M, K, outliers=True)

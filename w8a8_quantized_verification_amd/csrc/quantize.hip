@@ -28,7 +28,9 @@
 
 namespace w8a8 {
 
-constexpr int kQuantThreads = 256;
+constexpr int kQuantThreads = 256;      // threads per row (weights, short activation rows)
+constexpr int kQuantThreadsLong = 1024; // threads per row for activation rows longer than
+constexpr int64_t kLongRow = 8192;      //   this: every element then stays in registers
 constexpr int kCache = 4;  // groups of 8 elements kept in registers between the passes
 
 __host__ __device__ __forceinline__ size_t tiled_offset(int64_t n, int64_t k, int64_t steps) {
@@ -65,25 +67,26 @@ __device__ __forceinline__ void load8(const void* __restrict__ in_row, const flo
 
 // Rows [0, R) are real; with kTiled the grid also covers the padding rows of
 // the last 16-row tile and the k range is padded to a multiple of 64.
-template <bool kBf16In, bool kSmooth, bool kDivide, bool kTiled>
-__global__ __launch_bounds__(kQuantThreads) void quantize_rows_kernel(
+template <int kThreads, bool kBf16In, bool kSmooth, bool kDivide, bool kTiled>
+__global__ __launch_bounds__(kThreads) void quantize_rows_kernel(
     const void* __restrict__ in, const float* __restrict__ smooth, int64_t R, int64_t K,
     int8_t* __restrict__ q, float* __restrict__ scale) {
-  __shared__ float red[kQuantThreads / kWave];
+  constexpr int kWaves = kThreads / kWave;
+  __shared__ float red[kWaves];
   const int64_t row = blockIdx.x;
   const int tid = threadIdx.x;
   const int64_t steps = (K + 63) >> 6;
   const int64_t k_end = kTiled ? steps * 64 : K;
 
   if (kTiled && row >= R) {  // padding row of the last tile: zeros
-    for (int64_t k = (int64_t)tid * 8; k < k_end; k += kQuantThreads * 8)
+    for (int64_t k = (int64_t)tid * 8; k < k_end; k += kThreads * 8)
       *reinterpret_cast<uint2*>(q + tiled_offset(row, k, steps)) = make_uint2(0u, 0u);
     return;
   }
 
   const size_t elt = kBf16In ? sizeof(uint16_t) : sizeof(float);
   const void* in_row = reinterpret_cast<const char*>(in) + (size_t)row * (size_t)K * elt;
-  constexpr int64_t kStride = kQuantThreads * 8;
+  constexpr int64_t kStride = kThreads * 8;
 
   // pass 1: row maximum; the first kCache groups of 8 stay in registers
   float cache[kCache][8];
@@ -106,7 +109,9 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_rows_kernel(
   amax = wave_max(amax);
   if ((tid & (kWave - 1)) == 0) red[tid / kWave] = amax;
   __syncthreads();
-  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  amax = red[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) amax = fmaxf(amax, red[w]);
 
   const float s = amax / 127.0f;
   const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
@@ -171,10 +176,16 @@ hipError_t w8a8_launch_quantize_rows(const void* in, bool in_is_bf16, const floa
   const int64_t grid_rows = tiled ? (R + 15) / 16 * 16 : R;
   const dim3 grid((unsigned)grid_rows), block(kQuantThreads);
 #define W8A8_QLAUNCH(BF, SM, DIV, TL) \
-  hipLaunchKernelGGL((quantize_rows_kernel<BF, SM, DIV, TL>), grid, block, 0, stream, in, smooth, R, K, q, scale)
+  hipLaunchKernelGGL((quantize_rows_kernel<kQuantThreads, BF, SM, DIV, TL>), grid, block, 0, stream, in, smooth, R, K, q, scale)
+#define W8A8_QLAUNCH_LONG(SM) \
+  hipLaunchKernelGGL((quantize_rows_kernel<kQuantThreadsLong, true, SM, false, false>), grid, \
+                     dim3(kQuantThreadsLong), 0, stream, in, smooth, R, K, q, scale)
   if (in_is_bf16) {
-    // activations: row-major output only
-    if (!smooth) W8A8_QLAUNCH(true, false, false, false);
+    // activations: row-major output only; few rows, so long rows get more threads
+    if (K > kLongRow) {
+      if (!smooth) W8A8_QLAUNCH_LONG(false);
+      else W8A8_QLAUNCH_LONG(true);
+    } else if (!smooth) W8A8_QLAUNCH(true, false, false, false);
     else W8A8_QLAUNCH(true, true, false, false);
   } else if (!tiled) {
     if (!smooth) W8A8_QLAUNCH(false, false, false, false);
@@ -185,6 +196,7 @@ hipError_t w8a8_launch_quantize_rows(const void* in, bool in_is_bf16, const floa
     else if (smooth_divides) W8A8_QLAUNCH(false, true, true, true);
     else W8A8_QLAUNCH(false, true, false, true);
   }
+#undef W8A8_QLAUNCH_LONG
 #undef W8A8_QLAUNCH
   return hipGetLastError();
 }
