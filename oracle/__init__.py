@@ -12,7 +12,8 @@ the pages by eye:
 * per-token symmetric int8 activation quantization, optionally after the
   smoothing multiply (``quant.quantize_act``);
 * per-output-channel symmetric int8 weight quantization, optionally after the
-  smoothing divide (``quant.quantize_weight``);
+  smoothing divide (``quant.quantize_weight``), and its 4-bit form for the
+  W4A8 verifier (``quant.quantize_weight_int4``);
 * the exact int8 x int8 -> int32 product (``gemm.int8_gemm``);
 * the dequant epilogue to fp32 and bf16 (``gemm.dequant``);
 * LM-head argmax and greedy acceptance (``accept``);
@@ -40,7 +41,7 @@ function's docstring.  Parity status: every function here is pinned by the
 library cast, exhaustive small cases, invariants); none is unpinned.
 """
 from .bf16 import bf16_to_f32, f32_to_bf16
-from .quant import quantize_rows, quantize_act, quantize_weight
+from .quant import quantize_rows, quantize_act, quantize_weight, quantize_weight_int4
 from .gemm import int8_gemm, dequant, w8a8_linear, INT32_MAX_K
 from .accept import argmax_rows, greedy_accept, verify_accept
 from .sample import exp_f32, fixed_weights, verify_sample
@@ -52,5 +53,5 @@ __all__ = [
     "quantize_weight", "int8_gemm", "dequant", "w8a8_linear", "INT32_MAX_K",
     "argmax_rows", "greedy_accept", "verify_accept", "bf16_reference_logits",
     "w8a8_linear_bytes", "bf16_linear_bytes", "weight_bytes_int8",
-    "weight_bytes_bf16", "exp_f32", "fixed_weights", "verify_sample",
+    "weight_bytes_bf16", "exp_f32", "fixed_weights", "verify_sample", "quantize_weight_int4",
 ]
