@@ -267,6 +267,55 @@ w8a8_status w8a8_lm_head_verify(const int8_t* xq, const float* x_scale,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * W4A8: the verifier's weights in 4 bits (int4 codes, one fp32 scale per
+ * output channel), activations as in W8A8.
+ *
+ * Pages: lower-bit verifiers, INT4 among them, are named as explored and as
+ * the next step ([zh] 关键设计; [it] §5; [ja] §5); no scheme is given.
+ * Reading: the int8 weight scheme with codes in [-7, 7]:
+ *   w_scale[n] = fp32(amax_n / 7); q = clip(rint(fp32(w' * fp32(7/amax_n))), -7, 7)
+ *   (w' = fp32(w / smooth[k]) when smooth != NULL; q = 0 where w' == 0),
+ * and the same exact contraction and dequant as w8a8_linear:
+ *   acc[m][n] = sum_k xq[m][k] * q[n][k]; y_f32 = fp32(fp32(acc * x_scale[m]) * w_scale[n]).
+ *
+ * Layout (int4 tiled, w8a8_w4_weight_bytes(N, K) bytes): per 16-channel tile
+ * t and 128-wide k pair p, 1 KiB at offset (t * ceil(K/128) + p) * 1024;
+ * lane l = (n % 16) + 16 * ((k % 64) / 16) owns bytes l*16 .. l*16+15: bytes
+ * 0..7 for k % 128 < 64, bytes 8..15 for k % 128 >= 64.  With j = k % 16,
+ * the code of (n, k) sits in byte (j % 4) of word (j / 4) % 2 of that
+ * 8-byte half, in the low nibble for j < 8 and the high nibble for j >= 8;
+ * codes are two's-complement nibbles, padding (n >= N, k >= K) is 0.
+ *
+ * w (fp32 [N][K]) and wq4 16-byte aligned; K % 16 == 0; K <= W8A8_MAX_K.
+ */
+size_t      w8a8_w4_weight_bytes(int64_t N, int64_t K);
+w8a8_status w8a8_quantize_weight_w4(const float* w, const float* smooth,
+                                    int64_t N, int64_t K,
+                                    int8_t* wq4, float* w_scale, void* stream);
+
+/*
+ * The W4A8 linear: w8a8_linear's arguments and outputs with int4 tiled
+ * weights (bit-exact int32 acc, fp32 y32, bf16 y).  No workspace.
+ */
+w8a8_status w8a8_linear_w4(const int8_t* xq, const float* x_scale,
+                           const int8_t* wq4, const float* w_scale,
+                           int64_t M, int64_t N, int64_t K,
+                           uint16_t* y_bf16, float* y_f32, int32_t* acc,
+                           void* stream);
+
+/*
+ * The W4A8 LM head with the row argmax folded into its epilogue, as
+ * w8a8_lm_head_argmax (same key workspace; follow it with
+ * w8a8_accept_from_keys).
+ */
+w8a8_status w8a8_lm_head_argmax_w4(const int8_t* xq, const float* x_scale,
+                                   const int8_t* wq4, const float* w_scale,
+                                   int64_t M, int64_t V, int64_t K,
+                                   float* logits,
+                                   void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
+/*
  * Stochastic verification at temperature T > 0: speculative sampling of a
  * block of single-token drafts on the fp32 dequantized logits.
  *

@@ -147,6 +147,26 @@ def test_verify_sample_validation(lib):
     assert f(None, 0, 1000, 1.0, None, None, 0, None) == OK
 
 
+def test_w4a8_validation(lib):
+    assert lib.w8a8_w4_weight_bytes(151936, 4096) == 151936 * 4096 // 2
+    assert lib.w8a8_w4_weight_bytes(17, 80) == 32 * 128 // 2
+    q = lib.w8a8_quantize_weight_w4
+    assert q(A16, None, 512, 250, A16b, A16, None) == INVALID        # K % 16
+    assert q(A16 + 4, None, 512, 256, A16b, A16, None) == INVALID    # w alignment
+    assert q(A16, None, 512, 256, None, A16, None) == INVALID
+    assert q(None, None, 0, 256, None, None, None) == OK
+    f = lib.w8a8_linear_w4
+    assert f(A16, A16, A16b, A16, 5, 512, 256, None, None, None, None) == INVALID   # no output
+    assert f(A16, A16, A16b + 8, A16, 5, 512, 256, A16, None, None, None) == INVALID
+    assert f(A16, A16, A16b, A16, 5, 512, 136000, A16, None, None, None) == INVALID  # K too big
+    assert f(None, None, None, None, 0, 512, 256, None, None, None, None) == OK
+    g = lib.w8a8_lm_head_argmax_w4
+    need = lib.w8a8_lm_head_verify_workspace_bytes(1, 4, 151936, 4096)
+    assert g(A16, A16, A16b, A16, 5, 151936, 4096, None, A16, 8, None) == WORKSPACE
+    assert g(A16, A16, A16b, A16, 5, 151936, 4096, None, A16 + 16, need, None) == INVALID
+    assert g(A16, A16, A16b, A16, 5, 0, 4096, None, A16, need, None) == INVALID
+
+
 def test_bf16_linear_validation(lib):
     f = lib.w8a8_bf16_linear
     assert f(A16, A16b, 17, 512, 256, A16, None, None) == UNSUPPORTED

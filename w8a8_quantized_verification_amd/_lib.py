@@ -47,6 +47,10 @@ SIGNATURES = {
                                   _vp, _sz, _vp]),
     "w8a8_sample_weights_workspace_bytes": (_sz, [_i64, _i64]),
     "w8a8_sample_weights": (_i32, [_vp, _i64, _i64, _c.c_float, _vp, _vp, _sz, _vp]),
+    "w8a8_w4_weight_bytes": (_sz, [_i64, _i64]),
+    "w8a8_quantize_weight_w4": (_i32, [_vp, _vp, _i64, _i64, _vp, _vp, _vp]),
+    "w8a8_linear_w4": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp]),
+    "w8a8_lm_head_argmax_w4": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _sz, _vp]),
 }
 
 _lib = None

@@ -17,7 +17,8 @@ __all__ = [
     "linear_workspace_bytes",
     "verify_accept", "verify_accept_workspace_bytes", "lm_head_verify", "lm_head_argmax",
     "accept_from_keys", "bf16_linear", "Workspace", "verify_sample",
-    "verify_sample_workspace_bytes", "sample_weights",
+    "verify_sample_workspace_bytes", "sample_weights", "w4_shape", "quantize_weight_w4",
+    "linear_w4", "lm_head_argmax_w4",
 ]
 
 
@@ -348,3 +349,72 @@ def sample_weights(logits, temperature: float, *, weights=None, workspace: Works
     check(lib().w8a8_sample_weights(_ptr(logits), R, V, float(temperature), _ptr(weights),
                                     _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev)))
     return weights
+
+
+def w4_shape(N: int, K: int) -> tuple:
+    """Shape of the int4 tiled weight layout as an int8 tensor: [ceil(N/16),
+    ceil(K/128), 64 lanes, 16 bytes] (two int4 codes per byte; see
+    include/w8a8.h)."""
+    return ((N + 15) // 16, (K + 127) // 128, 64, 16)
+
+
+def quantize_weight_w4(w: torch.Tensor, smooth: torch.Tensor | None = None, *, wq4=None,
+                       w_scale=None):
+    """Per-output-channel symmetric int4 quantization of fp32 ``w[N][K]``
+    into the int4 tiled layout; returns ``(wq4, w_scale float32[N])``."""
+    _need(w, "w", torch.float32, 2)
+    N, K = w.shape
+    if smooth is not None:
+        _need(smooth, "smooth", torch.float32, 1, w.device)
+    wq4 = _out(wq4, w4_shape(N, K), torch.int8, w.device, "wq4")
+    w_scale = _out(w_scale, (N,), torch.float32, w.device, "w_scale")
+    check(lib().w8a8_quantize_weight_w4(_ptr(w), _ptr(smooth), N, K, _ptr(wq4), _ptr(w_scale),
+                                        _stream(w.device)))
+    return wq4, w_scale
+
+
+def _need_w4(wq4, w_scale, K, dev):
+    _need(w_scale, "w_scale", torch.float32, 1, dev)
+    N = w_scale.shape[0]
+    _need(wq4, "wq4", torch.int8, 4, dev)
+    if tuple(wq4.shape) != w4_shape(N, K):
+        raise ValueError(f"wq4 must have shape {w4_shape(N, K)} (got {tuple(wq4.shape)})")
+    return N
+
+
+def linear_w4(xq, x_scale, wq4, w_scale, *, want_bf16=True, want_f32=False, want_acc=False,
+              y_bf16=None, y_f32=None, acc=None):
+    """The W4A8 linear (int4 tiled weights); outputs as :func:`linear`."""
+    _need(xq, "xq", torch.int8, 2)
+    dev = xq.device
+    _need(x_scale, "x_scale", torch.float32, 1, dev)
+    M, K = xq.shape
+    N = _need_w4(wq4, w_scale, K, dev)
+    if want_bf16 or y_bf16 is not None:
+        y_bf16 = _out(y_bf16, (M, N), torch.bfloat16, dev, "y_bf16")
+    if want_f32 or y_f32 is not None:
+        y_f32 = _out(y_f32, (M, N), torch.float32, dev, "y_f32")
+    if want_acc or acc is not None:
+        acc = _out(acc, (M, N), torch.int32, dev, "acc")
+    check(lib().w8a8_linear_w4(_ptr(xq), _ptr(x_scale), _ptr(wq4), _ptr(w_scale), M, N, K,
+                               _ptr(y_bf16), _ptr(y_f32), _ptr(acc), _stream(dev)))
+    return y_bf16, y_f32, acc
+
+
+def lm_head_argmax_w4(xq, x_scale, wq4, w_scale, *, logits=None,
+                      workspace: Workspace | None = None):
+    """:func:`lm_head_argmax` with int4 weights; follow with
+    :func:`accept_from_keys` on the same workspace."""
+    _need(xq, "xq", torch.int8, 2)
+    dev = xq.device
+    _need(x_scale, "x_scale", torch.float32, 1, dev)
+    M, K = xq.shape
+    V = _need_w4(wq4, w_scale, K, dev)
+    if logits is not None:
+        logits = _out(logits, (M, V), torch.float32, dev, "logits")
+    ws = (workspace or _default_ws).get(int(lib().w8a8_lm_head_verify_workspace_bytes(M, 0, V, K)),
+                                        dev, use="zeroed")
+    check(lib().w8a8_lm_head_argmax_w4(_ptr(xq), _ptr(x_scale), _ptr(wq4), _ptr(w_scale), M, V, K,
+                                       _ptr(logits), _ptr(ws), 0 if ws is None else ws.numel(),
+                                       _stream(dev)))
+    return logits

@@ -378,4 +378,75 @@ w8a8_status w8a8_verify_sample(const float* logits, int64_t V, const int32_t* dr
                                               reinterpret_cast<hipStream_t>(stream)), fn);
 }
 
+
+// ---- W4A8: int4 per-channel weights ----
+
+size_t w8a8_w4_weight_bytes(int64_t N, int64_t K) {
+  if (N <= 0 || K <= 0 || N > kMaxRows || K > W8A8_MAX_K) return 0;
+  return w8a8_w4_weight_bytes_impl(N, K);
+}
+
+w8a8_status w8a8_quantize_weight_w4(const float* w, const float* smooth, int64_t N, int64_t K,
+                                    int8_t* wq4, float* w_scale, void* stream) {
+  static const char* fn = "w8a8_quantize_weight_w4";
+  g_last_error.clear();
+  if (w8a8_status s = check_rows_k(fn, N, K)) return s;
+  if (N == 0) return W8A8_OK;
+  if (!w_scale || (K > 0 && (!w || !wq4)))
+    return fail(W8A8_ERR_INVALID_ARG, fn, "required pointer is NULL");
+  if (!aligned(w, 16) || !aligned(wq4, 16))
+    return fail(W8A8_ERR_INVALID_ARG, fn, "w and wq4 must be 16-byte aligned");
+  if (!aligned(smooth, 4) || !aligned(w_scale, 4))
+    return fail(W8A8_ERR_INVALID_ARG, fn, "smooth or w_scale misaligned");
+  return hip_status(w8a8_launch_quantize_w4(w, smooth, N, K, wq4, w_scale,
+                                            reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
+static w8a8_status check_w4(const char* fn, const int8_t* xq, const float* x_scale,
+                            const int8_t* wq4, const float* w_scale, int64_t M, int64_t N,
+                            int64_t K) {
+  if (w8a8_status s = check_rows_k(fn, M, K)) return s;
+  if (N < 0 || N > kMaxRows) return fail(W8A8_ERR_INVALID_ARG, fn, "N out of range");
+  if (M == 0 || N == 0) return W8A8_OK;
+  if (!x_scale || !w_scale) return fail(W8A8_ERR_INVALID_ARG, fn, "x_scale or w_scale is NULL");
+  if (K > 0 && (!xq || !wq4)) return fail(W8A8_ERR_INVALID_ARG, fn, "xq or wq4 is NULL");
+  if (!aligned(xq, 16) || !aligned(wq4, 16))
+    return fail(W8A8_ERR_INVALID_ARG, fn, "xq and wq4 must be 16-byte aligned");
+  if (!aligned(x_scale, 4) || !aligned(w_scale, 4))
+    return fail(W8A8_ERR_INVALID_ARG, fn, "scale pointer misaligned");
+  return W8A8_OK;
+}
+
+w8a8_status w8a8_linear_w4(const int8_t* xq, const float* x_scale, const int8_t* wq4,
+                           const float* w_scale, int64_t M, int64_t N, int64_t K,
+                           uint16_t* y_bf16, float* y_f32, int32_t* acc, void* stream) {
+  static const char* fn = "w8a8_linear_w4";
+  g_last_error.clear();
+  if (w8a8_status s = check_w4(fn, xq, x_scale, wq4, w_scale, M, N, K)) return s;
+  if (M == 0 || N == 0) return W8A8_OK;
+  if (!y_bf16 && !y_f32 && !acc) return fail(W8A8_ERR_INVALID_ARG, fn, "all outputs are NULL");
+  if (!aligned(y_bf16, 2) || !aligned(y_f32, 4) || !aligned(acc, 4))
+    return fail(W8A8_ERR_INVALID_ARG, fn, "output pointer misaligned");
+  return hip_status(w8a8_launch_gemm_w4(xq, x_scale, wq4, w_scale, M, N, K, y_bf16, y_f32, acc,
+                                        nullptr, reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
+w8a8_status w8a8_lm_head_argmax_w4(const int8_t* xq, const float* x_scale, const int8_t* wq4,
+                                   const float* w_scale, int64_t M, int64_t V, int64_t K,
+                                   float* logits, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  static const char* fn = "w8a8_lm_head_argmax_w4";
+  g_last_error.clear();
+  if (V < 1 || V > kMaxRows) return fail(W8A8_ERR_INVALID_ARG, fn, "V out of range [1, 2^30]");
+  if (w8a8_status s = check_w4(fn, xq, x_scale, wq4, w_scale, M, V, K)) return s;
+  if (M == 0) return W8A8_OK;
+  if (!aligned(logits, 4)) return fail(W8A8_ERR_INVALID_ARG, fn, "logits misaligned");
+  if (!workspace || workspace_bytes < w8a8_lm_head_workspace_bytes(M))
+    return fail(W8A8_ERR_WORKSPACE, fn, "workspace NULL or smaller than w8a8_lm_head_verify_workspace_bytes()");
+  if (!aligned(workspace, 256)) return fail(W8A8_ERR_INVALID_ARG, fn, "workspace must be 256-byte aligned");
+  return hip_status(w8a8_launch_gemm_w4(xq, x_scale, wq4, w_scale, M, V, K, nullptr, logits,
+                                        nullptr, workspace, reinterpret_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 }  // extern "C"

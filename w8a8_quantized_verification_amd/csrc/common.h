@@ -42,6 +42,24 @@ __device__ __forceinline__ void wave_argmax(float& v, int& idx) {
   }
 }
 
+// Fused-argmax keys: row m keeps kArgmaxSubkeys running maxima; workgroup w
+// folds into sub-key w % kArgmaxSubkeys, at keys[(m * kArgmaxSubkeys + s) *
+// kArgmaxKeyStride].  Spreading the folds over 64 addresses 256 bytes apart
+// keeps same-address atomics (which serialize) to a few dozen per key.
+constexpr int kArgmaxSubkeys = 64;
+constexpr int kArgmaxKeyStride = 32;  // in 8-byte words: 256 bytes
+
+// Pack (value, index) into a 64-bit key whose unsigned order is "larger value
+// first, then lower index": the value's bits mapped to an order-preserving
+// unsigned (negatives complemented, positives with the sign bit set; -0 made
+// +0 first so that it ties with +0), the index complemented.  Key 0 means
+// "empty".
+__device__ __forceinline__ unsigned long long argmax_key(float v, int idx) {
+  uint32_t u = __float_as_uint(v == 0.0f ? 0.0f : v);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((unsigned long long)u << 32) | (unsigned long long)(~(uint32_t)idx);
+}
+
 }  // namespace w8a8
 
 // ---------------------------------------------------------------------------
@@ -99,3 +117,11 @@ hipError_t w8a8_launch_verify_sample(const float* logits, int64_t V, const int32
                                      int64_t B, int64_t G, float inv_t, const uint32_t* u_accept,
                                      const uint64_t* u_sample, int32_t* accept_len,
                                      int32_t* next_token, void* workspace, hipStream_t stream);
+
+size_t w8a8_w4_weight_bytes_impl(int64_t N, int64_t K);
+hipError_t w8a8_launch_quantize_w4(const float* w, const float* smooth, int64_t N, int64_t K,
+                                   int8_t* wq4, float* scale, hipStream_t stream);
+hipError_t w8a8_launch_gemm_w4(const int8_t* xq, const float* x_scale, const int8_t* wq4,
+                               const float* w_scale, int64_t M, int64_t N, int64_t K,
+                               uint16_t* y_bf16, float* y_f32, int32_t* acc, void* keys,
+                               hipStream_t stream);

@@ -68,24 +68,6 @@ struct GemmArgs {
                              // kArgmaxSubkeys (zero before the call), or null
 };
 
-// Fused-argmax keys: row m keeps kArgmaxSubkeys running maxima; workgroup w
-// folds into sub-key w % kArgmaxSubkeys, at keys[(m * kArgmaxSubkeys + s) *
-// kArgmaxKeyStride].  Spreading the folds over 64 addresses 256 bytes apart
-// keeps same-address atomics (which serialize) to a few dozen per key.
-constexpr int kArgmaxSubkeys = 64;
-constexpr int kArgmaxKeyStride = 32;  // in 8-byte words: 256 bytes
-
-// Pack (value, index) into a 64-bit key whose unsigned order is "larger value
-// first, then lower index": the value's bits mapped to an order-preserving
-// unsigned (negatives complemented, positives with the sign bit set; -0 made
-// +0 first so that it ties with +0), the index complemented.  Key 0 means
-// "empty".
-__device__ __forceinline__ unsigned long long argmax_key(float v, int idx) {
-  uint32_t u = __float_as_uint(v == 0.0f ? 0.0f : v);
-  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return ((unsigned long long)u << 32) | (unsigned long long)(~(uint32_t)idx);
-}
-
 __device__ __forceinline__ float epilogue_store(const GemmArgs& g, int m, int n, int32_t a) {
   const float y = (static_cast<float>(a) * g.xs[m]) * g.ws[n];
   const size_t o = (size_t)m * (size_t)g.N + (size_t)n;

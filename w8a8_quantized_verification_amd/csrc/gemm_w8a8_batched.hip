@@ -52,12 +52,6 @@ struct BatchedArgs {
   int subkeys, key_stride;
 };
 
-__device__ __forceinline__ unsigned long long batched_argmax_key(float v, int idx) {
-  uint32_t u = __float_as_uint(v == 0.0f ? 0.0f : v);
-  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return ((unsigned long long)u << 32) | (unsigned long long)(~(uint32_t)idx);
-}
-
 template <int MB, int TN, int WR, int KW, int U, bool kTiled, bool kArgmax>
 __global__ __launch_bounds__(WR * KW * kWave) void gemm_w8a8_batched(BatchedArgs g) {
   // workgroup id -> (row tile, channel group), XCD-aware (see header)
@@ -220,7 +214,7 @@ __global__ __launch_bounds__(WR * KW * kWave) void gemm_w8a8_batched(BatchedArgs
           }
           if (col == 0 && m < g.M && idx != INT_MAX) {
             const size_t sub = (size_t)m * g.subkeys + (t16 % g.subkeys);
-            __hip_atomic_fetch_max(&g.keys[sub * g.key_stride], batched_argmax_key(v, idx),
+            __hip_atomic_fetch_max(&g.keys[sub * g.key_stride], argmax_key(v, idx),
                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           }
         }
