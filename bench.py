@@ -509,6 +509,69 @@ def layer_measurement(dev, wsp, M, workload):
             "timing": "HIP graph over the rotating weight copies, mean of 10 replays"}
 
 
+def w4a8_measurement(dev, x_dev, xq, xsc, wsp):
+    """The W4A8 verifier (int4 per-channel weights): the LM-head verify step
+    at M = 5 (quantize_act -> lm_head_argmax_w4 -> accept_from_keys) with
+    two alternating 311 MB int4 copies of the LM head, the fused GEMM's
+    weight-read rate, and the Qwen3-8B layer linears at M = 5 in int4."""
+    import numpy as np
+    import torch
+
+    import synth
+    import w8a8_quantized_verification_amd as w8
+
+    M, K, V, G, B = 5, 4096, synth.QWEN3_VOCAB, 4, 1
+
+    def w4(N, Kk, workload, index):
+        w = synth.weights_device(workload, index, N, Kk, dev)
+        out = w8.quantize_weight_w4(w)
+        del w
+        return out
+
+    cp = [w4(V, K, synth.W_LM_HEAD, 1000 + i) for i in range(2)]
+    draft = torch.from_numpy(synth.draft_ids(synth.W_LM_HEAD, B, G, V)).to(dev)
+    am = torch.empty(M, dtype=torch.int32, device=dev)
+    al = torch.empty(B, dtype=torch.int32, device=dev)
+    nt = torch.empty(B, dtype=torch.int32, device=dev)
+
+    def step(i):
+        w8.quantize_act(x_dev[i % len(x_dev)], xq=xq, x_scale=xsc)
+        w8.lm_head_argmax_w4(xq, xsc, *cp[i % 2], workspace=wsp)
+        w8.accept_from_keys(draft, argmax=am, accept_len=al, next_token=nt, workspace=wsp)
+
+    t_step = graph_time([lambda: step(0), lambda: step(1)], replays=50) / 2
+    t_gemm = graph_time([lambda: w8.lm_head_argmax_w4(xq, xsc, *cp[0], workspace=wsp),
+                         lambda: w8.accept_from_keys(draft, argmax=am, accept_len=al,
+                                                     next_token=nt, workspace=wsp),
+                         lambda: w8.lm_head_argmax_w4(xq, xsc, *cp[1], workspace=wsp),
+                         lambda: w8.accept_from_keys(draft, argmax=am, accept_len=al,
+                                                     next_token=nt, workspace=wsp)],
+                        replays=50) / 2
+    wbytes = V * K // 2 + 4 * V + M * K + 4 * M + 8 * M * ((V + 31) // 32)
+    res = {"ms_per_step": round(t_step * 1e3, 5), "verified_tokens_per_s": round(M / t_step, 1),
+           "lm_head_plus_accept_us": round(t_gemm * 1e6, 2),
+           "lm_head_weight_GBs_incl_accept": round(wbytes / t_gemm / 1e9, 1),
+           "int4_weight_bytes": V * K // 2,
+           "timing": "HIP graph; 2 int4 LM-head copies alternating"}
+    del cp
+    layer = []
+    for li, lin in enumerate(synth.QWEN3_8B_LAYER):
+        nc = rotation_copies(lin.N, lin.K // 2)
+        wl = [w4(lin.N, lin.K, synth.W_LAYER_M5, 3000 + 200 * li + c) for c in range(nc)]
+        x = torch.from_numpy(synth.activations_bf16(synth.W_LAYER_M5, M, lin.K, outliers=True)
+                             .view(np.int16).copy()).view(torch.bfloat16).to(dev)
+        lxq, lxs = w8.quantize_act(x)
+        y = torch.empty(M, lin.N, dtype=torch.bfloat16, device=dev)
+        t = graph_time([(lambda c=c: w8.linear_w4(lxq, lxs, *wl[c], y_bf16=y)) for c in range(nc)],
+                       replays=10) / nc
+        b = lin.N * lin.K // 2 + 4 * lin.N + M * lin.K + 4 * M + 2 * M * lin.N
+        layer.append({"name": lin.name, "us": round(t * 1e6, 2), "GBs": round(b / t / 1e9, 1)})
+        del wl
+    res["qwen3_8b_layer_linears_m5"] = {"per_linear": layer,
+                                        "sum_us": round(sum(e["us"] for e in layer), 2)}
+    return res
+
+
 def extra_measurements(dev, copies, x_dev, xq, xsc, wsp):
     """Secondary figures: Qwen3-8B decoder-layer linears at M=5 (8 rotating
     copies of each weight, graph-replayed), the row-major layout and the
@@ -581,6 +644,7 @@ def extra_measurements(dev, copies, x_dev, xq, xsc, wsp):
     t_vs = graph_time([lambda: w8.verify_sample(lg, draft, 1.0, ua, us, accept_len=al,
                                                 next_token=nt, workspace=wsp)] * 8,
                       replays=50) / 8
+    res["w4a8_lm_head_m5"] = w4a8_measurement(dev, x_dev, xq, xsc, wsp)
     res["stochastic_step_m5_t1"] = {
         "ms_per_step": round(t_st * 1e3, 5), "verified_tokens_per_s": round(M / t_st, 1),
         "verify_sample_us": round(t_vs * 1e6, 2),
