@@ -645,6 +645,24 @@ def extra_measurements(dev, copies, x_dev, xq, xsc, wsp):
                                                 next_token=nt, workspace=wsp)] * 8,
                       replays=50) / 8
     res["w4a8_lm_head_m5"] = w4a8_measurement(dev, x_dev, xq, xsc, wsp)
+
+    # the online smoothing multiply fused into quantize_act, on the outlier
+    # activations of the layer inputs: 16 launches per graph over 16 inputs
+    sm = {}
+    for Mq, Kq in ((5, 4096), (5, 12288), (8, 25600)):
+        xs_l = [torch.from_numpy(synth.activations_bf16(synth.W_LAYER_M5, Mq, Kq, index=i,
+                                                        outliers=True).view(np.int16).copy())
+                .view(torch.bfloat16).to(dev) for i in range(16)]
+        svec = torch.from_numpy(synth.smoothing_vector(synth.W_LAYER_M5, Kq)).to(dev)
+        oq = torch.empty(Mq, Kq, dtype=torch.int8, device=dev)
+        osc = torch.empty(Mq, dtype=torch.float32, device=dev)
+        t_plain = graph_time([(lambda i=i: w8.quantize_act(xs_l[i], xq=oq, x_scale=osc))
+                              for i in range(16)], replays=20) / 16
+        t_smooth = graph_time([(lambda i=i: w8.quantize_act(xs_l[i], svec, xq=oq, x_scale=osc))
+                               for i in range(16)], replays=20) / 16
+        sm[f"M{Mq}_K{Kq}"] = {"plain_us": round(t_plain * 1e6, 2),
+                              "smoothed_us": round(t_smooth * 1e6, 2)}
+    res["quantize_act_smoothing_cost"] = sm
     res["stochastic_step_m5_t1"] = {
         "ms_per_step": round(t_st * 1e3, 5), "verified_tokens_per_s": round(M / t_st, 1),
         "verify_sample_us": round(t_vs * 1e6, 2),
