@@ -20,6 +20,8 @@ the pages by eye:
 * stochastic verification at temperature T > 0: softmax of the dequantized
   logits, acceptance of each draft with its probability, residual or bonus
   sampling by inverse CDF (``sample``);
+* the BF16 glue between linears: residual add, RMSNorm and SwiGLU before
+  the next quantization (``glue``);
 * the bf16 reference layer and the weight-traffic closed forms
   (``reference``).
 
@@ -45,6 +47,7 @@ from .quant import quantize_rows, quantize_act, quantize_weight, quantize_weight
 from .gemm import int8_gemm, dequant, w8a8_linear, INT32_MAX_K
 from .accept import argmax_rows, greedy_accept, verify_accept
 from .sample import exp_f32, fixed_weights, verify_sample
+from .glue import residual_add, rmsnorm, silu_mul
 from .reference import (bf16_reference_logits, w8a8_linear_bytes,
                         bf16_linear_bytes, weight_bytes_int8, weight_bytes_bf16)
 
@@ -54,4 +57,5 @@ __all__ = [
     "argmax_rows", "greedy_accept", "verify_accept", "bf16_reference_logits",
     "w8a8_linear_bytes", "bf16_linear_bytes", "weight_bytes_int8",
     "weight_bytes_bf16", "exp_f32", "fixed_weights", "verify_sample", "quantize_weight_int4",
+    "residual_add", "rmsnorm", "silu_mul",
 ]
