@@ -267,6 +267,47 @@ w8a8_status w8a8_lm_head_verify(const int8_t* xq, const float* x_scale,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The BF16 glue between linears, fused with the per-token int8
+ * quantization of the next linear's input (it replaces that
+ * w8a8_quantize_act call).
+ *
+ * Pages: the INT32 results are dequantized to BF16 before the non-linear
+ * layers, which run in high precision ([de] §2 "De-Quantisierung"; [it] §2
+ * pipeline; [fr] §2; [ja] §2.2 item 3).  For the Qwen3 shapes: RMSNorm and
+ * the SiLU-gated MLP.  Computes, per token row m (fp32 arithmetic, bf16 =
+ * round to nearest even):
+ *
+ * w8a8_residual_rmsnorm_quant:
+ *   h1 = bf16(h + delta) (h1 = h when delta == NULL), written to h_out
+ *        (may equal h) when delta and h_out are given;
+ *   r  = 1 / sqrt(sum_k h1^2 / D + eps)   (summation order unspecified);
+ *   n  = bf16(bf16(h1 * r) * gamma), written to normed if not NULL;
+ *   xq, x_scale = w8a8_quantize_act(n, smooth).
+ * w8a8_silu_mul_quant:
+ *   a  = bf16(bf16(g / (1 + exp(-g))) * u), g = gate[m][k], u = up[m][k]
+ *        (rows row_stride elements apart: gate and up may be the two halves
+ *        of a fused [gate;up] linear's output), written to act [M][F] if not
+ *        NULL;
+ *   xq, x_scale = w8a8_quantize_act(a, smooth).
+ * The int8 codes are those w8a8_quantize_act gives for the bf16 row the
+ * call produced (n or a), bit for bit.
+ *
+ * h, delta, h_out, normed [M][D] bf16; gamma [D] bf16; smooth [D] fp32 or
+ * NULL; xq [M][D] int8; x_scale [M] fp32.  Pointers 16-byte aligned
+ * (x_scale 4); 16 <= D <= W8A8_MAX_GLUE_WIDTH, D % 16 == 0; eps >= 0.
+ */
+#define W8A8_MAX_GLUE_WIDTH 32768
+w8a8_status w8a8_residual_rmsnorm_quant(const uint16_t* h, const uint16_t* delta,
+                                        const uint16_t* gamma, float eps,
+                                        const float* smooth, int64_t M, int64_t D,
+                                        uint16_t* h_out, uint16_t* normed,
+                                        int8_t* xq, float* x_scale, void* stream);
+w8a8_status w8a8_silu_mul_quant(const uint16_t* gate, const uint16_t* up,
+                                int64_t row_stride, const float* smooth,
+                                int64_t M, int64_t F, uint16_t* act,
+                                int8_t* xq, float* x_scale, void* stream);
+
+/*
  * W4A8: the verifier's weights in 4 bits (int4 codes, one fp32 scale per
  * output channel), activations as in W8A8.
  *

@@ -167,6 +167,21 @@ def test_w4a8_validation(lib):
     assert g(A16, A16, A16b, A16, 5, 0, 4096, None, A16, need, None) == INVALID
 
 
+def test_glue_validation(lib):
+    f = lib.w8a8_residual_rmsnorm_quant
+    assert f(A16, None, A16, 1e-6, None, 5, 4008, None, None, A16b, A16, None) == INVALID  # D % 16
+    assert f(A16, None, A16, 1e-6, None, 5, 40000, None, None, A16b, A16, None) == INVALID  # > 32768
+    assert f(A16, None, A16, -1.0, None, 5, 4096, None, None, A16b, A16, None) == INVALID   # eps
+    assert f(A16 + 8, None, A16, 1e-6, None, 5, 4096, None, None, A16b, A16, None) == INVALID
+    assert f(None, None, A16, 1e-6, None, 5, 4096, None, None, A16b, A16, None) == INVALID
+    assert f(None, None, None, 1e-6, None, 0, 4096, None, None, None, None, None) == OK
+    g = lib.w8a8_silu_mul_quant
+    assert g(A16, A16b, 100, None, 5, 128, None, A16, A16, None) == INVALID   # stride < F
+    assert g(A16, A16b, 132, None, 5, 128, None, A16, A16, None) == INVALID   # stride % 8
+    assert g(A16, None, 256, None, 5, 128, None, A16, A16, None) == INVALID
+    assert g(None, None, 256, None, 0, 128, None, None, None, None) == OK
+
+
 def test_bf16_linear_validation(lib):
     f = lib.w8a8_bf16_linear
     assert f(A16, A16b, 17, 512, 256, A16, None, None) == UNSUPPORTED

@@ -1,0 +1,113 @@
+"""GPU parity of the BF16 glue fused with quantization (w8a8_residual_rmsnorm_quant,
+w8a8_silu_mul_quant, through the C ABI) against the oracle (oracle/glue.py,
+oracle.quantize_act).
+
+Bars: the residual sum bit-exact; the normed / SwiGLU bf16 rows within the
+stated tolerance (1e-2 relative / 1e-3 absolute) of the oracle's float64
+computation, and bit-exact on at least 99% of elements (an fp32 kernel can
+differ by one bf16 step next to a rounding boundary); the int8 codes and
+scales bit-exact against the oracle's quantizer applied to the bf16 row the
+kernel produced (the same decision in the same precision)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.gpu_util import announce, dev, dev_bf16, gpu_available, host
+
+pytestmark = pytest.mark.gpu
+
+if gpu_available():
+    import w8a8_quantized_verification_amd as w8
+
+W_GLUE = 8
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not gpu_available():
+        pytest.skip("no ROCm GPU")
+
+
+def bf16_rows(M, D, index, scale=1.0, outliers=False):
+    return synth.activations_bf16(W_GLUE, M, D, index=index, outliers=outliers,
+                                  outlier_scale=20.0) if scale == 1.0 else \
+        oracle.f32_to_bf16(oracle.bf16_to_f32(synth.activations_bf16(W_GLUE, M, D, index=index))
+                           * np.float32(scale))
+
+
+def check_bf16_close(got_bits, want_bits):
+    got = oracle.bf16_to_f32(got_bits).astype(np.float64)
+    want = oracle.bf16_to_f32(want_bits).astype(np.float64)
+    assert np.all(np.abs(got - want) <= 1e-3 + 1e-2 * np.abs(want))
+    exact = np.mean(got_bits == want_bits)
+    assert exact >= 0.99, exact
+    return exact
+
+
+@pytest.mark.parametrize("M,D,with_delta,smooth", [(5, 4096, True, False), (5, 4096, False, False),
+                                                   (8, 5120, True, True), (288, 4096, True, False),
+                                                   (3, 25600, True, False), (1, 16, True, False),
+                                                   (2, 32768, False, True), (7, 8208, True, False)])
+def test_residual_rmsnorm_quant(M, D, with_delta, smooth):
+    announce(f"residual_rmsnorm_quant M={M} D={D} delta={with_delta} smooth={smooth}")
+    h = bf16_rows(M, D, 1, scale=4.0)
+    delta = bf16_rows(M, D, 2, outliers=True) if with_delta else None
+    gamma = oracle.f32_to_bf16(synth.rng(W_GLUE, 20, D).uniform(0.5, 1.5, D).astype(np.float32))
+    s = synth.smoothing_vector(W_GLUE, D) if smooth else None
+    eps = 1e-6
+    h_d = dev_bf16(h)
+    xq, xsc, normed, h_out = w8.residual_rmsnorm_quant(
+        h_d, dev_bf16(gamma), eps, delta=None if delta is None else dev_bf16(delta),
+        smooth=None if s is None else dev(s), want_normed=True)
+    xq2, xsc2, _, _ = w8.residual_rmsnorm_quant(          # no normed output requested
+        h_d, dev_bf16(gamma), eps, delta=None if delta is None else dev_bf16(delta),
+        smooth=None if s is None else dev(s))
+    torch.cuda.synchronize()
+    h1 = oracle.residual_add(h, delta)
+    if delta is not None:
+        np.testing.assert_array_equal(host(h_out), h1)
+    n_gpu = host(normed)
+    exact = check_bf16_close(n_gpu, oracle.rmsnorm(h1, gamma, eps))
+    print(f"[gpu] normed bit-exact fraction {exact:.6f}", flush=True)
+    q_r, s_r = oracle.quantize_act(n_gpu, smooth=s)
+    np.testing.assert_array_equal(host(xq), q_r)
+    np.testing.assert_array_equal(host(xsc).view(np.uint32), s_r.view(np.uint32))
+    np.testing.assert_array_equal(host(xq2), q_r)
+    np.testing.assert_array_equal(host(xsc2).view(np.uint32), s_r.view(np.uint32))
+
+
+def test_residual_rmsnorm_in_place():
+    announce("residual_rmsnorm_quant in place")
+    M, D = 5, 4096
+    h = bf16_rows(M, D, 3)
+    delta = bf16_rows(M, D, 4)
+    gamma = oracle.f32_to_bf16(np.ones(D, dtype=np.float32))
+    h_d = dev_bf16(h)
+    w8.residual_rmsnorm_quant(h_d, dev_bf16(gamma), 1e-6, delta=dev_bf16(delta), h_out=h_d)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(h_d), oracle.residual_add(h, delta))
+
+
+@pytest.mark.parametrize("M,F,fused,smooth", [(5, 12288, True, False), (8, 25600, True, True),
+                                              (288, 12288, False, False), (3, 16, False, False),
+                                              (5, 3088, True, False)])
+def test_silu_mul_quant(M, F, fused, smooth):
+    announce(f"silu_mul_quant M={M} F={F} fused={fused} smooth={smooth}")
+    g = bf16_rows(M, F, 5, scale=3.0)
+    u = bf16_rows(M, F, 6)
+    s = synth.smoothing_vector(W_GLUE, F) if smooth else None
+    if fused:
+        gu = dev_bf16(np.concatenate([g, u], axis=1))      # a [gate;up] linear's output
+        gd, ud = gu[:, :F], gu[:, F:]
+    else:
+        gd, ud = dev_bf16(g), dev_bf16(u)
+    xq, xsc, act = w8.silu_mul_quant(gd, ud, smooth=None if s is None else dev(s), want_act=True)
+    torch.cuda.synchronize()
+    a_gpu = host(act)
+    exact = check_bf16_close(a_gpu, oracle.silu_mul(g, u))
+    print(f"[gpu] act bit-exact fraction {exact:.6f}", flush=True)
+    q_r, s_r = oracle.quantize_act(a_gpu, smooth=s)
+    np.testing.assert_array_equal(host(xq), q_r)
+    np.testing.assert_array_equal(host(xsc).view(np.uint32), s_r.view(np.uint32))

@@ -8,7 +8,8 @@ from .api import (W8A8Error, Workspace, accept_from_keys, bf16_linear, linear,
                   linear_workspace_bytes, lm_head_argmax, lm_head_verify, quantize_act,
                   quantize_weight, sample_weights, tile_weight, tiled_shape, verify_accept,
                   verify_accept_workspace_bytes, verify_sample, verify_sample_workspace_bytes,
-                  w4_shape, quantize_weight_w4, linear_w4, lm_head_argmax_w4)
+                  w4_shape, quantize_weight_w4, linear_w4, lm_head_argmax_w4,
+                  residual_rmsnorm_quant, silu_mul_quant)
 
 __all__ = [
     "W8A8Error", "Workspace", "accept_from_keys", "bf16_linear", "linear", "linear_workspace_bytes",
@@ -16,4 +17,5 @@ __all__ = [
     "quantize_act", "quantize_weight", "tile_weight", "tiled_shape", "verify_accept",
     "verify_accept_workspace_bytes", "verify_sample", "verify_sample_workspace_bytes",
     "sample_weights", "w4_shape", "quantize_weight_w4", "linear_w4", "lm_head_argmax_w4",
+    "residual_rmsnorm_quant", "silu_mul_quant",
 ]

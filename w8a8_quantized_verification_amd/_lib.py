@@ -51,6 +51,9 @@ SIGNATURES = {
     "w8a8_quantize_weight_w4": (_i32, [_vp, _vp, _i64, _i64, _vp, _vp, _vp]),
     "w8a8_linear_w4": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp]),
     "w8a8_lm_head_argmax_w4": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _sz, _vp]),
+    "w8a8_residual_rmsnorm_quant": (_i32, [_vp, _vp, _vp, _c.c_float, _vp, _i64, _i64, _vp, _vp,
+                                           _vp, _vp, _vp]),
+    "w8a8_silu_mul_quant": (_i32, [_vp, _vp, _i64, _vp, _i64, _i64, _vp, _vp, _vp, _vp]),
 }
 
 _lib = None

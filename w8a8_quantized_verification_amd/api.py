@@ -18,7 +18,7 @@ __all__ = [
     "verify_accept", "verify_accept_workspace_bytes", "lm_head_verify", "lm_head_argmax",
     "accept_from_keys", "bf16_linear", "Workspace", "verify_sample",
     "verify_sample_workspace_bytes", "sample_weights", "w4_shape", "quantize_weight_w4",
-    "linear_w4", "lm_head_argmax_w4",
+    "linear_w4", "lm_head_argmax_w4", "residual_rmsnorm_quant", "silu_mul_quant",
 ]
 
 
@@ -418,3 +418,61 @@ def lm_head_argmax_w4(xq, x_scale, wq4, w_scale, *, logits=None,
                                        _ptr(logits), _ptr(ws), 0 if ws is None else ws.numel(),
                                        _stream(dev)))
     return logits
+
+
+def residual_rmsnorm_quant(h, gamma, eps: float, *, delta=None, smooth=None, h_out=None,
+                           want_normed=False, normed=None, xq=None, x_scale=None):
+    """Residual add (when ``delta`` is given; the sum goes to ``h_out``, which
+    may be ``h``), RMSNorm with bf16 ``gamma[D]``, then the per-token int8
+    quantization of the normed row.  ``h``, ``delta``: bf16 ``[M][D]``.
+    Returns ``(xq, x_scale, normed or None, h_out or None)``."""
+    _need(h, "h", torch.bfloat16, 2)
+    dev = h.device
+    M, D = h.shape
+    _need(gamma, "gamma", torch.bfloat16, 1, dev)
+    if gamma.shape[0] != D:
+        raise ValueError("gamma must have length D")
+    if delta is not None:
+        _need(delta, "delta", torch.bfloat16, 2, dev)
+        if tuple(delta.shape) != (M, D):
+            raise ValueError("delta must have h's shape")
+        h_out = _out(h_out, (M, D), torch.bfloat16, dev, "h_out")
+    elif h_out is not None:
+        raise ValueError("h_out is written only with delta")
+    if smooth is not None:
+        _need(smooth, "smooth", torch.float32, 1, dev)
+    if want_normed or normed is not None:
+        normed = _out(normed, (M, D), torch.bfloat16, dev, "normed")
+    xq = _out(xq, (M, D), torch.int8, dev, "xq")
+    x_scale = _out(x_scale, (M,), torch.float32, dev, "x_scale")
+    check(lib().w8a8_residual_rmsnorm_quant(_ptr(h), _ptr(delta), _ptr(gamma), float(eps),
+                                            _ptr(smooth), M, D, _ptr(h_out), _ptr(normed),
+                                            _ptr(xq), _ptr(x_scale), _stream(dev)))
+    return xq, x_scale, normed, h_out
+
+
+def silu_mul_quant(gate, up, *, smooth=None, want_act=False, act=None, xq=None, x_scale=None):
+    """SwiGLU product ``bf16(bf16(silu(gate)) * up)`` then the per-token int8
+    quantization.  ``gate`` and ``up`` are bf16 ``[M][F]`` views with the same
+    row stride (e.g. the two column halves of a fused [gate;up] output).
+    Returns ``(xq, x_scale, act or None)``."""
+    for t, n in ((gate, "gate"), (up, "up")):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or t.dim() != 2:
+            raise TypeError(f"{n} must be a 2-D bfloat16 tensor")
+        if t.device.type != "cuda":
+            raise TypeError(f"{n} must be on a ROCm device; there is no CPU path")
+        if t.stride(1) != 1:
+            raise ValueError(f"{n} rows must be contiguous")
+    if gate.shape != up.shape or gate.stride(0) != up.stride(0) or gate.device != up.device:
+        raise ValueError("gate and up must have the same shape, row stride and device")
+    dev = gate.device
+    M, F = gate.shape
+    if smooth is not None:
+        _need(smooth, "smooth", torch.float32, 1, dev)
+    if want_act or act is not None:
+        act = _out(act, (M, F), torch.bfloat16, dev, "act")
+    xq = _out(xq, (M, F), torch.int8, dev, "xq")
+    x_scale = _out(x_scale, (M,), torch.float32, dev, "x_scale")
+    check(lib().w8a8_silu_mul_quant(_ptr(gate), _ptr(up), gate.stride(0), _ptr(smooth), M, F,
+                                    _ptr(act), _ptr(xq), _ptr(x_scale), _stream(dev)))
+    return xq, x_scale, act

@@ -449,4 +449,53 @@ w8a8_status w8a8_lm_head_argmax_w4(const int8_t* xq, const float* x_scale, const
                     fn);
 }
 
+
+// ---- BF16 glue fused with the next quantization ----
+
+static w8a8_status check_glue_row(const char* fn, int64_t M, int64_t D) {
+  if (M < 0 || M > kMaxRows) return fail(W8A8_ERR_INVALID_ARG, fn, "row count out of range");
+  if (D < 16 || D > W8A8_MAX_GLUE_WIDTH || D % 16 != 0)
+    return fail(W8A8_ERR_INVALID_ARG, fn, "width must be a multiple of 16 in [16, 32768]");
+  return W8A8_OK;
+}
+
+w8a8_status w8a8_residual_rmsnorm_quant(const uint16_t* h, const uint16_t* delta,
+                                        const uint16_t* gamma, float eps, const float* smooth,
+                                        int64_t M, int64_t D, uint16_t* h_out, uint16_t* normed,
+                                        int8_t* xq, float* x_scale, void* stream) {
+  static const char* fn = "w8a8_residual_rmsnorm_quant";
+  g_last_error.clear();
+  if (w8a8_status s = check_glue_row(fn, M, D)) return s;
+  if (!(std::isfinite(eps) && eps >= 0.0f)) return fail(W8A8_ERR_INVALID_ARG, fn, "eps must be finite and >= 0");
+  if (M == 0) return W8A8_OK;
+  if (!h || !gamma || !xq || !x_scale) return fail(W8A8_ERR_INVALID_ARG, fn, "required pointer is NULL");
+  if (!aligned(h, 16) || !aligned(delta, 16) || !aligned(gamma, 16) || !aligned(h_out, 16) ||
+      !aligned(normed, 16) || !aligned(xq, 16) || !aligned(smooth, 16))
+    return fail(W8A8_ERR_INVALID_ARG, fn, "tensors must be 16-byte aligned");
+  if (!aligned(x_scale, 4)) return fail(W8A8_ERR_INVALID_ARG, fn, "x_scale misaligned");
+  return hip_status(w8a8_launch_residual_rmsnorm_quant(h, delta, gamma, eps, smooth, M, D, h_out,
+                                                       normed, xq, x_scale,
+                                                       reinterpret_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+w8a8_status w8a8_silu_mul_quant(const uint16_t* gate, const uint16_t* up, int64_t row_stride,
+                                const float* smooth, int64_t M, int64_t F, uint16_t* act,
+                                int8_t* xq, float* x_scale, void* stream) {
+  static const char* fn = "w8a8_silu_mul_quant";
+  g_last_error.clear();
+  if (w8a8_status s = check_glue_row(fn, M, F)) return s;
+  if (row_stride < F || row_stride % 8 != 0)
+    return fail(W8A8_ERR_INVALID_ARG, fn, "row_stride must be >= F and a multiple of 8");
+  if (M == 0) return W8A8_OK;
+  if (!gate || !up || !xq || !x_scale) return fail(W8A8_ERR_INVALID_ARG, fn, "required pointer is NULL");
+  if (!aligned(gate, 16) || !aligned(up, 16) || !aligned(act, 16) || !aligned(xq, 16) ||
+      !aligned(smooth, 16))
+    return fail(W8A8_ERR_INVALID_ARG, fn, "tensors must be 16-byte aligned");
+  if (!aligned(x_scale, 4)) return fail(W8A8_ERR_INVALID_ARG, fn, "x_scale misaligned");
+  return hip_status(w8a8_launch_silu_mul_quant(gate, up, row_stride, smooth, M, F, act, xq,
+                                               x_scale, reinterpret_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 }  // extern "C"

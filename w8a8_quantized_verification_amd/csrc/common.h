@@ -125,3 +125,12 @@ hipError_t w8a8_launch_gemm_w4(const int8_t* xq, const float* x_scale, const int
                                const float* w_scale, int64_t M, int64_t N, int64_t K,
                                uint16_t* y_bf16, float* y_f32, int32_t* acc, void* keys,
                                hipStream_t stream);
+
+hipError_t w8a8_launch_residual_rmsnorm_quant(const uint16_t* h, const uint16_t* delta,
+                                              const uint16_t* gamma, float eps,
+                                              const float* smooth, int64_t M, int64_t D,
+                                              uint16_t* h_out, uint16_t* normed, int8_t* xq,
+                                              float* x_scale, hipStream_t stream);
+hipError_t w8a8_launch_silu_mul_quant(const uint16_t* gate, const uint16_t* up, int64_t stride,
+                                      const float* smooth, int64_t M, int64_t F, uint16_t* act,
+                                      int8_t* xq, float* x_scale, hipStream_t stream);
