@@ -459,6 +459,8 @@ def main():
             extra["qwen3_32b_stack_m8"] = stack32b_measurement(dev, wsp)
         out["extra"] = extra
 
+    if not args.no_cpu_baseline and not args.no_extra:
+        out["extra"]["oracle_timings"] = oracle_timings()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(dev, xs_host, synth.draft_ids(synth.W_LM_HEAD, B, G, V),
                                            args.cpu_seconds, M)
@@ -645,6 +647,7 @@ def extra_measurements(dev, copies, x_dev, xq, xsc, wsp):
                                                 next_token=nt, workspace=wsp)] * 8,
                       replays=50) / 8
     res["w4a8_lm_head_m5"] = w4a8_measurement(dev, x_dev, xq, xsc, wsp)
+    res["qwen3_8b_layer_step_m5"] = layer_step_measurement(dev, wsp)
 
     # the online smoothing multiply fused into quantize_act, on the outlier
     # activations of the layer inputs: 16 launches per graph over 16 inputs
@@ -802,6 +805,111 @@ def stack32b_measurement(dev, wsp, replays=10):
            "weights": "q/k/v and gate/up fused per layer (one launch each)"}
     del wts, lm, parts
     torch.cuda.empty_cache()
+    return res
+
+
+def oracle_timings():
+    """The oracle's time for the other workloads' steps on this host (a
+    reported baseline beside the GPU figures, never a target): per linear,
+    quantize_act + the exact int product + dequant on random int8 codes of
+    the workload's shapes (the codes do not change the oracle's work).  The
+    32B stack is timed as one layer plus the LM head and extrapolated to 64
+    layers."""
+    import numpy as np
+
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas = os.cpu_count() or 1
+    r = np.random.default_rng([9, 9, 9])
+
+    def lin_time(M, N, K):
+        xbits = synth.activations_bf16(99, M, K)
+        wq = r.integers(-127, 128, size=(N, K), dtype=np.int8)
+        ws = r.uniform(1e-4, 1e-3, N).astype(np.float32)
+        t0 = time.perf_counter()
+        xq, xs = oracle.quantize_act(xbits)
+        oracle.w8a8_linear(xq, xs, wq, ws)
+        return time.perf_counter() - t0
+
+    out = {"blas_threads": int(blas), "kind": "oracle"}
+    for name, M in (("qwen3_8b_layer_linears_m5", 5), ("qwen3_8b_layer_linears_m288", 288)):
+        per = {l.name: round(lin_time(M, l.N, l.K) * 1e3, 2) for l in synth.QWEN3_8B_LAYER}
+        out[name] = {"per_linear_ms": per, "sum_ms": round(sum(per.values()), 2)}
+    layer_s = sum(lin_time(8, l.N, l.K) for l in synth.QWEN3_32B_LAYER)
+    head = synth.QWEN3_32B_LM_HEAD
+    head_s = lin_time(8, head.N, head.K)
+    out["qwen3_32b_stack_m8"] = {"one_layer_ms": round(layer_s * 1e3, 1),
+                                 "lm_head_ms": round(head_s * 1e3, 1),
+                                 "step_ms_extrapolated_x64": round((64 * layer_s + head_s) * 1e3, 1),
+                                 "verified_tokens_per_s_extrapolated":
+                                     round(8 / (64 * layer_s + head_s), 3)}
+    return out
+
+
+def layer_step_measurement(dev, wsp, reps_copies=4):
+    """One Qwen3-8B decoder-layer step at M = 5 through the library, with
+    the BF16 glue fused into the quantizations: residual + RMSNorm + quant ->
+    [q;k;v] linear -> (attention is not built: a seeded bf16 stand-in for its
+    output) quant -> o linear -> residual + RMSNorm + quant -> [gate;up]
+    linear -> SwiGLU + quant -> down linear.  8 launches; 4 distinct layers'
+    weights rotate (775 MB, past the Infinity Cache)."""
+    import numpy as np
+    import torch
+
+    import synth
+    import w8a8_quantized_verification_amd as w8
+
+    M, D, F = 5, 4096, 12288
+    lins = synth.QWEN3_8B_LAYER
+    groups = ((0, 1, 2), (3,), (4, 5), (6,))
+    layers = []
+    for c in range(reps_copies):
+        row = []
+        for j, grp in enumerate(groups):
+            w = torch.cat([synth.weights_device(synth.W_LAYER_M5, 5000 + 10 * c + li,
+                                                lins[li].N, lins[li].K, dev) for li in grp])
+            row.append(w8.quantize_weight(w, tiled=True))
+            del w
+        layers.append(row)
+
+    def bf(x):
+        return torch.from_numpy(x.view(np.int16).copy()).view(torch.bfloat16).to(dev)
+
+    h = bf(synth.activations_bf16(synth.W_LAYER_M5, M, D, index=50))
+    attn = bf(synth.activations_bf16(synth.W_LAYER_M5, M, D, index=51))
+    gamma = bf(synth.to_bf16_bits(np.ones(D, dtype=np.float32)))
+    y_qkv = torch.empty(M, 6144, dtype=torch.bfloat16, device=dev)
+    y_o = torch.empty(M, D, dtype=torch.bfloat16, device=dev)
+    y_gu = torch.empty(M, 2 * F, dtype=torch.bfloat16, device=dev)
+    y_down = torch.zeros(M, D, dtype=torch.bfloat16, device=dev)
+    xq_d = torch.empty(M, D, dtype=torch.int8, device=dev)
+    xq_f = torch.empty(M, F, dtype=torch.int8, device=dev)
+    xs = torch.empty(M, dtype=torch.float32, device=dev)
+
+    def layer(c):
+        L = layers[c]
+        w8.residual_rmsnorm_quant(h, gamma, 1e-6, delta=y_down, h_out=h, xq=xq_d, x_scale=xs)
+        w8.linear(xq_d, xs, *L[0], y_bf16=y_qkv, workspace=wsp)
+        w8.quantize_act(attn, xq=xq_d, x_scale=xs)
+        w8.linear(xq_d, xs, *L[1], y_bf16=y_o, workspace=wsp)
+        w8.residual_rmsnorm_quant(h, gamma, 1e-6, delta=y_o, h_out=h, xq=xq_d, x_scale=xs)
+        w8.linear(xq_d, xs, *L[2], y_bf16=y_gu, workspace=wsp)
+        w8.silu_mul_quant(y_gu[:, :F], y_gu[:, F:], xq=xq_f, x_scale=xs)
+        w8.linear(xq_f, xs, *L[3], y_bf16=y_down, workspace=wsp)
+
+    t = graph_time([(lambda c=c: layer(c)) for c in range(reps_copies)], replays=20) / reps_copies
+    wbytes = sum(l.N * l.K for l in lins)
+    res = {"M": M, "us_per_layer": round(t * 1e6, 2),
+           "weight_GBs": round(wbytes / t / 1e9, 1),
+           "weight_frac_of_peak": round(wbytes / t / 1e9 / HBM_PEAK_GBS, 4),
+           "launches": 8,
+           "step": "rmsnorm+quant, qkv, quant(attn stand-in), o, rmsnorm+quant, gate_up, "
+                   "swiglu+quant, down"}
+    del layers
     return res
 
 
