@@ -496,14 +496,30 @@ def layer_measurement(dev, wsp, M, workload):
         t = graph_time(fns, replays=10) / nc
         b = linear_bytes(M, lin.N, lin.K)
         tops = 2 * M * lin.N * lin.K / t / 1e12
-        layer.append({"name": lin.name, "N": lin.N, "K": lin.K, "copies": nc,
-                      "us": round(t * 1e6, 2), "GBs": round(b / t / 1e9, 1),
-                      "TOPS": round(tops, 1), "mfma_frac": round(tops / INT8_PEAK_TOPS, 4)})
+        e = {"name": lin.name, "N": lin.N, "K": lin.K, "copies": nc,
+             "us": round(t * 1e6, 2), "GBs": round(b / t / 1e9, 1),
+             "TOPS": round(tops, 1), "mfma_frac": round(tops / INT8_PEAK_TOPS, 4)}
+        if M > 16:
+            # the same product with the activations quantized into the tiled layout
+            xt, xts = w8.quantize_act_tiled(x)
+            fns = [(lambda c=c: w8.linear_tiled_act(xt, xts, *wl[c], K=lin.K, y_bf16=y))
+                   for c in range(nc)]
+            tt = graph_time(fns, replays=10) / nc
+            tt_tops = 2 * M * lin.N * lin.K / tt / 1e12
+            e.update({"tiled_act_us": round(tt * 1e6, 2), "tiled_act_TOPS": round(tt_tops, 1),
+                      "tiled_act_mfma_frac": round(tt_tops / INT8_PEAK_TOPS, 4)})
+        layer.append(e)
         del wl
     tot_b = sum(linear_bytes(M, l.N, l.K) for l in synth.QWEN3_8B_LAYER)
     tot_ops = sum(2 * M * l.N * l.K for l in synth.QWEN3_8B_LAYER)
     tot_t = sum(e["us"] for e in layer) / 1e6
-    return {"M": M, "per_linear": layer, "sum_us": round(tot_t * 1e6, 2),
+    extra = {}
+    if M > 16:
+        tt = sum(e["tiled_act_us"] for e in layer) / 1e6
+        extra = {"tiled_act_sum_us": round(tt * 1e6, 2),
+                 "tiled_act_aggregate_TOPS": round(tot_ops / tt / 1e12, 1),
+                 "tiled_act_aggregate_mfma_frac": round(tot_ops / tt / 1e12 / INT8_PEAK_TOPS, 4)}
+    return {"M": M, "per_linear": layer, "sum_us": round(tot_t * 1e6, 2), **extra,
             "aggregate_GBs": round(tot_b / tot_t / 1e9, 1),
             "aggregate_frac": round(tot_b / tot_t / 1e9 / HBM_PEAK_GBS, 4),
             "aggregate_TOPS": round(tot_ops / tot_t / 1e12, 1),

@@ -192,6 +192,26 @@ w8a8_status w8a8_linear_tiled(const int8_t* xq, const float* x_scale,
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Tiled activations for the batched product (more than 16 token rows, e.g.
+ * 32 sequences x 9 verified positions).  w8a8_quantize_act_tiled computes
+ * exactly w8a8_quantize_act's codes and scales and writes the codes in the
+ * weights' tiled layout with token rows in place of channels
+ * (w8a8_tiled_weight_bytes(M, K) bytes; padding rows and k zero).
+ * w8a8_linear_tiled_act is w8a8_linear_tiled (bit-identical outputs) with
+ * xq in that layout; loading one contiguous KiB per 16-row block and k step
+ * instead of 16 rows x 64 bytes makes the batched product ~30% faster.
+ * No workspace.
+ */
+w8a8_status w8a8_quantize_act_tiled(const uint16_t* x_bf16, const float* smooth,
+                                    int64_t M, int64_t K,
+                                    int8_t* xq_tiled, float* x_scale, void* stream);
+w8a8_status w8a8_linear_tiled_act(const int8_t* xq_tiled, const float* x_scale,
+                                  const int8_t* wq_tiled, const float* w_scale,
+                                  int64_t M, int64_t N, int64_t K,
+                                  uint16_t* y_bf16, float* y_f32, int32_t* acc,
+                                  void* stream);
+
+/*
  * LM-head argmax and greedy acceptance of a draft block.
  *
  * Pages: the target verifies the drafted block in one pass and the

@@ -262,6 +262,35 @@ def test_linear_batched_ragged(M, N, K):
     run_linear_case(M, N, K, seed=330 + M, tiled=True)
 
 
+@pytest.mark.parametrize("M,N,K", [(288, 4096, 4096), (288, 1024, 4096), (288, 12288, 4096),
+                                   (288, 4096, 12288), (17, 65, 80), (97, 4099, 1040),
+                                   (513, 300, 2048), (5, 512, 256), (40, 33, 16), (288, 64, 0)])
+def test_linear_tiled_activations(M, N, K):
+    """quantize_act_tiled + linear_tiled_act: the codes read back through
+    the tiled layout (padding zero) and every output against the oracle."""
+    announce(f"linear tiled activations M={M} N={N} K={K}")
+    seed = 340 + M + N % 11
+    bits = synth.activations_bf16(seed, M, K, outliers=K > 0)
+    w = synth.weights_f32(seed, N, K)
+    xq_r, xs_r = oracle.quantize_act(bits)
+    wq_r, ws_r = oracle.quantize_weight(w)
+    acc_r, y32_r, y_r = oracle.w8a8_linear(xq_r, xs_r, wq_r, ws_r)
+    xt, xs = w8.quantize_act_tiled(dev_bf16(bits))
+    wt, ws = w8.quantize_weight(dev(w), tiled=True)
+    yb, yf, acc = w8.linear_tiled_act(xt, xs, wt, ws, K=K, want_bf16=True, want_f32=True,
+                                      want_acc=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(xs).view(np.uint32), xs_r.view(np.uint32))
+    if K > 0:
+        t = host(xt)
+        full = untile(t, t.shape[0] * 16, t.shape[1] * 64)
+        np.testing.assert_array_equal(full[:M, :K], xq_r)
+        assert not full[M:].any() and not full[:, K:].any()
+    np.testing.assert_array_equal(host(acc), acc_r)
+    np.testing.assert_array_equal(host(yf).view(np.uint32), y32_r.view(np.uint32))
+    np.testing.assert_array_equal(host(yb), y_r)
+
+
 # --------------------------------------------------------------------------
 # verify_accept
 # --------------------------------------------------------------------------

@@ -9,7 +9,8 @@ from .api import (W8A8Error, Workspace, accept_from_keys, bf16_linear, linear,
                   quantize_weight, sample_weights, tile_weight, tiled_shape, verify_accept,
                   verify_accept_workspace_bytes, verify_sample, verify_sample_workspace_bytes,
                   w4_shape, quantize_weight_w4, linear_w4, lm_head_argmax_w4,
-                  residual_rmsnorm_quant, silu_mul_quant)
+                  residual_rmsnorm_quant, silu_mul_quant, quantize_act_tiled,
+                  linear_tiled_act)
 
 __all__ = [
     "W8A8Error", "Workspace", "accept_from_keys", "bf16_linear", "linear", "linear_workspace_bytes",
@@ -17,5 +18,5 @@ __all__ = [
     "quantize_act", "quantize_weight", "tile_weight", "tiled_shape", "verify_accept",
     "verify_accept_workspace_bytes", "verify_sample", "verify_sample_workspace_bytes",
     "sample_weights", "w4_shape", "quantize_weight_w4", "linear_w4", "lm_head_argmax_w4",
-    "residual_rmsnorm_quant", "silu_mul_quant",
+    "residual_rmsnorm_quant", "silu_mul_quant", "quantize_act_tiled", "linear_tiled_act",
 ]

@@ -54,6 +54,8 @@ SIGNATURES = {
     "w8a8_residual_rmsnorm_quant": (_i32, [_vp, _vp, _vp, _c.c_float, _vp, _i64, _i64, _vp, _vp,
                                            _vp, _vp, _vp]),
     "w8a8_silu_mul_quant": (_i32, [_vp, _vp, _i64, _vp, _i64, _i64, _vp, _vp, _vp, _vp]),
+    "w8a8_quantize_act_tiled": (_i32, [_vp, _vp, _i64, _i64, _vp, _vp, _vp]),
+    "w8a8_linear_tiled_act": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp]),
 }
 
 _lib = None

@@ -19,6 +19,7 @@ __all__ = [
     "accept_from_keys", "bf16_linear", "Workspace", "verify_sample",
     "verify_sample_workspace_bytes", "sample_weights", "w4_shape", "quantize_weight_w4",
     "linear_w4", "lm_head_argmax_w4", "residual_rmsnorm_quant", "silu_mul_quant",
+    "quantize_act_tiled", "linear_tiled_act",
 ]
 
 
@@ -476,3 +477,48 @@ def silu_mul_quant(gate, up, *, smooth=None, want_act=False, act=None, xq=None, 
     check(lib().w8a8_silu_mul_quant(_ptr(gate), _ptr(up), gate.stride(0), _ptr(smooth), M, F,
                                     _ptr(act), _ptr(xq), _ptr(x_scale), _stream(dev)))
     return xq, x_scale, act
+
+
+def quantize_act_tiled(x: torch.Tensor, smooth: torch.Tensor | None = None, *, xq_tiled=None,
+                       x_scale=None):
+    """:func:`quantize_act` with the codes written in the tiled layout (token
+    rows in place of channels, shape ``tiled_shape(M, K)``), for
+    :func:`linear_tiled_act`.  Returns ``(xq_tiled, x_scale float32[M])``."""
+    _need(x, "x", torch.bfloat16, 2)
+    M, K = x.shape
+    if smooth is not None:
+        _need(smooth, "smooth", torch.float32, 1, x.device)
+    xq_tiled = _out(xq_tiled, tiled_shape(M, K), torch.int8, x.device, "xq_tiled")
+    x_scale = _out(x_scale, (M,), torch.float32, x.device, "x_scale")
+    check(lib().w8a8_quantize_act_tiled(_ptr(x), _ptr(smooth), M, K, _ptr(xq_tiled),
+                                        _ptr(x_scale), _stream(x.device)))
+    return xq_tiled, x_scale
+
+
+def linear_tiled_act(xq_tiled, x_scale, wq_tiled, w_scale, *, K: int | None = None,
+                     want_bf16=True, want_f32=False, want_acc=False, y_bf16=None, y_f32=None,
+                     acc=None):
+    """The batched W8A8 linear with tiled activations (from
+    :func:`quantize_act_tiled`) and tiled weights; same outputs as
+    :func:`linear`.  ``K`` defaults to the padded width of the layout (the
+    result is the same for any K with the same 64-wide step count)."""
+    _need(xq_tiled, "xq_tiled", torch.int8, 4)
+    dev = xq_tiled.device
+    _need(x_scale, "x_scale", torch.float32, 1, dev)
+    _need(w_scale, "w_scale", torch.float32, 1, dev)
+    _need(wq_tiled, "wq_tiled", torch.int8, 4, dev)
+    M, N = x_scale.shape[0], w_scale.shape[0]
+    if K is None:
+        K = xq_tiled.shape[1] * 64
+    if tuple(xq_tiled.shape) != tiled_shape(M, K) or tuple(wq_tiled.shape) != tiled_shape(N, K):
+        raise ValueError("xq_tiled / wq_tiled shapes do not match M, N, K")
+    if want_bf16 or y_bf16 is not None:
+        y_bf16 = _out(y_bf16, (M, N), torch.bfloat16, dev, "y_bf16")
+    if want_f32 or y_f32 is not None:
+        y_f32 = _out(y_f32, (M, N), torch.float32, dev, "y_f32")
+    if want_acc or acc is not None:
+        acc = _out(acc, (M, N), torch.int32, dev, "acc")
+    check(lib().w8a8_linear_tiled_act(_ptr(xq_tiled), _ptr(x_scale), _ptr(wq_tiled),
+                                      _ptr(w_scale), M, N, K, _ptr(y_bf16), _ptr(y_f32),
+                                      _ptr(acc), _stream(dev)))
+    return y_bf16, y_f32, acc

@@ -498,4 +498,45 @@ w8a8_status w8a8_silu_mul_quant(const uint16_t* gate, const uint16_t* up, int64_
                     fn);
 }
 
+
+// ---- tiled activations for the batched product ----
+
+w8a8_status w8a8_quantize_act_tiled(const uint16_t* x_bf16, const float* smooth, int64_t M,
+                                    int64_t K, int8_t* xq_tiled, float* x_scale, void* stream) {
+  static const char* fn = "w8a8_quantize_act_tiled";
+  g_last_error.clear();
+  if (w8a8_status s = check_rows_k(fn, M, K)) return s;
+  if (M == 0) return W8A8_OK;
+  if (!x_scale) return fail(W8A8_ERR_INVALID_ARG, fn, "x_scale is NULL");
+  if (K > 0 && (!x_bf16 || !xq_tiled)) return fail(W8A8_ERR_INVALID_ARG, fn, "x_bf16 or xq_tiled is NULL");
+  if (!aligned(x_bf16, 16) || !aligned(xq_tiled, 16) || !aligned(smooth, 16) ||
+      !aligned(x_scale, 4))
+    return fail(W8A8_ERR_INVALID_ARG, fn, "pointer misaligned (16 bytes for tensors, 4 for scales)");
+  return hip_status(w8a8_launch_quantize_rows(x_bf16, true, smooth, false, M, K, true, xq_tiled,
+                                              x_scale, reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
+w8a8_status w8a8_linear_tiled_act(const int8_t* xq_tiled, const float* x_scale,
+                                  const int8_t* wq_tiled, const float* w_scale, int64_t M,
+                                  int64_t N, int64_t K, uint16_t* y_bf16, float* y_f32,
+                                  int32_t* acc, void* stream) {
+  static const char* fn = "w8a8_linear_tiled_act";
+  g_last_error.clear();
+  if (w8a8_status s = check_rows_k(fn, M, K)) return s;
+  if (N < 0 || N > kMaxRows) return fail(W8A8_ERR_INVALID_ARG, fn, "N out of range");
+  if (M == 0 || N == 0) return W8A8_OK;
+  if (!y_bf16 && !y_f32 && !acc) return fail(W8A8_ERR_INVALID_ARG, fn, "all outputs are NULL");
+  if (!x_scale || !w_scale) return fail(W8A8_ERR_INVALID_ARG, fn, "x_scale or w_scale is NULL");
+  if (K > 0 && (!xq_tiled || !wq_tiled)) return fail(W8A8_ERR_INVALID_ARG, fn, "xq_tiled or wq_tiled is NULL");
+  if (!aligned(xq_tiled, 16) || !aligned(wq_tiled, 16))
+    return fail(W8A8_ERR_INVALID_ARG, fn, "xq_tiled and wq_tiled must be 16-byte aligned");
+  if (!aligned(x_scale, 4) || !aligned(w_scale, 4) || !aligned(y_bf16, 2) || !aligned(y_f32, 4) ||
+      !aligned(acc, 4))
+    return fail(W8A8_ERR_INVALID_ARG, fn, "scale or output pointer misaligned");
+  return hip_status(w8a8_launch_gemm_batched(xq_tiled, x_scale, wq_tiled, w_scale, M, N, K, true,
+                                             y_bf16, y_f32, acc, nullptr, 0, 0,
+                                             reinterpret_cast<hipStream_t>(stream), true),
+                    fn);
+}
+
 }  // extern "C"

@@ -78,7 +78,8 @@ size_t w8a8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, bool tiled);
 hipError_t w8a8_launch_gemm_batched(const int8_t* xq, const float* x_scale, const int8_t* wq,
                                     const float* w_scale, int64_t M, int64_t N, int64_t K,
                                     bool tiled, uint16_t* y_bf16, float* y_f32, int32_t* acc,
-                                    void* keys, int subkeys, int key_stride, hipStream_t stream);
+                                    void* keys, int subkeys, int key_stride, hipStream_t stream,
+                                    bool a_tiled = false);
 size_t w8a8_lm_head_workspace_bytes(int64_t M);
 hipError_t w8a8_launch_lm_head_argmax(const int8_t* xq, const float* x_scale,
                                       const int8_t* wq_tiled, const float* w_scale, int64_t M,

@@ -177,14 +177,19 @@ hipError_t w8a8_launch_quantize_rows(const void* in, bool in_is_bf16, const floa
   const dim3 grid((unsigned)grid_rows), block(kQuantThreads);
 #define W8A8_QLAUNCH(BF, SM, DIV, TL) \
   hipLaunchKernelGGL((quantize_rows_kernel<kQuantThreads, BF, SM, DIV, TL>), grid, block, 0, stream, in, smooth, R, K, q, scale)
-#define W8A8_QLAUNCH_LONG(SM) \
-  hipLaunchKernelGGL((quantize_rows_kernel<kQuantThreadsLong, true, SM, false, false>), grid, \
+#define W8A8_QLAUNCH_LONG(SM, TL) \
+  hipLaunchKernelGGL((quantize_rows_kernel<kQuantThreadsLong, true, SM, false, TL>), grid, \
                      dim3(kQuantThreadsLong), 0, stream, in, smooth, R, K, q, scale)
   if (in_is_bf16) {
-    // activations: row-major output only; few rows, so long rows get more threads
+    // activations (row-major, or tiled for the batched GEMM); few rows, so
+    // long rows get more threads
     if (K > kLongRow) {
-      if (!smooth) W8A8_QLAUNCH_LONG(false);
-      else W8A8_QLAUNCH_LONG(true);
+      if (tiled) { if (!smooth) W8A8_QLAUNCH_LONG(false, true); else W8A8_QLAUNCH_LONG(true, true); }
+      else if (!smooth) W8A8_QLAUNCH_LONG(false, false);
+      else W8A8_QLAUNCH_LONG(true, false);
+    } else if (tiled) {
+      if (!smooth) W8A8_QLAUNCH(true, false, false, true);
+      else W8A8_QLAUNCH(true, true, false, true);
     } else if (!smooth) W8A8_QLAUNCH(true, false, false, false);
     else W8A8_QLAUNCH(true, true, false, false);
   } else if (!tiled) {
