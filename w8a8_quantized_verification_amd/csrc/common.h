@@ -11,6 +11,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
+constexpr int kXcds = 8;   // MI355X: 8 XCDs, each with its own L2; workgroups go round-robin
 
 // fp32 -> bf16 bit pattern, round to nearest with ties to even; NaN stays a
 // quiet NaN with its sign.

@@ -33,8 +33,6 @@
 
 namespace w8a8 {
 
-constexpr int kXcds = 8;
-
 struct BatchedArgs {
   const int8_t* xq;
   const float* xs;
