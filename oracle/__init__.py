@@ -21,7 +21,8 @@ the pages by eye:
   logits, acceptance of each draft with its probability, residual or bonus
   sampling by inverse CDF (``sample``);
 * the BF16 glue between linears: residual add, RMSNorm and SwiGLU before
-  the next quantization (``glue``);
+  the next quantization (``glue``), and the verified block's causal,
+  grouped-query attention over the KV cache (``attention``);
 * the bf16 reference layer and the weight-traffic closed forms
   (``reference``).
 
@@ -48,6 +49,7 @@ from .gemm import int8_gemm, dequant, w8a8_linear, INT32_MAX_K
 from .accept import argmax_rows, greedy_accept, verify_accept
 from .sample import exp_f32, fixed_weights, verify_sample
 from .glue import residual_add, rmsnorm, silu_mul
+from .attention import verify_attention
 from .reference import (bf16_reference_logits, w8a8_linear_bytes,
                         bf16_linear_bytes, weight_bytes_int8, weight_bytes_bf16)
 
@@ -57,5 +59,5 @@ __all__ = [
     "argmax_rows", "greedy_accept", "verify_accept", "bf16_reference_logits",
     "w8a8_linear_bytes", "bf16_linear_bytes", "weight_bytes_int8",
     "weight_bytes_bf16", "exp_f32", "fixed_weights", "verify_sample", "quantize_weight_int4",
-    "residual_add", "rmsnorm", "silu_mul",
+    "residual_add", "rmsnorm", "silu_mul", "verify_attention",
 ]

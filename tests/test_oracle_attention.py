@@ -1,0 +1,80 @@
+"""Pins of the oracle's verify attention (oracle/attention.py): closed forms
+(one visible key returns its value; equal keys average the values), the
+causal limit (keys beyond a query's position do not change it), the
+grouped-query head mapping, and torch's float64 scaled-dot-product attention
+with an explicit mask as an independent library reference."""
+import numpy as np
+import torch
+
+import oracle
+
+RNG = np.random.default_rng(55)
+
+
+def bits(x):
+    return oracle.f32_to_bf16(np.asarray(x, dtype=np.float32))
+
+
+def val(b):
+    return oracle.bf16_to_f32(b).astype(np.float64)
+
+
+def rand_case(B=2, T=3, Hq=4, Hkv=2, Dh=16, Lmax=20):
+    q = bits(RNG.standard_normal((B, T, Hq, Dh)))
+    k = bits(RNG.standard_normal((B, Hkv, Lmax, Dh)))
+    v = bits(RNG.standard_normal((B, Hkv, Lmax, Dh)))
+    return q, k, v
+
+
+def test_single_visible_key_returns_its_value():
+    q, k, v = rand_case(B=1, T=1, Hq=2, Hkv=1)
+    o = val(oracle.verify_attention(q, k, v, [1]))
+    np.testing.assert_array_equal(o[0, 0, 0], val(v)[0, 0, 0])
+    np.testing.assert_array_equal(o[0, 0, 1], val(v)[0, 0, 0])
+
+
+def test_equal_keys_average_the_values():
+    q, k, v = rand_case(B=1, T=1, Hq=1, Hkv=1, Lmax=8)
+    k[:] = k[:, :, :1]                      # every key the same
+    o = val(oracle.verify_attention(q, k, v, [8]))
+    want = val(oracle.glue._f64_to_bf16_bits(val(v)[0, 0].mean(axis=0)))
+    np.testing.assert_array_equal(o[0, 0, 0], want)
+
+
+def test_causal_limit_and_group_mapping():
+    q, k, v = rand_case(B=2, T=3, Hq=4, Hkv=2, Lmax=20)
+    L = [10, 20]
+    o = oracle.verify_attention(q, k, v, L)
+    k2, v2 = k.copy(), v.copy()
+    k2[0, :, 10:] = bits(RNG.standard_normal(k2[0, :, 10:].shape))   # beyond L_0
+    v2[0, :, 10:] = bits(RNG.standard_normal(v2[0, :, 10:].shape))
+    np.testing.assert_array_equal(oracle.verify_attention(q, k2, v2, L), o)
+    # query 0 of sequence 1 sees keys 0..17 only; changing key 18 leaves it alone
+    k3 = k.copy()
+    k3[1, :, 18] = bits(RNG.standard_normal(k3[1, :, 18].shape))
+    o3 = oracle.verify_attention(q, k3, v, L)
+    np.testing.assert_array_equal(o3[1, 0], o[1, 0])
+    assert not np.array_equal(o3[1, 1], o[1, 1])
+    # heads 0, 1 read kv head 0; changing kv head 1 leaves them alone
+    k4 = k.copy()
+    k4[:, 1] = bits(RNG.standard_normal(k4[:, 1].shape))
+    o4 = oracle.verify_attention(q, k4, v, L)
+    np.testing.assert_array_equal(o4[:, :, :2], o[:, :, :2])
+
+
+def test_against_torch_sdpa_float64():
+    B, T, Hq, Hkv, Dh, Lmax = 2, 5, 8, 2, 64, 40
+    q, k, v = rand_case(B, T, Hq, Hkv, Dh, Lmax)
+    L = [33, 40]
+    o = val(oracle.verify_attention(q, k, v, L))
+    for b in range(B):
+        qt = torch.from_numpy(val(q)[b]).permute(1, 0, 2)                      # Hq T Dh
+        kt = torch.from_numpy(val(k)[b, :, :L[b]]).repeat_interleave(Hq // Hkv, 0)
+        vt = torch.from_numpy(val(v)[b, :, :L[b]]).repeat_interleave(Hq // Hkv, 0)
+        pos = torch.arange(L[b])[None, :]
+        last = L[b] - T + torch.arange(T)[:, None]
+        mask = pos <= last                                                      # T x L
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask)
+        ref = ref.permute(1, 0, 2).numpy()                                       # T Hq Dh
+        got = o[b]
+        assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-12)
