@@ -328,6 +328,30 @@ w8a8_status w8a8_silu_mul_quant(const uint16_t* gate, const uint16_t* up,
                                 int8_t* xq, float* x_scale, void* stream);
 
 /*
+ * Attention of the verified block over the KV cache (the softmax part of
+ * the verifier, kept in high precision after the dequant step: [de] §2
+ * "De-Quantisierung"; [it] §2 pipeline; [ja] §2.2 item 3).
+ * For sequence b with L_b = lengths[b] valid cache positions, the last T of
+ * which are the verified block's own keys and values, query i (0 <= i < T)
+ * and head h read kv head h / (Hq / Hkv) and positions j <= L_b - T + i:
+ *   out[b][i][h] = softmax_j(q[b][i][h] . k[b][kvh][j] / sqrt(Dh)) . v[b][kvh][j]
+ * in fp32 (summation order unspecified), rounded to bf16.
+ *
+ * q [B][T][Hq][Dh], k_cache and v_cache [B][Hkv][Lmax][Dh], out
+ * [B][T][Hq][Dh], all bf16; q, k, v 16-byte aligned; lengths [B] int32 on
+ * the device (values outside [T, Lmax] are clamped into it).  Requires Dh
+ * == 128 (else W8A8_ERR_UNSUPPORTED), Hq % Hkv == 0, T * Hq / Hkv <= 64.
+ * workspace: at least w8a8_verify_attention_workspace_bytes(B, Hkv, Lmax)
+ * bytes, 256-byte aligned; no initial contents needed.
+ */
+size_t      w8a8_verify_attention_workspace_bytes(int64_t B, int64_t Hkv, int64_t Lmax);
+w8a8_status w8a8_verify_attention(const uint16_t* q, const uint16_t* k_cache,
+                                  const uint16_t* v_cache, const int32_t* lengths,
+                                  int64_t B, int64_t T, int64_t Hq, int64_t Hkv,
+                                  int64_t Dh, int64_t Lmax, uint16_t* out,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * W4A8: the verifier's weights in 4 bits (int4 codes, one fp32 scale per
  * output channel), activations as in W8A8.
  *

@@ -182,6 +182,27 @@ def test_glue_validation(lib):
     assert g(None, None, 256, None, 0, 128, None, None, None, None) == OK
 
 
+def test_verify_attention_validation(lib):
+    f = lib.w8a8_verify_attention
+    need = lib.w8a8_verify_attention_workspace_bytes(1, 8, 4096)
+    assert need > 0
+    args = dict(q=A16, k=A16b, v=A16, ln=A16, B=1, T=5, Hq=32, Hkv=8, Dh=128, L=4096, out=A16,
+                w=A16, wb=need)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(a["q"], a["k"], a["v"], a["ln"], a["B"], a["T"], a["Hq"], a["Hkv"], a["Dh"],
+                 a["L"], a["out"], a["w"], a["wb"], None)
+    assert call(Dh=64) == UNSUPPORTED
+    assert call(T=17) == UNSUPPORTED          # 17 * 4 > 64 query rows per kv head
+    assert call(Hq=30) == INVALID
+    assert call(L=4) == INVALID
+    assert call(q=A16 + 8) == INVALID
+    assert call(ln=None) == INVALID
+    assert call(wb=8) == WORKSPACE
+    assert call(B=0, q=None, k=None, v=None, ln=None, out=None, w=None) == OK
+
+
 def test_bf16_linear_validation(lib):
     f = lib.w8a8_bf16_linear
     assert f(A16, A16b, 17, 512, 256, A16, None, None) == UNSUPPORTED

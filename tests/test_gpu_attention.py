@@ -1,0 +1,78 @@
+"""GPU parity of the verified block's attention (w8a8_verify_attention,
+through the C ABI) against the oracle's float64 computation
+(oracle.verify_attention).
+
+Bar: every bf16 output within 1e-2 relative / 1e-3 absolute of the oracle
+(the stated bf16 tolerance); the fraction of bit-identical outputs is
+reported.  Shapes: the Qwen3-8B heads (32 query, 8 kv, dim 128) at M = 5
+(1 sequence, T = 5) over 4096 cached positions, the 32B heads (64 / 8) at
+T = 8, 32 sequences of T = 9 with ragged lengths, and lengths at the edges
+(exactly T, a split boundary, Lmax)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.gpu_util import announce, dev, dev_bf16, gpu_available, host
+
+pytestmark = pytest.mark.gpu
+
+if gpu_available():
+    import w8a8_quantized_verification_amd as w8
+
+W_ATT = 9
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not gpu_available():
+        pytest.skip("no ROCm GPU")
+
+
+def draw(shape, index, scale=1.0):
+    z = synth.rng(W_ATT, 30, index).standard_normal(shape, dtype=np.float32) * np.float32(scale)
+    return synth.to_bf16_bits(z)
+
+
+@pytest.mark.parametrize("B,T,Hq,Hkv,Lmax,lengths", [
+    (1, 5, 32, 8, 4096, [4096]),
+    (1, 5, 32, 8, 4096, [1000]),
+    (1, 8, 64, 8, 2048, [2048]),
+    (32, 9, 32, 8, 600, None),                  # ragged lengths
+    (3, 4, 16, 4, 700, [4, 256 + 4, 700]),       # exactly T; a split boundary; Lmax
+    (2, 1, 8, 8, 64, [1, 64]),
+])
+def test_verify_attention(B, T, Hq, Hkv, Lmax, lengths):
+    announce(f"verify_attention B={B} T={T} Hq={Hq} Hkv={Hkv} Lmax={Lmax}")
+    q = draw((B, T, Hq, 128), 1)
+    k = draw((B, Hkv, Lmax, 128), 2)
+    v = draw((B, Hkv, Lmax, 128), 3)
+    if lengths is None:
+        lengths = synth.rng(W_ATT, 31, B).integers(T, Lmax + 1, size=B)
+    lengths = np.asarray(lengths, dtype=np.int32)
+    want = oracle.verify_attention(q, k, v, lengths)
+    out = w8.verify_attention(dev_bf16(q), dev_bf16(k), dev_bf16(v), dev(lengths))
+    torch.cuda.synchronize()
+    got = host(out)
+    g = oracle.bf16_to_f32(got).astype(np.float64)
+    w = oracle.bf16_to_f32(want).astype(np.float64)
+    assert np.all(np.abs(g - w) <= 1e-3 + 1e-2 * np.abs(w))
+    print(f"[gpu] bit-identical fraction {np.mean(got == want):.4f}", flush=True)
+
+
+def test_verify_attention_sharp_softmax():
+    """Large scores (a nearly one-hot softmax) and all-equal keys."""
+    announce("verify_attention sharp and flat softmax")
+    B, T, Hq, Hkv, Lmax = 2, 5, 8, 2, 300
+    q = draw((B, T, Hq, 128), 4, scale=3.0)
+    k = draw((B, Hkv, Lmax, 128), 5, scale=3.0)
+    v = draw((B, Hkv, Lmax, 128), 6)
+    k[1] = k[1, :, :1]                          # sequence 1: every key equal
+    lengths = np.array([300, 257], dtype=np.int32)
+    want = oracle.verify_attention(q, k, v, lengths)
+    out = w8.verify_attention(dev_bf16(q), dev_bf16(k), dev_bf16(v), dev(lengths))
+    torch.cuda.synchronize()
+    g = oracle.bf16_to_f32(host(out)).astype(np.float64)
+    w = oracle.bf16_to_f32(want).astype(np.float64)
+    assert np.all(np.abs(g - w) <= 1e-3 + 1e-2 * np.abs(w))

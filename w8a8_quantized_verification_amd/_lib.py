@@ -56,6 +56,9 @@ SIGNATURES = {
     "w8a8_silu_mul_quant": (_i32, [_vp, _vp, _i64, _vp, _i64, _i64, _vp, _vp, _vp, _vp]),
     "w8a8_quantize_act_tiled": (_i32, [_vp, _vp, _i64, _i64, _vp, _vp, _vp]),
     "w8a8_linear_tiled_act": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp]),
+    "w8a8_verify_attention_workspace_bytes": (_sz, [_i64, _i64, _i64]),
+    "w8a8_verify_attention": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _vp,
+                                     _vp, _sz, _vp]),
 }
 
 _lib = None

@@ -19,7 +19,7 @@ __all__ = [
     "accept_from_keys", "bf16_linear", "Workspace", "verify_sample",
     "verify_sample_workspace_bytes", "sample_weights", "w4_shape", "quantize_weight_w4",
     "linear_w4", "lm_head_argmax_w4", "residual_rmsnorm_quant", "silu_mul_quant",
-    "quantize_act_tiled", "linear_tiled_act",
+    "quantize_act_tiled", "linear_tiled_act", "verify_attention",
 ]
 
 
@@ -522,3 +522,28 @@ def linear_tiled_act(xq_tiled, x_scale, wq_tiled, w_scale, *, K: int | None = No
                                       _ptr(w_scale), M, N, K, _ptr(y_bf16), _ptr(y_f32),
                                       _ptr(acc), _stream(dev)))
     return y_bf16, y_f32, acc
+
+
+def verify_attention(q, k_cache, v_cache, lengths, *, out=None, workspace: Workspace | None = None):
+    """Causal grouped-query attention of the verified block: ``q`` bf16
+    ``[B][T][Hq][128]``, ``k_cache``/``v_cache`` bf16 ``[B][Hkv][Lmax][128]``,
+    ``lengths`` int32 ``[B]`` (valid cache positions, the block's own T
+    included).  Returns ``out`` bf16 ``[B][T][Hq][128]``."""
+    _need(q, "q", torch.bfloat16, 4)
+    dev = q.device
+    _need(k_cache, "k_cache", torch.bfloat16, 4, dev)
+    _need(v_cache, "v_cache", torch.bfloat16, 4, dev)
+    _need(lengths, "lengths", torch.int32, 1, dev)
+    B, T, Hq, Dh = q.shape
+    _, Hkv, Lmax, _ = k_cache.shape
+    if tuple(k_cache.shape) != (B, Hkv, Lmax, Dh) or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache must be [B][Hkv][Lmax][Dh]")
+    if lengths.shape[0] != B:
+        raise ValueError("lengths must have B entries")
+    out = _out(out, (B, T, Hq, Dh), torch.bfloat16, dev, "out")
+    need = int(lib().w8a8_verify_attention_workspace_bytes(B, Hkv, Lmax))
+    ws = (workspace or _default_ws).get(need, dev, use="verify")
+    check(lib().w8a8_verify_attention(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(lengths), B, T,
+                                      Hq, Hkv, Dh, Lmax, _ptr(out), _ptr(ws),
+                                      0 if ws is None else ws.numel(), _stream(dev)))
+    return out

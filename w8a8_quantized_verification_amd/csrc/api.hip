@@ -539,4 +539,40 @@ w8a8_status w8a8_linear_tiled_act(const int8_t* xq_tiled, const float* x_scale,
                     fn);
 }
 
+
+// ---- attention of the verified block ----
+
+size_t w8a8_verify_attention_workspace_bytes(int64_t B, int64_t Hkv, int64_t Lmax) {
+  if (B <= 0 || Hkv <= 0 || Lmax <= 0 || B > 65535 || Hkv > 65535 || Lmax > (1 << 24)) return 0;
+  return w8a8_attention_workspace_bytes_impl(B, Hkv, Lmax);
+}
+
+w8a8_status w8a8_verify_attention(const uint16_t* q, const uint16_t* k_cache,
+                                  const uint16_t* v_cache, const int32_t* lengths, int64_t B,
+                                  int64_t T, int64_t Hq, int64_t Hkv, int64_t Dh, int64_t Lmax,
+                                  uint16_t* out, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  static const char* fn = "w8a8_verify_attention";
+  g_last_error.clear();
+  if (B < 0 || B > 65535) return fail(W8A8_ERR_INVALID_ARG, fn, "B out of range");
+  if (B == 0) return W8A8_OK;
+  if (Dh != 128) return fail(W8A8_ERR_UNSUPPORTED, fn, "head dimension must be 128");
+  if (T < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || Hkv > 65535 || Hq > 65535)
+    return fail(W8A8_ERR_INVALID_ARG, fn, "T, Hq, Hkv must be >= 1 with Hq % Hkv == 0");
+  if (T * (Hq / Hkv) > 64)
+    return fail(W8A8_ERR_UNSUPPORTED, fn, "T * Hq / Hkv must be <= 64");
+  if (Lmax < T || Lmax > (1 << 24)) return fail(W8A8_ERR_INVALID_ARG, fn, "Lmax out of range [T, 2^24]");
+  if (!q || !k_cache || !v_cache || !lengths || !out)
+    return fail(W8A8_ERR_INVALID_ARG, fn, "required pointer is NULL");
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 4) ||
+      !aligned(lengths, 4))
+    return fail(W8A8_ERR_INVALID_ARG, fn, "q/k/v must be 16-byte aligned, out and lengths 4");
+  if (!workspace || workspace_bytes < w8a8_attention_workspace_bytes_impl(B, Hkv, Lmax))
+    return fail(W8A8_ERR_WORKSPACE, fn, "workspace NULL or smaller than w8a8_verify_attention_workspace_bytes()");
+  if (!aligned(workspace, 256)) return fail(W8A8_ERR_INVALID_ARG, fn, "workspace must be 256-byte aligned");
+  return hip_status(w8a8_launch_verify_attention(q, k_cache, v_cache, lengths, B, T, Hq, Hkv, Lmax,
+                                                 out, workspace,
+                                                 reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
 }  // extern "C"

@@ -136,3 +136,9 @@ hipError_t w8a8_launch_residual_rmsnorm_quant(const uint16_t* h, const uint16_t*
 hipError_t w8a8_launch_silu_mul_quant(const uint16_t* gate, const uint16_t* up, int64_t stride,
                                       const float* smooth, int64_t M, int64_t F, uint16_t* act,
                                       int8_t* xq, float* x_scale, hipStream_t stream);
+
+size_t w8a8_attention_workspace_bytes_impl(int64_t B, int64_t Hkv, int64_t Lmax);
+hipError_t w8a8_launch_verify_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                        const int32_t* lengths, int64_t B, int64_t T,
+                                        int64_t Hq, int64_t Hkv, int64_t Lmax, uint16_t* out,
+                                        void* workspace, hipStream_t stream);
