@@ -866,23 +866,26 @@ def oracle_timings():
     return out
 
 
-def layer_step_measurement(dev, wsp, reps_copies=4):
-    """One Qwen3-8B decoder-layer step at M = 5 through the library, with
-    the BF16 glue fused into the quantizations: residual + RMSNorm + quant ->
-    [q;k;v] linear -> (attention is not built: a seeded bf16 stand-in for its
-    output) quant -> o linear -> residual + RMSNorm + quant -> [gate;up]
-    linear -> SwiGLU + quant -> down linear.  8 launches; 4 distinct layers'
-    weights rotate (775 MB, past the Infinity Cache)."""
+def layer_step_measurement(dev, wsp, reps_copies=4, ctx=4096):
+    """One Qwen3-8B decoder-layer step at M = 5 (one sequence, 4 drafts + 1)
+    through the library, glue fused into the quantizations and attention
+    over a 4096-position KV cache: residual + RMSNorm + quant -> [q;k;v]
+    linear -> attention (the cache already holds the block's keys and
+    values; per-head q/k norms and RoPE are not built) -> quant -> o linear -> residual + RMSNorm +
+    quant -> [gate;up] linear -> SwiGLU + quant -> down linear.  10 launches;
+    the query is a seeded stand-in buffer;
+    4 distinct layers' weights and caches rotate (775 MB of weights, past the
+    Infinity Cache).  Also attention alone."""
     import numpy as np
     import torch
 
     import synth
     import w8a8_quantized_verification_amd as w8
 
-    M, D, F = 5, 4096, 12288
+    M, D, F, Hq, Hkv, Dh = 5, 4096, 12288, 32, 8, 128
     lins = synth.QWEN3_8B_LAYER
     groups = ((0, 1, 2), (3,), (4, 5), (6,))
-    layers = []
+    layers, caches = [], []
     for c in range(reps_copies):
         row = []
         for j, grp in enumerate(groups):
@@ -891,26 +894,36 @@ def layer_step_measurement(dev, wsp, reps_copies=4):
             row.append(w8.quantize_weight(w, tiled=True))
             del w
         layers.append(row)
+        kv = torch.randn(2, 1, Hkv, ctx, Dh, device=dev, generator=torch.Generator(device=dev)
+                         .manual_seed(900 + c)).to(torch.bfloat16)
+        caches.append((kv[0].contiguous(), kv[1].contiguous()))
 
     def bf(x):
         return torch.from_numpy(x.view(np.int16).copy()).view(torch.bfloat16).to(dev)
 
     h = bf(synth.activations_bf16(synth.W_LAYER_M5, M, D, index=50))
-    attn = bf(synth.activations_bf16(synth.W_LAYER_M5, M, D, index=51))
     gamma = bf(synth.to_bf16_bits(np.ones(D, dtype=np.float32)))
+    lengths = torch.full((1,), ctx, dtype=torch.int32, device=dev)
     y_qkv = torch.empty(M, 6144, dtype=torch.bfloat16, device=dev)
+    attn = torch.empty(1, M, Hq, Dh, dtype=torch.bfloat16, device=dev)
+    qbuf = torch.randn(1, M, Hq, Dh, device=dev, generator=torch.Generator(device=dev)
+                       .manual_seed(899)).to(torch.bfloat16)
     y_o = torch.empty(M, D, dtype=torch.bfloat16, device=dev)
     y_gu = torch.empty(M, 2 * F, dtype=torch.bfloat16, device=dev)
     y_down = torch.zeros(M, D, dtype=torch.bfloat16, device=dev)
     xq_d = torch.empty(M, D, dtype=torch.int8, device=dev)
     xq_f = torch.empty(M, F, dtype=torch.int8, device=dev)
     xs = torch.empty(M, dtype=torch.float32, device=dev)
+    awsp = w8.Workspace()
 
     def layer(c):
         L = layers[c]
         w8.residual_rmsnorm_quant(h, gamma, 1e-6, delta=y_down, h_out=h, xq=xq_d, x_scale=xs)
         w8.linear(xq_d, xs, *L[0], y_bf16=y_qkv, workspace=wsp)
-        w8.quantize_act(attn, xq=xq_d, x_scale=xs)
+        # the query: a [B][T][Hq][128] buffer standing in for the normed,
+        # rotated q columns of [q;k;v] (those steps are not built)
+        w8.verify_attention(qbuf, *caches[c], lengths, out=attn, workspace=awsp)
+        w8.quantize_act(attn.view(M, D), xq=xq_d, x_scale=xs)
         w8.linear(xq_d, xs, *L[1], y_bf16=y_o, workspace=wsp)
         w8.residual_rmsnorm_quant(h, gamma, 1e-6, delta=y_o, h_out=h, xq=xq_d, x_scale=xs)
         w8.linear(xq_d, xs, *L[2], y_bf16=y_gu, workspace=wsp)
@@ -918,14 +931,21 @@ def layer_step_measurement(dev, wsp, reps_copies=4):
         w8.linear(xq_f, xs, *L[3], y_bf16=y_down, workspace=wsp)
 
     t = graph_time([(lambda c=c: layer(c)) for c in range(reps_copies)], replays=20) / reps_copies
+    t_att = graph_time([(lambda c=c: w8.verify_attention(qbuf, *caches[c], lengths, out=attn,
+                                                         workspace=awsp))
+                        for c in range(reps_copies)], replays=20) / reps_copies
     wbytes = sum(l.N * l.K for l in lins)
-    res = {"M": M, "us_per_layer": round(t * 1e6, 2),
+    kvbytes = 2 * Hkv * ctx * Dh * 2
+    res = {"M": M, "context": ctx, "us_per_layer": round(t * 1e6, 2),
            "weight_GBs": round(wbytes / t / 1e9, 1),
-           "weight_frac_of_peak": round(wbytes / t / 1e9 / HBM_PEAK_GBS, 4),
-           "launches": 8,
-           "step": "rmsnorm+quant, qkv, quant(attn stand-in), o, rmsnorm+quant, gate_up, "
-                   "swiglu+quant, down"}
-    del layers
+           "weight_plus_kv_GBs": round((wbytes + kvbytes) / t / 1e9, 1),
+           "weight_plus_kv_frac_of_peak": round((wbytes + kvbytes) / t / 1e9 / HBM_PEAK_GBS, 4),
+           "attention_us": round(t_att * 1e6, 2),
+           "attention_kv_GBs": round(kvbytes / t_att / 1e9, 1),
+           "launches": 10,
+           "step": "rmsnorm+quant, qkv, attention (2 kernels), quant, o, rmsnorm+quant, gate_up, "
+                   "swiglu+quant, down; no q/k norms or RoPE, cache pre-filled"}
+    del layers, caches
     return res
 
 

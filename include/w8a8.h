@@ -340,7 +340,8 @@ w8a8_status w8a8_silu_mul_quant(const uint16_t* gate, const uint16_t* up,
  * q [B][T][Hq][Dh], k_cache and v_cache [B][Hkv][Lmax][Dh], out
  * [B][T][Hq][Dh], all bf16; q, k, v 16-byte aligned; lengths [B] int32 on
  * the device (values outside [T, Lmax] are clamped into it).  Requires Dh
- * == 128 (else W8A8_ERR_UNSUPPORTED), Hq % Hkv == 0, T * Hq / Hkv <= 64.
+ * == 128 (else W8A8_ERR_UNSUPPORTED), Hq % Hkv == 0, T * Hq / Hkv <= 64,
+ * T <= Lmax <= 131072.
  * workspace: at least w8a8_verify_attention_workspace_bytes(B, Hkv, Lmax)
  * bytes, 256-byte aligned; no initial contents needed.
  */

@@ -543,7 +543,7 @@ w8a8_status w8a8_linear_tiled_act(const int8_t* xq_tiled, const float* x_scale,
 // ---- attention of the verified block ----
 
 size_t w8a8_verify_attention_workspace_bytes(int64_t B, int64_t Hkv, int64_t Lmax) {
-  if (B <= 0 || Hkv <= 0 || Lmax <= 0 || B > 65535 || Hkv > 65535 || Lmax > (1 << 24)) return 0;
+  if (B <= 0 || Hkv <= 0 || Lmax <= 0 || B > 65535 || Hkv > 65535 || Lmax > (1 << 17)) return 0;
   return w8a8_attention_workspace_bytes_impl(B, Hkv, Lmax);
 }
 
@@ -561,7 +561,7 @@ w8a8_status w8a8_verify_attention(const uint16_t* q, const uint16_t* k_cache,
     return fail(W8A8_ERR_INVALID_ARG, fn, "T, Hq, Hkv must be >= 1 with Hq % Hkv == 0");
   if (T * (Hq / Hkv) > 64)
     return fail(W8A8_ERR_UNSUPPORTED, fn, "T * Hq / Hkv must be <= 64");
-  if (Lmax < T || Lmax > (1 << 24)) return fail(W8A8_ERR_INVALID_ARG, fn, "Lmax out of range [T, 2^24]");
+  if (Lmax < T || Lmax > (1 << 17)) return fail(W8A8_ERR_INVALID_ARG, fn, "Lmax out of range [T, 131072]");
   if (!q || !k_cache || !v_cache || !lengths || !out)
     return fail(W8A8_ERR_INVALID_ARG, fn, "required pointer is NULL");
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 4) ||

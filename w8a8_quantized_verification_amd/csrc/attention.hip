@@ -9,11 +9,12 @@
 // fp32 arithmetic, bf16 output.
 //
 // Split over the keys (flash-decoding): workgroup (split, kv head, b) takes
-// 256 cache positions and every query row that reads its kv head (T x
-// Hq/Hkv rows, <= 64); 64-key tiles of K and V go through LDS, each wave
-// keeps an online softmax (running max, sum, unnormalised output) for its
-// rows, one key per lane for the scores and two output dimensions per lane
-// for the value sum.  A second kernel merges the splits of each row.  Bound
+// 64 cache positions and every query row that reads its kv head (T x
+// Hq/Hkv rows, <= 64, a contiguous run of them per wave); the 64-key tile of
+// K and V goes through LDS, and each wave keeps an online softmax (running max,
+// sum, unnormalised output) for its rows, one key per lane for the scores
+// and two output dimensions per lane for the value sum, all of its rows at
+// once so that each LDS value feeds several independent accumulations.  A second kernel merges the splits of each row.  Bound
 // by reading the cache (2 * 128 * 2 bytes per position and kv head).
 #include "common.h"
 
@@ -22,11 +23,11 @@
 namespace w8a8 {
 
 constexpr int kDh = 128;
-constexpr int kAttnChunk = 256;     // cache positions per workgroup
+constexpr int kAttnChunk = 64;      // cache positions per workgroup (one LDS tile)
 constexpr int kAttnTile = 64;       // keys per LDS tile
 constexpr int kAttnThreads = 256;
 constexpr int kAttnMaxRows = 64;    // T * Hq / Hkv
-constexpr int kKRow = kDh + 2;      // padded LDS row (bf16): row j starts at bank j
+constexpr int kAttnMaxSplits = 2048; // cache positions up to 2048 * 64 = 131072
 
 struct AttnArgs {
   const uint16_t* q;      // [B][T][Hq][128]
@@ -39,10 +40,18 @@ struct AttnArgs {
   uint16_t* out;          // [B][T][Hq][128]
 };
 
+// RW: query rows per wave (rows r = wave * RW + jr); the rows of a wave are
+// processed together so that every K or V value read from LDS feeds RW
+// independent accumulations.
+template <int RW>
 __global__ __launch_bounds__(kAttnThreads) void attn_partial_kernel(AttnArgs a) {
   __shared__ uint32_t qs[kAttnMaxRows][kDh / 2];   // bf16 pairs
-  __shared__ uint16_t ks[kAttnTile][kKRow];
-  __shared__ uint16_t vs[kAttnTile][kKRow];
+  // K rows as bf16 pairs with word w of row j stored at word w ^ j (a
+  // lane-per-row read of one word is then conflict-free); V rows plain (a
+  // row is read across the lanes)
+  __shared__ uint32_t ks[kAttnTile][kDh / 2];
+  __shared__ uint32_t vs[kAttnTile][kDh / 2];
+  __shared__ float ps[kAttnThreads / kWave][RW][kAttnTile];
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int group = a.Hq / a.Hkv;
   const int rows = a.T * group;
@@ -61,78 +70,104 @@ __global__ __launch_bounds__(kAttnThreads) void attn_partial_kernel(AttnArgs a) 
         a.q + (((size_t)b * a.T + i) * a.Hq + h) * kDh + 2 * d2);
   }
 
-  // this wave's rows: r = wave + 4 * jr
-  constexpr int kMaxR = kAttnMaxRows / (kAttnThreads / kWave);
-  float m[kMaxR], l[kMaxR], o0[kMaxR], o1[kMaxR];
+  const int r0 = wave * RW;
+  float m[RW], l[RW], o0[RW], o1[RW];
 #pragma unroll
-  for (int jr = 0; jr < kMaxR; ++jr) { m[jr] = -INFINITY; l[jr] = 0.0f; o0[jr] = 0.0f; o1[jr] = 0.0f; }
+  for (int jr = 0; jr < RW; ++jr) { m[jr] = -INFINITY; l[jr] = 0.0f; o0[jr] = 0.0f; o1[jr] = 0.0f; }
 
   const uint16_t* kb = a.k + ((size_t)b * a.Hkv + kvh) * (size_t)a.Lmax * kDh;
   const uint16_t* vb = a.v + ((size_t)b * a.Hkv + kvh) * (size_t)a.Lmax * kDh;
   for (int t0 = c0; t0 < c1; t0 += kAttnTile) {
     __syncthreads();   // previous tile's reads (and the q fill) done
-    // 64 rows x 128 bf16 of K and V: 16 bytes per thread per pass
-    for (int e = tid; e < kAttnTile * (kDh / 8); e += kAttnThreads) {
+    // 64 rows x 128 bf16 of K and V, 16 bytes per load: all loads first, then
+    // the LDS stores (the loads of one tile are independent)
+    constexpr int kLoads = kAttnTile * (kDh / 8) / kAttnThreads;
+    uint4 kk[kLoads], vv[kLoads];
+#pragma unroll
+    for (int u = 0; u < kLoads; ++u) {
+      const int e = tid + u * kAttnThreads;
       const int j = e / (kDh / 8), d8 = (e % (kDh / 8)) * 8;
-      uint4 kk = make_uint4(0u, 0u, 0u, 0u), vv = make_uint4(0u, 0u, 0u, 0u);
+      kk[u] = make_uint4(0u, 0u, 0u, 0u);
+      vv[u] = make_uint4(0u, 0u, 0u, 0u);
       if (t0 + j < c1) {
-        kk = *reinterpret_cast<const uint4*>(kb + (size_t)(t0 + j) * kDh + d8);
-        vv = *reinterpret_cast<const uint4*>(vb + (size_t)(t0 + j) * kDh + d8);
+        kk[u] = *reinterpret_cast<const uint4*>(kb + (size_t)(t0 + j) * kDh + d8);
+        vv[u] = *reinterpret_cast<const uint4*>(vb + (size_t)(t0 + j) * kDh + d8);
       }
-      const uint32_t kw[4] = {kk.x, kk.y, kk.z, kk.w}, vw[4] = {vv.x, vv.y, vv.z, vv.w};
+    }
+#pragma unroll
+    for (int u = 0; u < kLoads; ++u) {
+      const int e = tid + u * kAttnThreads;
+      const int j = e / (kDh / 8), w0 = (e % (kDh / 8)) * 4;
+      const uint32_t kw[4] = {kk[u].x, kk[u].y, kk[u].z, kk[u].w};
+      const uint32_t vw[4] = {vv[u].x, vv[u].y, vv[u].z, vv[u].w};
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        // padded rows are 4-byte aligned: store 32-bit pairs
-        *reinterpret_cast<uint32_t*>(&ks[j][d8 + 2 * w]) = kw[w];
-        *reinterpret_cast<uint32_t*>(&vs[j][d8 + 2 * w]) = vw[w];
+        ks[j][(w0 + w) ^ j] = kw[w];
+        vs[j][w0 + w] = vw[w];
       }
     }
     __syncthreads();
+    if (r0 >= rows) continue;      // (every wave still meets both barriers)
+
+    // scores of key t0 + lane against the wave's rows
+    float acc[RW];
 #pragma unroll
-    for (int jr = 0; jr < kMaxR; ++jr) {
-      const int r = wave + 4 * jr;
-      if (r >= rows) break;
-      const int i = r / group;
-      const int last = L - a.T + i;                 // inclusive
-      // score of key t0 + lane
-      const int p = t0 + lane;
-      float s = -INFINITY;
-      if (p < c1 && p <= last) {
-        float acc = 0.0f;
-#pragma unroll 8
-        for (int d = 0; d < kDh; d += 2) {
-          const uint32_t kw = *reinterpret_cast<const uint32_t*>(&ks[lane][d]);
-          const uint32_t qw = qs[r][d / 2];
-          acc += __uint_as_float(qw << 16) * __uint_as_float(kw << 16);
-          acc += __uint_as_float(qw & 0xffff0000u) * __uint_as_float(kw & 0xffff0000u);
-        }
-        s = acc * scale;
+    for (int jr = 0; jr < RW; ++jr) acc[jr] = 0.0f;
+#pragma unroll 4
+    for (int d2 = 0; d2 < kDh / 2; ++d2) {
+      const uint32_t kw = ks[lane][d2 ^ lane];
+      const float k0 = __uint_as_float(kw << 16), k1 = __uint_as_float(kw & 0xffff0000u);
+#pragma unroll
+      for (int jr = 0; jr < RW; ++jr) {
+        const uint32_t qw = qs[r0 + jr < rows ? r0 + jr : 0][d2];
+        acc[jr] += __uint_as_float(qw << 16) * k0;
+        acc[jr] += __uint_as_float(qw & 0xffff0000u) * k1;
       }
-      const float tmax = wave_max(s);
-      const float mnew = fmaxf(m[jr], tmax);
-      if (mnew == -INFINITY) continue;              // nothing visible yet
-      const float alpha = expf(m[jr] - mnew);       // 0 when m was -inf
-      const float pj = (s == -INFINITY) ? 0.0f : expf(s - mnew);
+    }
+    const int p = t0 + lane;
+    float alpha[RW];
+#pragma unroll
+    for (int jr = 0; jr < RW; ++jr) {
+      const int last = L - a.T + (r0 + jr) / group;          // inclusive
+      const bool vis = r0 + jr < rows && p < c1 && p <= last;
+      const float s = vis ? acc[jr] * scale : -INFINITY;
+      const float mnew = fmaxf(m[jr], wave_max(s));
+      float pj = 0.0f;
+      alpha[jr] = 1.0f;
+      if (mnew != -INFINITY) {
+        alpha[jr] = expf(m[jr] - mnew);                     // 0 when m was -inf
+        pj = vis ? expf(s - mnew) : 0.0f;
+        m[jr] = mnew;
+      }
       float psum = pj;
 #pragma unroll
       for (int off = 32; off > 0; off >>= 1) psum += __shfl_xor(psum, off, kWave);
-      l[jr] = l[jr] * alpha + psum;
-      float a0 = o0[jr] * alpha, a1 = o1[jr] * alpha;
-      for (int j = 0; j < kAttnTile; ++j) {
-        const float pk = __shfl(pj, j, kWave);
-        const uint32_t vw = *reinterpret_cast<const uint32_t*>(&vs[j][2 * lane]);
-        a0 += pk * __uint_as_float(vw << 16);
-        a1 += pk * __uint_as_float(vw & 0xffff0000u);
-      }
-      o0[jr] = a0; o1[jr] = a1;
-      m[jr] = mnew;
+      l[jr] = l[jr] * alpha[jr] + psum;
+      ps[wave][jr][lane] = pj;
     }
+    // (the wave's own LDS rows: written and read by the same wave, in order)
+    float a0[RW], a1[RW];
+#pragma unroll
+    for (int jr = 0; jr < RW; ++jr) { a0[jr] = o0[jr] * alpha[jr]; a1[jr] = o1[jr] * alpha[jr]; }
+#pragma unroll 4
+    for (int j = 0; j < kAttnTile; ++j) {
+      const uint32_t vw = vs[j][lane];
+      const float v0 = __uint_as_float(vw << 16), v1 = __uint_as_float(vw & 0xffff0000u);
+#pragma unroll
+      for (int jr = 0; jr < RW; ++jr) {
+        const float pk = ps[wave][jr][j];
+        a0[jr] += pk * v0;
+        a1[jr] += pk * v1;
+      }
+    }
+#pragma unroll
+    for (int jr = 0; jr < RW; ++jr) { o0[jr] = a0[jr]; o1[jr] = a1[jr]; }
   }
   // partial results of this split
   const size_t base = (((size_t)b * a.Hkv + kvh) * a.nsplit + split) * kAttnMaxRows;
 #pragma unroll
-  for (int jr = 0; jr < kMaxR; ++jr) {
-    const int r = wave + 4 * jr;
+  for (int jr = 0; jr < RW; ++jr) {
+    const int r = r0 + jr;
     if (r >= rows) break;
     float* po = a.part_o + (base + r) * kDh;
     po[2 * lane] = o0[jr];
@@ -145,26 +180,57 @@ __global__ __launch_bounds__(kAttnThreads) void attn_partial_kernel(AttnArgs a) 
 }
 
 __global__ __launch_bounds__(kDh) void attn_combine_kernel(AttnArgs a) {
+  __shared__ float wts[kAttnMaxSplits];
+  __shared__ float red[kDh / kWave];
   const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int d = threadIdx.x;
   const int group = a.Hq / a.Hkv;
   const int kvh = h / group, r = i * group + h % group;
+  const size_t row0 = ((size_t)b * a.Hkv + kvh) * a.nsplit;   // split s: (row0 + s) * rows + r
+  // each thread reads the (max, sum) of its splits; block max, then weights
+  float ms[kAttnMaxSplits / kDh], lsn[kAttnMaxSplits / kDh];
   float mmax = -INFINITY;
-  for (int s = 0; s < a.nsplit; ++s) {
-    const size_t idx = (((size_t)b * a.Hkv + kvh) * a.nsplit + s) * kAttnMaxRows + r;
-    mmax = fmaxf(mmax, a.part_ml[idx * 2]);
-  }
-  float lsum = 0.0f, o = 0.0f;
-  if (mmax != -INFINITY) {
-    for (int s = 0; s < a.nsplit; ++s) {
-      const size_t idx = (((size_t)b * a.Hkv + kvh) * a.nsplit + s) * kAttnMaxRows + r;
-      const float ms = a.part_ml[idx * 2];
-      if (ms == -INFINITY) continue;
-      const float w = expf(ms - mmax);
-      lsum += a.part_ml[idx * 2 + 1] * w;
-      o += a.part_o[idx * kDh + d] * w;
+#pragma unroll
+  for (int u = 0; u < kAttnMaxSplits / kDh; ++u) {
+    const int s = d + u * kDh;
+    ms[u] = -INFINITY;
+    lsn[u] = 0.0f;
+    if (s < a.nsplit) {
+      const size_t idx = (row0 + s) * kAttnMaxRows + r;
+      ms[u] = a.part_ml[idx * 2];
+      lsn[u] = a.part_ml[idx * 2 + 1];
     }
+    mmax = fmaxf(mmax, ms[u]);
   }
+  mmax = wave_max(mmax);
+  if ((d & (kWave - 1)) == 0) red[d / kWave] = mmax;
+  __syncthreads();
+  mmax = fmaxf(red[0], red[1]);
+  float lpart = 0.0f;
+#pragma unroll
+  for (int u = 0; u < kAttnMaxSplits / kDh; ++u) {
+    const int s = d + u * kDh;
+    const float w = (ms[u] == -INFINITY) ? 0.0f : expf(ms[u] - mmax);
+    if (s < a.nsplit) wts[s] = w;
+    lpart += lsn[u] * w;
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) lpart += __shfl_xor(lpart, off, kWave);
+  __syncthreads();   // wts complete; red[] reused below
+  if ((d & (kWave - 1)) == 0) red[d / kWave] = lpart;
+  __syncthreads();
+  const float lsum = red[0] + red[1];
+  // (a split with no visible key has weight 0 and a zero partial output)
+  float o = 0.0f;
+  int s = 0;
+  for (; s + 8 <= a.nsplit; s += 8) {
+    float po[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) po[u] = a.part_o[((row0 + s + u) * kAttnMaxRows + r) * kDh + d];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) o += po[u] * wts[s + u];
+  }
+  for (; s < a.nsplit; ++s) o += a.part_o[((row0 + s) * kAttnMaxRows + r) * kDh + d] * wts[s];
   const float y = lsum > 0.0f ? o / lsum : 0.0f;
   a.out[(((size_t)b * a.T + i) * a.Hq + h) * kDh + d] = f32_to_bf16_rne(y);
 }
@@ -194,8 +260,22 @@ hipError_t w8a8_launch_verify_attention(const uint16_t* q, const uint16_t* k, co
   a.part_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
                                        ((rows * kDh * sizeof(float) + 255) & ~(size_t)255));
   a.out = out;
-  hipLaunchKernelGGL(attn_partial_kernel, dim3((unsigned)a.nsplit, (unsigned)Hkv, (unsigned)B),
-                     dim3(kAttnThreads), 0, stream, a);
+  const dim3 grid((unsigned)a.nsplit, (unsigned)Hkv, (unsigned)B);
+  const int rw = (int)((T * (Hq / Hkv) + 3) / 4);   // rows per wave, 4 waves
+#define W8A8_ATT(RW) hipLaunchKernelGGL(attn_partial_kernel<RW>, grid, dim3(kAttnThreads), 0, stream, a)
+  switch (rw) {
+    case 1: W8A8_ATT(1); break;
+    case 2: W8A8_ATT(2); break;
+    case 3: W8A8_ATT(3); break;
+    case 4: W8A8_ATT(4); break;
+    case 5: W8A8_ATT(5); break;
+    case 6: W8A8_ATT(6); break;
+    case 7: case 8: W8A8_ATT(8); break;
+    case 9: case 10: W8A8_ATT(10); break;
+    case 11: case 12: W8A8_ATT(12); break;
+    default: W8A8_ATT(16); break;
+  }
+#undef W8A8_ATT
   hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)T, (unsigned)Hq, (unsigned)B), dim3(kDh),
                      0, stream, a);
   return hipGetLastError();
