@@ -49,7 +49,7 @@ from .gemm import int8_gemm, dequant, w8a8_linear, INT32_MAX_K
 from .accept import argmax_rows, greedy_accept, verify_accept
 from .sample import exp_f32, fixed_weights, verify_sample
 from .glue import residual_add, rmsnorm, silu_mul
-from .attention import verify_attention
+from .attention import verify_attention, qk_norm_rope
 from .reference import (bf16_reference_logits, w8a8_linear_bytes,
                         bf16_linear_bytes, weight_bytes_int8, weight_bytes_bf16)
 
@@ -59,5 +59,5 @@ __all__ = [
     "argmax_rows", "greedy_accept", "verify_accept", "bf16_reference_logits",
     "w8a8_linear_bytes", "bf16_linear_bytes", "weight_bytes_int8",
     "weight_bytes_bf16", "exp_f32", "fixed_weights", "verify_sample", "quantize_weight_int4",
-    "residual_add", "rmsnorm", "silu_mul", "verify_attention",
+    "residual_add", "rmsnorm", "silu_mul", "verify_attention", "qk_norm_rope",
 ]

@@ -49,3 +49,42 @@ def verify_attention(q_bits, k_bits, v_bits, lengths) -> np.ndarray:
                 p /= p.sum()
                 out[b, i, h] = p @ v[b, kh, :last + 1]
     return _f64_to_bf16_bits(out)
+
+
+def qk_norm_rope(qkv_bits, B, T, Hq, Hkv, q_gamma_bits, k_gamma_bits, eps, start, base):
+    """The steps between the [q;k;v] linear and attention, per token row
+    (b, i) of ``qkv [B*T][(Hq + 2 Hkv) * 128]`` (bf16; heads of q, then k,
+    then v, 128 columns each):
+
+    * per-head RMSNorm of q and k over their 128 dims with bf16 gammas:
+      n = bf16(bf16(x * r) * gamma), r = 1/sqrt(mean(x^2) + eps);
+    * rotary position embedding at position p = start[b] + i, rotating dim
+      pairs (d, d + 64), d < 64, by the angle p * base^(-d/64):
+      (x1, x2) -> (x1 cos - x2 sin, x2 cos + x1 sin), rounded to bf16;
+    * v unchanged.
+
+    Returns bf16 bits ``q [B][T][Hq][128]``, ``k [B][T][Hkv][128]``,
+    ``v [B][T][Hkv][128]``, in float64 with direct bf16 rounding (Qwen3's
+    q/k norms and its rotate-half RoPE; the pages do not describe the
+    attention block)."""
+    from .glue import rmsnorm
+    x = np.asarray(qkv_bits, dtype=np.uint16).reshape(B, T, Hq + 2 * Hkv, 128)
+    qg = np.asarray(q_gamma_bits, dtype=np.uint16)
+    kg = np.asarray(k_gamma_bits, dtype=np.uint16)
+    qn = rmsnorm(x[:, :, :Hq].reshape(-1, 128), qg, eps).reshape(B, T, Hq, 128)
+    kn = rmsnorm(x[:, :, Hq:Hq + Hkv].reshape(-1, 128), kg, eps).reshape(B, T, Hkv, 128)
+    v = x[:, :, Hq + Hkv:].copy()
+    d = np.arange(64, dtype=np.float64)
+    inv_freq = float(base) ** (-d / 64.0)
+    pos = np.asarray(start, dtype=np.float64)[:, None] + np.arange(T, dtype=np.float64)[None, :]
+    ang = pos[:, :, None] * inv_freq[None, None, :]            # B T 64
+    cos, sin = np.cos(ang), np.sin(ang)
+
+    def rope(h_bits):
+        h = bf16_to_f32(h_bits).astype(np.float64)
+        x1, x2 = h[..., :64], h[..., 64:]
+        c, s = cos[:, :, None, :], sin[:, :, None, :]
+        out = np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+        return _f64_to_bf16_bits(out)
+
+    return rope(qn), rope(kn), v

@@ -78,3 +78,38 @@ def test_against_torch_sdpa_float64():
         ref = ref.permute(1, 0, 2).numpy()                                       # T Hq Dh
         got = o[b]
         assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-12)
+
+
+def test_qk_norm_rope_position_zero_and_rotation_identities():
+    B, T, Hq, Hkv = 2, 3, 4, 2
+    x = bits(RNG.standard_normal((B * T, (Hq + 2 * Hkv) * 128)) * 2)
+    g = bits(np.ones(128))
+    q, k, v = oracle.qk_norm_rope(x, B, T, Hq, Hkv, g, g, 1e-6, [0, 0], 1e6)
+    xr = x.reshape(B, T, Hq + 2 * Hkv, 128)
+    # v passes through
+    np.testing.assert_array_equal(v, xr[:, :, Hq + Hkv:])
+    # position 0: no rotation, only the norm
+    qn = oracle.rmsnorm(xr[:, 0, :Hq].reshape(-1, 128), g, 1e-6).reshape(B, Hq, 128)
+    np.testing.assert_array_equal(q[:, 0], qn)
+    # a rotation keeps each pair's norm (up to the bf16 roundings)
+    h = val(oracle.rmsnorm(xr[:, :, :Hq].reshape(-1, 128), g, 1e-6)).reshape(B, T, Hq, 128)
+    r = val(q)
+    n_in = h[..., :64] ** 2 + h[..., 64:] ** 2
+    n_out = r[..., :64] ** 2 + r[..., 64:] ** 2
+    assert np.all(np.abs(n_out - n_in) <= 2.0 ** -6 * n_in + 1e-6)
+
+
+def test_qk_norm_rope_known_angle():
+    # dim pair d = 0 rotates by the position itself (base^0 = 1); at p = 3:
+    # (x1, x2) -> (x1 cos 3 - x2 sin 3, x2 cos 3 + x1 sin 3)
+    B, T, Hq, Hkv = 1, 1, 1, 1
+    row = np.zeros((1, 3 * 128), dtype=np.float32)
+    row[0, 0] = 1.0                         # q: x1 = 1 at d = 0, so its norm is sqrt(1/128)
+    row[0, 128] = 1.0                       # k likewise
+    x = bits(row)
+    g = bits(np.ones(128))
+    q, k, _ = oracle.qk_norm_rope(x, B, T, Hq, Hkv, g, g, 0.0, [3], 1e6)
+    n = np.sqrt(128.0)                       # the normed x1 before its bf16 rounding
+    n_bf = val(oracle.glue._f64_to_bf16_bits(np.array([n])))[0]
+    assert val(q)[0, 0, 0, 0] == val(oracle.glue._f64_to_bf16_bits(np.array([n_bf * np.cos(3)])))[0]
+    assert val(q)[0, 0, 0, 64] == val(oracle.glue._f64_to_bf16_bits(np.array([n_bf * np.sin(3)])))[0]
