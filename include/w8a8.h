@@ -328,6 +328,29 @@ w8a8_status w8a8_silu_mul_quant(const uint16_t* gate, const uint16_t* up,
                                 int8_t* xq, float* x_scale, void* stream);
 
 /*
+ * The steps between the [q;k;v] linear and w8a8_verify_attention (Qwen3's
+ * attention block; the pages do not describe it).  For token row (b, i) of
+ * qkv [B*T][(Hq + 2*Hkv) * Dh] bf16 (heads of q, then k, then v) and
+ * position p = L_b - T + i (L_b = lengths[b] clamped into [T, Lmax]):
+ *   q, k heads: per-head RMSNorm over Dh with bf16 gammas
+ *     n = bf16(bf16(x * r) * gamma), r = 1/sqrt(mean(x^2) + eps);
+ *   then rotary embedding: dims (d, d + 64), d < 64, turned by the fp32
+ *     angle fp32(fp32(p) * f_d), f_d = fp32(rope_base^(-d/64)) (computed on the
+ *     host in double): (x1, x2) -> bf16(x1 cos - x2 sin), bf16(x2 cos + x1 sin);
+ *   q goes to q_out [B][T][Hq][Dh]; k and v (unchanged) are written into
+ *   k_cache / v_cache [B][Hkv][Lmax][Dh] at position p.
+ * fp32 arithmetic (sine and cosine of the fp32 angle in fp32).  Dh == 128
+ * (else W8A8_ERR_UNSUPPORTED); Hq % Hkv == 0; T <= Lmax <= 131072;
+ * rope_base > 1; eps >= 0.
+ */
+w8a8_status w8a8_qk_norm_rope_append(const uint16_t* qkv, int64_t B, int64_t T,
+                                     int64_t Hq, int64_t Hkv, int64_t Dh,
+                                     const uint16_t* q_gamma, const uint16_t* k_gamma,
+                                     float eps, float rope_base, const int32_t* lengths,
+                                     int64_t Lmax, uint16_t* q_out, uint16_t* k_cache,
+                                     uint16_t* v_cache, void* stream);
+
+/*
  * Attention of the verified block over the KV cache (the softmax part of
  * the verifier, kept in high precision after the dequant step: [de] §2
  * "De-Quantisierung"; [it] §2 pipeline; [ja] §2.2 item 3).

@@ -59,8 +59,11 @@ def qk_norm_rope(qkv_bits, B, T, Hq, Hkv, q_gamma_bits, k_gamma_bits, eps, start
     * per-head RMSNorm of q and k over their 128 dims with bf16 gammas:
       n = bf16(bf16(x * r) * gamma), r = 1/sqrt(mean(x^2) + eps);
     * rotary position embedding at position p = start[b] + i, rotating dim
-      pairs (d, d + 64), d < 64, by the angle p * base^(-d/64):
-      (x1, x2) -> (x1 cos - x2 sin, x2 cos + x1 sin), rounded to bf16;
+      pairs (d, d + 64), d < 64, by the angle a = fp32(fp32(p) * f_d) with
+      f_d = fp32(base^(-d/64)) (the fp32 angle of bf16/fp32 inference: at
+      positions near 1e5 its rounding moves the angle by up to ~4e-3, which
+      this reproduces rather than corrects): (x1, x2) -> (x1 cos a - x2 sin a,
+      x2 cos a + x1 sin a), cos and sin in float64, rounded to bf16;
     * v unchanged.
 
     Returns bf16 bits ``q [B][T][Hq][128]``, ``k [B][T][Hkv][128]``,
@@ -75,10 +78,10 @@ def qk_norm_rope(qkv_bits, B, T, Hq, Hkv, q_gamma_bits, k_gamma_bits, eps, start
     kn = rmsnorm(x[:, :, Hq:Hq + Hkv].reshape(-1, 128), kg, eps).reshape(B, T, Hkv, 128)
     v = x[:, :, Hq + Hkv:].copy()
     d = np.arange(64, dtype=np.float64)
-    inv_freq = float(base) ** (-d / 64.0)
-    pos = np.asarray(start, dtype=np.float64)[:, None] + np.arange(T, dtype=np.float64)[None, :]
-    ang = pos[:, :, None] * inv_freq[None, None, :]            # B T 64
-    cos, sin = np.cos(ang), np.sin(ang)
+    inv_freq = (float(base) ** (-d / 64.0)).astype(np.float32)
+    pos = (np.asarray(start, dtype=np.int64)[:, None] + np.arange(T)[None, :]).astype(np.float32)
+    ang = (pos[:, :, None] * inv_freq[None, None, :]).astype(np.float32)   # B T 64, fp32 product
+    cos, sin = np.cos(ang.astype(np.float64)), np.sin(ang.astype(np.float64))
 
     def rope(h_bits):
         h = bf16_to_f32(h_bits).astype(np.float64)

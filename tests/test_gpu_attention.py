@@ -76,3 +76,43 @@ def test_verify_attention_sharp_softmax():
     g = oracle.bf16_to_f32(host(out)).astype(np.float64)
     w = oracle.bf16_to_f32(want).astype(np.float64)
     assert np.all(np.abs(g - w) <= 1e-3 + 1e-2 * np.abs(w))
+
+
+@pytest.mark.parametrize("B,T,Hq,Hkv,Lmax,lengths", [(2, 5, 32, 8, 300, [300, 123]),
+                                                     (1, 3, 8, 2, 100000, [99999]),
+                                                     (3, 1, 4, 4, 16, [1, 16, 7])])
+def test_qk_norm_rope_append(B, T, Hq, Hkv, Lmax, lengths):
+    announce(f"qk_norm_rope_append B={B} T={T} Hq={Hq} Hkv={Hkv} Lmax={Lmax}")
+    qkv = draw((B * T, (Hq + 2 * Hkv) * 128), 10, scale=2.0)
+    qg = synth.to_bf16_bits(synth.rng(W_ATT, 32, 0).uniform(0.5, 1.5, 128).astype(np.float32))
+    kg = synth.to_bf16_bits(synth.rng(W_ATT, 32, 1).uniform(0.5, 1.5, 128).astype(np.float32))
+    kc0 = draw((B, Hkv, Lmax, 128), 11)
+    vc0 = draw((B, Hkv, Lmax, 128), 12)
+    lengths = np.asarray(lengths, dtype=np.int32)
+    kc, vc = dev_bf16(kc0), dev_bf16(vc0)
+    q = w8.qk_norm_rope_append(dev_bf16(qkv), dev_bf16(qg), dev_bf16(kg), dev(lengths), kc, vc,
+                               T=T, Hq=Hq, Hkv=Hkv, eps=1e-6, rope_base=1e6)
+    torch.cuda.synchronize()
+    start = lengths - T
+    q_r, k_r, v_r = oracle.qk_norm_rope(qkv, B, T, Hq, Hkv, qg, kg, 1e-6, start, 1e6)
+
+    def close(got, want):
+        g = oracle.bf16_to_f32(got).astype(np.float64)
+        w = oracle.bf16_to_f32(want).astype(np.float64)
+        assert np.all(np.abs(g - w) <= 1e-3 + 1e-2 * np.abs(w))
+        return np.mean(got == want)
+
+    fq = close(host(q), q_r)
+    kh, vh = host(kc), host(vc)
+    want_k, want_v = kc0.copy(), vc0.copy()
+    for b in range(B):
+        for i in range(T):
+            want_k[b, :, start[b] + i] = k_r[b, i]
+            want_v[b, :, start[b] + i] = v_r[b, i]
+    fk = close(kh, want_k)
+    np.testing.assert_array_equal(vh, want_v)
+    touched = np.zeros(kh.shape[:3], dtype=bool)
+    for b in range(B):
+        touched[b, :, start[b]:start[b] + T] = True
+    np.testing.assert_array_equal(kh[~touched], kc0[~touched])
+    print(f"[gpu] bit-identical q {fq:.4f} k(all) {fk:.6f}", flush=True)

@@ -19,7 +19,7 @@ __all__ = [
     "accept_from_keys", "bf16_linear", "Workspace", "verify_sample",
     "verify_sample_workspace_bytes", "sample_weights", "w4_shape", "quantize_weight_w4",
     "linear_w4", "lm_head_argmax_w4", "residual_rmsnorm_quant", "silu_mul_quant",
-    "quantize_act_tiled", "linear_tiled_act", "verify_attention",
+    "quantize_act_tiled", "linear_tiled_act", "verify_attention", "qk_norm_rope_append",
 ]
 
 
@@ -547,3 +547,31 @@ def verify_attention(q, k_cache, v_cache, lengths, *, out=None, workspace: Works
                                       Hq, Hkv, Dh, Lmax, _ptr(out), _ptr(ws),
                                       0 if ws is None else ws.numel(), _stream(dev)))
     return out
+
+
+def qk_norm_rope_append(qkv, q_gamma, k_gamma, lengths, k_cache, v_cache, *, T: int, Hq: int,
+                        Hkv: int, eps: float = 1e-6, rope_base: float = 1e6, q_out=None):
+    """Per-head q/k RMSNorm, rotary embedding at position L_b - T + i, and the
+    append of k, v into the caches.  ``qkv`` bf16 ``[B*T][(Hq + 2 Hkv) * 128]``
+    (e.g. a fused [q;k;v] linear's output), ``lengths`` int32 ``[B]`` (valid
+    positions after the append).  Returns ``q_out`` bf16 ``[B][T][Hq][128]``."""
+    _need(qkv, "qkv", torch.bfloat16, 2)
+    dev = qkv.device
+    R, W = qkv.shape
+    if W != (Hq + 2 * Hkv) * 128 or R % T != 0:
+        raise ValueError("qkv must be [B*T][(Hq + 2*Hkv) * 128]")
+    B = R // T
+    _need(q_gamma, "q_gamma", torch.bfloat16, 1, dev)
+    _need(k_gamma, "k_gamma", torch.bfloat16, 1, dev)
+    _need(lengths, "lengths", torch.int32, 1, dev)
+    _need(k_cache, "k_cache", torch.bfloat16, 4, dev)
+    _need(v_cache, "v_cache", torch.bfloat16, 4, dev)
+    Lmax = k_cache.shape[2]
+    if tuple(k_cache.shape) != (B, Hkv, Lmax, 128) or v_cache.shape != k_cache.shape:
+        raise ValueError("caches must be [B][Hkv][Lmax][128]")
+    q_out = _out(q_out, (B, T, Hq, 128), torch.bfloat16, dev, "q_out")
+    check(lib().w8a8_qk_norm_rope_append(_ptr(qkv), B, T, Hq, Hkv, 128, _ptr(q_gamma),
+                                         _ptr(k_gamma), float(eps), float(rope_base),
+                                         _ptr(lengths), Lmax, _ptr(q_out), _ptr(k_cache),
+                                         _ptr(v_cache), _stream(dev)))
+    return q_out

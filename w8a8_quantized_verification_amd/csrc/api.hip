@@ -575,4 +575,31 @@ w8a8_status w8a8_verify_attention(const uint16_t* q, const uint16_t* k_cache,
                                                  reinterpret_cast<hipStream_t>(stream)), fn);
 }
 
+
+w8a8_status w8a8_qk_norm_rope_append(const uint16_t* qkv, int64_t B, int64_t T, int64_t Hq,
+                                     int64_t Hkv, int64_t Dh, const uint16_t* q_gamma,
+                                     const uint16_t* k_gamma, float eps, float rope_base,
+                                     const int32_t* lengths, int64_t Lmax, uint16_t* q_out,
+                                     uint16_t* k_cache, uint16_t* v_cache, void* stream) {
+  static const char* fn = "w8a8_qk_norm_rope_append";
+  g_last_error.clear();
+  if (B < 0 || B > 65535) return fail(W8A8_ERR_INVALID_ARG, fn, "B out of range");
+  if (B == 0) return W8A8_OK;
+  if (Dh != 128) return fail(W8A8_ERR_UNSUPPORTED, fn, "head dimension must be 128");
+  if (T < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || Hq + 2 * Hkv > 65535 || B * T > (1 << 30))
+    return fail(W8A8_ERR_INVALID_ARG, fn, "T, Hq, Hkv out of range");
+  if (Lmax < T || Lmax > (1 << 17)) return fail(W8A8_ERR_INVALID_ARG, fn, "Lmax out of range [T, 131072]");
+  if (!(std::isfinite(eps) && eps >= 0.0f) || !(std::isfinite(rope_base) && rope_base > 1.0f))
+    return fail(W8A8_ERR_INVALID_ARG, fn, "eps must be >= 0 and rope_base > 1");
+  if (!qkv || !q_gamma || !k_gamma || !lengths || !q_out || !k_cache || !v_cache)
+    return fail(W8A8_ERR_INVALID_ARG, fn, "required pointer is NULL");
+  if (!aligned(qkv, 2) || !aligned(q_gamma, 2) || !aligned(k_gamma, 2) || !aligned(q_out, 2) ||
+      !aligned(k_cache, 2) || !aligned(v_cache, 2) || !aligned(lengths, 4))
+    return fail(W8A8_ERR_INVALID_ARG, fn, "pointer misaligned");
+  return hip_status(w8a8_launch_qk_norm_rope_append(qkv, B, T, Hq, Hkv, q_gamma, k_gamma, eps,
+                                                    rope_base, lengths, Lmax, q_out, k_cache,
+                                                    v_cache, reinterpret_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 }  // extern "C"

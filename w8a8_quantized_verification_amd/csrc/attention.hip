@@ -235,6 +235,57 @@ __global__ __launch_bounds__(kDh) void attn_combine_kernel(AttnArgs a) {
   a.out[(((size_t)b * a.T + i) * a.Hq + h) * kDh + d] = f32_to_bf16_rne(y);
 }
 
+
+// Between the [q;k;v] linear and attention (Qwen3's attention block; the
+// pages do not describe it): per-head RMSNorm of q and k over their 128 dims
+// with bf16 gammas, rotate-half rotary embedding at position p = L_b - T + i
+// (dim pairs (d, d+64) turned by p * base^(-d/64)), and the append of k and
+// v to the cache at that position.  One wave per (token row, head); lane l
+// holds dims l and l + 64, i.e. exactly one rotation pair.
+struct RopeFreqs {
+  float f[64];   // fp32(base^(-d/64)), computed on the host in double and rounded
+};
+
+__global__ __launch_bounds__(kWave) void qk_norm_rope_append_kernel(
+    const uint16_t* qkv, int T, int Hq, int Hkv, const uint16_t* q_gamma,
+    const uint16_t* k_gamma, float eps, RopeFreqs freqs, const int32_t* len, int Lmax,
+    uint16_t* q_out, uint16_t* k_cache, uint16_t* v_cache) {
+  const int row = blockIdx.x;          // b * T + i
+  const int h = blockIdx.y;            // 0..Hq+2Hkv-1
+  const int b = row / T, i = row % T;
+  const int lane = threadIdx.x;
+  const int heads = Hq + 2 * Hkv;
+  int L = len[b];
+  L = L < T ? T : (L > Lmax ? Lmax : L);
+  const int pos = L - T + i;
+  const uint16_t* x = qkv + ((size_t)row * heads + h) * kDh;
+  float x1 = bf16_to_f32(x[lane]), x2 = bf16_to_f32(x[lane + 64]);
+  if (h >= Hq + Hkv) {                 // v: appended as is
+    const int kvh = h - Hq - Hkv;
+    uint16_t* dst = v_cache + (((size_t)b * Hkv + kvh) * Lmax + pos) * kDh;
+    dst[lane] = x[lane];
+    dst[lane + 64] = x[lane + 64];
+    return;
+  }
+  float ss = x1 * x1 + x2 * x2;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, kWave);
+  const float r = 1.0f / sqrtf(ss / 128.0f + eps);
+  const uint16_t* g = h < Hq ? q_gamma : k_gamma;
+  const float n1 = bf16_to_f32(f32_to_bf16_rne(bf16_to_f32(f32_to_bf16_rne(x1 * r)) * bf16_to_f32(g[lane])));
+  const float n2 = bf16_to_f32(f32_to_bf16_rne(bf16_to_f32(f32_to_bf16_rne(x2 * r)) * bf16_to_f32(g[lane + 64])));
+  // the angle is one fp32 product, as in fp32 inference
+  float sn, cs;
+  sincosf((float)pos * freqs.f[lane], &sn, &cs);
+  const uint16_t o1 = f32_to_bf16_rne(n1 * cs - n2 * sn);
+  const uint16_t o2 = f32_to_bf16_rne(n2 * cs + n1 * sn);
+  uint16_t* dst;
+  if (h < Hq) dst = q_out + ((size_t)row * Hq + h) * kDh;
+  else dst = k_cache + (((size_t)b * Hkv + (h - Hq)) * Lmax + pos) * kDh;
+  dst[lane] = o1;
+  dst[lane + 64] = o2;
+}
+
 }  // namespace w8a8
 
 size_t w8a8_attention_workspace_bytes_impl(int64_t B, int64_t Hkv, int64_t Lmax) {
@@ -278,5 +329,21 @@ hipError_t w8a8_launch_verify_attention(const uint16_t* q, const uint16_t* k, co
 #undef W8A8_ATT
   hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)T, (unsigned)Hq, (unsigned)B), dim3(kDh),
                      0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t w8a8_launch_qk_norm_rope_append(const uint16_t* qkv, int64_t B, int64_t T, int64_t Hq,
+                                           int64_t Hkv, const uint16_t* q_gamma,
+                                           const uint16_t* k_gamma, float eps, float rope_base,
+                                           const int32_t* lengths, int64_t Lmax, uint16_t* q_out,
+                                           uint16_t* k_cache, uint16_t* v_cache,
+                                           hipStream_t stream) {
+  using namespace w8a8;
+  if (B == 0) return hipSuccess;
+  RopeFreqs freqs;
+  for (int d = 0; d < 64; ++d) freqs.f[d] = (float)std::pow((double)rope_base, -(double)d / 64.0);
+  hipLaunchKernelGGL(qk_norm_rope_append_kernel, dim3((unsigned)(B * T), (unsigned)(Hq + 2 * Hkv)),
+                     dim3(kWave), 0, stream, qkv, (int)T, (int)Hq, (int)Hkv, q_gamma, k_gamma, eps,
+                     freqs, lengths, (int)Lmax, q_out, k_cache, v_cache);
   return hipGetLastError();
 }
