@@ -868,13 +868,11 @@ def oracle_timings():
 
 def layer_step_measurement(dev, wsp, reps_copies=4, ctx=4096):
     """One Qwen3-8B decoder-layer step at M = 5 (one sequence, 4 drafts + 1)
-    through the library, glue fused into the quantizations and attention
-    over a 4096-position KV cache: residual + RMSNorm + quant -> [q;k;v]
-    linear -> attention (the cache already holds the block's keys and
-    values; per-head q/k norms and RoPE are not built) -> quant -> o linear -> residual + RMSNorm +
-    quant -> [gate;up] linear -> SwiGLU + quant -> down linear.  10 launches;
-    the query is a seeded stand-in buffer;
-    4 distinct layers' weights and caches rotate (775 MB of weights, past the
+    entirely through the library: residual + RMSNorm + quant -> [q;k;v]
+    linear -> per-head q/k norms + RoPE + KV-cache append -> attention over
+    4096 cached positions -> quant -> o linear -> residual + RMSNorm + quant
+    -> [gate;up] linear -> SwiGLU + quant -> down linear (11 launches).  4
+    distinct layers' weights and caches rotate (775 MB of weights, past the
     Infinity Cache).  Also attention alone."""
     import numpy as np
     import torch
@@ -903,11 +901,11 @@ def layer_step_measurement(dev, wsp, reps_copies=4, ctx=4096):
 
     h = bf(synth.activations_bf16(synth.W_LAYER_M5, M, D, index=50))
     gamma = bf(synth.to_bf16_bits(np.ones(D, dtype=np.float32)))
+    head_gamma = bf(synth.to_bf16_bits(np.ones(Dh, dtype=np.float32)))
     lengths = torch.full((1,), ctx, dtype=torch.int32, device=dev)
-    y_qkv = torch.empty(M, 6144, dtype=torch.bfloat16, device=dev)
+    y_qkv = torch.zeros(M, (Hq + 2 * Hkv) * Dh, dtype=torch.bfloat16, device=dev)
+    qbuf = torch.empty(1, M, Hq, Dh, dtype=torch.bfloat16, device=dev)
     attn = torch.empty(1, M, Hq, Dh, dtype=torch.bfloat16, device=dev)
-    qbuf = torch.randn(1, M, Hq, Dh, device=dev, generator=torch.Generator(device=dev)
-                       .manual_seed(899)).to(torch.bfloat16)
     y_o = torch.empty(M, D, dtype=torch.bfloat16, device=dev)
     y_gu = torch.empty(M, 2 * F, dtype=torch.bfloat16, device=dev)
     y_down = torch.zeros(M, D, dtype=torch.bfloat16, device=dev)
@@ -918,11 +916,12 @@ def layer_step_measurement(dev, wsp, reps_copies=4, ctx=4096):
 
     def layer(c):
         L = layers[c]
+        kc, vc = caches[c]
         w8.residual_rmsnorm_quant(h, gamma, 1e-6, delta=y_down, h_out=h, xq=xq_d, x_scale=xs)
         w8.linear(xq_d, xs, *L[0], y_bf16=y_qkv, workspace=wsp)
-        # the query: a [B][T][Hq][128] buffer standing in for the normed,
-        # rotated q columns of [q;k;v] (those steps are not built)
-        w8.verify_attention(qbuf, *caches[c], lengths, out=attn, workspace=awsp)
+        w8.qk_norm_rope_append(y_qkv, head_gamma, head_gamma, lengths, kc, vc, T=M, Hq=Hq,
+                               Hkv=Hkv, q_out=qbuf)
+        w8.verify_attention(qbuf, kc, vc, lengths, out=attn, workspace=awsp)
         w8.quantize_act(attn.view(M, D), xq=xq_d, x_scale=xs)
         w8.linear(xq_d, xs, *L[1], y_bf16=y_o, workspace=wsp)
         w8.residual_rmsnorm_quant(h, gamma, 1e-6, delta=y_o, h_out=h, xq=xq_d, x_scale=xs)
@@ -942,9 +941,9 @@ def layer_step_measurement(dev, wsp, reps_copies=4, ctx=4096):
            "weight_plus_kv_frac_of_peak": round((wbytes + kvbytes) / t / 1e9 / HBM_PEAK_GBS, 4),
            "attention_us": round(t_att * 1e6, 2),
            "attention_kv_GBs": round(kvbytes / t_att / 1e9, 1),
-           "launches": 10,
-           "step": "rmsnorm+quant, qkv, attention (2 kernels), quant, o, rmsnorm+quant, gate_up, "
-                   "swiglu+quant, down; no q/k norms or RoPE, cache pre-filled"}
+           "launches": 12,
+           "step": "rmsnorm+quant, qkv, q/k norm+rope+kv append, attention (2 kernels), quant, "
+                   "o, rmsnorm+quant, gate_up, swiglu+quant, down"}
     del layers, caches
     return res
 
