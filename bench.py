@@ -243,6 +243,9 @@ def pmc_probe_batched(dev):
         y = torch.empty(M, lin.N, dtype=torch.bfloat16, device=dev)
         for i in range(4):
             w8.linear(xq, xs, *wl[i % 2], y_bf16=y)
+        xt, xts = w8.quantize_act_tiled(x)
+        for i in range(4):
+            w8.linear_tiled_act(xt, xts, *wl[i % 2], K=lin.K, y_bf16=y)
         torch.cuda.synchronize()
         del wl
     print(json.dumps({"pmc_probe_batched": "done", "shapes": BATCHED_SHAPES}), flush=True)
@@ -258,30 +261,38 @@ def ingest_pmc_batched(dirs, command):
 
     import synth
     M = 288
-    per = {n: {} for n in BATCHED_SHAPES}
-    kname = ""
+    variants = (("row_major_act", ", false>("), ("tiled_act", ", true>("))
+    per = {(n, v): {} for n in BATCHED_SHAPES for v, _ in variants}
+    kname = {}
     for d in dirs:
         rows = _csv_rows(d, "counter_collection.csv")
         for cname in sorted({r["Counter_Name"] for r in rows}):
             rr = [r for r in rows if r["Counter_Name"] == cname]
-            gem = sorted([r for r in rr if "gemm_w8a8_batched" in r["Kernel_Name"]],
-                         key=lambda r: int(r["Dispatch_Id"]))
-            if len(gem) != 4 * len(BATCHED_SHAPES):
-                raise SystemExit(f"{d}: {cname}: expected {4 * len(BATCHED_SHAPES)} batched "
-                                 f"dispatches, found {len(gem)}")
-            kname = gem[0]["Kernel_Name"]
             scale = 1.0
             if cname in ("FETCH_SIZE", "WRITE_SIZE"):
                 copy = [float(r["Counter_Value"]) for r in rr if "copy" in r["Kernel_Name"].lower()]
                 scale = (1 << 30) / (max(copy) * 1024.0) * 1024.0   # KiB -> calibrated bytes
+            # the probe: per shape, 4 row-major-activation launches then 4 tiled ones
+            gem = sorted([r for r in rr if "gemm_w8a8_batched" in r["Kernel_Name"]],
+                         key=lambda r: int(r["Dispatch_Id"]))
+            if len(gem) != 8 * len(BATCHED_SHAPES):
+                raise SystemExit(f"{d}: {cname}: expected {8 * len(BATCHED_SHAPES)} batched "
+                                 f"dispatches, found {len(gem)}")
             for i, n in enumerate(BATCHED_SHAPES):
-                vals = [float(r["Counter_Value"]) * scale for r in gem[4 * i:4 * i + 4]]
-                durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e9
-                        for r in gem[4 * i:4 * i + 4]]
-                per[n][cname] = float(np.median(vals))
-                per[n].setdefault("dur_s", []).extend(durs)
-    lines = ["# Counters of the batched W8A8 GEMM at M=288 (Qwen3-8B linears, tiled int8 weights)",
-             f"# kernel: {kname[:120]}",
+                for j, (v, tag) in enumerate(variants):
+                    sel = gem[8 * i + 4 * j:8 * i + 4 * j + 4]
+                    if not all(tag in r["Kernel_Name"] for r in sel):
+                        raise SystemExit(f"{d}: unexpected kernel order for {n} {v}")
+                    kname[v] = sel[0]["Kernel_Name"]
+                    vals = [float(r["Counter_Value"]) * scale for r in sel]
+                    durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e9
+                            for r in sel]
+                    per[(n, v)][cname] = float(np.median(vals))
+                    per[(n, v)].setdefault("dur_s", []).extend(durs)
+    lines = ["# Counters of the batched W8A8 GEMM at M=288 (Qwen3-8B linears, tiled int8 weights),",
+             "# with row-major activations (w8a8_linear_tiled) and tiled activations",
+             "# (w8a8_linear_tiled_act)",
+             *[f"# kernel ({v}): {k[:120]}" for v, k in kname.items()],
              f"# commands: {command}",
              "# per shape: medians over 4 dispatches.  FETCH_SIZE/WRITE_SIZE in bytes, calibrated",
              "# by the probe's 1 GiB copy.  MfmaUtil = 100*sum(SQ_VALU_MFMA_BUSY_CYCLES) /",
@@ -290,16 +301,17 @@ def ingest_pmc_batched(dirs, command):
     for n in BATCHED_SHAPES:
         lin = next(l for l in synth.QWEN3_8B_LAYER if l.name == n)
         alg = linear_bytes(M, lin.N, lin.K)
-        e = per[n]
-        dur = float(np.median(e.pop("dur_s")))
-        lines.append(f"[{n}] N={lin.N} K={lin.K}")
-        lines.append(f"  duration_us_under_counters: {dur * 1e6:.2f}")
-        lines.append(f"  implied_mfma_pct: {100 * 2 * M * lin.N * lin.K / dur / 5.0e15:.2f}")
-        for k, v in sorted(e.items()):
-            lines.append(f"  {k}: {v:.1f}")
-        if "FETCH_SIZE" in e and "WRITE_SIZE" in e:
-            lines.append(f"  algorithmic_bytes: {alg}")
-            lines.append(f"  hbm_over_algorithmic: {(e['FETCH_SIZE'] + e['WRITE_SIZE']) / alg:.3f}")
+        for v, _ in variants:
+            e = per[(n, v)]
+            dur = float(np.median(e.pop("dur_s")))
+            lines.append(f"[{n} {v}] N={lin.N} K={lin.K}")
+            lines.append(f"  duration_us_under_counters: {dur * 1e6:.2f}")
+            lines.append(f"  implied_mfma_pct: {100 * 2 * M * lin.N * lin.K / dur / 5.0e15:.2f}")
+            for k, val in sorted(e.items()):
+                lines.append(f"  {k}: {val:.1f}")
+            if "FETCH_SIZE" in e and "WRITE_SIZE" in e:
+                lines.append(f"  algorithmic_bytes: {alg}")
+                lines.append(f"  hbm_over_algorithmic: {(e['FETCH_SIZE'] + e['WRITE_SIZE']) / alg:.3f}")
     lines.append(f"kernel_source_sha: {file_sha(BATCHED_SRC)}")
     with open(BATCHED_PMC_FILE, "w") as f:
         f.write("\n".join(lines) + "\n")
