@@ -602,6 +602,47 @@ def w4a8_measurement(dev, x_dev, xq, xsc, wsp):
     return res
 
 
+def fused_layer_measurement(dev, wsp, M):
+    """The Qwen3-8B layer's linears at M rows with q/k/v and gate/up fused
+    (their output channels stacked in one weight, per-channel codes and
+    scales unchanged): 4 launches instead of 7, each graph-replayed over
+    enough weight copies to pass 600 MB."""
+    import numpy as np
+    import torch
+
+    import synth
+    import w8a8_quantized_verification_amd as w8
+
+    lins = synth.QWEN3_8B_LAYER
+    groups = (("qkv", (0, 1, 2)), ("o", (3,)), ("gate_up", (4, 5)), ("down", (6,)))
+    out, tot_t, tot_b = [], 0.0, 0
+    for gi, (name, grp) in enumerate(groups):
+        N, K = sum(lins[i].N for i in grp), lins[grp[0]].K
+        nc = rotation_copies(N, K)
+        wl = []
+        for c in range(nc):
+            w = torch.cat([synth.weights_device(synth.W_LAYER_M5, 7000 + 100 * gi + 10 * c + i,
+                                                lins[i].N, K, dev) for i in grp])
+            wl.append(w8.quantize_weight(w, tiled=True))
+            del w
+        x = torch.from_numpy(synth.activations_bf16(synth.W_LAYER_M5, M, K, outliers=True)
+                             .view(np.int16).copy()).view(torch.bfloat16).to(dev)
+        lxq, lxs = w8.quantize_act(x)
+        y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        t = graph_time([(lambda c=c: w8.linear(lxq, lxs, *wl[c], y_bf16=y, workspace=wsp))
+                        for c in range(nc)], replays=10) / nc
+        b = linear_bytes(M, N, K)
+        out.append({"name": name, "N": N, "K": K, "copies": nc, "us": round(t * 1e6, 2),
+                    "GBs": round(b / t / 1e9, 1)})
+        tot_t += t
+        tot_b += b
+        del wl
+    return {"M": M, "per_launch": out, "sum_us": round(tot_t * 1e6, 2),
+            "aggregate_GBs": round(tot_b / tot_t / 1e9, 1),
+            "aggregate_frac": round(tot_b / tot_t / 1e9 / HBM_PEAK_GBS, 4),
+            "timing": "HIP graph over the rotating weight copies, mean of 10 replays"}
+
+
 def extra_measurements(dev, copies, x_dev, xq, xsc, wsp):
     """Secondary figures: Qwen3-8B decoder-layer linears at M=5 (8 rotating
     copies of each weight, graph-replayed), the row-major layout and the
@@ -615,6 +656,7 @@ def extra_measurements(dev, copies, x_dev, xq, xsc, wsp):
     M = 5
     res = {}
     res["qwen3_8b_layer_linears_m5"] = layer_measurement(dev, wsp, M, synth.W_LAYER_M5)
+    res["qwen3_8b_layer_linears_m5_fused"] = fused_layer_measurement(dev, wsp, M)
     res["qwen3_8b_layer_linears_m288"] = layer_measurement(dev, wsp, 288, synth.W_BATCHED)
 
     K, V = 4096, synth.QWEN3_VOCAB

@@ -10,11 +10,8 @@
 //
 // Split over the keys (flash-decoding): workgroup (split, kv head, b) takes
 // 64 cache positions and every query row that reads its kv head (T x
-// Hq/Hkv rows, <= 64, a contiguous run of them per wave); the 64-key tile of
-// K and V goes through LDS, and each wave keeps an online softmax (running max,
-// sum, unnormalised output) for its rows, one key per lane for the scores
-// and two output dimensions per lane for the value sum, all of its rows at
-// once so that each LDS value feeds several independent accumulations.  A second kernel merges the splits of each row.  Bound
+// Hq/Hkv rows, <= 64); the tile's K and V go through LDS and both products
+// run on the bf16 MFMA (details at the kernel).  A second kernel merges the splits of each row.  Bound
 // by reading the cache (2 * 128 * 2 bytes per position and kv head).
 #include "common.h"
 
@@ -40,142 +37,193 @@ struct AttnArgs {
   uint16_t* out;          // [B][T][Hq][128]
 };
 
-// RW: query rows per wave (rows r = wave * RW + jr); the rows of a wave are
-// processed together so that every K or V value read from LDS feeds RW
-// independent accumulations.
-template <int RW>
-__global__ __launch_bounds__(kAttnThreads) void attn_partial_kernel(AttnArgs a) {
-  __shared__ uint32_t qs[kAttnMaxRows][kDh / 2];   // bf16 pairs
-  // K rows as bf16 pairs with word w of row j stored at word w ^ j (a
-  // lane-per-row read of one word is then conflict-free); V rows plain (a
-  // row is read across the lanes)
-  __shared__ uint32_t ks[kAttnTile][kDh / 2];
-  __shared__ uint32_t vs[kAttnTile][kDh / 2];
-  __shared__ float ps[kAttnThreads / kWave][RW][kAttnTile];
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+// The partial kernel on v_mfma_f32_16x16x32_bf16 (one 64-key tile per
+// workgroup).  S = Q K^T: wave w takes the 16 keys of key block w against
+// every 16-row query block (4 steps of 32 dims).  The row maxima and sums
+// over the 64 keys meet in LDS; P = exp(S - m) goes to LDS as two bf16
+// parts (hi = bf16(P), lo = bf16(P - hi)), each multiplied by V, which keeps
+// the weights to ~16 significant bits.  O = P V: wave w takes
+// dims 32w .. 32w+31 (2 dim blocks) against every query block (2 steps of
+// 32 keys); each lane gathers its 8 keys' values of one dim from the
+// row-major V tile (2-byte LDS reads).  LDS rows are padded so that the 16
+// rows a wave reads at once fall in distinct banks.
+constexpr int kQRow = kDh + 8;         // bf16 per padded Q / K row (272 bytes)
+constexpr int kVtRow = kAttnTile + 8;  // bf16 per padded P row (144 bytes)
+
+__global__ __launch_bounds__(kAttnThreads) void attn_partial_mfma_kernel(AttnArgs a) {
+  // Q rows; after the scores, the same bytes hold the low parts of P
+  __shared__ __attribute__((aligned(16))) uint16_t qs[kAttnMaxRows][kQRow];
+  static_assert(sizeof(uint16_t) * kAttnMaxRows * kVtRow <= sizeof(qs), "P low parts fit");
+  uint16_t(*ps_lo)[kVtRow] = reinterpret_cast<uint16_t(*)[kVtRow]>(&qs[0][0]);
+  __shared__ __attribute__((aligned(16))) uint16_t ks[kAttnTile][kQRow];
+  __shared__ __attribute__((aligned(16))) uint16_t vs[kAttnTile][kQRow];
+  __shared__ __attribute__((aligned(16))) uint16_t ps[kAttnMaxRows][kVtRow];
+  __shared__ float red[kAttnThreads / kWave][kAttnMaxRows];
+  __shared__ float rowm[kAttnMaxRows];
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int group = a.Hq / a.Hkv;
   const int rows = a.T * group;
+  const int rblocks = (rows + 15) / 16;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int col = lane & 15, grp = lane >> 4;
   int L = a.len[b];
   L = L < a.T ? a.T : (L > a.Lmax ? a.Lmax : L);
-  const int c0 = split * kAttnChunk;
-  const int c1 = min(c0 + kAttnChunk, L);
+  const int t0 = split * kAttnTile;
+  const int c1 = min(t0 + kAttnTile, L);
   const float scale = 0.08838834764831845f;   // 1/sqrt(128)
+  const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
 
-  // query rows r = i * group + g (position i, head kvh * group + g), bf16 pairs in LDS
-  for (int e = tid; e < rows * (kDh / 2); e += kAttnThreads) {
-    const int r = e / (kDh / 2), d2 = e % (kDh / 2);
-    const int i = r / group, h = kvh * group + r % group;
-    qs[r][d2] = *reinterpret_cast<const uint32_t*>(
-        a.q + (((size_t)b * a.T + i) * a.Hq + h) * kDh + 2 * d2);
-  }
-
-  const int r0 = wave * RW;
-  float m[RW], l[RW], o0[RW], o1[RW];
-#pragma unroll
-  for (int jr = 0; jr < RW; ++jr) { m[jr] = -INFINITY; l[jr] = 0.0f; o0[jr] = 0.0f; o1[jr] = 0.0f; }
-
+  // Q rows (zero beyond `rows`), K rows, V transposed: every global load is
+  // issued before the first LDS store
+  constexpr int kQLoads = kAttnMaxRows * (kDh / 8) / kAttnThreads;
+  constexpr int kLoads = kAttnTile * (kDh / 8) / kAttnThreads;
   const uint16_t* kb = a.k + ((size_t)b * a.Hkv + kvh) * (size_t)a.Lmax * kDh;
   const uint16_t* vb = a.v + ((size_t)b * a.Hkv + kvh) * (size_t)a.Lmax * kDh;
-  for (int t0 = c0; t0 < c1; t0 += kAttnTile) {
-    __syncthreads();   // previous tile's reads (and the q fill) done
-    // 64 rows x 128 bf16 of K and V, 16 bytes per load: all loads first, then
-    // the LDS stores (the loads of one tile are independent)
-    constexpr int kLoads = kAttnTile * (kDh / 8) / kAttnThreads;
-    uint4 kk[kLoads], vv[kLoads];
+  uint4 qq[kQLoads], kk[kLoads], vv[kLoads];
 #pragma unroll
-    for (int u = 0; u < kLoads; ++u) {
-      const int e = tid + u * kAttnThreads;
-      const int j = e / (kDh / 8), d8 = (e % (kDh / 8)) * 8;
-      kk[u] = make_uint4(0u, 0u, 0u, 0u);
-      vv[u] = make_uint4(0u, 0u, 0u, 0u);
-      if (t0 + j < c1) {
-        kk[u] = *reinterpret_cast<const uint4*>(kb + (size_t)(t0 + j) * kDh + d8);
-        vv[u] = *reinterpret_cast<const uint4*>(vb + (size_t)(t0 + j) * kDh + d8);
-      }
+  for (int u = 0; u < kLoads; ++u) {
+    const int e = tid + u * kAttnThreads;
+    const int j = e / (kDh / 8), d8 = (e % (kDh / 8)) * 8;
+    kk[u] = z4;
+    vv[u] = z4;
+    if (t0 + j < c1) {
+      kk[u] = *reinterpret_cast<const uint4*>(kb + (size_t)(t0 + j) * kDh + d8);
+      vv[u] = *reinterpret_cast<const uint4*>(vb + (size_t)(t0 + j) * kDh + d8);
     }
-#pragma unroll
-    for (int u = 0; u < kLoads; ++u) {
-      const int e = tid + u * kAttnThreads;
-      const int j = e / (kDh / 8), w0 = (e % (kDh / 8)) * 4;
-      const uint32_t kw[4] = {kk[u].x, kk[u].y, kk[u].z, kk[u].w};
-      const uint32_t vw[4] = {vv[u].x, vv[u].y, vv[u].z, vv[u].w};
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        ks[j][(w0 + w) ^ j] = kw[w];
-        vs[j][w0 + w] = vw[w];
-      }
-    }
-    __syncthreads();
-    if (r0 >= rows) continue;      // (every wave still meets both barriers)
-
-    // scores of key t0 + lane against the wave's rows
-    float acc[RW];
-#pragma unroll
-    for (int jr = 0; jr < RW; ++jr) acc[jr] = 0.0f;
-#pragma unroll 4
-    for (int d2 = 0; d2 < kDh / 2; ++d2) {
-      const uint32_t kw = ks[lane][d2 ^ lane];
-      const float k0 = __uint_as_float(kw << 16), k1 = __uint_as_float(kw & 0xffff0000u);
-#pragma unroll
-      for (int jr = 0; jr < RW; ++jr) {
-        const uint32_t qw = qs[r0 + jr < rows ? r0 + jr : 0][d2];
-        acc[jr] += __uint_as_float(qw << 16) * k0;
-        acc[jr] += __uint_as_float(qw & 0xffff0000u) * k1;
-      }
-    }
-    const int p = t0 + lane;
-    float alpha[RW];
-#pragma unroll
-    for (int jr = 0; jr < RW; ++jr) {
-      const int last = L - a.T + (r0 + jr) / group;          // inclusive
-      const bool vis = r0 + jr < rows && p < c1 && p <= last;
-      const float s = vis ? acc[jr] * scale : -INFINITY;
-      const float mnew = fmaxf(m[jr], wave_max(s));
-      float pj = 0.0f;
-      alpha[jr] = 1.0f;
-      if (mnew != -INFINITY) {
-        alpha[jr] = expf(m[jr] - mnew);                     // 0 when m was -inf
-        pj = vis ? expf(s - mnew) : 0.0f;
-        m[jr] = mnew;
-      }
-      float psum = pj;
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) psum += __shfl_xor(psum, off, kWave);
-      l[jr] = l[jr] * alpha[jr] + psum;
-      ps[wave][jr][lane] = pj;
-    }
-    // (the wave's own LDS rows: written and read by the same wave, in order)
-    float a0[RW], a1[RW];
-#pragma unroll
-    for (int jr = 0; jr < RW; ++jr) { a0[jr] = o0[jr] * alpha[jr]; a1[jr] = o1[jr] * alpha[jr]; }
-#pragma unroll 4
-    for (int j = 0; j < kAttnTile; ++j) {
-      const uint32_t vw = vs[j][lane];
-      const float v0 = __uint_as_float(vw << 16), v1 = __uint_as_float(vw & 0xffff0000u);
-#pragma unroll
-      for (int jr = 0; jr < RW; ++jr) {
-        const float pk = ps[wave][jr][j];
-        a0[jr] += pk * v0;
-        a1[jr] += pk * v1;
-      }
-    }
-#pragma unroll
-    for (int jr = 0; jr < RW; ++jr) { o0[jr] = a0[jr]; o1[jr] = a1[jr]; }
   }
-  // partial results of this split
+#pragma unroll
+  for (int u = 0; u < kQLoads; ++u) {
+    const int e = tid + u * kAttnThreads;
+    const int r = e / (kDh / 8), d8 = (e % (kDh / 8)) * 8;
+    qq[u] = z4;
+    if (r < rows) {
+      const int i = r / group, h = kvh * group + r % group;
+      qq[u] = *reinterpret_cast<const uint4*>(a.q + (((size_t)b * a.T + i) * a.Hq + h) * kDh + d8);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kQLoads; ++u) {
+    const int e = tid + u * kAttnThreads;
+    const int r = e / (kDh / 8), d8 = (e % (kDh / 8)) * 8;
+    if (r < rblocks * 16) *reinterpret_cast<uint4*>(&qs[r][d8]) = qq[u];
+  }
+#pragma unroll
+  for (int u = 0; u < kLoads; ++u) {
+    const int e = tid + u * kAttnThreads;
+    const int j = e / (kDh / 8), d8 = (e % (kDh / 8)) * 8;
+    *reinterpret_cast<uint4*>(&ks[j][d8]) = kk[u];
+    *reinterpret_cast<uint4*>(&vs[j][d8]) = vv[u];
+  }
+  __syncthreads();
+
+  // S for key block `wave`: lane holds rows 16*qb + 4*grp + r, key 16*wave + col
+  v4f sacc[kAttnMaxRows / 16];
+#pragma unroll
+  for (int qb = 0; qb < kAttnMaxRows / 16; ++qb) {
+    sacc[qb] = v4f{0.f, 0.f, 0.f, 0.f};
+    if (qb < rblocks) {
+#pragma unroll
+      for (int st = 0; st < kDh / 32; ++st) {
+        const v4i qa = *reinterpret_cast<const v4i*>(&qs[qb * 16 + col][st * 32 + grp * 8]);
+        const v4i kb4 = *reinterpret_cast<const v4i*>(&ks[wave * 16 + col][st * 32 + grp * 8]);
+        sacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, qa),
+                                                            __builtin_bit_cast(v8bf, kb4),
+                                                            sacc[qb], 0, 0, 0);
+      }
+    }
+  }
+  const int p = t0 + wave * 16 + col;
+  // scale and mask; row maxima over this wave's 16 keys, then over the 4 waves
+#pragma unroll
+  for (int qb = 0; qb < kAttnMaxRows / 16; ++qb) {
+    if (qb >= rblocks) break;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int qr = qb * 16 + 4 * grp + r;
+      const bool vis = qr < rows && p < c1 && p <= L - a.T + qr / group;
+      float s = vis ? sacc[qb][r] * scale : -INFINITY;
+      sacc[qb][r] = s;
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) s = fmaxf(s, __shfl_xor(s, off, kWave));
+      if (col == 0) red[wave][qr] = s;
+    }
+  }
+  __syncthreads();
+  // P = exp(S - m) as bf16 into LDS; partial row sums of the rounded values
+#pragma unroll
+  for (int qb = 0; qb < kAttnMaxRows / 16; ++qb) {
+    if (qb >= rblocks) break;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int qr = qb * 16 + 4 * grp + r;
+      const float m = fmaxf(fmaxf(red[0][qr], red[1][qr]), fmaxf(red[2][qr], red[3][qr]));
+      if (wave == 0 && col == 0) rowm[qr] = m;
+      const float s = sacc[qb][r];
+      // P as the sum of two bf16 values (hi + lo carries ~16 significant
+      // bits), so that the product keeps the softmax weights at fp32-like
+      // precision through the bf16 MFMA
+      const float pf = (s == -INFINITY) ? 0.0f : expf(s - m);
+      const uint16_t hi = f32_to_bf16_rne(pf);
+      const uint16_t lo = f32_to_bf16_rne(pf - bf16_to_f32(hi));
+      ps[qr][wave * 16 + col] = hi;
+      ps_lo[qr][wave * 16 + col] = lo;
+      sacc[qb][r] = pf;
+    }
+  }
+  __syncthreads();   // all maxima read before red is reused; P complete
+#pragma unroll
+  for (int qb = 0; qb < kAttnMaxRows / 16; ++qb) {
+    if (qb >= rblocks) break;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int qr = qb * 16 + 4 * grp + r;
+      float l = sacc[qb][r];
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) l += __shfl_xor(l, off, kWave);
+      if (col == 0) red[wave][qr] = l;
+    }
+  }
+
+  // O = P V for dims 32*wave .. +31; lane holds rows 16*qb + 4*grp + r, dim 16*db + col
   const size_t base = (((size_t)b * a.Hkv + kvh) * a.nsplit + split) * kAttnMaxRows;
 #pragma unroll
-  for (int jr = 0; jr < RW; ++jr) {
-    const int r = r0 + jr;
-    if (r >= rows) break;
-    float* po = a.part_o + (base + r) * kDh;
-    po[2 * lane] = o0[jr];
-    po[2 * lane + 1] = o1[jr];
-    if (lane == 0) {
-      a.part_ml[(base + r) * 2] = m[jr];
-      a.part_ml[(base + r) * 2 + 1] = l[jr];
+  for (int qb = 0; qb < kAttnMaxRows / 16; ++qb) {
+    if (qb >= rblocks) break;
+#pragma unroll
+    for (int dbi = 0; dbi < 2; ++dbi) {
+      const int db = wave * 2 + dbi;
+      v4f o = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < kAttnTile / 32; ++st) {
+        const v4i ph = *reinterpret_cast<const v4i*>(&ps[qb * 16 + col][st * 32 + grp * 8]);
+        const v4i pl = *reinterpret_cast<const v4i*>(&ps_lo[qb * 16 + col][st * 32 + grp * 8]);
+        // the B operand: dim 16*db + col of keys 32*st + 8*grp .. +7, gathered
+        // from the row-major V tile
+        uint32_t vw[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int j = st * 32 + grp * 8 + 2 * q;
+          vw[q] = (uint32_t)vs[j][db * 16 + col] | ((uint32_t)vs[j + 1][db * 16 + col] << 16);
+        }
+        const v4i vb4 = v4i{(int)vw[0], (int)vw[1], (int)vw[2], (int)vw[3]};
+        o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, ph),
+                                                     __builtin_bit_cast(v8bf, vb4), o, 0, 0, 0);
+        o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, pl),
+                                                     __builtin_bit_cast(v8bf, vb4), o, 0, 0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int qr = qb * 16 + 4 * grp + r;
+        if (qr < rows) a.part_o[(base + qr) * kDh + db * 16 + col] = o[r];
+      }
     }
+  }
+  __syncthreads();   // the partial sums in red and the maxima in rowm are complete
+  if (tid < rows) {
+    a.part_ml[(base + tid) * 2] = rowm[tid];
+    a.part_ml[(base + tid) * 2 + 1] = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
   }
 }
 
@@ -223,12 +271,12 @@ __global__ __launch_bounds__(kDh) void attn_combine_kernel(AttnArgs a) {
   // (a split with no visible key has weight 0 and a zero partial output)
   float o = 0.0f;
   int s = 0;
-  for (; s + 8 <= a.nsplit; s += 8) {
-    float po[8];
+  for (; s + 32 <= a.nsplit; s += 32) {
+    float po[32];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) po[u] = a.part_o[((row0 + s + u) * kAttnMaxRows + r) * kDh + d];
+    for (int u = 0; u < 32; ++u) po[u] = a.part_o[((row0 + s + u) * kAttnMaxRows + r) * kDh + d];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) o += po[u] * wts[s + u];
+    for (int u = 0; u < 32; ++u) o += po[u] * wts[s + u];
   }
   for (; s < a.nsplit; ++s) o += a.part_o[((row0 + s) * kAttnMaxRows + r) * kDh + d] * wts[s];
   const float y = lsum > 0.0f ? o / lsum : 0.0f;
@@ -312,21 +360,7 @@ hipError_t w8a8_launch_verify_attention(const uint16_t* q, const uint16_t* k, co
                                        ((rows * kDh * sizeof(float) + 255) & ~(size_t)255));
   a.out = out;
   const dim3 grid((unsigned)a.nsplit, (unsigned)Hkv, (unsigned)B);
-  const int rw = (int)((T * (Hq / Hkv) + 3) / 4);   // rows per wave, 4 waves
-#define W8A8_ATT(RW) hipLaunchKernelGGL(attn_partial_kernel<RW>, grid, dim3(kAttnThreads), 0, stream, a)
-  switch (rw) {
-    case 1: W8A8_ATT(1); break;
-    case 2: W8A8_ATT(2); break;
-    case 3: W8A8_ATT(3); break;
-    case 4: W8A8_ATT(4); break;
-    case 5: W8A8_ATT(5); break;
-    case 6: W8A8_ATT(6); break;
-    case 7: case 8: W8A8_ATT(8); break;
-    case 9: case 10: W8A8_ATT(10); break;
-    case 11: case 12: W8A8_ATT(12); break;
-    default: W8A8_ATT(16); break;
-  }
-#undef W8A8_ATT
+  hipLaunchKernelGGL(attn_partial_mfma_kernel, grid, dim3(kAttnThreads), 0, stream, a);
   hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)T, (unsigned)Hq, (unsigned)B), dim3(kDh),
                      0, stream, a);
   return hipGetLastError();
