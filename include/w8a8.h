@@ -337,11 +337,12 @@ w8a8_status w8a8_silu_mul_quant(const uint16_t* gate, const uint16_t* up,
  *   then rotary embedding: dims (d, d + 64), d < 64, turned by the fp32
  *     angle fp32(fp32(p) * f_d), f_d = fp32(rope_base^(-d/64)) (computed on the
  *     host in double): (x1, x2) -> bf16(x1 cos - x2 sin), bf16(x2 cos + x1 sin);
- *   q goes to q_out [B][T][Hq][Dh]; k and v (unchanged) are written into
- *   k_cache / v_cache [B][Hkv][Lmax][Dh] at position p.
+ *   q goes to q_out [B][T][Hq][Dh]; k is written into k_cache
+ *   [B][Hkv][Lmax][Dh] and v (unchanged) into the blocked v_cache (layout
+ *   at w8a8_verify_attention) at position p.
  * fp32 arithmetic (sine and cosine of the fp32 angle in fp32).  Dh == 128
- * (else W8A8_ERR_UNSUPPORTED); Hq % Hkv == 0; T <= Lmax <= 131072;
- * rope_base > 1; eps >= 0.
+ * (else W8A8_ERR_UNSUPPORTED); Hq % Hkv == 0; T <= Lmax <= 131072 with
+ * Lmax % 16 == 0; rope_base > 1; eps >= 0.
  */
 w8a8_status w8a8_qk_norm_rope_append(const uint16_t* qkv, int64_t B, int64_t T,
                                      int64_t Hq, int64_t Hkv, int64_t Dh,
@@ -360,13 +361,20 @@ w8a8_status w8a8_qk_norm_rope_append(const uint16_t* qkv, int64_t B, int64_t T,
  *   out[b][i][h] = softmax_j(q[b][i][h] . k[b][kvh][j] / sqrt(Dh)) . v[b][kvh][j]
  * in fp32 (summation order unspecified), rounded to bf16.
  *
- * q [B][T][Hq][Dh], k_cache and v_cache [B][Hkv][Lmax][Dh], out
- * [B][T][Hq][Dh], all bf16; q, k, v 16-byte aligned; lengths [B] int32 on
- * the device (values outside [T, Lmax] are clamped into it).  Requires Dh
- * == 128 (else W8A8_ERR_UNSUPPORTED), Hq % Hkv == 0, T * Hq / Hkv <= 64,
- * T <= Lmax <= 131072.
+ * q [B][T][Hq][Dh], k_cache [B][Hkv][Lmax][Dh] (one row per position),
+ * out [B][T][Hq][Dh], all bf16.  v_cache is bf16 in a blocked layout of
+ * the same size: for each (b, kv head) a slab of Lmax * Dh elements in
+ * blocks of 16 positions, position p and dim d at element
+ *   (p / 16) * 2048 + ((p % 16 / 4) * 16 + d % 16) * 32 + (d / 16) * 4 + p % 4
+ * of slab (b * Hkv + kvh) (w8a8_pack_v_cache converts a row-major cache;
+ * w8a8_qk_norm_rope_append appends in this layout).  Positions >= L_b may
+ * hold any bits.  q, k, v 16-byte aligned; lengths [B] int32 on the device
+ * (values outside [T, Lmax] are clamped into it).  Requires Dh == 128
+ * (else W8A8_ERR_UNSUPPORTED), Hq % Hkv == 0, T * Hq / Hkv <= 64,
+ * T <= Lmax <= 131072, Lmax % 16 == 0.
  * workspace: at least w8a8_verify_attention_workspace_bytes(B, Hkv, Lmax)
- * bytes, 256-byte aligned; no initial contents needed.
+ * bytes (0 for arguments out of range), 256-byte aligned; no initial
+ * contents needed.
  */
 size_t      w8a8_verify_attention_workspace_bytes(int64_t B, int64_t Hkv, int64_t Lmax);
 w8a8_status w8a8_verify_attention(const uint16_t* q, const uint16_t* k_cache,
@@ -374,6 +382,16 @@ w8a8_status w8a8_verify_attention(const uint16_t* q, const uint16_t* k_cache,
                                   int64_t B, int64_t T, int64_t Hq, int64_t Hkv,
                                   int64_t Dh, int64_t Lmax, uint16_t* out,
                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Converts a row-major V cache v [B][Hkv][Lmax][Dh] bf16 into the blocked
+ * layout w8a8_verify_attention reads (written to v_blocked, same size, not
+ * overlapping v; 16-byte aligned).  A pure permutation of the bf16 values.
+ * Dh == 128 (else W8A8_ERR_UNSUPPORTED); Lmax a multiple of 16 in
+ * [16, 131072].
+ */
+w8a8_status w8a8_pack_v_cache(const uint16_t* v, int64_t B, int64_t Hkv, int64_t Lmax,
+                              int64_t Dh, uint16_t* v_blocked, void* stream);
 
 /*
  * W4A8: the verifier's weights in 4 bits (int4 codes, one fp32 scale per

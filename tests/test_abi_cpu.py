@@ -197,10 +197,22 @@ def test_verify_attention_validation(lib):
     assert call(T=17) == UNSUPPORTED          # 17 * 4 > 64 query rows per kv head
     assert call(Hq=30) == INVALID
     assert call(L=4) == INVALID
+    assert call(L=4100) == INVALID            # not a multiple of 16
+    assert lib.w8a8_verify_attention_workspace_bytes(1, 8, 4100) == 0
     assert call(q=A16 + 8) == INVALID
     assert call(ln=None) == INVALID
     assert call(wb=8) == WORKSPACE
     assert call(B=0, q=None, k=None, v=None, ln=None, out=None, w=None) == OK
+
+
+def test_pack_v_cache_validation(lib):
+    f = lib.w8a8_pack_v_cache
+    assert f(A16, 1, 8, 4096, 64, A16b, None) == UNSUPPORTED
+    assert f(A16, 1, 8, 4100, 128, A16b, None) == INVALID
+    assert f(A16, 1, 8, 4096, 128, None, None) == INVALID
+    assert f(A16, 1, 8, 4096, 128, A16b + 8, None) == INVALID       # output 16-byte alignment
+    assert f(A16, 1, 1, 64, 128, A16 + 64, None) == INVALID         # overlap
+    assert f(None, 0, 8, 4096, 128, None, None) == OK
 
 
 def test_bf16_linear_validation(lib):

@@ -20,6 +20,7 @@ __all__ = [
     "verify_sample_workspace_bytes", "sample_weights", "w4_shape", "quantize_weight_w4",
     "linear_w4", "lm_head_argmax_w4", "residual_rmsnorm_quant", "silu_mul_quant",
     "quantize_act_tiled", "linear_tiled_act", "verify_attention", "qk_norm_rope_append",
+    "pack_v_cache",
 ]
 
 
@@ -524,11 +525,23 @@ def linear_tiled_act(xq_tiled, x_scale, wq_tiled, w_scale, *, K: int | None = No
     return y_bf16, y_f32, acc
 
 
+def pack_v_cache(v, *, out=None):
+    """A row-major V cache bf16 ``[B][Hkv][Lmax][128]`` in the blocked layout
+    that ``verify_attention`` reads (same shape and dtype, values permuted
+    within each 16-position block)."""
+    _need(v, "v", torch.bfloat16, 4)
+    B, Hkv, Lmax, Dh = v.shape
+    out = _out(out, (B, Hkv, Lmax, Dh), torch.bfloat16, v.device, "out")
+    check(lib().w8a8_pack_v_cache(_ptr(v), B, Hkv, Lmax, Dh, _ptr(out), _stream(v.device)))
+    return out
+
+
 def verify_attention(q, k_cache, v_cache, lengths, *, out=None, workspace: Workspace | None = None):
     """Causal grouped-query attention of the verified block: ``q`` bf16
-    ``[B][T][Hq][128]``, ``k_cache``/``v_cache`` bf16 ``[B][Hkv][Lmax][128]``,
-    ``lengths`` int32 ``[B]`` (valid cache positions, the block's own T
-    included).  Returns ``out`` bf16 ``[B][T][Hq][128]``."""
+    ``[B][T][Hq][128]``, ``k_cache`` bf16 ``[B][Hkv][Lmax][128]``,
+    ``v_cache`` bf16 of the same shape in the blocked layout (see
+    ``pack_v_cache``), ``lengths`` int32 ``[B]`` (valid cache positions, the
+    block's own T included).  Returns ``out`` bf16 ``[B][T][Hq][128]``."""
     _need(q, "q", torch.bfloat16, 4)
     dev = q.device
     _need(k_cache, "k_cache", torch.bfloat16, 4, dev)
@@ -552,7 +565,7 @@ def verify_attention(q, k_cache, v_cache, lengths, *, out=None, workspace: Works
 def qk_norm_rope_append(qkv, q_gamma, k_gamma, lengths, k_cache, v_cache, *, T: int, Hq: int,
                         Hkv: int, eps: float = 1e-6, rope_base: float = 1e6, q_out=None):
     """Per-head q/k RMSNorm, rotary embedding at position L_b - T + i, and the
-    append of k, v into the caches.  ``qkv`` bf16 ``[B*T][(Hq + 2 Hkv) * 128]``
+    append of k, v into the caches (v in the blocked layout).  ``qkv`` bf16 ``[B*T][(Hq + 2 Hkv) * 128]``
     (e.g. a fused [q;k;v] linear's output), ``lengths`` int32 ``[B]`` (valid
     positions after the append).  Returns ``q_out`` bf16 ``[B][T][Hq][128]``."""
     _need(qkv, "qkv", torch.bfloat16, 2)

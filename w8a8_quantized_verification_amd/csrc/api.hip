@@ -543,7 +543,9 @@ w8a8_status w8a8_linear_tiled_act(const int8_t* xq_tiled, const float* x_scale,
 // ---- attention of the verified block ----
 
 size_t w8a8_verify_attention_workspace_bytes(int64_t B, int64_t Hkv, int64_t Lmax) {
-  if (B <= 0 || Hkv <= 0 || Lmax <= 0 || B > 65535 || Hkv > 65535 || Lmax > (1 << 17)) return 0;
+  if (B <= 0 || Hkv <= 0 || Lmax <= 0 || B > 65535 || Hkv > 65535 || Lmax > (1 << 17) ||
+      Lmax % 16 != 0)
+    return 0;
   return w8a8_attention_workspace_bytes_impl(B, Hkv, Lmax);
 }
 
@@ -561,7 +563,8 @@ w8a8_status w8a8_verify_attention(const uint16_t* q, const uint16_t* k_cache,
     return fail(W8A8_ERR_INVALID_ARG, fn, "T, Hq, Hkv must be >= 1 with Hq % Hkv == 0");
   if (T * (Hq / Hkv) > 64)
     return fail(W8A8_ERR_UNSUPPORTED, fn, "T * Hq / Hkv must be <= 64");
-  if (Lmax < T || Lmax > (1 << 17)) return fail(W8A8_ERR_INVALID_ARG, fn, "Lmax out of range [T, 131072]");
+  if (Lmax < T || Lmax > (1 << 17) || Lmax % 16 != 0)
+    return fail(W8A8_ERR_INVALID_ARG, fn, "Lmax must be a multiple of 16 in [T, 131072]");
   if (!q || !k_cache || !v_cache || !lengths || !out)
     return fail(W8A8_ERR_INVALID_ARG, fn, "required pointer is NULL");
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 4) ||
@@ -573,6 +576,27 @@ w8a8_status w8a8_verify_attention(const uint16_t* q, const uint16_t* k_cache,
   return hip_status(w8a8_launch_verify_attention(q, k_cache, v_cache, lengths, B, T, Hq, Hkv, Lmax,
                                                  out, workspace,
                                                  reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
+
+w8a8_status w8a8_pack_v_cache(const uint16_t* v, int64_t B, int64_t Hkv, int64_t Lmax,
+                              int64_t Dh, uint16_t* v_blocked, void* stream) {
+  static const char* fn = "w8a8_pack_v_cache";
+  g_last_error.clear();
+  if (B < 0 || Hkv < 0 || B > 65535 || Hkv > 65535) return fail(W8A8_ERR_INVALID_ARG, fn, "B, Hkv out of range");
+  if (B == 0 || Hkv == 0) return W8A8_OK;
+  if (Dh != 128) return fail(W8A8_ERR_UNSUPPORTED, fn, "head dimension must be 128");
+  if (Lmax < 16 || Lmax > (1 << 17) || Lmax % 16 != 0)
+    return fail(W8A8_ERR_INVALID_ARG, fn, "Lmax must be a multiple of 16 in [16, 131072]");
+  if (!v || !v_blocked) return fail(W8A8_ERR_INVALID_ARG, fn, "required pointer is NULL");
+  if (!aligned(v, 2) || !aligned(v_blocked, 16))
+    return fail(W8A8_ERR_INVALID_ARG, fn, "v must be 2-byte aligned, v_blocked 16");
+  const char* vb = reinterpret_cast<const char*>(v);
+  const char* ob = reinterpret_cast<const char*>(v_blocked);
+  const size_t bytes = (size_t)B * Hkv * Lmax * 128 * 2;
+  if (vb < ob + bytes && ob < vb + bytes) return fail(W8A8_ERR_INVALID_ARG, fn, "v and v_blocked overlap");
+  return hip_status(w8a8_launch_pack_v_cache(v, B * Hkv, Lmax, v_blocked,
+                                             reinterpret_cast<hipStream_t>(stream)), fn);
 }
 
 
@@ -588,7 +612,8 @@ w8a8_status w8a8_qk_norm_rope_append(const uint16_t* qkv, int64_t B, int64_t T, 
   if (Dh != 128) return fail(W8A8_ERR_UNSUPPORTED, fn, "head dimension must be 128");
   if (T < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || Hq + 2 * Hkv > 65535 || B * T > (1 << 30))
     return fail(W8A8_ERR_INVALID_ARG, fn, "T, Hq, Hkv out of range");
-  if (Lmax < T || Lmax > (1 << 17)) return fail(W8A8_ERR_INVALID_ARG, fn, "Lmax out of range [T, 131072]");
+  if (Lmax < T || Lmax > (1 << 17) || Lmax % 16 != 0)
+    return fail(W8A8_ERR_INVALID_ARG, fn, "Lmax must be a multiple of 16 in [T, 131072]");
   if (!(std::isfinite(eps) && eps >= 0.0f) || !(std::isfinite(rope_base) && rope_base > 1.0f))
     return fail(W8A8_ERR_INVALID_ARG, fn, "eps must be >= 0 and rope_base > 1");
   if (!qkv || !q_gamma || !k_gamma || !lengths || !q_out || !k_cache || !v_cache)

@@ -142,6 +142,8 @@ hipError_t w8a8_launch_verify_attention(const uint16_t* q, const uint16_t* k, co
                                         const int32_t* lengths, int64_t B, int64_t T,
                                         int64_t Hq, int64_t Hkv, int64_t Lmax, uint16_t* out,
                                         void* workspace, hipStream_t stream);
+hipError_t w8a8_launch_pack_v_cache(const uint16_t* v, int64_t BH, int64_t Lmax, uint16_t* out,
+                                    hipStream_t stream);
 hipError_t w8a8_launch_qk_norm_rope_append(const uint16_t* qkv, int64_t B, int64_t T, int64_t Hq,
                                            int64_t Hkv, const uint16_t* q_gamma,
                                            const uint16_t* k_gamma, float eps, float rope_base,
