@@ -63,6 +63,10 @@ def parse_args():
     p.add_argument("--ingest-trace", metavar="TRACE_DIR",
                    help="turn a rocprofv3 --kernel-trace --stats csv run into a summary")
     p.add_argument("--command", default="", help="the command that produced the ingested run")
+    p.add_argument("--attention-probe", action="store_true",
+                   help="only the attention scaling runs (for rocprofv3 --kernel-trace)")
+    p.add_argument("--ingest-attention-trace", metavar="TRACE_DIR",
+                   help="per-launch-shape summary of a --kernel-trace run of --attention-probe")
     return p.parse_args()
 
 
@@ -216,6 +220,47 @@ def ingest_trace(trace_dir, command, out_path):
     print("\n".join(lines))
 
 
+ATTENTION_WORKLOADS = [(1, 5, 32, 8, 4096), (1, 8, 64, 8, 4096), (1, 5, 32, 8, 16384),
+                       (1, 8, 64, 8, 65536), (1, 5, 32, 8, 65536), (32, 5, 32, 8, 4096)]
+
+
+def ingest_attention_trace(trace_dir, command, out_path):
+    """Median durations of the split and combine kernels per workload of a
+    rocprofv3 --kernel-trace csv run of --attention-probe.  Each split
+    launch is paired with the combine launch after it; the workloads run in
+    ATTENTION_WORKLOADS order, and adjacent ones differ in their (split
+    kernel, split grid, combine grid), which is where a new one starts."""
+    import numpy as np
+    rows = sorted((r for r in _csv_rows(trace_dir, "kernel_trace.csv") if "attn_" in r["Kernel_Name"]),
+                  key=lambda r: int(r["Start_Timestamp"]))
+
+    def grid(r):
+        return f"{r['Grid_Size_X']}x{r['Grid_Size_Y']}x{r['Grid_Size_Z']}"
+
+    segs, sig = [], None
+    for a, b in zip(rows, rows[1:]):
+        if "split" not in a["Kernel_Name"] or "combine" not in b["Kernel_Name"]:
+            continue
+        s_ = (a["Kernel_Name"].split("(")[0].replace("void ", ""), grid(a), grid(b))
+        if s_ != sig:
+            segs.append((s_, [], []))
+            sig = s_
+        segs[-1][1].append(int(a["End_Timestamp"]) - int(a["Start_Timestamp"]))
+        segs[-1][2].append(int(b["End_Timestamp"]) - int(b["Start_Timestamp"]))
+    lines = ["# rocprofv3 kernel trace of verify_attention (the attention_scaling workloads)",
+             f"# command: {command}",
+             "# medians over the calls of each workload; grid = work-items x, y, z",
+             f"{'split_us':>9} {'combine_us':>10} {'calls':>6}  {'split kernel':<32} "
+             f"{'split grid':<12} workload (B, T, Hq, Hkv, positions)"]
+    for k, ((name, g1, g2), sp, cb) in enumerate(segs):
+        wl = ATTENTION_WORKLOADS[k] if k < len(ATTENTION_WORKLOADS) else "?"
+        lines.append(f"{np.median(sp) / 1e3:9.2f} {np.median(cb) / 1e3:10.2f} {len(sp):6d}  "
+                     f"{name:<32} {g1:<12} {wl}")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 BATCHED_SHAPES = ("q", "gate", "down")   # probe order; 4 dispatches each
 BATCHED_PMC_FILE = os.path.join(ROOT, "profiles", "gemm_w8a8_batched_m288_counters.txt")
 BATCHED_SRC = os.path.join(ROOT, "w8a8_quantized_verification_amd", "csrc", "gemm_w8a8_batched.hip")
@@ -330,6 +375,10 @@ def main():
         ingest_trace(args.ingest_trace, args.command,
                      os.path.join(ROOT, "profiles", "lm_head_verify_m5_kernel_trace.txt"))
         return
+    if args.ingest_attention_trace:
+        ingest_attention_trace(args.ingest_attention_trace, args.command,
+                               os.path.join(ROOT, "profiles", "verify_attention_kernel_trace.txt"))
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -345,6 +394,10 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a ROCm GPU", file=sys.stderr)
         sys.exit(1)
+    if args.attention_probe:
+        print(json.dumps({"attention_scaling": attention_scaling(torch.device("cuda:0"))}),
+              flush=True)
+        return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
@@ -718,6 +771,7 @@ def extra_measurements(dev, copies, x_dev, xq, xsc, wsp):
                       replays=50) / 8
     res["w4a8_lm_head_m5"] = w4a8_measurement(dev, x_dev, xq, xsc, wsp)
     res["qwen3_8b_layer_step_m5"] = layer_step_measurement(dev, wsp)
+    res["attention_scaling"] = attention_scaling(dev)
 
     # the online smoothing multiply fused into quantize_act, on the outlier
     # activations of the layer inputs: 16 launches per graph over 16 inputs
@@ -917,6 +971,41 @@ def oracle_timings():
                                  "step_ms_extrapolated_x64": round((64 * layer_s + head_s) * 1e3, 1),
                                  "verified_tokens_per_s_extrapolated":
                                      round(8 / (64 * layer_s + head_s), 3)}
+    return out
+
+
+def attention_scaling(dev):
+    """verify_attention alone over growing caches: Qwen3-8B heads (32 / 8)
+    at T = 5 and Qwen3-32B heads (64 / 8) at T = 8, one sequence, and 32
+    sequences of 4096 positions.  Two caches alternate inside a HIP graph;
+    GB/s counts the K and V bytes the call must read."""
+    import torch
+
+    import w8a8_quantized_verification_amd as w8
+
+    out = []
+    # (adjacent workloads launch different grids: the trace summary splits on that)
+    for (B, T, Hq, Hkv, ctx) in ATTENTION_WORKLOADS:
+        g = torch.Generator(device=dev)
+        g.manual_seed(77)
+        caches = []
+        for _ in range(2):
+            kv = torch.randn(2, B, Hkv, ctx, 128, device=dev, generator=g).to(torch.bfloat16)
+            caches.append((kv[0].contiguous(), kv[1].contiguous()))
+            del kv
+        q = torch.randn(B, T, Hq, 128, device=dev, generator=g).to(torch.bfloat16)
+        lengths = torch.full((B,), ctx, dtype=torch.int32, device=dev)
+        ws = w8.Workspace()
+        o = torch.empty_like(q)
+        t = graph_time([(lambda c=c: w8.verify_attention(q, *caches[c], lengths, out=o,
+                                                         workspace=ws)) for c in range(2)],
+                       replays=20) / 2
+        kvb = 2 * B * Hkv * ctx * 128 * 2
+        out.append({"B": B, "T": T, "Hq": Hq, "Hkv": Hkv, "positions": ctx,
+                    "us": round(t * 1e6, 2), "kv_GBs": round(kvb / t / 1e9, 1),
+                    "kv_frac_of_peak": round(kvb / t / 1e9 / HBM_PEAK_GBS, 4)})
+        del caches
+        torch.cuda.empty_cache()
     return out
 
 
