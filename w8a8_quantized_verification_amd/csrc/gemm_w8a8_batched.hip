@@ -50,6 +50,56 @@ struct BatchedArgs {
   int subkeys, key_stride;
 };
 
+// Epilogue of one wave's MB x TN accumulator tiles: rows (mb0+i)*16 + 4*grp
+// + r, columns (t0 + t)*16 + col.  y32 = (acc * x_scale[m]) * w_scale[n],
+// written as fp32 / bf16 / int32 as requested, and the fused argmax fold.
+template <int MB, int TN, bool kArgmax>
+__device__ __forceinline__ void batched_epilogue(const BatchedArgs& g, const v4i (&acc)[MB][TN],
+                                                 int mb0, int t0, int lane) {
+  const int col = lane & 15, grp = lane >> 4;
+#pragma unroll
+  for (int t = 0; t < TN; ++t) {
+    const int t16 = t0 + t;
+    const int n = t16 * 16 + col;
+    const bool n_ok = n < g.N;
+    const float wsn = n_ok ? g.ws[n] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = (mb0 + i) * 16 + 4 * grp + r;
+        float v = -INFINITY;
+        int idx = INT_MAX;
+        if (m < g.M && n_ok) {
+          const int32_t a = acc[i][t][r];
+          const float y = (static_cast<float>(a) * g.xs[m]) * wsn;
+          const size_t o = (size_t)m * (size_t)g.N + (size_t)n;
+          if (g.y_f32) g.y_f32[o] = y;
+          if (g.y_bf16) g.y_bf16[o] = f32_to_bf16_rne(y);
+          if (g.acc) g.acc[o] = a;
+          v = y;
+          idx = n;
+        }
+        if constexpr (kArgmax) {
+          // (max, lowest index) of row m over this tile's 16 columns, then one
+          // atomic fold into the row's sub-key for this tile
+#pragma unroll
+          for (int off = 1; off < 16; off <<= 1) {
+            const float ov = __shfl_xor(v, off, kWave);
+            const int oi = __shfl_xor(idx, off, kWave);
+            if (ov > v || (ov == v && oi < idx)) { v = ov; idx = oi; }
+          }
+          if (col == 0 && m < g.M && idx != INT_MAX) {
+            const size_t sub = (size_t)m * g.subkeys + (t16 % g.subkeys);
+            __hip_atomic_fetch_max(&g.keys[sub * g.key_stride], argmax_key(v, idx),
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+        }
+      }
+    }
+  }
+}
+
 template <int MB, int TN, int WR, int KW, int U, bool kTiled, bool kArgmax, bool kTiledA>
 __global__ __launch_bounds__(WR * KW * kWave) void gemm_w8a8_batched(BatchedArgs g) {
   // workgroup id -> (row tile, channel group), XCD-aware (see header)
@@ -186,48 +236,124 @@ __global__ __launch_bounds__(WR * KW * kWave) void gemm_w8a8_batched(BatchedArgs
         for (int t = 0; t < TN; ++t) acc[i][t] += red[j][wr][i * TN + t][lane];
   }
 
-  // epilogue: rows (mb0+i)*16 + 4*grp + r, columns (ng*TN + t)*16 + col
+  batched_epilogue<MB, TN, kArgmax>(g, acc, mb0, ng * TN, lane);
+}
+
+// The LDS-pipelined kernel (tiled activations and tiled weights).  A
+// workgroup of 2 x 2 waves computes 2*MB row blocks x 2*TN channel tiles;
+// wave (wr, wc) owns row blocks wr*MB .. +MB-1 and tiles wc*TN .. +TN-1 of
+// it, so each activation fragment feeds two waves and each weight fragment
+// two.  Both operands are 1 KiB per (16-row block or 16-channel tile, k
+// step) in lane order, so one direct-to-LDS load per wave instruction
+// (global_load_lds_dwordx4: lane l's 16 bytes land at l*16) copies a whole
+// fragment, and a lane's ds_read_b128 at l*16 gets its MFMA operand back.
+// P stages of LDS, one k step each: steps s+1 .. s+P-2 are in flight while
+// step s is multiplied.  Each wave issues a quarter of a step's fragments
+// and waits for its own with an explicit vmcnt; one barrier per step then
+// makes the step visible to all four waves and frees the stage of step s-1
+// for step s + P - 1.  Fragments past the last row block or channel tile
+// are fetched from block / tile 0 (in bounds) and their results dropped by
+// the epilogue; the steps past the end are fetched again from the last one,
+// and the step's fragment count is padded to a multiple of four (so every
+// wave issues the same number of loads per step).
+constexpr int kLdsWaves = 4;
+
+__device__ __forceinline__ void lds_dma16(const void* src, void* lds_dst) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
+}
+
+// keeps the compiler from moving LDS reads across the explicit waits and
+// barriers (the direct-to-LDS loads are not ordinary stores to it)
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
+// s_waitcnt with vmcnt = n and the other counters at their maxima (gfx9
+// encoding: vmcnt[3:0] in bits 3:0 and vmcnt[5:4] in bits 15:14)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+template <int MB, int TN, int P, bool kArgmax>
+__global__ __launch_bounds__(kLdsWaves * kWave) void gemm_w8a8_lds(BatchedArgs g) {
+  constexpr int FA = 2 * MB, FB = 2 * TN, F = FA + FB;   // fragments per k step
+  // each wave issues FW loads per k step; the F..4*FW-1 padding loads fetch
+  // fragment 0 again into LDS nobody reads, so that all waves wait alike
+  constexpr int FW = (F + kLdsWaves - 1) / kLdsWaves;
+  static_assert(P >= 3, "one stage read, one refilled, at least one in flight");
+  __shared__ __attribute__((aligned(1024))) int8_t stage[P][FW * kLdsWaves * 1024];
+
+  // workgroup id -> (row tile, channel group), XCD-aware as above
+  const int b = blockIdx.x;
+  const int xcd = b % kXcds;
+  const int slot = b / kXcds;
+  const int mt = slot % g.mtiles;
+  const int ng = (slot / g.mtiles) * kXcds + xcd;
+  if (ng >= g.ngroups) return;
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int wr = wave & 1, wc = wave >> 1;
+  const int steps = g.steps;             // >= 1 (the launcher routes K = 0 elsewhere)
+  const int mblocks = (g.M + 15) / 16;
+
+  // this wave's fragment loads of every k step: fragment f = wave + 4 j
+  const int8_t* src[FW];
 #pragma unroll
-  for (int t = 0; t < TN; ++t) {
-    const int t16 = ng * TN + t;
-    const int n = t16 * 16 + col;
-    const bool n_ok = n < g.N;
-    const float wsn = n_ok ? g.ws[n] : 0.0f;
-#pragma unroll
-    for (int i = 0; i < MB; ++i) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = (mb0 + i) * 16 + 4 * grp + r;
-        float v = -INFINITY;
-        int idx = INT_MAX;
-        if (m < g.M && n_ok) {
-          const int32_t a = acc[i][t][r];
-          const float y = (static_cast<float>(a) * g.xs[m]) * wsn;
-          const size_t o = (size_t)m * (size_t)g.N + (size_t)n;
-          if (g.y_f32) g.y_f32[o] = y;
-          if (g.y_bf16) g.y_bf16[o] = f32_to_bf16_rne(y);
-          if (g.acc) g.acc[o] = a;
-          v = y;
-          idx = n;
-        }
-        if constexpr (kArgmax) {
-          // (max, lowest index) of row m over this tile's 16 columns, then one
-          // atomic fold into the row's sub-key for this tile
-#pragma unroll
-          for (int off = 1; off < 16; off <<= 1) {
-            const float ov = __shfl_xor(v, off, kWave);
-            const int oi = __shfl_xor(idx, off, kWave);
-            if (ov > v || (ov == v && oi < idx)) { v = ov; idx = oi; }
-          }
-          if (col == 0 && m < g.M && idx != INT_MAX) {
-            const size_t sub = (size_t)m * g.subkeys + (t16 % g.subkeys);
-            __hip_atomic_fetch_max(&g.keys[sub * g.key_stride], argmax_key(v, idx),
-                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          }
-        }
-      }
+  for (int j = 0; j < FW; ++j) {
+    const int f = wave + kLdsWaves * j;
+    if (f >= F) {
+      src[j] = g.xq + (lane << 4);
+    } else if (f < FA) {
+      const int rb = mt * FA + f;
+      src[j] = g.xq + ((size_t)(rb < mblocks ? rb : 0) * (size_t)steps << 10) + (lane << 4);
+    } else {
+      const int t16 = ng * FB + (f - FA);
+      src[j] = g.wq + ((size_t)(t16 < g.tiles16 ? t16 : 0) * (size_t)steps << 10) + (lane << 4);
     }
   }
+  // stage p <- k step s (clamped to the last one)
+  auto issue = [&](int p, int s) {
+    s = min(s, steps - 1);
+#pragma unroll
+    for (int j = 0; j < FW; ++j)
+      lds_dma16(src[j] + ((size_t)s << 10), &stage[p][(wave + kLdsWaves * j) * 1024]);
+  };
+
+  v4i acc[MB][TN];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int t = 0; t < TN; ++t) acc[i][t] = v4i{0, 0, 0, 0};
+
+  // steps 0 .. P-2 in flight; at step s, after the barrier (every wave is
+  // past step s-1's reads), step s-1's stage is refilled with step s + P - 1
+#pragma unroll
+  for (int u = 0; u < P - 1; ++u) issue(u, u);
+  for (int s = 0; s < steps; ++s) {
+    wait_vmcnt<(P - 2) * FW>();     // this wave's loads of step s are in LDS
+    __builtin_amdgcn_s_barrier();   // ... and every wave's; step s-1's stage is free
+    compiler_fence();
+    issue((s + P - 1) % P, s + P - 1);
+    const int8_t* st = stage[s % P];
+    v4i a[MB], bb[TN];
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+      a[i] = *reinterpret_cast<const v4i*>(st + (wr * MB + i) * 1024 + (lane << 4));
+#pragma unroll
+    for (int t = 0; t < TN; ++t)
+      bb[t] = *reinterpret_cast<const v4i*>(st + (FA + wc * TN + t) * 1024 + (lane << 4));
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int t = 0; t < TN; ++t)
+        acc[i][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i], bb[t], acc[i][t], 0, 0, 0);
+    compiler_fence();
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this step's LDS reads are done
+  }
+  wait_vmcnt<0>();   // the redundant tail loads land before the workgroup's LDS is released
+
+  batched_epilogue<MB, TN, kArgmax>(g, acc, mt * FA + wr * MB, ng * FB + wc * TN, lane);
 }
 
 // Launch shapes, measured on MI355X at 288 rows over the Qwen3-8B linears
@@ -241,10 +367,39 @@ __global__ __launch_bounds__(WR * KW * kWave) void gemm_w8a8_batched(BatchedArgs
 struct BatchedShape {
   int mb, tn, wr, kw, u;
 };
+
+template <int MB, int TN, int P>
+static hipError_t launch_lds(BatchedArgs g, bool argmax, hipStream_t stream) {
+  g.ngroups = (g.tiles16 + 2 * TN - 1) / (2 * TN);
+  g.mtiles = (g.M + 32 * MB - 1) / (32 * MB);
+  const int64_t ng_padded = ((int64_t)g.ngroups + kXcds - 1) / kXcds * kXcds;
+  const dim3 grid((unsigned)(ng_padded * g.mtiles)), block(kLdsWaves * kWave);
+  if (argmax) hipLaunchKernelGGL((gemm_w8a8_lds<MB, TN, P, true>), grid, block, 0, stream, g);
+  else hipLaunchKernelGGL((gemm_w8a8_lds<MB, TN, P, false>), grid, block, 0, stream, g);
+  return hipGetLastError();
+}
 constexpr BatchedShape kWide{3, 4, 1, 4, 4};
 constexpr BatchedShape kNarrow{3, 2, 1, 8, 2};
 constexpr BatchedShape kTiledAWide{3, 2, 1, 4, 4};
 constexpr int64_t kMinWorkgroups = 256;
+
+// The LDS-pipelined kernel (tiled activations and weights): 96 rows x 64
+// channels per workgroup, 4 stages.  It wins once the grid is wide enough
+// to keep ~2 workgroups per CU busy (288 rows: gate/up 4096 -> 12288 34.7
+// vs 41.5 us, the fused 24576-wide gate_up 61.3 vs 74.8 us); on narrower
+// grids each workgroup's chain of 64+ k steps is too long and the
+// register-fragment kernel above is faster (q 18.9 vs 22.7 us).
+struct LdsShape {
+  int mb, tn, p;
+};
+constexpr LdsShape kLdsShape{3, 2, 4};
+constexpr int64_t kLdsMinWorkgroups = 512;
+
+static int64_t lds_workgroups(int64_t M, int64_t N) {
+  const int64_t ngroups = ((N + 15) / 16 + 2 * kLdsShape.tn - 1) / (2 * kLdsShape.tn);
+  const int64_t mtiles = (M + 32 * kLdsShape.mb - 1) / (32 * kLdsShape.mb);
+  return ngroups * mtiles;
+}
 
 static int64_t batched_workgroups(const BatchedShape& c, int64_t M, int64_t N) {
   const int64_t ngroups = ((N + 15) / 16 + c.tn - 1) / c.tn;
@@ -291,6 +446,8 @@ hipError_t w8a8_launch_gemm_batched(const int8_t* xq, const float* x_scale, cons
   g.keys = reinterpret_cast<unsigned long long*>(keys);
   g.subkeys = subkeys; g.key_stride = key_stride;
   const bool argmax = keys != nullptr;
+  if (a_tiled && tiled && g.steps > 0 && lds_workgroups(M, N) >= kLdsMinWorkgroups)
+    return launch_lds<kLdsShape.mb, kLdsShape.tn, kLdsShape.p>(g, argmax, stream);
   if (a_tiled) {
     if (batched_workgroups(kTiledAWide, M, N) >= kMinWorkgroups)
       return launch_batched<kTiledAWide.mb, kTiledAWide.tn, kTiledAWide.wr, kTiledAWide.kw,
