@@ -255,7 +255,11 @@ __global__ __launch_bounds__(WR * KW * kWave) void gemm_w8a8_batched(BatchedArgs
 // are fetched from block / tile 0 (in bounds) and their results dropped by
 // the epilogue; the steps past the end are fetched again from the last one,
 // and the step's fragment count is padded to a multiple of four (so every
-// wave issues the same number of loads per step).
+// wave issues the same number of loads per step).  With KH > 1 the
+// workgroup holds KH such groups of four waves, each with its own stages
+// over one of KH equal slices of the k steps; their int32 tiles meet in
+// LDS at the end (exact in any order) and the first group applies the
+// epilogue.
 constexpr int kLdsWaves = 4;
 
 __device__ __forceinline__ void lds_dma16(const void* src, void* lds_dst) {
@@ -274,14 +278,16 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
-template <int MB, int TN, int P, bool kArgmax>
-__global__ __launch_bounds__(kLdsWaves * kWave) void gemm_w8a8_lds(BatchedArgs g) {
+template <int MB, int TN, int P, int KH, bool kArgmax>
+__global__ __launch_bounds__(KH * kLdsWaves * kWave) void gemm_w8a8_lds(BatchedArgs g) {
   constexpr int FA = 2 * MB, FB = 2 * TN, F = FA + FB;   // fragments per k step
   // each wave issues FW loads per k step; the F..4*FW-1 padding loads fetch
   // fragment 0 again into LDS nobody reads, so that all waves wait alike
   constexpr int FW = (F + kLdsWaves - 1) / kLdsWaves;
+  constexpr int STAGE = FW * kLdsWaves * 1024;
   static_assert(P >= 3, "one stage read, one refilled, at least one in flight");
-  __shared__ __attribute__((aligned(1024))) int8_t stage[P][FW * kLdsWaves * 1024];
+  static_assert((KH - 1) * kLdsWaves * MB * TN * 1024 <= KH * P * STAGE, "k-half tiles fit the stages");
+  __shared__ __attribute__((aligned(1024))) int8_t stage[KH][P][STAGE];
 
   // workgroup id -> (row tile, channel group), XCD-aware as above
   const int b = blockIdx.x;
@@ -292,10 +298,15 @@ __global__ __launch_bounds__(kLdsWaves * kWave) void gemm_w8a8_lds(BatchedArgs g
   if (ng >= g.ngroups) return;
 
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+  const int wave = (threadIdx.x / kWave) % kLdsWaves;   // position in its k half
+  const int kh = threadIdx.x / (kWave * kLdsWaves);     // k half
   const int wr = wave & 1, wc = wave >> 1;
   const int steps = g.steps;             // >= 1 (the launcher routes K = 0 elsewhere)
   const int mblocks = (g.M + 15) / 16;
+  // k slice kh takes steps [s0, s0 + nmax) (the launcher keeps steps % KH
+  // == 0, so every slice runs the same iterations and the barriers match)
+  const int nmax = steps / KH;
+  const int s0 = kh * nmax;
 
   // this wave's fragment loads of every k step: fragment f = wave + 4 j
   const int8_t* src[FW];
@@ -312,12 +323,12 @@ __global__ __launch_bounds__(kLdsWaves * kWave) void gemm_w8a8_lds(BatchedArgs g
       src[j] = g.wq + ((size_t)(t16 < g.tiles16 ? t16 : 0) * (size_t)steps << 10) + (lane << 4);
     }
   }
-  // stage p <- k step s (clamped to the last one)
+  // stage p of this slice <- its k step s (clamped to the slice's last)
   auto issue = [&](int p, int s) {
-    s = min(s, steps - 1);
+    s = s0 + min(s, nmax - 1);
 #pragma unroll
     for (int j = 0; j < FW; ++j)
-      lds_dma16(src[j] + ((size_t)s << 10), &stage[p][(wave + kLdsWaves * j) * 1024]);
+      lds_dma16(src[j] + ((size_t)s << 10), &stage[kh][p][(wave + kLdsWaves * j) * 1024]);
   };
 
   v4i acc[MB][TN];
@@ -330,12 +341,12 @@ __global__ __launch_bounds__(kLdsWaves * kWave) void gemm_w8a8_lds(BatchedArgs g
   // past step s-1's reads), step s-1's stage is refilled with step s + P - 1
 #pragma unroll
   for (int u = 0; u < P - 1; ++u) issue(u, u);
-  for (int s = 0; s < steps; ++s) {
+  for (int s = 0; s < nmax; ++s) {
     wait_vmcnt<(P - 2) * FW>();     // this wave's loads of step s are in LDS
     __builtin_amdgcn_s_barrier();   // ... and every wave's; step s-1's stage is free
     compiler_fence();
     issue((s + P - 1) % P, s + P - 1);
-    const int8_t* st = stage[s % P];
+    const int8_t* st = stage[kh][s % P];
     v4i a[MB], bb[TN];
 #pragma unroll
     for (int i = 0; i < MB; ++i)
@@ -351,7 +362,31 @@ __global__ __launch_bounds__(kLdsWaves * kWave) void gemm_w8a8_lds(BatchedArgs g
     compiler_fence();
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this step's LDS reads are done
   }
-  wait_vmcnt<0>();   // the redundant tail loads land before the workgroup's LDS is released
+  wait_vmcnt<0>();   // the redundant tail loads land before the LDS is reused
+
+  if constexpr (KH > 1) {
+    // the k halves' int32 tiles meet in LDS (exact in any order): halves
+    // 1.. store theirs over their stages, half 0 adds them
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+    v4i* red = reinterpret_cast<v4i*>(&stage[0][0][0]);
+    if (kh > 0) {
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int t = 0; t < TN; ++t)
+          red[((((kh - 1) * kLdsWaves + wave) * MB + i) * TN + t) * kWave + lane] = acc[i][t];
+    }
+    __syncthreads();
+    if (kh > 0) return;
+#pragma unroll
+    for (int h = 1; h < KH; ++h)
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int t = 0; t < TN; ++t)
+          acc[i][t] += red[((((h - 1) * kLdsWaves + wave) * MB + i) * TN + t) * kWave + lane];
+  }
 
   batched_epilogue<MB, TN, kArgmax>(g, acc, mt * FA + wr * MB, ng * FB + wc * TN, lane);
 }
@@ -368,14 +403,14 @@ struct BatchedShape {
   int mb, tn, wr, kw, u;
 };
 
-template <int MB, int TN, int P>
+template <int MB, int TN, int P, int KH>
 static hipError_t launch_lds(BatchedArgs g, bool argmax, hipStream_t stream) {
   g.ngroups = (g.tiles16 + 2 * TN - 1) / (2 * TN);
   g.mtiles = (g.M + 32 * MB - 1) / (32 * MB);
   const int64_t ng_padded = ((int64_t)g.ngroups + kXcds - 1) / kXcds * kXcds;
-  const dim3 grid((unsigned)(ng_padded * g.mtiles)), block(kLdsWaves * kWave);
-  if (argmax) hipLaunchKernelGGL((gemm_w8a8_lds<MB, TN, P, true>), grid, block, 0, stream, g);
-  else hipLaunchKernelGGL((gemm_w8a8_lds<MB, TN, P, false>), grid, block, 0, stream, g);
+  const dim3 grid((unsigned)(ng_padded * g.mtiles)), block(KH * kLdsWaves * kWave);
+  if (argmax) hipLaunchKernelGGL((gemm_w8a8_lds<MB, TN, P, KH, true>), grid, block, 0, stream, g);
+  else hipLaunchKernelGGL((gemm_w8a8_lds<MB, TN, P, KH, false>), grid, block, 0, stream, g);
   return hipGetLastError();
 }
 constexpr BatchedShape kWide{3, 4, 1, 4, 4};
@@ -384,16 +419,23 @@ constexpr BatchedShape kTiledAWide{3, 2, 1, 4, 4};
 constexpr int64_t kMinWorkgroups = 256;
 
 // The LDS-pipelined kernel (tiled activations and weights): 96 rows x 64
-// channels per workgroup, 4 stages.  It wins once the grid is wide enough
-// to keep ~2 workgroups per CU busy (288 rows: gate/up 4096 -> 12288 34.7
-// vs 41.5 us, the fused 24576-wide gate_up 61.3 vs 74.8 us); on narrower
-// grids each workgroup's chain of 64+ k steps is too long and the
-// register-fragment kernel above is faster (q 18.9 vs 22.7 us).
+// channels per workgroup.  Measured at 288 rows:
+//  * 4 stages, whole K per workgroup, once the grid is wide enough to keep
+//    ~2 workgroups per CU busy: gate/up 4096 -> 12288 34.3 vs 41.5 us with
+//    the register-fragment kernel, the fused 24576-wide gate_up 59.0 vs
+//    74.8 us;
+//  * K cut into 4 slices of 4 waves each (3 stages each, tiles summed in
+//    LDS) on narrower grids, where one workgroup's chain of k steps would
+//    be too long: down 12288 -> 4096 34.7 vs 41.2 us, q 18.3 vs 19.0 us;
+//  * below ~128 workgroups (k/v, 1024 channels) the register-fragment
+//    kernel stays faster (11.2 vs 16.4 us).
 struct LdsShape {
   int mb, tn, p;
 };
 constexpr LdsShape kLdsShape{3, 2, 4};
 constexpr int64_t kLdsMinWorkgroups = 512;
+constexpr int kLdsSplit = 4, kLdsSplitStages = 3;
+constexpr int64_t kLdsSplitMinWorkgroups = 128;
 
 static int64_t lds_workgroups(int64_t M, int64_t N) {
   const int64_t ngroups = ((N + 15) / 16 + 2 * kLdsShape.tn - 1) / (2 * kLdsShape.tn);
@@ -446,8 +488,13 @@ hipError_t w8a8_launch_gemm_batched(const int8_t* xq, const float* x_scale, cons
   g.keys = reinterpret_cast<unsigned long long*>(keys);
   g.subkeys = subkeys; g.key_stride = key_stride;
   const bool argmax = keys != nullptr;
-  if (a_tiled && tiled && g.steps > 0 && lds_workgroups(M, N) >= kLdsMinWorkgroups)
-    return launch_lds<kLdsShape.mb, kLdsShape.tn, kLdsShape.p>(g, argmax, stream);
+  if (a_tiled && tiled && g.steps > 0) {
+    const int64_t lwg = lds_workgroups(M, N);
+    if (lwg >= kLdsMinWorkgroups)
+      return launch_lds<kLdsShape.mb, kLdsShape.tn, kLdsShape.p, 1>(g, argmax, stream);
+    if (lwg >= kLdsSplitMinWorkgroups && g.steps % kLdsSplit == 0)
+      return launch_lds<kLdsShape.mb, kLdsShape.tn, kLdsSplitStages, kLdsSplit>(g, argmax, stream);
+  }
   if (a_tiled) {
     if (batched_workgroups(kTiledAWide, M, N) >= kMinWorkgroups)
       return launch_batched<kTiledAWide.mb, kTiledAWide.tn, kTiledAWide.wr, kTiledAWide.kw,
