@@ -306,7 +306,11 @@ def ingest_pmc_batched(dirs, command):
 
     import synth
     M = 288
-    variants = (("row_major_act", ", false>("), ("tiled_act", ", true>("))
+    # row-major activations run the register-fragment kernel; tiled ones that
+    # kernel's tiled form or the LDS-pipelined kernel, by shape
+    variants = (("row_major_act", lambda k: "gemm_w8a8_batched" in k and ", false>(" in k),
+                ("tiled_act", lambda k: "gemm_w8a8_lds" in k or
+                 ("gemm_w8a8_batched" in k and ", true>(" in k)))
     per = {(n, v): {} for n in BATCHED_SHAPES for v, _ in variants}
     kname = {}
     for d in dirs:
@@ -318,7 +322,8 @@ def ingest_pmc_batched(dirs, command):
                 copy = [float(r["Counter_Value"]) for r in rr if "copy" in r["Kernel_Name"].lower()]
                 scale = (1 << 30) / (max(copy) * 1024.0) * 1024.0   # KiB -> calibrated bytes
             # the probe: per shape, 4 row-major-activation launches then 4 tiled ones
-            gem = sorted([r for r in rr if "gemm_w8a8_batched" in r["Kernel_Name"]],
+            gem = sorted([r for r in rr if "gemm_w8a8_batched" in r["Kernel_Name"]
+                          or "gemm_w8a8_lds" in r["Kernel_Name"]],
                          key=lambda r: int(r["Dispatch_Id"]))
             if len(gem) != 8 * len(BATCHED_SHAPES):
                 raise SystemExit(f"{d}: {cname}: expected {8 * len(BATCHED_SHAPES)} batched "
@@ -326,9 +331,9 @@ def ingest_pmc_batched(dirs, command):
             for i, n in enumerate(BATCHED_SHAPES):
                 for j, (v, tag) in enumerate(variants):
                     sel = gem[8 * i + 4 * j:8 * i + 4 * j + 4]
-                    if not all(tag in r["Kernel_Name"] for r in sel):
+                    if not all(tag(r["Kernel_Name"]) for r in sel):
                         raise SystemExit(f"{d}: unexpected kernel order for {n} {v}")
-                    kname[v] = sel[0]["Kernel_Name"]
+                    kname[(n, v)] = sel[0]["Kernel_Name"].split("(w8a8")[0].replace("void ", "")
                     vals = [float(r["Counter_Value"]) * scale for r in sel]
                     durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e9
                             for r in sel]
@@ -337,7 +342,7 @@ def ingest_pmc_batched(dirs, command):
     lines = ["# Counters of the batched W8A8 GEMM at M=288 (Qwen3-8B linears, tiled int8 weights),",
              "# with row-major activations (w8a8_linear_tiled) and tiled activations",
              "# (w8a8_linear_tiled_act)",
-             *[f"# kernel ({v}): {k[:120]}" for v, k in kname.items()],
+             *[f"# kernel ({n}, {v}): {k[:110]}" for (n, v), k in kname.items()],
              f"# commands: {command}",
              "# per shape: medians over 4 dispatches.  FETCH_SIZE/WRITE_SIZE in bytes, calibrated",
              "# by the probe's 1 GiB copy.  MfmaUtil = 100*sum(SQ_VALU_MFMA_BUSY_CYCLES) /",
