@@ -158,18 +158,28 @@ __global__ __launch_bounds__(WAVES * kWave) void gemm_w8a8_skinny(GemmArgs g) {
       for (int t = 0; t < TN; ++t)
         acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[u], b[u][t], acc[t], 0, 0, 0);
   }
-  for (; j < J; ++j) {
-    const int s = sw + kStride * j;
-    const int k = s * 64;
-    const bool kin = k + grp * 16 < K;
-    const v4i a = (a_ok && kin) ? load16(a_ptr + k) : zero;
+  if (j < J) {
+    // the last J - j < U steps, requested together (one round trip); the
+    // slots past J load nothing and multiply zeros, which add nothing
+    v4i a[U], b[U][TN];
 #pragma unroll
-    for (int t = 0; t < TN; ++t) {
-      v4i b;
-      if constexpr (kTiled) b = (TN == 1 || b_ok[t]) ? load16_stream(b_ptr[t] + b_off(s)) : zero;
-      else b = (b_ok[t] && kin) ? load16(b_ptr[t] + b_off(s)) : zero;
-      acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[t], 0, 0, 0);
+    for (int u = 0; u < U; ++u) {
+      const bool live = j + u < J;
+      const int s = sw + kStride * (live ? j + u : j);
+      const int k = s * 64;
+      const bool kin = k + grp * 16 < K;
+      a[u] = (live && a_ok && kin) ? load16(a_ptr + k) : zero;
+#pragma unroll
+      for (int t = 0; t < TN; ++t) {
+        if constexpr (kTiled) b[u][t] = (live && (TN == 1 || b_ok[t])) ? load16_stream(b_ptr[t] + b_off(s)) : zero;
+        else b[u][t] = (live && b_ok[t] && kin) ? load16(b_ptr[t] + b_off(s)) : zero;
+      }
     }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int t = 0; t < TN; ++t)
+        acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[u], b[u][t], acc[t], 0, 0, 0);
   }
 
   if constexpr (WAVES > 1) {
@@ -283,9 +293,13 @@ struct SkinnyPlan {
   int tiles, split, mblocks, waves, tn;
 };
 
-constexpr int kUnroll = 8;
+#ifndef W8A8_SKINNY_UNROLL
+#define W8A8_SKINNY_UNROLL 8
+#endif
+constexpr int kUnroll = W8A8_SKINNY_UNROLL;
 constexpr int64_t kSkinnyMaxRows = 16;  // more token rows go to the batched kernel
-constexpr int kSplitBelowTiles = 32;  // split k across workgroups only below this
+constexpr int kSplitBelowTiles = 32;  // split k across workgroups below this ...
+constexpr int64_t kLongChain = 32;    // ... or above this many k steps per wave
 
 // Tuning overrides (results do not depend on them: int32 sums are exact in
 // any order): W8A8_SPLITK forces the cross-workgroup split, W8A8_WAVES the
@@ -296,10 +310,12 @@ static int env_int(const char* name) {
 }
 
 // Measured on MI355X at M=5 over the Qwen3-8B shapes (N = 1024..12288, K =
-// 4096/12288) and the LM head: 4 waves per workgroup once there are >= 512
-// column tiles, 8 below; splitting k across workgroups never paid (its
-// atomic handoff costs more than the extra parallelism), so it is kept for
-// outputs too narrow to occupy more than a few dozen CUs.
+// 4096/12288), at M=8 over the Qwen3-32B shapes (K up to 25600) and on the
+// LM head: 4 waves per workgroup once there are >= 512 column tiles, 8
+// below.  Splitting k across workgroups (its atomic handoff) pays only for
+// outputs too narrow to occupy more than a few dozen CUs and for long
+// reductions over few tiles (32B down, 5120 x 25600: 400 steps, 50 per
+// wave: 31.5-32.4 us with 4 slices against 37.2 us without).
 static SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, bool tiled, bool no_split = false) {
   SkinnyPlan p;
   const int64_t tiles16 = (N + 15) / 16;
@@ -316,6 +332,11 @@ static SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, bool tiled, bool 
   p.split = 1;
   while (!no_split && wgs * p.split < kSplitBelowTiles &&
          steps / ((int64_t)p.split * 2 * p.waves) >= 2)
+    p.split *= 2;
+  // long reductions over few tiles: more than kLongChain k steps per wave is
+  // a chain of dependent round trips that the grid cannot hide, so K is cut
+  // across workgroups until a wave walks at most about half of that
+  while (!no_split && p.split < 8 && steps / ((int64_t)p.split * p.waves) > kLongChain)
     p.split *= 2;
   const int fw = env_int("W8A8_WAVES");
   if (fw == 4 || fw == 8 || fw == 16) p.waves = fw;
