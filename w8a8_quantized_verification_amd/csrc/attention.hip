@@ -8,17 +8,20 @@
 // heads (query head h reads kv head h / (Hq / Hkv)); head dimension 128;
 // fp32 softmax, bf16 output.
 //
-// Split over the keys (flash-decoding): one wave per (split, kv head, b)
-// streams its range of cache positions in blocks of 16, with every query
-// row that reads its kv head (T x Hq/Hkv rows, <= 64) held in registers, an
-// online softmax per row, and the next block's K and V loaded while the
-// current one is computed.  Both products run on the bf16 MFMA straight
-// from registers (no LDS):
-//   S^T = K Q^T  (v_mfma_f32_16x16x32_bf16; A = 16 keys, B = 16 query rows),
-//   O^T += V^T P^T (v_mfma_f32_16x16x16_bf16; A = 16 dims x 16 keys,
-//                   B = P^T whose lane layout is exactly S^T's).
-// A second kernel merges the splits of each row.  Bound by reading the
-// cache: 2 * 128 * 2 bytes per position and kv head.
+// Split over the keys (flash-decoding): a workgroup of four waves per
+// (split, kv head, b); each wave streams its quarter of the split's cache
+// positions in blocks of 16, with every query row that reads its kv head
+// (T x Hq/Hkv rows, <= 64) held in registers, an online softmax per row,
+// and its blocks requested in bursts of 2-6 before they are multiplied.
+// Both products run on the bf16 MFMA straight from registers (no LDS
+// staging), blocks taken in pairs:
+//   S^T = K Q^T  (v_mfma_f32_16x16x32_bf16 per block; A = 16 keys,
+//                 B = 16 query rows),
+//   O^T += V^T P^T (v_mfma_f32_16x16x32_bf16 over the pair's 32 positions;
+//                   A = 16 dims, B = P^T in exactly the lanes S^T left it).
+// The four waves' states merge in LDS into one partial result per
+// workgroup; a second kernel merges the splits of each row.  Bound by
+// reading the cache: 2 * 128 * 2 bytes per position and kv head.
 //
 // Cache layouts.  K: [B][Hkv][Lmax][128], one row per position.  The MFMA
 // sums over the 128 dims in any order, so lane (c, g) = (lane % 16, lane /
