@@ -403,14 +403,15 @@ struct BatchedShape {
   int mb, tn, wr, kw, u;
 };
 
+// (no fused argmax: the LM-head argmax path passes row-major activations,
+// which take the register-fragment kernel)
 template <int MB, int TN, int P, int KH>
-static hipError_t launch_lds(BatchedArgs g, bool argmax, hipStream_t stream) {
+static hipError_t launch_lds(BatchedArgs g, hipStream_t stream) {
   g.ngroups = (g.tiles16 + 2 * TN - 1) / (2 * TN);
   g.mtiles = (g.M + 32 * MB - 1) / (32 * MB);
   const int64_t ng_padded = ((int64_t)g.ngroups + kXcds - 1) / kXcds * kXcds;
   const dim3 grid((unsigned)(ng_padded * g.mtiles)), block(KH * kLdsWaves * kWave);
-  if (argmax) hipLaunchKernelGGL((gemm_w8a8_lds<MB, TN, P, KH, true>), grid, block, 0, stream, g);
-  else hipLaunchKernelGGL((gemm_w8a8_lds<MB, TN, P, KH, false>), grid, block, 0, stream, g);
+  hipLaunchKernelGGL((gemm_w8a8_lds<MB, TN, P, KH, false>), grid, block, 0, stream, g);
   return hipGetLastError();
 }
 constexpr BatchedShape kWide{3, 4, 1, 4, 4};
@@ -488,12 +489,12 @@ hipError_t w8a8_launch_gemm_batched(const int8_t* xq, const float* x_scale, cons
   g.keys = reinterpret_cast<unsigned long long*>(keys);
   g.subkeys = subkeys; g.key_stride = key_stride;
   const bool argmax = keys != nullptr;
-  if (a_tiled && tiled && g.steps > 0) {
+  if (a_tiled && tiled && !argmax && g.steps > 0) {
     const int64_t lwg = lds_workgroups(M, N);
     if (lwg >= kLdsMinWorkgroups)
-      return launch_lds<kLdsShape.mb, kLdsShape.tn, kLdsShape.p, 1>(g, argmax, stream);
+      return launch_lds<kLdsShape.mb, kLdsShape.tn, kLdsShape.p, 1>(g, stream);
     if (lwg >= kLdsSplitMinWorkgroups && g.steps % kLdsSplit == 0)
-      return launch_lds<kLdsShape.mb, kLdsShape.tn, kLdsSplitStages, kLdsSplit>(g, argmax, stream);
+      return launch_lds<kLdsShape.mb, kLdsShape.tn, kLdsSplitStages, kLdsSplit>(g, stream);
   }
   if (a_tiled) {
     if (batched_workgroups(kTiledAWide, M, N) >= kMinWorkgroups)
