@@ -501,6 +501,45 @@ def test_lm_head_verify(B, G, V, K):
         np.testing.assert_array_equal(host(n), nt_r)
 
 
+@pytest.mark.parametrize("B,G,V,K", [(1, 4, 151936, 4096), (2, 7, 5000, 256), (16, 0, 4099, 128),
+                                     (1, 0, 64, 64)])
+def test_lm_head_verify_repeats_leave_workspace_zeroed(B, G, V, K):
+    """Three calls in a row on one workspace (different drafts and hidden
+    states) each match the two-phase path and the oracle, and leave the
+    workspace (the argmax keys) zero-filled for the next call."""
+    announce(f"lm_head_verify repeats B={B} G={G} V={V} K={K}")
+    R = B * (G + 1)
+    w = synth.weights_f32(710, V, K)
+    wq_r, ws_r = oracle.quantize_weight(w)
+    wt, ws = w8.quantize_weight(dev(w), tiled=True)
+    wsp = w8.Workspace()
+    for call in range(3):
+        bits = synth.activations_bf16(711 + call, R, K)
+        xq_r, xs_r = oracle.quantize_act(bits)
+        _, y32_r, _ = oracle.w8a8_linear(xq_r, xs_r, wq_r, ws_r)
+        draft = synth.draft_ids(712 + call, B, G, V)
+        am0 = oracle.argmax_rows(y32_r).reshape(B, G + 1)
+        for b in range(B):
+            p = (b + call) % (G + 1)
+            draft[b, :p] = am0[b, :p]
+        am_r, al_r, nt_r = oracle.verify_accept(y32_r, draft)
+        xq, xs = w8.quantize_act(dev_bf16(bits))
+        d = dev(draft)
+        _, am, al, nt = w8.lm_head_verify(xq, xs, wt, ws, d, workspace=wsp)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(am), am_r)
+        np.testing.assert_array_equal(host(al), al_r)
+        np.testing.assert_array_equal(host(nt), nt_r)
+        buf = wsp.get(1, xq.device, use="zeroed")
+        assert not bool(buf.any()), "workspace not left zero-filled"
+        w8.lm_head_argmax(xq, xs, wt, ws, workspace=wsp)                 # the two phases
+        am2, al2, nt2 = w8.accept_from_keys(d, workspace=wsp)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(am2), am_r)
+        np.testing.assert_array_equal(host(al2), al_r)
+        np.testing.assert_array_equal(host(nt2), nt_r)
+
+
 def test_lm_head_verify_ties_across_workgroups():
     """Equal maxima in columns owned by different workgroups (and inside one
     16-column tile): the lowest index wins."""
