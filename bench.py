@@ -716,6 +716,7 @@ def extra_measurements(dev, copies, x_dev, xq, xsc, wsp):
     res["qwen3_8b_layer_linears_m5"] = layer_measurement(dev, wsp, M, synth.W_LAYER_M5)
     res["qwen3_8b_layer_linears_m5_fused"] = fused_layer_measurement(dev, wsp, M)
     res["qwen3_8b_layer_linears_m288"] = layer_measurement(dev, wsp, 288, synth.W_BATCHED)
+    res["library_int8_gemm_m288"] = library_int8_gemm(dev)
 
     K, V = 4096, synth.QWEN3_VOCAB
     lg = torch.empty(M, V, dtype=torch.float32, device=dev)
@@ -976,6 +977,33 @@ def oracle_timings():
                                  "step_ms_extrapolated_x64": round((64 * layer_s + head_s) * 1e3, 1),
                                  "verified_tokens_per_s_extrapolated":
                                      round(8 / (64 * layer_s + head_s), 3)}
+    return out
+
+
+def library_int8_gemm(dev):
+    """Context for the 288-row linears: the vendor int8 GEMM behind
+    torch._int_mm (int8 x int8 -> int32, no scales, no epilogue) at the same
+    shapes, weights rotated past the Infinity Cache as for ours.  Not part of
+    the verification path."""
+    import torch
+    out = {}
+    for name, M, N, K in (("q", 288, 4096, 4096), ("gate", 288, 12288, 4096),
+                          ("down", 288, 4096, 12288), ("gate_up", 288, 24576, 4096)):
+        g = torch.Generator(device=dev)
+        g.manual_seed(11)
+        a = torch.randint(-127, 128, (M, K), dtype=torch.int8, device=dev, generator=g)
+        ncp = max(2, int(600e6 // (N * K)) + 1)
+        ws = [torch.randint(-127, 128, (N, K), dtype=torch.int8, device=dev, generator=g)
+              for _ in range(ncp)]
+        try:
+            t = graph_time([(lambda c=c: torch._int_mm(a, ws[c].t())) for c in range(ncp)],
+                           replays=10) / ncp
+            out[name] = {"us": round(t * 1e6, 2), "TOPS": round(2 * M * N * K / t / 1e12, 1)}
+        except Exception as e:   # the op is missing or unsupported on this build
+            out[name] = {"error": str(e)[:160]}
+        del ws
+        torch.cuda.empty_cache()
+    out["what"] = "torch._int_mm (vendor int8 GEMM, int32 out, no dequant), HIP graph"
     return out
 
 
