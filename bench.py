@@ -716,7 +716,7 @@ def extra_measurements(dev, copies, x_dev, xq, xsc, wsp):
     res["qwen3_8b_layer_linears_m5"] = layer_measurement(dev, wsp, M, synth.W_LAYER_M5)
     res["qwen3_8b_layer_linears_m5_fused"] = fused_layer_measurement(dev, wsp, M)
     res["qwen3_8b_layer_linears_m288"] = layer_measurement(dev, wsp, 288, synth.W_BATCHED)
-    res["library_int8_gemm_m288"] = library_int8_gemm(dev)
+    res["library_gemm_reference"] = library_int8_gemm(dev)
 
     K, V = 4096, synth.QWEN3_VOCAB
     lg = torch.empty(M, V, dtype=torch.float32, device=dev)
@@ -1004,6 +1004,19 @@ def library_int8_gemm(dev):
         del ws
         torch.cuda.empty_cache()
     out["what"] = "torch._int_mm (vendor int8 GEMM, int32 out, no dequant), HIP graph"
+    # and the vendor bf16 GEMM on the M = 5 LM head (the 2x-traffic baseline
+    # our own bf16 kernel also measures)
+    g = torch.Generator(device=dev)
+    g.manual_seed(12)
+    x = torch.randn(5, 4096, device=dev, generator=g).to(torch.bfloat16)
+    ws = [(torch.randn(151936, 4096, device=dev, generator=g) * 0.02).to(torch.bfloat16)
+          for _ in range(2)]
+    t = graph_time([(lambda c=c: torch.matmul(x, ws[c].t())) for c in range(2)], replays=10) / 2
+    out["bf16_lm_head_m5"] = {"us": round(t * 1e6, 2),
+                              "GBs": round(2 * 151936 * 4096 / t / 1e9, 1),
+                              "what": "torch.matmul bf16, M=5, K=4096, N=151936"}
+    del ws
+    torch.cuda.empty_cache()
     return out
 
 
