@@ -660,11 +660,12 @@ def w4a8_measurement(dev, x_dev, xq, xsc, wsp):
     return res
 
 
-def fused_layer_measurement(dev, wsp, M):
+def fused_layer_measurement(dev, wsp, M, tiled_act=False):
     """The Qwen3-8B layer's linears at M rows with q/k/v and gate/up fused
     (their output channels stacked in one weight, per-channel codes and
     scales unchanged): 4 launches instead of 7, each graph-replayed over
-    enough weight copies to pass 600 MB."""
+    enough weight copies to pass 600 MB.  With ``tiled_act`` the
+    activations go in the tiled layout (the batched kernels' fast path)."""
     import numpy as np
     import torch
 
@@ -685,20 +686,35 @@ def fused_layer_measurement(dev, wsp, M):
             del w
         x = torch.from_numpy(synth.activations_bf16(synth.W_LAYER_M5, M, K, outliers=True)
                              .view(np.int16).copy()).view(torch.bfloat16).to(dev)
-        lxq, lxs = w8.quantize_act(x)
         y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
-        t = graph_time([(lambda c=c: w8.linear(lxq, lxs, *wl[c], y_bf16=y, workspace=wsp))
-                        for c in range(nc)], replays=10) / nc
+        if tiled_act:
+            lxq, lxs = w8.quantize_act_tiled(x)
+            t = graph_time([(lambda c=c: w8.linear_tiled_act(lxq, lxs, *wl[c], K=K, y_bf16=y))
+                            for c in range(nc)], replays=10) / nc
+        else:
+            lxq, lxs = w8.quantize_act(x)
+            t = graph_time([(lambda c=c: w8.linear(lxq, lxs, *wl[c], y_bf16=y, workspace=wsp))
+                            for c in range(nc)], replays=10) / nc
         b = linear_bytes(M, N, K)
-        out.append({"name": name, "N": N, "K": K, "copies": nc, "us": round(t * 1e6, 2),
-                    "GBs": round(b / t / 1e9, 1)})
+        e = {"name": name, "N": N, "K": K, "copies": nc, "us": round(t * 1e6, 2),
+             "GBs": round(b / t / 1e9, 1)}
+        if M > 16:
+            e["TOPS"] = round(2 * M * N * K / t / 1e12, 1)
+            e["mfma_frac"] = round(2 * M * N * K / t / 1e12 / INT8_PEAK_TOPS, 4)
+        out.append(e)
         tot_t += t
         tot_b += b
         del wl
-    return {"M": M, "per_launch": out, "sum_us": round(tot_t * 1e6, 2),
-            "aggregate_GBs": round(tot_b / tot_t / 1e9, 1),
-            "aggregate_frac": round(tot_b / tot_t / 1e9 / HBM_PEAK_GBS, 4),
-            "timing": "HIP graph over the rotating weight copies, mean of 10 replays"}
+    res = {"M": M, "per_launch": out, "sum_us": round(tot_t * 1e6, 2),
+           "aggregate_GBs": round(tot_b / tot_t / 1e9, 1),
+           "aggregate_frac": round(tot_b / tot_t / 1e9 / HBM_PEAK_GBS, 4),
+           "timing": "HIP graph over the rotating weight copies, mean of 10 replays"}
+    if M > 16:
+        ops = 2 * M * sum(l.N * l.K for l in lins)
+        res["aggregate_TOPS"] = round(ops / tot_t / 1e12, 1)
+        res["aggregate_mfma_frac"] = round(ops / tot_t / 1e12 / INT8_PEAK_TOPS, 4)
+        res["activations"] = "tiled" if tiled_act else "row-major"
+    return res
 
 
 def extra_measurements(dev, copies, x_dev, xq, xsc, wsp):
@@ -716,6 +732,8 @@ def extra_measurements(dev, copies, x_dev, xq, xsc, wsp):
     res["qwen3_8b_layer_linears_m5"] = layer_measurement(dev, wsp, M, synth.W_LAYER_M5)
     res["qwen3_8b_layer_linears_m5_fused"] = fused_layer_measurement(dev, wsp, M)
     res["qwen3_8b_layer_linears_m288"] = layer_measurement(dev, wsp, 288, synth.W_BATCHED)
+    res["qwen3_8b_layer_linears_m288_fused"] = fused_layer_measurement(dev, wsp, 288,
+                                                                       tiled_act=True)
     res["library_gemm_reference"] = library_int8_gemm(dev)
 
     K, V = 4096, synth.QWEN3_VOCAB
