@@ -420,16 +420,15 @@ constexpr BatchedShape kTiledAWide{3, 2, 1, 4, 4};
 constexpr int64_t kMinWorkgroups = 256;
 
 // The LDS-pipelined kernel (tiled activations and weights): 96 rows x 64
-// channels per workgroup.  Measured at 288 rows:
+// channels per workgroup.  Measured at 288 rows, weights rotated past the
+// Infinity Cache, against the register-fragment kernel above:
 //  * 4 stages, whole K per workgroup, once the grid is wide enough to keep
-//    ~2 workgroups per CU busy: gate/up 4096 -> 12288 34.3 vs 41.5 us with
-//    the register-fragment kernel, the fused 24576-wide gate_up 59.0 vs
-//    74.8 us;
+//    ~2 workgroups per CU busy: gate/up 4096 -> 12288 40.2 vs 49.8 us;
 //  * K cut into 4 slices of 4 waves each (3 stages each, tiles summed in
 //    LDS) on narrower grids, where one workgroup's chain of k steps would
-//    be too long: down 12288 -> 4096 34.7 vs 41.2 us, q 18.3 vs 19.0 us;
+//    be too long: down 12288 -> 4096 41.8 vs 46.6 us, q 19.7 vs 20.5 us;
 //  * below ~128 workgroups (k/v, 1024 channels) the register-fragment
-//    kernel stays faster (11.2 vs 16.4 us).
+//    kernel stays faster.
 struct LdsShape {
   int mb, tn, p;
 };
