@@ -11,8 +11,9 @@ weights in the 256 MB Infinity Cache.
 
 Printed: one JSON line with verified tokens/s (value; eager launches, K
 timed steps between synchronizations), the roofline of the dominant kernel
-(the LM-head GEMM: algorithmic bytes per launch over its HIP-event-timed
-average duration, against 8 TB/s; HBM traffic from the committed rocprofv3
+(the LM-head GEMM: algorithmic bytes per launch over its average duration from
+HIP events that take the kernel's own start and end timestamps, against
+8 TB/s; HBM traffic from the committed rocprofv3
 counters), the CPU oracle timed on this host on a bounded sample, and
 secondary figures ("extra"): the step as a HIP graph and through the
 separate calls; the Qwen3-8B decoder-layer linears at M = 5 and M = 288
@@ -423,14 +424,12 @@ def main():
     def step(i, ev=None):
         """One verify step: quantize the 5 hidden rows, then the LM-head
         linear with the argmax's first pass fused into its epilogue, then
-        greedy acceptance (the logits themselves are not written)."""
+        greedy acceptance (the logits themselves are not written).  With
+        ``ev``, the LM-head kernel records its own start and end timestamps
+        into the two events (no marker packets join the stream)."""
         w8.quantize_act(x_dev[i % n_x], xq=xq, x_scale=xsc)
         wq, ws, _ = copies[i % 2]
-        if ev is not None:
-            ev[0].record()
-        w8.lm_head_argmax(xq, xsc, wq, ws, workspace=wsp)
-        if ev is not None:
-            ev[1].record()
+        w8.lm_head_argmax(xq, xsc, wq, ws, workspace=wsp, events=ev)
         w8.accept_from_keys(draft, argmax=am, accept_len=al, next_token=nt, workspace=wsp)
 
     def step_separate(i):
@@ -462,6 +461,9 @@ def main():
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
+    for a, b in evs:            # torch creates each event on its first record
+        a.record()
+        b.record()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -477,6 +479,8 @@ def main():
     gemm_avg_s = float(np.mean(gemm_ms)) / 1e3
     ms_per_step = total_ms / args.steps
     tok_s = M * args.steps / (total_ms / 1e3)
+    # gemm_ms: the LM-head kernel's own durations (its start and end
+    # timestamps, recorded into the events by hipExtLaunchKernel)
     # the fused kernel reads the weights, scales and activations; its only
     # writes are the atomic folds of the row maxima (8 bytes per row per
     # 32-channel workgroup)

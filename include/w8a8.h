@@ -273,6 +273,19 @@ w8a8_status w8a8_lm_head_argmax(const int8_t* xq, const float* x_scale,
                                 const int8_t* wq_tiled, const float* w_scale,
                                 int64_t M, int64_t V, int64_t K, float* logits,
                                 void* workspace, size_t workspace_bytes, void* stream);
+/* w8a8_lm_head_argmax launched with hipExtLaunchKernel, which records the
+ * LM-head kernel's own start and end timestamps into start_event and
+ * stop_event (hipEvent_t handles the caller created with timing enabled):
+ * hipEventElapsedTime(start, stop) is then that kernel's execution time as a
+ * profiler's kernel trace reports it, and no marker packets are added to the
+ * stream.  For measurement.  Results, arguments and errors as for
+ * w8a8_lm_head_argmax; both events are required (W8A8_ERR_INVALID_ARG if
+ * NULL); M <= 16 (W8A8_ERR_UNSUPPORTED above). */
+w8a8_status w8a8_lm_head_argmax_timed(const int8_t* xq, const float* x_scale,
+                                      const int8_t* wq_tiled, const float* w_scale,
+                                      int64_t M, int64_t V, int64_t K, float* logits,
+                                      void* workspace, size_t workspace_bytes,
+                                      void* start_event, void* stop_event, void* stream);
 w8a8_status w8a8_accept_from_keys(void* workspace, size_t workspace_bytes,
                                   const int32_t* draft, int64_t B, int64_t G,
                                   int32_t* argmax, int32_t* accept_len,

@@ -215,6 +215,24 @@ def test_pack_v_cache_validation(lib):
     assert f(None, 0, 8, 4096, 128, None, None) == OK
 
 
+def test_lm_head_argmax_timed_validation(lib):
+    """The kernel-timestamped LM-head launch: both events required, M <= 16,
+    and the checks of w8a8_lm_head_argmax before any launch."""
+    ws = 32 * 64 * 256
+    EV0, EV1 = 0x30000, 0x40000   # fake handles: validation never touches them
+
+    def f(M=5, ev0=EV0, ev1=EV1, wsb=ws, xq=A16):
+        return lib.w8a8_lm_head_argmax_timed(xq, A16, A16b, A16, M, 151936, 4096, None, A16, wsb,
+                                             ev0, ev1, None)
+
+    assert f(ev0=None) == INVALID
+    assert f(ev1=None) == INVALID
+    assert f(M=17) == UNSUPPORTED
+    assert f(wsb=ws // 64) == WORKSPACE
+    assert f(xq=A16 + 4) == INVALID
+    assert f(M=0, ev0=EV0) == OK
+
+
 def test_bf16_linear_validation(lib):
     f = lib.w8a8_bf16_linear
     assert f(A16, A16b, 17, 512, 256, A16, None, None) == UNSUPPORTED

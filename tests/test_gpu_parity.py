@@ -561,3 +561,39 @@ def test_lm_head_verify_ties_across_workgroups():
     torch.cuda.synchronize()
     assert host(am).tolist() == [100, 5, 64, 0, 31]
     assert int(host(al)[0]) == 4 and int(host(nt)[0]) == 31
+
+
+def test_lm_head_argmax_timed_matches_and_times():
+    """The launch that records the kernel's own timestamps into two events
+    gives the same keys (acceptance) as the plain launch, and a positive
+    duration for each call."""
+    announce("lm_head_argmax timed")
+    B, G, V, K = 1, 4, 151936, 4096
+    R = B * (G + 1)
+    bits = synth.activations_bf16(740, R, K)
+    w = synth.weights_f32(740, V, K)
+    xq_r, xs_r = oracle.quantize_act(bits)
+    wq_r, ws_r = oracle.quantize_weight(w)
+    _, y32_r, _ = oracle.w8a8_linear(xq_r, xs_r, wq_r, ws_r)
+    draft = synth.draft_ids(740, B, G, V)
+    draft[0, :2] = oracle.argmax_rows(y32_r)[:2]
+    am_r, al_r, nt_r = oracle.verify_accept(y32_r, draft)
+    xq, xs = w8.quantize_act(dev_bf16(bits))
+    wt, ws = w8.quantize_weight(dev(w), tiled=True)
+    d = dev(draft)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(3)]
+    for a, b in evs:                 # torch creates the events on their first record
+        a.record()
+        b.record()
+    for e in evs:
+        lg = w8.lm_head_argmax(xq, xs, wt, ws, logits=torch.empty(R, V, dtype=torch.float32,
+                                                                  device=xq.device), events=e)
+        am, al, nt = w8.accept_from_keys(d)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(lg).view(np.uint32), y32_r.view(np.uint32))
+        np.testing.assert_array_equal(host(am), am_r)
+        np.testing.assert_array_equal(host(al), al_r)
+        np.testing.assert_array_equal(host(nt), nt_r)
+        t = e[0].elapsed_time(e[1])
+        assert 0.0 < t < 100.0, t

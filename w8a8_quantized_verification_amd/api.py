@@ -231,10 +231,13 @@ def lm_head_verify(xq, x_scale, wq_tiled, w_scale, draft, *, want_logits=False,
 
 
 def lm_head_argmax(xq, x_scale, wq_tiled, w_scale, *, logits=None,
-                   workspace: Workspace | None = None):
+                   workspace: Workspace | None = None, events=None):
     """Phase 1 of :func:`lm_head_verify`: the LM-head linear with the row
     maxima folded into the workspace keys (and the logits written if
-    ``logits`` is given)."""
+    ``logits`` is given).  ``events=(start, stop)``: two timing-enabled
+    ``torch.cuda.Event`` objects, each recorded at least once before (torch
+    creates the underlying event lazily), that receive the kernel's own start
+    and end timestamps (``start.elapsed_time(stop)`` is its duration)."""
     _need(xq, "xq", torch.int8, 2)
     dev = xq.device
     _need(x_scale, "x_scale", torch.float32, 1, dev)
@@ -248,6 +251,16 @@ def lm_head_argmax(xq, x_scale, wq_tiled, w_scale, *, logits=None,
         logits = _out(logits, (M, V), torch.float32, dev, "logits")
     ws = (workspace or _default_ws).get(int(lib().w8a8_lm_head_verify_workspace_bytes(M, 0, V, K)),
                                         dev, use="zeroed")
+    if events is not None:
+        start, stop = events
+        if not (start.cuda_event and stop.cuda_event):
+            raise ValueError("record each timing event once before passing it (torch creates "
+                             "the underlying event lazily)")
+        check(lib().w8a8_lm_head_argmax_timed(_ptr(xq), _ptr(x_scale), _ptr(wq_tiled),
+                                              _ptr(w_scale), M, V, K, _ptr(logits), _ptr(ws),
+                                              0 if ws is None else ws.numel(), start.cuda_event,
+                                              stop.cuda_event, _stream(dev)))
+        return logits
     check(lib().w8a8_lm_head_argmax(_ptr(xq), _ptr(x_scale), _ptr(wq_tiled), _ptr(w_scale), M, V,
                                     K, _ptr(logits), _ptr(ws), 0 if ws is None else ws.numel(),
                                     _stream(dev)))

@@ -249,6 +249,27 @@ w8a8_status w8a8_lm_head_argmax(const int8_t* xq, const float* x_scale, const in
                     fn);
 }
 
+w8a8_status w8a8_lm_head_argmax_timed(const int8_t* xq, const float* x_scale,
+                                      const int8_t* wq_tiled, const float* w_scale, int64_t M,
+                                      int64_t V, int64_t K, float* logits, void* workspace,
+                                      size_t workspace_bytes, void* start_event,
+                                      void* stop_event, void* stream) {
+  static const char* fn = "w8a8_lm_head_argmax_timed";
+  g_last_error.clear();
+  if (w8a8_status s = check_lm_head(fn, xq, x_scale, wq_tiled, w_scale, M, V, K, logits,
+                                    workspace, workspace_bytes))
+    return s;
+  if (!start_event || !stop_event)
+    return fail(W8A8_ERR_INVALID_ARG, fn, "start_event and stop_event are required");
+  if (M > 16) return fail(W8A8_ERR_UNSUPPORTED, fn, "kernel timestamps are taken for M <= 16 only");
+  if (M == 0) return W8A8_OK;
+  return hip_status(w8a8_launch_lm_head_argmax(xq, x_scale, wq_tiled, w_scale, M, V, K, logits,
+                                               workspace, reinterpret_cast<hipStream_t>(stream),
+                                               reinterpret_cast<hipEvent_t>(start_event),
+                                               reinterpret_cast<hipEvent_t>(stop_event)),
+                    fn);
+}
+
 w8a8_status w8a8_accept_from_keys(void* workspace, size_t workspace_bytes, const int32_t* draft,
                                   int64_t B, int64_t G, int32_t* argmax, int32_t* accept_len,
                                   int32_t* next_token, void* stream) {

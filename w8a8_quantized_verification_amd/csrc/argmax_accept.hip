@@ -79,10 +79,13 @@ __global__ __launch_bounds__(kAcceptWaves * kWave) void accept_kernel(
   __shared__ float sv[kAcceptWaves];
   __shared__ int si[kAcceptWaves];
   __shared__ int row_arg[kMaxDraftRows];
+  __shared__ int s_draft[kMaxDraftRows];
   const int b = blockIdx.x;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int rows = G + 1;
+  // the draft is read in parallel up front, so the walk below is LDS-only
+  for (int i = threadIdx.x; i < G; i += blockDim.x) s_draft[i] = draft[(size_t)b * G + i];
   const int wpr = rows >= kAcceptWaves ? 1 : kAcceptWaves / rows;  // waves per row
   const int rows_per_pass = kAcceptWaves / wpr;
   const int sub = wave % wpr;
@@ -117,7 +120,7 @@ __global__ __launch_bounds__(kAcceptWaves * kWave) void accept_kernel(
   }
   if (threadIdx.x == 0) {
     int n = 0;
-    while (n < G && draft[(size_t)b * G + n] == row_arg[n]) ++n;
+    while (n < G && s_draft[n] == row_arg[n]) ++n;
     accept_len[b] = n;
     next_token[b] = row_arg[n];
   }
@@ -143,10 +146,14 @@ __global__ __launch_bounds__(kAcceptKeyWaves * kWave) void accept_keys_kernel(
     const int32_t* __restrict__ draft, int G, int32_t* __restrict__ argmax,
     int32_t* __restrict__ accept_len, int32_t* __restrict__ next_token) {
   __shared__ int row_arg[kMaxDraftRows];
+  __shared__ int s_draft[kMaxDraftRows];
   const int b = blockIdx.x;
   const int rows = G + 1;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
+  // the draft is read in parallel with the key exchanges, so the walk below
+  // is LDS-only (no chain of dependent global loads)
+  for (int i = threadIdx.x; i < G; i += blockDim.x) s_draft[i] = draft[(size_t)b * G + i];
   // up to 8 rows' sub-key exchanges per wave are issued before any is reduced
   unsigned long long k[8];
   for (int i0 = wave; i0 < rows; i0 += 8 * kAcceptKeyWaves) {
@@ -174,7 +181,7 @@ __global__ __launch_bounds__(kAcceptKeyWaves * kWave) void accept_keys_kernel(
   __syncthreads();
   if (threadIdx.x == 0) {
     int n = 0;
-    while (n < G && draft[(size_t)b * G + n] == row_arg[n]) ++n;
+    while (n < G && s_draft[n] == row_arg[n]) ++n;
     accept_len[b] = n;
     next_token[b] = row_arg[n];
   }

@@ -85,7 +85,8 @@ size_t w8a8_lm_head_workspace_bytes(int64_t M);
 hipError_t w8a8_launch_lm_head_argmax(const int8_t* xq, const float* x_scale,
                                       const int8_t* wq_tiled, const float* w_scale, int64_t M,
                                       int64_t V, int64_t K, float* logits, void* keys,
-                                      hipStream_t stream);
+                                      hipStream_t stream, hipEvent_t ev0 = nullptr,
+                                      hipEvent_t ev1 = nullptr);
 hipError_t w8a8_launch_accept_from_keys(void* keys, const int32_t* draft, int64_t B, int64_t G,
                                         int32_t* argmax, int32_t* accept_len, int32_t* next_token,
                                         hipStream_t stream);

@@ -44,6 +44,8 @@
 // rows go to the batched kernel (gemm_w8a8_batched.hip).
 #include "common.h"
 
+#include <hip/hip_ext.h>
+
 #include <climits>
 #include <cstdlib>
 
@@ -358,13 +360,22 @@ size_t w8a8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, bool tiled) {
   return part_aligned + (size_t)p.tiles * p.mblocks * sizeof(uint32_t);
 }
 
+// With ev0/ev1 set, the launch goes through hipExtLaunchKernel, which
+// records the kernel's own start and end timestamps into the two events.
 static hipError_t launch_plan(const w8a8::SkinnyPlan& p, const w8a8::GemmArgs& g, bool tiled,
-                              bool argmax, hipStream_t stream) {
+                              bool argmax, hipStream_t stream, hipEvent_t ev0 = nullptr,
+                              hipEvent_t ev1 = nullptr) {
   using namespace w8a8;
   const dim3 grid((unsigned)p.tiles, (unsigned)p.split, (unsigned)p.mblocks);
-#define W8A8_GEMM(TN, W, TL, AM)                                                            \
-  hipLaunchKernelGGL((gemm_w8a8_skinny<TN, W, kUnroll, TL, AM>), grid, dim3(W * kWave), 0, \
-                     stream, g)
+#define W8A8_GEMM(TN, W, TL, AM)                                                              \
+  do {                                                                                        \
+    if (ev0)                                                                                  \
+      hipExtLaunchKernelGGL((gemm_w8a8_skinny<TN, W, kUnroll, TL, AM>), grid, dim3(W * kWave), \
+                            0, stream, ev0, ev1, 0, g);                                      \
+    else                                                                                      \
+      hipLaunchKernelGGL((gemm_w8a8_skinny<TN, W, kUnroll, TL, AM>), grid, dim3(W * kWave), 0, \
+                         stream, g);                                                          \
+  } while (0)
 #define W8A8_GEMM_W(TN, TL, AM)                   \
   do {                                            \
     if (p.waves == 4) W8A8_GEMM(TN, 4, TL, AM);   \
@@ -430,16 +441,18 @@ size_t w8a8_lm_head_workspace_bytes(int64_t M) {
 hipError_t w8a8_launch_lm_head_argmax(const int8_t* xq, const float* x_scale,
                                       const int8_t* wq_tiled, const float* w_scale, int64_t M,
                                       int64_t V, int64_t K, float* logits, void* keys,
-                                      hipStream_t stream) {
+                                      hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   using namespace w8a8;
   if (M == 0) return hipSuccess;
-  if (M > kSkinnyMaxRows)
+  if (M > kSkinnyMaxRows) {
+    if (ev0 || ev1) return hipErrorNotSupported;  // kernel timestamps: skinny kernel only
     return w8a8_launch_gemm_batched(xq, x_scale, wq_tiled, w_scale, M, V, K, true, nullptr, logits,
                                     nullptr, keys, kArgmaxSubkeys, kArgmaxKeyStride, stream);
+  }
   const SkinnyPlan p = plan_skinny(M, V, K, true, true);
   GemmArgs g = make_args(p, xq, x_scale, wq_tiled, w_scale, M, V, K, nullptr, logits, nullptr);
   g.keys = reinterpret_cast<unsigned long long*>(keys);
-  return launch_plan(p, g, true, true, stream);
+  return launch_plan(p, g, true, true, stream, ev0, ev1);
 }
 
 hipError_t w8a8_launch_accept_from_keys(void* keys, const int32_t* draft, int64_t B, int64_t G,
