@@ -89,7 +89,7 @@ __device__ __forceinline__ v4i load16_stream(const int8_t* p) {
 template <int TN, int WAVES, int U, bool kTiled, bool kArgmax>
 __global__ __launch_bounds__(WAVES * kWave) void gemm_w8a8_skinny(GemmArgs g) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
   const int col = lane & 15;
   const int grp = lane >> 4;
   const int tile = blockIdx.x;
