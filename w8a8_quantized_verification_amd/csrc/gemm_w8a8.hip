@@ -313,11 +313,16 @@ static int env_int(const char* name) {
 
 // Measured on MI355X at M=5 over the Qwen3-8B shapes (N = 1024..12288, K =
 // 4096/12288), at M=8 over the Qwen3-32B shapes (K up to 25600) and on the
-// LM head: 4 waves per workgroup once there are >= 512 column tiles, 8
-// below.  Splitting k across workgroups (its atomic handoff) pays only for
-// outputs too narrow to occupy more than a few dozen CUs and for long
-// reductions over few tiles (32B down, 5120 x 25600: 400 steps, 50 per
-// wave: 31.5-32.4 us with 4 slices against 37.2 us without).
+// LM head, sweeping tiles per workgroup, waves and slices: on the tiled
+// layout 4 waves per workgroup with two tiles each (>= 2048 tiles: the LM
+// heads, the 32B gate/up), 8 waves with one tile (Qwen3-8B gate/up at M=5:
+// 17.3 against 17.8-19.1 us with 4 waves; 32B q/k/v at M=8: 13.1 against
+// 13.3 us).  Splitting k across workgroups (its atomic handoff) pays only
+// for outputs too narrow to occupy more than a few dozen CUs and for long
+// reductions over few tiles; once a wave would walk more than 32 k steps,
+// the split goes on until it walks at most 16 (32B down, 5120 x 25600, 400
+// steps: 27.2 us with 4 slices, 31.2 us with 2, 37.2 us without; the 8B
+// down at M=5, 24 steps per wave, is fastest unsplit).
 static SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, bool tiled, bool no_split = false) {
   SkinnyPlan p;
   const int64_t tiles16 = (N + 15) / 16;
@@ -330,7 +335,7 @@ static SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, bool tiled, bool 
   p.tiles = (int)((tiles16 + p.tn - 1) / p.tn);
   const int64_t steps = (K + 63) / 64;
   const int64_t wgs = (int64_t)p.tiles * p.mblocks;
-  p.waves = wgs >= 512 ? 4 : (wgs >= kSplitBelowTiles ? 8 : 16);
+  p.waves = (wgs >= 512 && (p.tn == 2 || !tiled)) ? 4 : (wgs >= kSplitBelowTiles ? 8 : 16);
   p.split = 1;
   while (!no_split && wgs * p.split < kSplitBelowTiles &&
          steps / ((int64_t)p.split * 2 * p.waves) >= 2)
@@ -338,8 +343,8 @@ static SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, bool tiled, bool 
   // long reductions over few tiles: more than kLongChain k steps per wave is
   // a chain of dependent round trips that the grid cannot hide, so K is cut
   // across workgroups until a wave walks at most about half of that
-  while (!no_split && p.split < 8 && steps / ((int64_t)p.split * p.waves) > kLongChain)
-    p.split *= 2;
+  if (!no_split && steps / ((int64_t)p.split * p.waves) > kLongChain)
+    while (p.split < 8 && steps / ((int64_t)p.split * p.waves) > kLongChain / 2) p.split *= 2;
   const int fw = env_int("W8A8_WAVES");
   if (fw == 4 || fw == 8 || fw == 16) p.waves = fw;
   const int fs = env_int("W8A8_SPLITK");
