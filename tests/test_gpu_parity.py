@@ -266,14 +266,17 @@ def test_linear_batched_ragged(M, N, K):
                                    (288, 4096, 12288), (17, 65, 80), (97, 4099, 1040),
                                    (513, 300, 2048), (5, 512, 256), (40, 33, 16), (288, 64, 0),
                                    (200, 20008, 1040), (513, 8200, 144), (288, 24576, 64),
-                                   (200, 4000, 4096), (97, 4099, 1024)])
+                                   (200, 4000, 4096), (97, 4099, 1024), (288, 6144, 4096),
+                                   (300, 6152, 2048), (65, 16384, 1040)])
 def test_linear_tiled_activations(M, N, K):
     """quantize_act_tiled + linear_tiled_act: the codes read back through
     the tiled layout (padding zero) and every output against the oracle.
-    The wide grids (N >= 8200 here) take the LDS-pipelined kernel, with
-    ragged row blocks, channel tiles and k steps; 128-511 workgroups with
-    a step count divisible by 4 (q, down and the ragged 4000 / 4099-wide
-    cases) its k-sliced form; the rest the register-fragment kernel."""
+    Grids of 224+ workgroups of 64 rows x 128 channels (N >= 6144 here)
+    take the 32 x 32 LDS-pipelined kernel (3 stages from 512 workgroups, 4
+    below), with ragged row blocks, channel tiles and k steps; the 16 x 16
+    LDS kernel takes 128-511 of its own workgroups with a step count
+    divisible by 4 (q, down and the ragged 4000 / 4099-wide cases) in its
+    k-sliced form; the rest the register-fragment kernel."""
     announce(f"linear tiled activations M={M} N={N} K={K}")
     seed = 340 + M + N % 11
     bits = synth.activations_bf16(seed, M, K, outliers=K > 0)

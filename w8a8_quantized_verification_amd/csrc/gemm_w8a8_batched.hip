@@ -391,6 +391,128 @@ __global__ __launch_bounds__(KH * kLdsWaves * kWave) void gemm_w8a8_lds(BatchedA
   batched_epilogue<MB, TN, kArgmax>(g, acc, mt * FA + wr * MB, ng * FB + wc * TN, lane);
 }
 
+// The same pipeline on v_mfma_i32_32x32x32_i8: a workgroup of four waves
+// computes RB blocks of 32 rows x 4*CW blocks of 32 channels; wave w owns
+// channel blocks w*CW .. +CW-1 over all RB row blocks.  The staged
+// fragments are the same 1 KiB (16-row block or 16-channel tile, k step)
+// units; for the 32-wide half h of a step, lane l (r = l % 32, g = l / 32)
+// reads unit 2*b + r/16 of its 32-block b at tile lane (r % 16) + 16 (2h +
+// g), for both operands, so A and B pair the same k.  Lane l gets rows
+// 8 (v / 4) + 4 g + v % 4 of column r in accumulator v.
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+template <int RB, int CW, int P>
+__global__ __launch_bounds__(kLdsWaves * kWave) void gemm_w8a8_lds32(BatchedArgs g) {
+  constexpr int FA = 2 * RB, FB = 2 * kLdsWaves * CW, F = FA + FB;
+  constexpr int FW = (F + kLdsWaves - 1) / kLdsWaves;
+  constexpr int STAGE = FW * kLdsWaves * 1024;
+  static_assert(P >= 3, "one stage read, one refilled, at least one in flight");
+  __shared__ __attribute__((aligned(1024))) int8_t stage[P][STAGE];
+
+  const int b = blockIdx.x;
+  const int xcd = b % kXcds;
+  const int slot = b / kXcds;
+  const int mt = slot % g.mtiles;
+  const int ng = (slot / g.mtiles) * kXcds + xcd;
+  if (ng >= g.ngroups) return;
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int steps = g.steps;
+  const int mblocks = (g.M + 15) / 16;
+
+  const int8_t* src[FW];
+#pragma unroll
+  for (int j = 0; j < FW; ++j) {
+    const int f = wave + kLdsWaves * j;
+    if (f >= F) {
+      src[j] = g.xq + (lane << 4);
+    } else if (f < FA) {
+      const int rb = mt * FA + f;
+      src[j] = g.xq + ((size_t)(rb < mblocks ? rb : 0) * (size_t)steps << 10) + (lane << 4);
+    } else {
+      const int t16 = ng * FB + (f - FA);
+      src[j] = g.wq + ((size_t)(t16 < g.tiles16 ? t16 : 0) * (size_t)steps << 10) + (lane << 4);
+    }
+  }
+  auto issue = [&](int p, int s) {
+    s = min(s, steps - 1);
+#pragma unroll
+    for (int j = 0; j < FW; ++j)
+      lds_dma16(src[j] + ((size_t)s << 10), &stage[p][(wave + kLdsWaves * j) * 1024]);
+  };
+
+  const int r32 = lane & 31, hi = lane >> 5;
+  const int lane_off = ((r32 & 15) + 16 * hi) << 4;
+  v16i acc[RB][CW];
+#pragma unroll
+  for (int i = 0; i < RB; ++i)
+#pragma unroll
+    for (int j = 0; j < CW; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0;
+
+#pragma unroll
+  for (int u = 0; u < P - 1; ++u) issue(u, u);
+  for (int s = 0; s < steps; ++s) {
+    wait_vmcnt<(P - 2) * FW>();
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+    issue((s + P - 1) % P, s + P - 1);
+    const int8_t* st = stage[s % P];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      v4i a[RB], bb[CW];
+#pragma unroll
+      for (int i = 0; i < RB; ++i)
+        a[i] = *reinterpret_cast<const v4i*>(st + (2 * i + (r32 >> 4)) * 1024 + (h << 9) + lane_off);
+#pragma unroll
+      for (int j = 0; j < CW; ++j)
+        bb[j] = *reinterpret_cast<const v4i*>(st + (FA + 2 * (wave * CW + j) + (r32 >> 4)) * 1024 +
+                                              (h << 9) + lane_off);
+#pragma unroll
+      for (int i = 0; i < RB; ++i)
+#pragma unroll
+        for (int j = 0; j < CW; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], bb[j], acc[i][j], 0, 0, 0);
+    }
+    compiler_fence();
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this step's LDS reads are done
+  }
+  wait_vmcnt<0>();
+
+#pragma unroll
+  for (int j = 0; j < CW; ++j) {
+    const int n = (ng * kLdsWaves * CW + wave * CW + j) * 32 + r32;
+    const bool n_ok = n < g.N;
+    const float wsn = n_ok ? g.ws[n] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = (mt * RB + i) * 32 + 8 * (v >> 2) + 4 * hi + (v & 3);
+        if (m < g.M && n_ok) {
+          const int32_t a = acc[i][j][v];
+          const float y = (static_cast<float>(a) * g.xs[m]) * wsn;
+          const size_t o = (size_t)m * (size_t)g.N + (size_t)n;
+          if (g.y_f32) g.y_f32[o] = y;
+          if (g.y_bf16) g.y_bf16[o] = f32_to_bf16_rne(y);
+          if (g.acc) g.acc[o] = a;
+        }
+      }
+  }
+}
+
+template <int RB, int CW, int P>
+static hipError_t launch_lds32(BatchedArgs g, hipStream_t stream) {
+  g.ngroups = (g.tiles16 + 2 * kLdsWaves * CW - 1) / (2 * kLdsWaves * CW);
+  g.mtiles = (g.M + 32 * RB - 1) / (32 * RB);
+  const int64_t ng_padded = ((int64_t)g.ngroups + kXcds - 1) / kXcds * kXcds;
+  const dim3 grid((unsigned)(ng_padded * g.mtiles)), block(kLdsWaves * kWave);
+  hipLaunchKernelGGL((gemm_w8a8_lds32<RB, CW, P>), grid, block, 0, stream, g);
+  return hipGetLastError();
+}
+
 // Launch shapes, measured on MI355X at 288 rows over the Qwen3-8B linears
 // (tiled weights):
 //  * row-major activations: 48 rows x 64 channels per workgroup with K in 4
@@ -436,6 +558,20 @@ constexpr LdsShape kLdsShape{3, 2, 4};
 constexpr int64_t kLdsMinWorkgroups = 512;
 constexpr int kLdsSplit = 4, kLdsSplitStages = 3;
 constexpr int64_t kLdsSplitMinWorkgroups = 128;
+
+// The 32 x 32 form (64 rows x 128 channels per workgroup) where its grid
+// fills the chip, measured at 288 rows against the 16 x 16 pipeline:
+// q/k/v fused 4096 -> 6144 (240 workgroups, 4 stages) 22.8 vs 35.5 us,
+// gate 4096 -> 12288 (480) 33.3 vs 39.1 us, gate/up fused 4096 -> 24576
+// (960, 3 stages) 59.4 vs 66.7 us; with 160 workgroups (o, down at 4096
+// channels) it is slower (22.1 vs 19.3 us, 50.1 vs 41.6 us), so those keep
+// the k-sliced 16 x 16 form.
+constexpr int64_t kLds32MinWorkgroups = 224;
+constexpr int64_t kLds32DeepMinWorkgroups = 512;
+
+static int64_t lds32_workgroups(int64_t M, int64_t N) {
+  return ((N + 15) / 16 + 2 * kLdsWaves - 1) / (2 * kLdsWaves) * ((M + 63) / 64);
+}
 
 static int64_t lds_workgroups(int64_t M, int64_t N) {
   const int64_t ngroups = ((N + 15) / 16 + 2 * kLdsShape.tn - 1) / (2 * kLdsShape.tn);
@@ -489,6 +625,9 @@ hipError_t w8a8_launch_gemm_batched(const int8_t* xq, const float* x_scale, cons
   g.subkeys = subkeys; g.key_stride = key_stride;
   const bool argmax = keys != nullptr;
   if (a_tiled && tiled && !argmax && g.steps > 0) {
+    const int64_t wg32 = lds32_workgroups(M, N);
+    if (wg32 >= kLds32DeepMinWorkgroups) return launch_lds32<2, 1, 3>(g, stream);
+    if (wg32 >= kLds32MinWorkgroups) return launch_lds32<2, 1, 4>(g, stream);
     const int64_t lwg = lds_workgroups(M, N);
     if (lwg >= kLdsMinWorkgroups)
       return launch_lds<kLdsShape.mb, kLdsShape.tn, kLdsShape.p, 1>(g, stream);
