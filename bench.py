@@ -601,6 +601,54 @@ def layer_measurement(dev, wsp, M, workload):
             "timing": "HIP graph over the rotating weight copies, mean of 10 replays"}
 
 
+def batched_verify_measurement(dev, copies, wsp):
+    """Batched verification: 32 sequences x (8 drafts + 1) = 288 rows
+    through the LM head (4096 -> 151936) with greedy acceptance, two
+    alternating 622 MB LM-head copies, as a HIP graph.  Tiled activations
+    (quantize_act_tiled -> lm_head_argmax_tiled_act -> accept_from_keys)
+    against row-major ones (quantize_act -> lm_head_argmax ->
+    accept_from_keys)."""
+    import numpy as np
+    import torch
+
+    import synth
+    import w8a8_quantized_verification_amd as w8
+
+    B, G, K, V = 32, 8, 4096, synth.QWEN3_VOCAB
+    M = B * (G + 1)
+    xs_l = [torch.from_numpy(synth.activations_bf16(synth.W_BATCHED, M, K, index=i)
+                             .view(np.int16).copy()).view(torch.bfloat16).to(dev) for i in range(2)]
+    draft = torch.from_numpy(synth.draft_ids(synth.W_BATCHED, B, G, V)).to(dev)
+    xt = torch.empty(w8.tiled_shape(M, K), dtype=torch.int8, device=dev)
+    xq = torch.empty(M, K, dtype=torch.int8, device=dev)
+    xsc = torch.empty(M, dtype=torch.float32, device=dev)
+    am = torch.empty(M, dtype=torch.int32, device=dev)
+    al = torch.empty(B, dtype=torch.int32, device=dev)
+    nt = torch.empty(B, dtype=torch.int32, device=dev)
+
+    def step_tiled(i):
+        w8.quantize_act_tiled(xs_l[i % 2], xq_tiled=xt, x_scale=xsc)
+        w8.lm_head_argmax_tiled_act(xt, xsc, copies[i % 2][0], copies[i % 2][1], K=K,
+                                    workspace=wsp)
+        w8.accept_from_keys(draft, argmax=am, accept_len=al, next_token=nt, workspace=wsp)
+
+    def step_rows(i):
+        w8.quantize_act(xs_l[i % 2], xq=xq, x_scale=xsc)
+        w8.lm_head_argmax(xq, xsc, copies[i % 2][0], copies[i % 2][1], workspace=wsp)
+        w8.accept_from_keys(draft, argmax=am, accept_len=al, next_token=nt, workspace=wsp)
+
+    t_t = graph_time([lambda: step_tiled(0), lambda: step_tiled(1)], replays=10) / 2
+    t_r = graph_time([lambda: step_rows(0), lambda: step_rows(1)], replays=5) / 2
+    ops = 2 * M * V * K
+    return {"B": B, "G": G, "M": M, "ms_per_step": round(t_t * 1e3, 4),
+            "verified_tokens_per_s": round(M / t_t, 1),
+            "lm_head_TOPS": round(ops / t_t / 1e12, 1),
+            "lm_head_mfma_frac": round(ops / t_t / 1e12 / INT8_PEAK_TOPS, 4),
+            "row_major_ms_per_step": round(t_r * 1e3, 4),
+            "step": "quantize_act_tiled + lm_head_argmax_tiled_act + accept_from_keys",
+            "timing": "HIP graph, 2 LM-head copies alternating"}
+
+
 def w4a8_measurement(dev, x_dev, xq, xsc, wsp):
     """The W4A8 verifier (int4 per-channel weights): the LM-head verify step
     at M = 5 (quantize_act -> lm_head_argmax_w4 -> accept_from_keys) with
@@ -797,6 +845,7 @@ def extra_measurements(dev, copies, x_dev, xq, xsc, wsp):
     t_vs = graph_time([lambda: w8.verify_sample(lg, draft, 1.0, ua, us, accept_len=al,
                                                 next_token=nt, workspace=wsp)] * 8,
                       replays=50) / 8
+    res["batched_verify_step_m288"] = batched_verify_measurement(dev, copies, wsp)
     res["w4a8_lm_head_m5"] = w4a8_measurement(dev, x_dev, xq, xsc, wsp)
     res["qwen3_8b_layer_step_m5"] = layer_step_measurement(dev, wsp)
     res["attention_scaling"] = attention_scaling(dev)

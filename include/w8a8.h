@@ -286,6 +286,19 @@ w8a8_status w8a8_lm_head_argmax_timed(const int8_t* xq, const float* x_scale,
                                       int64_t M, int64_t V, int64_t K, float* logits,
                                       void* workspace, size_t workspace_bytes,
                                       void* start_event, void* stop_event, void* stream);
+/* w8a8_lm_head_argmax for many verified rows (e.g. 32 sequences x 9 = 288)
+ * with the activations in the tiled layout of w8a8_quantize_act_tiled: the
+ * batched product (the 32 x 32 MFMA pipeline where the grid is wide enough)
+ * folds each row's maximum into the same workspace keys, so a following
+ * w8a8_accept_from_keys accepts the drafts.  Results bit-identical to
+ * w8a8_lm_head_argmax on the row-major codes.  Arguments, workspace and
+ * errors as for w8a8_lm_head_argmax, with xq_tiled (w8a8_tiled_weight_bytes(M,
+ * K) bytes, 16-byte aligned) in place of xq; any M >= 1. */
+w8a8_status w8a8_lm_head_argmax_tiled_act(const int8_t* xq_tiled, const float* x_scale,
+                                          const int8_t* wq_tiled, const float* w_scale,
+                                          int64_t M, int64_t V, int64_t K, float* logits,
+                                          void* workspace, size_t workspace_bytes,
+                                          void* stream);
 w8a8_status w8a8_accept_from_keys(void* workspace, size_t workspace_bytes,
                                   const int32_t* draft, int64_t B, int64_t G,
                                   int32_t* argmax, int32_t* accept_len,

@@ -233,6 +233,18 @@ def test_lm_head_argmax_timed_validation(lib):
     assert f(M=0, ev0=EV0) == OK
 
 
+def test_lm_head_argmax_tiled_act_validation(lib):
+    f = lib.w8a8_lm_head_argmax_tiled_act
+    ws = 288 * 64 * 256
+    assert f(None, A16, A16b, A16, 288, 151936, 4096, None, A16, ws, None) == INVALID
+    assert f(A16 + 4, A16, A16b, A16, 288, 151936, 4096, None, A16, ws, None) == INVALID
+    assert f(A16, A16, A16b, A16, 288, 151936, 4100, None, A16, ws, None) == INVALID
+    assert f(A16, A16, A16b, A16, 288, 0, 4096, None, A16, ws, None) == INVALID
+    assert f(A16, A16, A16b, A16, 288, 151936, 4096, None, A16, ws - 1, None) == WORKSPACE
+    assert f(A16, A16, A16b, A16, 288, 151936, 4096, None, A16 + 16, ws, None) == INVALID
+    assert f(None, None, None, None, 0, 151936, 4096, None, None, 0, None) in (OK, WORKSPACE)
+
+
 def test_bf16_linear_validation(lib):
     f = lib.w8a8_bf16_linear
     assert f(A16, A16b, 17, 512, 256, A16, None, None) == UNSUPPORTED

@@ -600,3 +600,76 @@ def test_lm_head_argmax_timed_matches_and_times():
         np.testing.assert_array_equal(host(nt), nt_r)
         t = e[0].elapsed_time(e[1])
         assert 0.0 < t < 100.0, t
+
+
+# --------------------------------------------------------------------------
+# batched LM-head verification with tiled activations
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("B,G,V,K", [(32, 8, 151936, 4096), (32, 8, 4099, 1024), (32, 8, 20000, 256),
+                                     (7, 8, 12000, 1040), (30, 8, 16384, 64), (25, 8, 8200, 2048),
+                                     (1, 4, 40000, 256)])
+def test_lm_head_argmax_tiled_act(B, G, V, K):
+    """quantize_act_tiled -> lm_head_argmax_tiled_act -> accept_from_keys
+    for many verified rows: logits, argmax and acceptance against the oracle
+    and against the row-major lm_head_argmax (288 rows over the full
+    vocabulary and K = 4096 take the 32 x 32 MFMA kernel with the argmax
+    folded in; the narrower grids the register-fragment kernel)."""
+    announce(f"lm_head_argmax_tiled_act B={B} G={G} V={V} K={K}")
+    R = B * (G + 1)
+    bits = synth.activations_bf16(760, R, K)
+    w = synth.weights_f32(760, V, K)
+    xq_r, xs_r = oracle.quantize_act(bits)
+    wq_r, ws_r = oracle.quantize_weight(w)
+    _, y32_r, _ = oracle.w8a8_linear(xq_r, xs_r, wq_r, ws_r)
+    am_r = oracle.argmax_rows(y32_r).reshape(B, G + 1)
+    draft = synth.draft_ids(760, B, G, V)
+    for b in range(B):
+        p = b % (G + 1)
+        draft[b, :p] = am_r[b, :p]
+    am_r, al_r, nt_r = oracle.verify_accept(y32_r, draft)
+    x = dev_bf16(bits)
+    xt, xs = w8.quantize_act_tiled(x)
+    wt, ws = w8.quantize_weight(dev(w), tiled=True)
+    d = dev(draft)
+    wsp = w8.Workspace()
+    lg = w8.lm_head_argmax_tiled_act(xt, xs, wt, ws, K=K, workspace=wsp,
+                                     logits=torch.empty(R, V, dtype=torch.float32, device=x.device))
+    am, al, nt = w8.accept_from_keys(d, workspace=wsp)
+    w8.lm_head_argmax_tiled_act(xt, xs, wt, ws, K=K, workspace=wsp)        # no logits
+    am2, al2, nt2 = w8.accept_from_keys(d, workspace=wsp)
+    xq, xs3 = w8.quantize_act(x)
+    w8.lm_head_argmax(xq, xs3, wt, ws, workspace=wsp)
+    am3, al3, nt3 = w8.accept_from_keys(d, workspace=wsp)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(lg).view(np.uint32), y32_r.view(np.uint32))
+    for a, l, n in ((am, al, nt), (am2, al2, nt2), (am3, al3, nt3)):
+        np.testing.assert_array_equal(host(a), am_r)
+        np.testing.assert_array_equal(host(l), al_r)
+        np.testing.assert_array_equal(host(n), nt_r)
+    assert not bool(wsp.get(1, x.device, use="zeroed").any())
+
+
+def test_lm_head_argmax_tiled_act_ties():
+    """Equal maxima in different 32-channel blocks, workgroups and inside one
+    block, on a grid wide enough for the 32 x 32 kernel: the lowest index
+    wins."""
+    announce("lm_head_argmax_tiled_act ties")
+    M, K, V = 5, 64, 32768
+    hot = {0: [100, 3000], 1: [5, 7], 2: [32767, 16384, 64], 3: [0, 32767], 4: [31, 32, 33]}
+    xq = torch.zeros(M, K, dtype=torch.int8, device="cuda:0")
+    wq = torch.zeros(V, K, dtype=torch.int8, device="cuda:0")
+    for r, cols in hot.items():
+        xq[r, r] = 1
+        for c in cols:
+            wq[c, r] = 3
+    xs = torch.ones(M, dtype=torch.float32, device="cuda:0")
+    ws = torch.ones(V, dtype=torch.float32, device="cuda:0")
+    wt = w8.tile_weight(wq)
+    xt = w8.tile_weight(xq)            # the same tiled layout, token rows as channels
+    draft = torch.tensor([[100, 5, 64, 0]], dtype=torch.int32, device="cuda:0")
+    w8.lm_head_argmax_tiled_act(xt, xs, wt, ws, K=K)
+    am, al, nt = w8.accept_from_keys(draft)
+    torch.cuda.synchronize()
+    assert host(am).tolist() == [100, 5, 64, 0, 31]
+    assert int(host(al)[0]) == 4 and int(host(nt)[0]) == 31

@@ -5,7 +5,8 @@ this package is its thin torch-tensor binding.  Build the library with
 ``python -m w8a8_quantized_verification_amd.build``.
 """
 from .api import (W8A8Error, Workspace, accept_from_keys, bf16_linear, linear,
-                  linear_workspace_bytes, lm_head_argmax, lm_head_verify, quantize_act,
+                  linear_workspace_bytes, lm_head_argmax, lm_head_argmax_tiled_act, lm_head_verify,
+                  quantize_act,
                   quantize_weight, sample_weights, tile_weight, tiled_shape, verify_accept,
                   verify_accept_workspace_bytes, verify_sample, verify_sample_workspace_bytes,
                   w4_shape, quantize_weight_w4, linear_w4, lm_head_argmax_w4,
@@ -14,7 +15,7 @@ from .api import (W8A8Error, Workspace, accept_from_keys, bf16_linear, linear,
 
 __all__ = [
     "W8A8Error", "Workspace", "accept_from_keys", "bf16_linear", "linear", "linear_workspace_bytes",
-    "lm_head_argmax", "lm_head_verify",
+    "lm_head_argmax", "lm_head_argmax_tiled_act", "lm_head_verify",
     "quantize_act", "quantize_weight", "tile_weight", "tiled_shape", "verify_accept",
     "verify_accept_workspace_bytes", "verify_sample", "verify_sample_workspace_bytes",
     "sample_weights", "w4_shape", "quantize_weight_w4", "linear_w4", "lm_head_argmax_w4",

@@ -41,6 +41,8 @@ SIGNATURES = {
                                    _vp, _vp, _sz, _vp]),
     "w8a8_lm_head_argmax": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _sz, _vp]),
     "w8a8_accept_from_keys": (_i32, [_vp, _sz, _vp, _i64, _i64, _vp, _vp, _vp, _vp]),
+    "w8a8_lm_head_argmax_tiled_act": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _sz,
+                                             _vp]),
     "w8a8_lm_head_argmax_timed": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _sz, _vp,
                                          _vp, _vp]),
     "w8a8_bf16_linear": (_i32, [_vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp]),

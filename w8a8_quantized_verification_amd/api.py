@@ -267,6 +267,32 @@ def lm_head_argmax(xq, x_scale, wq_tiled, w_scale, *, logits=None,
     return logits
 
 
+def lm_head_argmax_tiled_act(xq_tiled, x_scale, wq_tiled, w_scale, *, K: int, logits=None,
+                             workspace: Workspace | None = None):
+    """:func:`lm_head_argmax` with the activations in the tiled layout of
+    :func:`quantize_act_tiled` (for many rows, e.g. 32 sequences x 9).
+    Follow with :func:`accept_from_keys` on the same workspace."""
+    _need(xq_tiled, "xq_tiled", torch.int8, 4)
+    dev = xq_tiled.device
+    _need(x_scale, "x_scale", torch.float32, 1, dev)
+    _need(w_scale, "w_scale", torch.float32, 1, dev)
+    M = x_scale.shape[0]
+    V = w_scale.shape[0]
+    if tuple(xq_tiled.shape) != tiled_shape(M, K):
+        raise ValueError(f"xq_tiled must have shape {tiled_shape(M, K)}")
+    _need(wq_tiled, "wq_tiled", torch.int8, 4, dev)
+    if tuple(wq_tiled.shape) != tiled_shape(V, K):
+        raise ValueError(f"wq_tiled must have shape {tiled_shape(V, K)}")
+    if logits is not None:
+        logits = _out(logits, (M, V), torch.float32, dev, "logits")
+    ws = (workspace or _default_ws).get(int(lib().w8a8_lm_head_verify_workspace_bytes(M, 0, V, K)),
+                                        dev, use="zeroed")
+    check(lib().w8a8_lm_head_argmax_tiled_act(_ptr(xq_tiled), _ptr(x_scale), _ptr(wq_tiled),
+                                              _ptr(w_scale), M, V, K, _ptr(logits), _ptr(ws),
+                                              0 if ws is None else ws.numel(), _stream(dev)))
+    return logits
+
+
 def accept_from_keys(draft, *, want_argmax=True, argmax=None, accept_len=None, next_token=None,
                      workspace: Workspace | None = None):
     """Phase 2 of :func:`lm_head_verify`: read and reset the keys a preceding

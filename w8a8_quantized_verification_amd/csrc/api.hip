@@ -560,6 +560,23 @@ w8a8_status w8a8_linear_tiled_act(const int8_t* xq_tiled, const float* x_scale,
                     fn);
 }
 
+w8a8_status w8a8_lm_head_argmax_tiled_act(const int8_t* xq_tiled, const float* x_scale,
+                                          const int8_t* wq_tiled, const float* w_scale,
+                                          int64_t M, int64_t V, int64_t K, float* logits,
+                                          void* workspace, size_t workspace_bytes,
+                                          void* stream) {
+  static const char* fn = "w8a8_lm_head_argmax_tiled_act";
+  g_last_error.clear();
+  if (w8a8_status s = check_lm_head(fn, xq_tiled, x_scale, wq_tiled, w_scale, M, V, K, logits,
+                                    workspace, workspace_bytes))
+    return s;
+  if (M == 0) return W8A8_OK;
+  return hip_status(w8a8_launch_gemm_batched(xq_tiled, x_scale, wq_tiled, w_scale, M, V, K, true,
+                                             nullptr, logits, nullptr, workspace,
+                                             w8a8_argmax_subkeys(), w8a8_argmax_key_stride(),
+                                             reinterpret_cast<hipStream_t>(stream), true),
+                    fn);
+}
 
 // ---- attention of the verified block ----
 

@@ -82,6 +82,8 @@ hipError_t w8a8_launch_gemm_batched(const int8_t* xq, const float* x_scale, cons
                                     void* keys, int subkeys, int key_stride, hipStream_t stream,
                                     bool a_tiled = false);
 size_t w8a8_lm_head_workspace_bytes(int64_t M);
+inline int w8a8_argmax_subkeys() { return w8a8::kArgmaxSubkeys; }
+inline int w8a8_argmax_key_stride() { return w8a8::kArgmaxKeyStride; }
 hipError_t w8a8_launch_lm_head_argmax(const int8_t* xq, const float* x_scale,
                                       const int8_t* wq_tiled, const float* w_scale, int64_t M,
                                       int64_t V, int64_t K, float* logits, void* keys,

@@ -401,7 +401,7 @@ __global__ __launch_bounds__(KH * kLdsWaves * kWave) void gemm_w8a8_lds(BatchedA
 // 8 (v / 4) + 4 g + v % 4 of column r in accumulator v.
 typedef int v16i __attribute__((ext_vector_type(16)));
 
-template <int RB, int CW, int P>
+template <int RB, int CW, int P, bool kArgmax>
 __global__ __launch_bounds__(kLdsWaves * kWave) void gemm_w8a8_lds32(BatchedArgs g) {
   constexpr int FA = 2 * RB, FB = 2 * kLdsWaves * CW, F = FA + FB;
   constexpr int FW = (F + kLdsWaves - 1) / kLdsWaves;
@@ -481,16 +481,35 @@ __global__ __launch_bounds__(kLdsWaves * kWave) void gemm_w8a8_lds32(BatchedArgs
   }
   wait_vmcnt<0>();
 
+  // argmax fold: each wave transposes its (row, column) keys of one 32 x 32
+  // block at a time through LDS (the stages, free once every wave is past
+  // its last step) so that lane r < 32 reduces row r over the block's 32
+  // columns; the waves' row maxima meet in LDS and wave 0 folds each of the
+  // workgroup's rows with one device-scope atomic max.  Keys order by value
+  // and then by lower index, so their maximum is the row's argmax.
+  constexpr int kTrStride = 33;                      // u64 per transposed row (no bank clash)
+  static_assert(kLdsWaves * 32 * kTrStride * 8 <= P * STAGE, "transpose fits the stages");
+  __shared__ unsigned long long row_key[kArgmax ? kLdsWaves : 1][kArgmax ? RB * 32 : 1];
+  unsigned long long* tr = reinterpret_cast<unsigned long long*>(&stage[0][0]) +
+                           (size_t)wave * 32 * kTrStride;
+  if constexpr (kArgmax) __syncthreads();
+  unsigned long long rk[RB];
+#pragma unroll
+  for (int i = 0; i < RB; ++i) rk[i] = 0ull;
+
 #pragma unroll
   for (int j = 0; j < CW; ++j) {
-    const int n = (ng * kLdsWaves * CW + wave * CW + j) * 32 + r32;
+    const int c32 = ng * kLdsWaves * CW + wave * CW + j;   // 32-channel block
+    const int n = c32 * 32 + r32;
     const bool n_ok = n < g.N;
     const float wsn = n_ok ? g.ws[n] : 0.0f;
 #pragma unroll
-    for (int i = 0; i < RB; ++i)
+    for (int i = 0; i < RB; ++i) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int m = (mt * RB + i) * 32 + 8 * (v >> 2) + 4 * hi + (v & 3);
+        const int rr = 8 * (v >> 2) + 4 * hi + (v & 3);     // row inside the 32-block
+        const int m = (mt * RB + i) * 32 + rr;
+        unsigned long long key = 0ull;
         if (m < g.M && n_ok) {
           const int32_t a = acc[i][j][v];
           const float y = (static_cast<float>(a) * g.xs[m]) * wsn;
@@ -498,18 +517,57 @@ __global__ __launch_bounds__(kLdsWaves * kWave) void gemm_w8a8_lds32(BatchedArgs
           if (g.y_f32) g.y_f32[o] = y;
           if (g.y_bf16) g.y_bf16[o] = f32_to_bf16_rne(y);
           if (g.acc) g.acc[o] = a;
+          key = argmax_key(y, n);
+        }
+        if constexpr (kArgmax) tr[rr * kTrStride + r32] = key;
+      }
+      if constexpr (kArgmax) {
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS writes landed
+        __builtin_amdgcn_wave_barrier();
+        if (lane < 32) {
+          unsigned long long k = rk[i];
+#pragma unroll 8
+          for (int c = 0; c < 32; ++c) {
+            const unsigned long long o = tr[lane * kTrStride + c];
+            k = o > k ? o : k;
+          }
+          rk[i] = k;
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_wave_barrier();
+      }
+    }
+  }
+  if constexpr (kArgmax) {
+    if (lane < 32) {
+#pragma unroll
+      for (int i = 0; i < RB; ++i) row_key[wave][i * 32 + lane] = rk[i];
+    }
+    __syncthreads();
+    if (wave == 0) {
+      for (int r = lane; r < RB * 32; r += kWave) {
+        unsigned long long k = row_key[0][r];
+#pragma unroll
+        for (int w = 1; w < kLdsWaves; ++w) k = row_key[w][r] > k ? row_key[w][r] : k;
+        const int m = mt * RB * 32 + r;
+        if (k != 0ull && m < g.M) {
+          const size_t sub = (size_t)m * g.subkeys + (ng % g.subkeys);
+          __hip_atomic_fetch_max(&g.keys[sub * g.key_stride], k, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
         }
       }
+    }
   }
 }
 
 template <int RB, int CW, int P>
-static hipError_t launch_lds32(BatchedArgs g, hipStream_t stream) {
+static hipError_t launch_lds32(BatchedArgs g, bool argmax, hipStream_t stream) {
   g.ngroups = (g.tiles16 + 2 * kLdsWaves * CW - 1) / (2 * kLdsWaves * CW);
   g.mtiles = (g.M + 32 * RB - 1) / (32 * RB);
   const int64_t ng_padded = ((int64_t)g.ngroups + kXcds - 1) / kXcds * kXcds;
   const dim3 grid((unsigned)(ng_padded * g.mtiles)), block(kLdsWaves * kWave);
-  hipLaunchKernelGGL((gemm_w8a8_lds32<RB, CW, P>), grid, block, 0, stream, g);
+  if (argmax) hipLaunchKernelGGL((gemm_w8a8_lds32<RB, CW, P, true>), grid, block, 0, stream, g);
+  else hipLaunchKernelGGL((gemm_w8a8_lds32<RB, CW, P, false>), grid, block, 0, stream, g);
   return hipGetLastError();
 }
 
@@ -624,10 +682,12 @@ hipError_t w8a8_launch_gemm_batched(const int8_t* xq, const float* x_scale, cons
   g.keys = reinterpret_cast<unsigned long long*>(keys);
   g.subkeys = subkeys; g.key_stride = key_stride;
   const bool argmax = keys != nullptr;
-  if (a_tiled && tiled && !argmax && g.steps > 0) {
+  if (a_tiled && tiled && g.steps > 0) {
     const int64_t wg32 = lds32_workgroups(M, N);
-    if (wg32 >= kLds32DeepMinWorkgroups) return launch_lds32<2, 1, 3>(g, stream);
-    if (wg32 >= kLds32MinWorkgroups) return launch_lds32<2, 1, 4>(g, stream);
+    if (wg32 >= kLds32DeepMinWorkgroups) return launch_lds32<2, 1, 3>(g, argmax, stream);
+    if (wg32 >= kLds32MinWorkgroups) return launch_lds32<2, 1, 4>(g, argmax, stream);
+  }
+  if (a_tiled && tiled && !argmax && g.steps > 0) {
     const int64_t lwg = lds_workgroups(M, N);
     if (lwg >= kLdsMinWorkgroups)
       return launch_lds<kLdsShape.mb, kLdsShape.tn, kLdsShape.p, 1>(g, stream);
