@@ -267,13 +267,14 @@ def test_linear_batched_ragged(M, N, K):
                                    (513, 300, 2048), (5, 512, 256), (40, 33, 16), (288, 64, 0),
                                    (200, 20008, 1040), (513, 8200, 144), (288, 24576, 64),
                                    (200, 4000, 4096), (97, 4099, 1024), (288, 6144, 4096),
-                                   (300, 6152, 2048), (65, 16384, 1040)])
+                                   (300, 6152, 2048), (65, 16384, 1040), (200, 131072, 64)])
 def test_linear_tiled_activations(M, N, K):
     """quantize_act_tiled + linear_tiled_act: the codes read back through
     the tiled layout (padding zero) and every output against the oracle.
     Grids of 224+ workgroups of 64 rows x 128 channels (N >= 6144 here)
     take the 32 x 32 LDS-pipelined kernel (3 stages from 512 workgroups, 4
-    below), with ragged row blocks, channel tiles and k steps; the 16 x 16
+    below; 96 x 256 workgroups from 1024 of those, N = 131072), with ragged
+    row blocks, channel tiles and k steps; the 16 x 16
     LDS kernel takes 128-511 of its own workgroups with a step count
     divisible by 4 (q, down and the ragged 4000 / 4099-wide cases) in its
     k-sliced form; the rest the register-fragment kernel."""
@@ -608,7 +609,7 @@ def test_lm_head_argmax_timed_matches_and_times():
 
 @pytest.mark.parametrize("B,G,V,K", [(32, 8, 151936, 4096), (32, 8, 4099, 1024), (32, 8, 20000, 256),
                                      (7, 8, 12000, 1040), (30, 8, 16384, 64), (25, 8, 8200, 2048),
-                                     (1, 4, 40000, 256)])
+                                     (1, 4, 40000, 256), (30, 8, 100000, 256)])
 def test_lm_head_argmax_tiled_act(B, G, V, K):
     """quantize_act_tiled -> lm_head_argmax_tiled_act -> accept_from_keys
     for many verified rows: logits, argmax and acceptance against the oracle

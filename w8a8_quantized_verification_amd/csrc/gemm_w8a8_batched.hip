@@ -624,11 +624,20 @@ constexpr int64_t kLdsSplitMinWorkgroups = 128;
 // (960, 3 stages) 59.4 vs 66.7 us; with 160 workgroups (o, down at 4096
 // channels) it is slower (22.1 vs 19.3 us, 50.1 vs 41.6 us), so those keep
 // the k-sliced 16 x 16 form.
+// Very wide grids (the LM head over many rows) take 96 rows x 256 channels
+// per workgroup, which reads each weight block once per 96 rows instead of
+// once per 64: 288 rows through the 4096 -> 151936 LM head with the argmax
+// folded in, 353 against 447 us.
 constexpr int64_t kLds32MinWorkgroups = 224;
 constexpr int64_t kLds32DeepMinWorkgroups = 512;
+constexpr int64_t kLds32WideMinWorkgroups = 1024;
 
 static int64_t lds32_workgroups(int64_t M, int64_t N) {
   return ((N + 15) / 16 + 2 * kLdsWaves - 1) / (2 * kLdsWaves) * ((M + 63) / 64);
+}
+
+static int64_t lds32_wide_workgroups(int64_t M, int64_t N) {
+  return ((N + 15) / 16 + 4 * kLdsWaves - 1) / (4 * kLdsWaves) * ((M + 95) / 96);
 }
 
 static int64_t lds_workgroups(int64_t M, int64_t N) {
@@ -683,6 +692,8 @@ hipError_t w8a8_launch_gemm_batched(const int8_t* xq, const float* x_scale, cons
   g.subkeys = subkeys; g.key_stride = key_stride;
   const bool argmax = keys != nullptr;
   if (a_tiled && tiled && g.steps > 0) {
+    if (lds32_wide_workgroups(M, N) >= kLds32WideMinWorkgroups)
+      return launch_lds32<3, 2, 3>(g, argmax, stream);
     const int64_t wg32 = lds32_workgroups(M, N);
     if (wg32 >= kLds32DeepMinWorkgroups) return launch_lds32<2, 1, 3>(g, argmax, stream);
     if (wg32 >= kLds32MinWorkgroups) return launch_lds32<2, 1, 4>(g, argmax, stream);
