@@ -406,8 +406,11 @@ __global__ __launch_bounds__(kLdsWaves * kWave) void gemm_w8a8_lds32(BatchedArgs
   constexpr int FA = 2 * RB, FB = 2 * kLdsWaves * CW, F = FA + FB;
   constexpr int FW = (F + kLdsWaves - 1) / kLdsWaves;
   constexpr int STAGE = FW * kLdsWaves * 1024;
-  static_assert(P >= 3, "one stage read, one refilled, at least one in flight");
-  __shared__ __attribute__((aligned(1024))) int8_t stage[P][STAGE];
+  static_assert(P >= 2, "one stage read while the next one fills");
+  // the stages, also the argmax fold's transpose buffer once the k loop is done
+  constexpr int kTrBytes = kArgmax ? kLdsWaves * 32 * 33 * 8 : 0;
+  constexpr int kStages = P * STAGE > kTrBytes ? P : (kTrBytes + STAGE - 1) / STAGE;
+  __shared__ __attribute__((aligned(1024))) int8_t stage[kStages][STAGE];
 
   const int b = blockIdx.x;
   const int xcd = b % kXcds;
@@ -488,7 +491,8 @@ __global__ __launch_bounds__(kLdsWaves * kWave) void gemm_w8a8_lds32(BatchedArgs
   // workgroup's rows with one device-scope atomic max.  Keys order by value
   // and then by lower index, so their maximum is the row's argmax.
   constexpr int kTrStride = 33;                      // u64 per transposed row (no bank clash)
-  static_assert(kLdsWaves * 32 * kTrStride * 8 <= P * STAGE, "transpose fits the stages");
+  static_assert(!kArgmax || kLdsWaves * 32 * kTrStride * 8 <= kStages * STAGE,
+                "transpose fits the stages");
   __shared__ unsigned long long row_key[kArgmax ? kLdsWaves : 1][kArgmax ? RB * 32 : 1];
   unsigned long long* tr = reinterpret_cast<unsigned long long*>(&stage[0][0]) +
                            (size_t)wave * 32 * kTrStride;
@@ -624,20 +628,27 @@ constexpr int64_t kLdsSplitMinWorkgroups = 128;
 // (960, 3 stages) 59.4 vs 66.7 us; with 160 workgroups (o, down at 4096
 // channels) it is slower (22.1 vs 19.3 us, 50.1 vs 41.6 us), so those keep
 // the k-sliced 16 x 16 form.
-// Very wide grids (the LM head over many rows) take 96 rows x 256 channels
-// per workgroup, which reads each weight block once per 96 rows instead of
-// once per 64: 288 rows through the 4096 -> 151936 LM head with the argmax
-// folded in, 353 against 447 us.
+// Stage count and tile by grid width, measured at 288 rows (A/B on one
+// box): wider grids keep more workgroups per CU with fewer stages, which
+// pays more than deeper prefetch (stages beyond these were slower
+// everywhere).  q/k/v 4096 -> 6144 (240 workgroups of 64 x 128): 4 stages,
+// 22.9 us (3: 27.8, 2: 44.1); gate 4096 -> 12288 (480): 3-4 stages, 32.4-33.0
+// us (2: 46.6); gate/up 4096 -> 24576 (960): 2 stages, 55.3 us (3: 58.0);
+// the 4096 -> 151936 LM head: 96 x 128 workgroups (each weight block read
+// once per 96 rows), 2 stages, 342-363 us with the argmax folded in (64 x
+// 128, 3 stages: ~447 us).
 constexpr int64_t kLds32MinWorkgroups = 224;
 constexpr int64_t kLds32DeepMinWorkgroups = 512;
-constexpr int64_t kLds32WideMinWorkgroups = 1024;
+constexpr int64_t kLds32DoubleBufferMinWorkgroups = 768;
+constexpr int64_t kLds32WideMinWorkgroups = 2048;
 
 static int64_t lds32_workgroups(int64_t M, int64_t N) {
   return ((N + 15) / 16 + 2 * kLdsWaves - 1) / (2 * kLdsWaves) * ((M + 63) / 64);
 }
 
+// the 96-row form's grid
 static int64_t lds32_wide_workgroups(int64_t M, int64_t N) {
-  return ((N + 15) / 16 + 4 * kLdsWaves - 1) / (4 * kLdsWaves) * ((M + 95) / 96);
+  return ((N + 15) / 16 + 2 * kLdsWaves - 1) / (2 * kLdsWaves) * ((M + 95) / 96);
 }
 
 static int64_t lds_workgroups(int64_t M, int64_t N) {
@@ -693,8 +704,9 @@ hipError_t w8a8_launch_gemm_batched(const int8_t* xq, const float* x_scale, cons
   const bool argmax = keys != nullptr;
   if (a_tiled && tiled && g.steps > 0) {
     if (lds32_wide_workgroups(M, N) >= kLds32WideMinWorkgroups)
-      return launch_lds32<3, 2, 3>(g, argmax, stream);
+      return launch_lds32<3, 1, 2>(g, argmax, stream);
     const int64_t wg32 = lds32_workgroups(M, N);
+    if (wg32 >= kLds32DoubleBufferMinWorkgroups) return launch_lds32<2, 1, 2>(g, argmax, stream);
     if (wg32 >= kLds32DeepMinWorkgroups) return launch_lds32<2, 1, 3>(g, argmax, stream);
     if (wg32 >= kLds32MinWorkgroups) return launch_lds32<2, 1, 4>(g, argmax, stream);
   }
