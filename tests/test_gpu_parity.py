@@ -272,9 +272,10 @@ def test_linear_tiled_activations(M, N, K):
     """quantize_act_tiled + linear_tiled_act: the codes read back through
     the tiled layout (padding zero) and every output against the oracle.
     Grids of 224+ workgroups of 64 rows x 128 channels (N >= 6144 here)
-    take the 32 x 32 LDS-pipelined kernel (3 stages from 512 workgroups, 4
-    below; 96 x 256 workgroups from 1024 of those, N = 131072), with ragged
-    row blocks, channel tiles and k steps; the 16 x 16
+    take the 32 x 32 LDS-pipelined kernel (4 stages below 512 workgroups, 3
+    below 768, 2 above; 96-row workgroups with 2 stages from 2048 of those,
+    N = 131072), with ragged row blocks, channel tiles and k steps; the
+    16 x 16
     LDS kernel takes 128-511 of its own workgroups with a step count
     divisible by 4 (q, down and the ragged 4000 / 4099-wide cases) in its
     k-sliced form; the rest the register-fragment kernel."""
@@ -613,9 +614,11 @@ def test_lm_head_argmax_timed_matches_and_times():
 def test_lm_head_argmax_tiled_act(B, G, V, K):
     """quantize_act_tiled -> lm_head_argmax_tiled_act -> accept_from_keys
     for many verified rows: logits, argmax and acceptance against the oracle
-    and against the row-major lm_head_argmax (288 rows over the full
-    vocabulary and K = 4096 take the 32 x 32 MFMA kernel with the argmax
-    folded in; the narrower grids the register-fragment kernel)."""
+    and against the row-major lm_head_argmax (the wide grids take the
+    32 x 32 MFMA kernel with the argmax folded in: 96-row workgroups for 288
+    rows over the full vocabulary and for the 100000-wide case, 64-row ones
+    with 2-4 stages for the others from 20000 channels up; the narrower
+    grids the register-fragment kernel)."""
     announce(f"lm_head_argmax_tiled_act B={B} G={G} V={V} K={K}")
     R = B * (G + 1)
     bits = synth.activations_bf16(760, R, K)
