@@ -623,11 +623,10 @@ constexpr int64_t kLdsSplitMinWorkgroups = 128;
 
 // The 32 x 32 form (64 rows x 128 channels per workgroup) where its grid
 // fills the chip, measured at 288 rows against the 16 x 16 pipeline:
-// q/k/v fused 4096 -> 6144 (240 workgroups, 4 stages) 22.8 vs 35.5 us,
-// gate 4096 -> 12288 (480) 33.3 vs 39.1 us, gate/up fused 4096 -> 24576
-// (960, 3 stages) 59.4 vs 66.7 us; with 160 workgroups (o, down at 4096
-// channels) it is slower (22.1 vs 19.3 us, 50.1 vs 41.6 us), so those keep
-// the k-sliced 16 x 16 form.
+// q/k/v fused 4096 -> 6144 (240 workgroups) 22.8 vs 35.5 us, gate 4096 ->
+// 12288 (480) 33.3 vs 39.1 us, gate/up fused 4096 -> 24576 (960) 55-59 vs
+// 67 us; with 160 workgroups (o, down at 4096 channels) it is slower (22.1
+// vs 19.3 us, 50.1 vs 41.6 us), so those keep the k-sliced 16 x 16 form.
 // Stage count and tile by grid width, measured at 288 rows (A/B on one
 // box): wider grids keep more workgroups per CU with fewer stages, which
 // pays more than deeper prefetch (stages beyond these were slower
