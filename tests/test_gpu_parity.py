@@ -255,9 +255,17 @@ def test_linear_batched_m288(N, K, tiled):
 
 
 @pytest.mark.parametrize("M,N,K", [(17, 65, 80), (96, 64, 64), (97, 4099, 1040), (200, 130, 16),
-                                   (513, 300, 2048)])
+                                   (513, 300, 2048), (97, 4099, 1024), (300, 8200, 2048),
+                                   (513, 20000, 64), (200, 131072, 64), (100, 4096, 256),
+                                   (33, 30000, 128)])
 def test_linear_batched_ragged(M, N, K):
-    """Row tiles of 96 with ragged last tiles in M, N and K (tiled layout)."""
+    """Ragged last tiles in M, N and K (tiled weights, row-major
+    activations).  K a multiple of 64 sends wide grids to the LDS-pipelined
+    kernels, which gather each 16-row activation fragment from the
+    row-major rows (rows past M repeat the last row and are dropped):
+    32 x 32 with 4, 3 or 2 stages and the 96-row form (N >= 8200 here),
+    the 16 x 16 k-sliced form (4096 x 256); the rest take the register
+    kernel."""
     announce(f"linear batched ragged M={M} N={N} K={K}")
     run_linear_case(M, N, K, seed=330 + M, tiled=True)
 

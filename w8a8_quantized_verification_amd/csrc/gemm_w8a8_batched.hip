@@ -278,7 +278,7 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
-template <int MB, int TN, int P, int KH, bool kArgmax>
+template <int MB, int TN, int P, int KH, bool kArgmax, bool kRowA = false>
 __global__ __launch_bounds__(KH * kLdsWaves * kWave) void gemm_w8a8_lds(BatchedArgs g) {
   constexpr int FA = 2 * MB, FB = 2 * TN, F = FA + FB;   // fragments per k step
   // each wave issues FW loads per k step; the F..4*FW-1 padding loads fetch
@@ -317,7 +317,14 @@ __global__ __launch_bounds__(KH * kLdsWaves * kWave) void gemm_w8a8_lds(BatchedA
       src[j] = g.xq + (lane << 4);
     } else if (f < FA) {
       const int rb = mt * FA + f;
-      src[j] = g.xq + ((size_t)(rb < mblocks ? rb : 0) * (size_t)steps << 10) + (lane << 4);
+      if constexpr (kRowA) {
+        // row-major activations, fetched into the tiled lane order (see
+        // gemm_w8a8_lds32)
+        const int row = min(rb * 16 + (lane & 15), g.M - 1);
+        src[j] = g.xq + (size_t)row * (size_t)g.K + ((lane >> 4) << 4);
+      } else {
+        src[j] = g.xq + ((size_t)(rb < mblocks ? rb : 0) * (size_t)steps << 10) + (lane << 4);
+      }
     } else {
       const int t16 = ng * FB + (f - FA);
       src[j] = g.wq + ((size_t)(t16 < g.tiles16 ? t16 : 0) * (size_t)steps << 10) + (lane << 4);
@@ -327,8 +334,11 @@ __global__ __launch_bounds__(KH * kLdsWaves * kWave) void gemm_w8a8_lds(BatchedA
   auto issue = [&](int p, int s) {
     s = s0 + min(s, nmax - 1);
 #pragma unroll
-    for (int j = 0; j < FW; ++j)
-      lds_dma16(src[j] + ((size_t)s << 10), &stage[kh][p][(wave + kLdsWaves * j) * 1024]);
+    for (int j = 0; j < FW; ++j) {
+      const int f = wave + kLdsWaves * j;
+      const size_t off = (kRowA && f < FA) ? (size_t)s * 64 : ((size_t)s << 10);
+      lds_dma16(src[j] + off, &stage[kh][p][f * 1024]);
+    }
   };
 
   v4i acc[MB][TN];
@@ -401,7 +411,7 @@ __global__ __launch_bounds__(KH * kLdsWaves * kWave) void gemm_w8a8_lds(BatchedA
 // 8 (v / 4) + 4 g + v % 4 of column r in accumulator v.
 typedef int v16i __attribute__((ext_vector_type(16)));
 
-template <int RB, int CW, int P, bool kArgmax>
+template <int RB, int CW, int P, bool kArgmax, bool kRowA = false>
 __global__ __launch_bounds__(kLdsWaves * kWave) void gemm_w8a8_lds32(BatchedArgs g) {
   constexpr int FA = 2 * RB, FB = 2 * kLdsWaves * CW, F = FA + FB;
   constexpr int FW = (F + kLdsWaves - 1) / kLdsWaves;
@@ -432,7 +442,16 @@ __global__ __launch_bounds__(kLdsWaves * kWave) void gemm_w8a8_lds32(BatchedArgs
       src[j] = g.xq + (lane << 4);
     } else if (f < FA) {
       const int rb = mt * FA + f;
-      src[j] = g.xq + ((size_t)(rb < mblocks ? rb : 0) * (size_t)steps << 10) + (lane << 4);
+      if constexpr (kRowA) {
+        // row-major activations (K a multiple of 64): lane l fetches row
+        // 16 rb + l % 16, bytes 16 (l / 16) .. +15 of the step, landing at
+        // l * 16 as in the tiled layout; rows past M repeat row M - 1 (they
+        // only feed accumulator rows the epilogue drops)
+        const int row = min(rb * 16 + (lane & 15), g.M - 1);
+        src[j] = g.xq + (size_t)row * (size_t)g.K + ((lane >> 4) << 4);
+      } else {
+        src[j] = g.xq + ((size_t)(rb < mblocks ? rb : 0) * (size_t)steps << 10) + (lane << 4);
+      }
     } else {
       const int t16 = ng * FB + (f - FA);
       src[j] = g.wq + ((size_t)(t16 < g.tiles16 ? t16 : 0) * (size_t)steps << 10) + (lane << 4);
@@ -441,8 +460,11 @@ __global__ __launch_bounds__(kLdsWaves * kWave) void gemm_w8a8_lds32(BatchedArgs
   auto issue = [&](int p, int s) {
     s = min(s, steps - 1);
 #pragma unroll
-    for (int j = 0; j < FW; ++j)
-      lds_dma16(src[j] + ((size_t)s << 10), &stage[p][(wave + kLdsWaves * j) * 1024]);
+    for (int j = 0; j < FW; ++j) {
+      const int f = wave + kLdsWaves * j;
+      const size_t off = (kRowA && f < FA) ? (size_t)s * 64 : ((size_t)s << 10);
+      lds_dma16(src[j] + off, &stage[p][f * 1024]);
+    }
   };
 
   const int r32 = lane & 31, hi = lane >> 5;
@@ -564,14 +586,16 @@ __global__ __launch_bounds__(kLdsWaves * kWave) void gemm_w8a8_lds32(BatchedArgs
   }
 }
 
-template <int RB, int CW, int P>
+template <int RB, int CW, int P, bool kRowA = false>
 static hipError_t launch_lds32(BatchedArgs g, bool argmax, hipStream_t stream) {
   g.ngroups = (g.tiles16 + 2 * kLdsWaves * CW - 1) / (2 * kLdsWaves * CW);
   g.mtiles = (g.M + 32 * RB - 1) / (32 * RB);
   const int64_t ng_padded = ((int64_t)g.ngroups + kXcds - 1) / kXcds * kXcds;
   const dim3 grid((unsigned)(ng_padded * g.mtiles)), block(kLdsWaves * kWave);
-  if (argmax) hipLaunchKernelGGL((gemm_w8a8_lds32<RB, CW, P, true>), grid, block, 0, stream, g);
-  else hipLaunchKernelGGL((gemm_w8a8_lds32<RB, CW, P, false>), grid, block, 0, stream, g);
+  if (argmax)
+    hipLaunchKernelGGL((gemm_w8a8_lds32<RB, CW, P, true, kRowA>), grid, block, 0, stream, g);
+  else
+    hipLaunchKernelGGL((gemm_w8a8_lds32<RB, CW, P, false, kRowA>), grid, block, 0, stream, g);
   return hipGetLastError();
 }
 
@@ -589,13 +613,13 @@ struct BatchedShape {
 
 // (no fused argmax: the LM-head argmax path passes row-major activations,
 // which take the register-fragment kernel)
-template <int MB, int TN, int P, int KH>
+template <int MB, int TN, int P, int KH, bool kRowA = false>
 static hipError_t launch_lds(BatchedArgs g, hipStream_t stream) {
   g.ngroups = (g.tiles16 + 2 * TN - 1) / (2 * TN);
   g.mtiles = (g.M + 32 * MB - 1) / (32 * MB);
   const int64_t ng_padded = ((int64_t)g.ngroups + kXcds - 1) / kXcds * kXcds;
   const dim3 grid((unsigned)(ng_padded * g.mtiles)), block(KH * kLdsWaves * kWave);
-  hipLaunchKernelGGL((gemm_w8a8_lds<MB, TN, P, KH, false>), grid, block, 0, stream, g);
+  hipLaunchKernelGGL((gemm_w8a8_lds<MB, TN, P, KH, false, kRowA>), grid, block, 0, stream, g);
   return hipGetLastError();
 }
 constexpr BatchedShape kWide{3, 4, 1, 4, 4};
@@ -662,6 +686,41 @@ static int64_t batched_workgroups(const BatchedShape& c, int64_t M, int64_t N) {
   return ngroups * mtiles;
 }
 
+// The LDS-pipelined kernels where the grid suits them (returns false to
+// leave the shape to the register-fragment kernel).
+template <bool kRowA>
+static bool launch_lds_path(const BatchedArgs& g, int64_t M, int64_t N, bool argmax,
+                            hipStream_t stream, hipError_t* err) {
+  if (lds32_wide_workgroups(M, N) >= kLds32WideMinWorkgroups) {
+    *err = launch_lds32<3, 1, 2, kRowA>(g, argmax, stream);
+    return true;
+  }
+  const int64_t wg32 = lds32_workgroups(M, N);
+  if (wg32 >= kLds32DoubleBufferMinWorkgroups) {
+    *err = launch_lds32<2, 1, 2, kRowA>(g, argmax, stream);
+    return true;
+  }
+  if (wg32 >= kLds32DeepMinWorkgroups) {
+    *err = launch_lds32<2, 1, 3, kRowA>(g, argmax, stream);
+    return true;
+  }
+  if (wg32 >= kLds32MinWorkgroups) {
+    *err = launch_lds32<2, 1, 4, kRowA>(g, argmax, stream);
+    return true;
+  }
+  if (argmax) return false;   // (the 16 x 16 pipeline has no argmax fold)
+  const int64_t lwg = lds_workgroups(M, N);
+  if (lwg >= kLdsMinWorkgroups) {
+    *err = launch_lds<kLdsShape.mb, kLdsShape.tn, kLdsShape.p, 1, kRowA>(g, stream);
+    return true;
+  }
+  if (lwg >= kLdsSplitMinWorkgroups && g.steps % kLdsSplit == 0) {
+    *err = launch_lds<kLdsShape.mb, kLdsShape.tn, kLdsSplitStages, kLdsSplit, kRowA>(g, stream);
+    return true;
+  }
+  return false;
+}
+
 template <int MB, int TN, int WR, int KW, int U, bool TA>
 static hipError_t launch_batched(BatchedArgs g, bool tiled, bool argmax, hipStream_t stream) {
   static_assert((KW - 1) * WR * MB * TN * 1024 <= 65536, "LDS reduction buffer");
@@ -701,20 +760,13 @@ hipError_t w8a8_launch_gemm_batched(const int8_t* xq, const float* x_scale, cons
   g.keys = reinterpret_cast<unsigned long long*>(keys);
   g.subkeys = subkeys; g.key_stride = key_stride;
   const bool argmax = keys != nullptr;
-  if (a_tiled && tiled && g.steps > 0) {
-    if (lds32_wide_workgroups(M, N) >= kLds32WideMinWorkgroups)
-      return launch_lds32<3, 1, 2>(g, argmax, stream);
-    const int64_t wg32 = lds32_workgroups(M, N);
-    if (wg32 >= kLds32DoubleBufferMinWorkgroups) return launch_lds32<2, 1, 2>(g, argmax, stream);
-    if (wg32 >= kLds32DeepMinWorkgroups) return launch_lds32<2, 1, 3>(g, argmax, stream);
-    if (wg32 >= kLds32MinWorkgroups) return launch_lds32<2, 1, 4>(g, argmax, stream);
-  }
-  if (a_tiled && tiled && !argmax && g.steps > 0) {
-    const int64_t lwg = lds_workgroups(M, N);
-    if (lwg >= kLdsMinWorkgroups)
-      return launch_lds<kLdsShape.mb, kLdsShape.tn, kLdsShape.p, 1>(g, stream);
-    if (lwg >= kLdsSplitMinWorkgroups && g.steps % kLdsSplit == 0)
-      return launch_lds<kLdsShape.mb, kLdsShape.tn, kLdsSplitStages, kLdsSplit>(g, stream);
+  // The LDS-pipelined kernels take tiled activations, or row-major ones
+  // when K is a multiple of 64 (each fragment then gathered from 16 rows
+  // into the same lane order)
+  if (tiled && g.steps > 0) {
+    hipError_t e = hipSuccess;
+    if (a_tiled && launch_lds_path<false>(g, M, N, argmax, stream, &e)) return e;
+    if (!a_tiled && K % 64 == 0 && launch_lds_path<true>(g, M, N, argmax, stream, &e)) return e;
   }
   if (a_tiled) {
     if (batched_workgroups(kTiledAWide, M, N) >= kMinWorkgroups)
