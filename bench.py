@@ -307,11 +307,10 @@ def ingest_pmc_batched(dirs, command):
 
     import synth
     M = 288
-    # row-major activations run the register-fragment kernel; tiled ones that
-    # kernel's tiled form or the LDS-pipelined kernel, by shape
-    variants = (("row_major_act", lambda k: "gemm_w8a8_batched" in k and ", false>(" in k),
-                ("tiled_act", lambda k: "gemm_w8a8_lds" in k or
-                 ("gemm_w8a8_batched" in k and ", true>(" in k)))
+    # both activation layouts run the register-fragment kernel or one of the
+    # LDS-pipelined ones, by shape; the probe's dispatch order tells them apart
+    batched_kernel = lambda k: "gemm_w8a8_batched" in k or "gemm_w8a8_lds" in k  # noqa: E731
+    variants = (("row_major_act", batched_kernel), ("tiled_act", batched_kernel))
     per = {(n, v): {} for n in BATCHED_SHAPES for v, _ in variants}
     kname = {}
     for d in dirs:
