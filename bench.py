@@ -572,6 +572,20 @@ def layer_measurement(dev, wsp, M, workload):
         e = {"name": lin.name, "N": lin.N, "K": lin.K, "copies": nc,
              "us": round(t * 1e6, 2), "GBs": round(b / t / 1e9, 1),
              "TOPS": round(tops, 1), "mfma_frac": round(tops / INT8_PEAK_TOPS, 4)}
+        if M <= 16:
+            # the in-build bf16 GEMM at the same shape (twice the weight bytes),
+            # over its own rotating bf16 copies
+            ncb = rotation_copies(lin.N, 2 * lin.K)
+            wb = [synth.weights_device(workload, 2000 + 200 * li + c, lin.N, lin.K, dev)
+                  .to(torch.bfloat16) for c in range(ncb)]
+            yb16 = torch.empty(M, lin.N, dtype=torch.bfloat16, device=dev)
+            tb = graph_time([(lambda c=c: w8.bf16_linear(x, wb[c], y_bf16=yb16))
+                             for c in range(ncb)], replays=10) / ncb
+            e.update({"bf16_us": round(tb * 1e6, 2),
+                      "bf16_GBs": round((2 * lin.N * lin.K + 2 * M * lin.K + 2 * M * lin.N)
+                                        / tb / 1e9, 1),
+                      "time_ratio_bf16_over_w8a8": round(tb / t, 3)})
+            del wb
         if M > 16:
             # the same product with the activations quantized into the tiled layout
             xt, xts = w8.quantize_act_tiled(x)
@@ -587,6 +601,10 @@ def layer_measurement(dev, wsp, M, workload):
     tot_ops = sum(2 * M * l.N * l.K for l in synth.QWEN3_8B_LAYER)
     tot_t = sum(e["us"] for e in layer) / 1e6
     extra = {}
+    if M <= 16:
+        tb = sum(e["bf16_us"] for e in layer) / 1e6
+        extra = {"bf16_sum_us": round(tb * 1e6, 2),
+                 "time_ratio_bf16_over_w8a8": round(tb / tot_t, 3)}
     if M > 16:
         tt = sum(e["tiled_act_us"] for e in layer) / 1e6
         extra = {"tiled_act_sum_us": round(tt * 1e6, 2),
