@@ -64,6 +64,10 @@ def parse_args():
     p.add_argument("--ingest-trace", metavar="TRACE_DIR",
                    help="turn a rocprofv3 --kernel-trace --stats csv run into a summary")
     p.add_argument("--command", default="", help="the command that produced the ingested run")
+    p.add_argument("--batched-verify-probe", action="store_true",
+                   help="only the 288-row LM-head verification step (for rocprofv3 --kernel-trace)")
+    p.add_argument("--ingest-batched-trace", metavar="TRACE_DIR",
+                   help="summary of a --kernel-trace --stats run of --batched-verify-probe")
     p.add_argument("--attention-probe", action="store_true",
                    help="only the attention scaling runs (for rocprofv3 --kernel-trace)")
     p.add_argument("--ingest-attention-trace", metavar="TRACE_DIR",
@@ -380,6 +384,10 @@ def main():
         ingest_trace(args.ingest_trace, args.command,
                      os.path.join(ROOT, "profiles", "lm_head_verify_m5_kernel_trace.txt"))
         return
+    if args.ingest_batched_trace:
+        ingest_trace(args.ingest_batched_trace, args.command,
+                     os.path.join(ROOT, "profiles", "lm_head_verify_m288_kernel_trace.txt"))
+        return
     if args.ingest_attention_trace:
         ingest_attention_trace(args.ingest_attention_trace, args.command,
                                os.path.join(ROOT, "profiles", "verify_attention_kernel_trace.txt"))
@@ -408,6 +416,10 @@ def main():
 
     M, K, V, G, B = 5, 4096, synth.QWEN3_VOCAB, 4, 1
     copies = [make_weight(V, K, synth.W_LM_HEAD, 1000 + i, dev, tiled=True) for i in range(2)]
+    if args.batched_verify_probe:
+        print(json.dumps({"batched_verify_step_m288":
+                          batched_verify_measurement(dev, copies, w8.Workspace())}), flush=True)
+        return
     n_x = 8
     xs_host = [synth.activations_bf16(synth.W_LM_HEAD, M, K, index=i) for i in range(n_x)]
     x_dev = [torch.from_numpy(x.view(np.int16).copy()).view(torch.bfloat16).to(dev) for x in xs_host]
