@@ -479,7 +479,8 @@ def test_graph_replay_matches_eager(forced_split):
 
 @pytest.mark.parametrize("B,G,V,K", [(1, 4, 512, 256), (1, 4, 151936, 4096), (32, 8, 4099, 1024),
                                      (1, 7, 5000, 5120), (3, 0, 1000, 256), (2, 3, 17, 64),
-                                     (1, 15, 40000, 2048)])
+                                     (1, 15, 40000, 2048), (8, 1, 3000, 512), (4, 3, 20000, 1024),
+                                     (3, 5, 9000, 256)])
 def test_lm_head_verify(B, G, V, K):
     """Fused LM-head linear + argmax + acceptance against the oracle and
     against the separate linear -> verify_accept path."""
