@@ -408,18 +408,22 @@ __global__ __launch_bounds__(KH * kLdsWaves * kWave) void gemm_w8a8_lds(BatchedA
 // units; for the 32-wide half h of a step, lane l (r = l % 32, g = l / 32)
 // reads unit 2*b + r/16 of its 32-block b at tile lane (r % 16) + 16 (2h +
 // g), for both operands, so A and B pair the same k.  Lane l gets rows
-// 8 (v / 4) + 4 g + v % 4 of column r in accumulator v.
+// 8 (v / 4) + 4 g + v % 4 of column r in accumulator v.  The launch bound
+// holds every form to 128 registers, so four workgroups share a CU (with
+// the argmax fold's transpose inside the stages, the 96-row form's LDS
+// allows four as well: 288 rows x 151936 channels 306 us against 362-384
+// at three per CU).
 typedef int v16i __attribute__((ext_vector_type(16)));
 
 template <int RB, int CW, int P, bool kArgmax, bool kRowA = false>
-__global__ __launch_bounds__(kLdsWaves * kWave) void gemm_w8a8_lds32(BatchedArgs g) {
+__global__ __launch_bounds__(kLdsWaves * kWave, 4) void gemm_w8a8_lds32(BatchedArgs g) {
   constexpr int FA = 2 * RB, FB = 2 * kLdsWaves * CW, F = FA + FB;
   constexpr int FW = (F + kLdsWaves - 1) / kLdsWaves;
   constexpr int STAGE = FW * kLdsWaves * 1024;
   static_assert(P >= 2, "one stage read while the next one fills");
   // the stages, also the argmax fold's transpose buffer once the k loop is done
-  constexpr int kTrBytes = kArgmax ? kLdsWaves * 32 * 33 * 8 : 0;
-  constexpr int kStages = P * STAGE > kTrBytes ? P : (kTrBytes + STAGE - 1) / STAGE;
+  constexpr int kTrBytes = kArgmax ? kLdsWaves * 32 * 32 * 8 : 0;
+  constexpr int kStages = P * STAGE >= kTrBytes ? P : (kTrBytes + STAGE - 1) / STAGE;
   __shared__ __attribute__((aligned(1024))) int8_t stage[kStages][STAGE];
 
   const int b = blockIdx.x;
@@ -512,7 +516,11 @@ __global__ __launch_bounds__(kLdsWaves * kWave) void gemm_w8a8_lds32(BatchedArgs
   // columns; the waves' row maxima meet in LDS and wave 0 folds each of the
   // workgroup's rows with one device-scope atomic max.  Keys order by value
   // and then by lower index, so their maximum is the row's argmax.
-  constexpr int kTrStride = 33;                      // u64 per transposed row (no bank clash)
+  // 32 u64 per transposed row, column c of row r stored at c ^ r: the
+  // half-wave's writes of one row and each lane's reads of its own row
+  // across the columns both touch 32 distinct bank pairs, with no padding
+  // (so the transpose fits in the stages of the 96-row form)
+  constexpr int kTrStride = 32;
   static_assert(!kArgmax || kLdsWaves * 32 * kTrStride * 8 <= kStages * STAGE,
                 "transpose fits the stages");
   __shared__ unsigned long long row_key[kArgmax ? kLdsWaves : 1][kArgmax ? RB * 32 : 1];
@@ -545,7 +553,7 @@ __global__ __launch_bounds__(kLdsWaves * kWave) void gemm_w8a8_lds32(BatchedArgs
           if (g.acc) g.acc[o] = a;
           key = argmax_key(y, n);
         }
-        if constexpr (kArgmax) tr[rr * kTrStride + r32] = key;
+        if constexpr (kArgmax) tr[rr * kTrStride + (r32 ^ rr)] = key;
       }
       if constexpr (kArgmax) {
         __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS writes landed
@@ -554,7 +562,7 @@ __global__ __launch_bounds__(kLdsWaves * kWave) void gemm_w8a8_lds32(BatchedArgs
           unsigned long long k = rk[i];
 #pragma unroll 8
           for (int c = 0; c < 32; ++c) {
-            const unsigned long long o = tr[lane * kTrStride + c];
+            const unsigned long long o = tr[lane * kTrStride + (c ^ lane)];
             k = o > k ? o : k;
           }
           rk[i] = k;
@@ -658,7 +666,7 @@ constexpr int64_t kLdsSplitMinWorkgroups = 128;
 // 22.9 us (3: 27.8, 2: 44.1); gate 4096 -> 12288 (480): 3-4 stages, 32.4-33.0
 // us (2: 46.6); gate/up 4096 -> 24576 (960): 2 stages, 55.3 us (3: 58.0);
 // the 4096 -> 151936 LM head: 96 x 128 workgroups (each weight block read
-// once per 96 rows), 2 stages, 342-363 us with the argmax folded in (64 x
+// once per 96 rows), 2 stages, ~306 us with the argmax folded in (64 x
 // 128, 3 stages: ~447 us).
 constexpr int64_t kLds32MinWorkgroups = 224;
 constexpr int64_t kLds32DeepMinWorkgroups = 512;
