@@ -409,10 +409,11 @@ __global__ __launch_bounds__(KH * kLdsWaves * kWave) void gemm_w8a8_lds(BatchedA
 // reads unit 2*b + r/16 of its 32-block b at tile lane (r % 16) + 16 (2h +
 // g), for both operands, so A and B pair the same k.  Lane l gets rows
 // 8 (v / 4) + 4 g + v % 4 of column r in accumulator v.  The launch bound
-// holds every form to 128 registers, so four workgroups share a CU (with
-// the argmax fold's transpose inside the stages, the 96-row form's LDS
-// allows four as well: 288 rows x 151936 channels 306 us against 362-384
-// at three per CU).
+// holds every form to 128 registers (at least four workgroups per CU).
+// With the argmax fold's transpose and row maxima inside the stages, the
+// 96-row form (90 registers, 32 KB of LDS) runs five per CU: 288 rows x
+// 151936 channels ~288 us, against ~309 at four per CU and 362-384 at
+// three (the transpose padded, in LDS of its own).
 typedef int v16i __attribute__((ext_vector_type(16)));
 
 template <int RB, int CW, int P, bool kArgmax, bool kRowA = false>
@@ -523,7 +524,9 @@ __global__ __launch_bounds__(kLdsWaves * kWave, 4) void gemm_w8a8_lds32(BatchedA
   constexpr int kTrStride = 32;
   static_assert(!kArgmax || kLdsWaves * 32 * kTrStride * 8 <= kStages * STAGE,
                 "transpose fits the stages");
-  __shared__ unsigned long long row_key[kArgmax ? kLdsWaves : 1][kArgmax ? RB * 32 : 1];
+  // each wave's RB * 32 row maxima go to the start of its own transpose
+  // region once its last transpose has been read (no LDS beyond the stages)
+  static_assert(RB * 32 <= 32 * kTrStride, "row maxima fit a transpose region");
   unsigned long long* tr = reinterpret_cast<unsigned long long*>(&stage[0][0]) +
                            (size_t)wave * 32 * kTrStride;
   if constexpr (kArgmax) __syncthreads();
@@ -575,14 +578,18 @@ __global__ __launch_bounds__(kLdsWaves * kWave, 4) void gemm_w8a8_lds32(BatchedA
   if constexpr (kArgmax) {
     if (lane < 32) {
 #pragma unroll
-      for (int i = 0; i < RB; ++i) row_key[wave][i * 32 + lane] = rk[i];
+      for (int i = 0; i < RB; ++i) tr[i * 32 + lane] = rk[i];
     }
     __syncthreads();
     if (wave == 0) {
       for (int r = lane; r < RB * 32; r += kWave) {
-        unsigned long long k = row_key[0][r];
+        const unsigned long long* rows0 = reinterpret_cast<const unsigned long long*>(&stage[0][0]);
+        unsigned long long k = rows0[r];
 #pragma unroll
-        for (int w = 1; w < kLdsWaves; ++w) k = row_key[w][r] > k ? row_key[w][r] : k;
+        for (int w = 1; w < kLdsWaves; ++w) {
+          const unsigned long long o = rows0[(size_t)w * 32 * kTrStride + r];
+          k = o > k ? o : k;
+        }
         const int m = mt * RB * 32 + r;
         if (k != 0ull && m < g.M) {
           const size_t sub = (size_t)m * g.subkeys + (ng % g.subkeys);
@@ -666,7 +673,7 @@ constexpr int64_t kLdsSplitMinWorkgroups = 128;
 // 22.9 us (3: 27.8, 2: 44.1); gate 4096 -> 12288 (480): 3-4 stages, 32.4-33.0
 // us (2: 46.6); gate/up 4096 -> 24576 (960): 2 stages, 55.3 us (3: 58.0);
 // the 4096 -> 151936 LM head: 96 x 128 workgroups (each weight block read
-// once per 96 rows), 2 stages, ~306 us with the argmax folded in (64 x
+// once per 96 rows), 2 stages, ~288 us with the argmax folded in (64 x
 // 128, 3 stages: ~447 us).
 constexpr int64_t kLds32MinWorkgroups = 224;
 constexpr int64_t kLds32DeepMinWorkgroups = 512;
