@@ -686,3 +686,41 @@ def test_lm_head_argmax_tiled_act_ties():
     torch.cuda.synchronize()
     assert host(am).tolist() == [100, 5, 64, 0, 31]
     assert int(host(al)[0]) == 4 and int(host(nt)[0]) == 31
+
+
+def test_lm_head_argmax_ties_96_row_workgroups():
+    """Ties on the grid that takes the 96-row 32 x 32 workgroups (288 rows,
+    100000 channels): each row reads one k, whose equal maxima sit in one
+    32-channel block, in adjacent blocks, in different workgroups and in the
+    last (partial) tile; the lowest index wins for tiled and row-major
+    activations alike."""
+    announce("lm_head_argmax ties, 96-row workgroups")
+    M, K, V = 288, 64, 100000
+    xq = torch.zeros(M, K, dtype=torch.int8, device="cuda:0")
+    wq = torch.zeros(V, K, dtype=torch.int8, device="cuda:0")
+    expect = []
+    for k in range(K):
+        base = (k * 1543) % (V - 64)
+        cols = {base + 31, base + 32, (k * 7919 + 50000) % V, V - 1 - k, base + 33}
+        for c in cols:
+            wq[c, k] = 3
+        expect.append(min(cols))
+    rows = np.arange(M) % K
+    xq[torch.arange(M, device="cuda:0"), torch.from_numpy(rows).long().to("cuda:0")] = 1
+    xs = torch.ones(M, dtype=torch.float32, device="cuda:0")
+    ws = torch.ones(V, dtype=torch.float32, device="cuda:0")
+    wt = w8.tile_weight(wq)
+    xt = w8.tile_weight(xq)            # the same tiled layout, token rows as channels
+    B, G = 32, 8
+    want = np.array([expect[r] for r in rows], dtype=np.int32)
+    draft = torch.from_numpy(want.reshape(B, G + 1)[:, :G].copy()).to("cuda:0")
+    for tiled_act in (True, False):
+        if tiled_act:
+            w8.lm_head_argmax_tiled_act(xt, xs, wt, ws, K=K)
+        else:
+            w8.lm_head_argmax(xq, xs, wt, ws)
+        am, al, nt = w8.accept_from_keys(draft)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(am), want)
+        assert host(al).tolist() == [G] * B
+        np.testing.assert_array_equal(host(nt), want.reshape(B, G + 1)[:, G])
