@@ -167,7 +167,7 @@ def _csv_rows(d, suffix):
     return rows
 
 
-GEMM_KERNEL = "gemm_w8a8_skinny<2, 4, 8, true, true>"
+GEMM_KERNEL = "gemm_w8a8_skinny<2, 4, 10, true, true>"
 COPY_KERNEL_HINT = "copy"
 
 
@@ -532,7 +532,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": "gemm_w8a8_skinny<2,4,8,tiled,argmax> (LM head 4096->151936, M=5)",
+                     "kernel": "gemm_w8a8_skinny<2,4,10,tiled,argmax> (LM head 4096->151936, M=5)",
                      "algorithmic_bytes_per_launch": bytes_launch,
                      "avg_launch_us": round(gemm_avg_s * 1e6, 3),
                      "launches_timed": len(gemm_ms)},

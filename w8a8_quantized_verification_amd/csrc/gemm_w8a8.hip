@@ -295,8 +295,12 @@ struct SkinnyPlan {
   int tiles, split, mblocks, waves, tn;
 };
 
+// k steps of loads issued per wave before their MFMAs.  Measured on the
+// LM head at M = 5 (same box, interleaved builds): 4: 97.8 us, 6: 97.0,
+// 8: 96.3-96.9, 10: 95.1-95.5 (three waves per SIMD), 12: 107 and 16: 101
+// (two waves per SIMD).
 #ifndef W8A8_SKINNY_UNROLL
-#define W8A8_SKINNY_UNROLL 8
+#define W8A8_SKINNY_UNROLL 10
 #endif
 constexpr int kUnroll = W8A8_SKINNY_UNROLL;
 constexpr int64_t kSkinnyMaxRows = 16;  // more token rows go to the batched kernel
