@@ -298,11 +298,15 @@ struct SkinnyPlan {
 // k steps of loads issued per wave before their MFMAs.  Measured on the
 // LM head at M = 5 (same box, interleaved builds): 4: 97.8 us, 6: 97.0,
 // 8: 96.3-96.9, 10: 95.1-95.5 (three waves per SIMD), 12: 107 and 16: 101
-// (two waves per SIMD).
+// (two waves per SIMD).  10 everywhere cost the mid-size shapes their
+// fourth wave per SIMD (gate/up 12288 x 4096 at M = 5: 12.5 against 10.7
+// us; the Qwen3-32B stack 7.80 against 7.37 ms), so only the LM head's
+// fused-argmax kernel takes 10.
 #ifndef W8A8_SKINNY_UNROLL
-#define W8A8_SKINNY_UNROLL 10
+#define W8A8_SKINNY_UNROLL 8
 #endif
 constexpr int kUnroll = W8A8_SKINNY_UNROLL;
+constexpr int kUnrollArgmax = 10;
 constexpr int64_t kSkinnyMaxRows = 16;  // more token rows go to the batched kernel
 constexpr int kSplitBelowTiles = 32;  // split k across workgroups below this ...
 constexpr int64_t kLongChain = 32;    // ... or above this many k steps per wave
@@ -379,11 +383,11 @@ static hipError_t launch_plan(const w8a8::SkinnyPlan& p, const w8a8::GemmArgs& g
 #define W8A8_GEMM(TN, W, TL, AM)                                                              \
   do {                                                                                        \
     if (ev0)                                                                                  \
-      hipExtLaunchKernelGGL((gemm_w8a8_skinny<TN, W, kUnroll, TL, AM>), grid, dim3(W * kWave), \
-                            0, stream, ev0, ev1, 0, g);                                      \
+      hipExtLaunchKernelGGL((gemm_w8a8_skinny<TN, W, (AM ? kUnrollArgmax : kUnroll), TL, AM>),  \
+                            grid, dim3(W * kWave), 0, stream, ev0, ev1, 0, g);               \
     else                                                                                      \
-      hipLaunchKernelGGL((gemm_w8a8_skinny<TN, W, kUnroll, TL, AM>), grid, dim3(W * kWave), 0, \
-                         stream, g);                                                          \
+      hipLaunchKernelGGL((gemm_w8a8_skinny<TN, W, (AM ? kUnrollArgmax : kUnroll), TL, AM>),     \
+                         grid, dim3(W * kWave), 0, stream, g);                                \
   } while (0)
 #define W8A8_GEMM_W(TN, TL, AM)                   \
   do {                                            \
