@@ -113,3 +113,93 @@ def test_qk_norm_rope_known_angle():
     n_bf = val(oracle.glue._f64_to_bf16_bits(np.array([n])))[0]
     assert val(q)[0, 0, 0, 0] == val(oracle.glue._f64_to_bf16_bits(np.array([n_bf * np.cos(3)])))[0]
     assert val(q)[0, 0, 0, 64] == val(oracle.glue._f64_to_bf16_bits(np.array([n_bf * np.sin(3)])))[0]
+
+
+# ---------------------------------------------------------------------------
+# Rotary angles for every dimension pair, pinned element by element.
+#
+# Reading (the pages give no attention formula; the workloads follow Qwen3's
+# rotate-half RoPE in fp32 inference): pair (d, d + 64) of a head at
+# position p turns by a = fp32(fp32(p) * fp32(base^(-d/64))).  The expected
+# outputs below are built per element with math.pow / math.cos / math.sin
+# and a bf16 rounding written here from its definition (8 significant bits,
+# nearest, ties to even), not with the oracle's vectorised helpers.  Each
+# plausible slip — exponent -d/128, a float64 angle, the pairs rotated the
+# other way — is checked to change at least one of these outputs.
+# ---------------------------------------------------------------------------
+import math  # noqa: E402
+
+
+def _bf16_round(x: float) -> float:
+    if x == 0.0:
+        return 0.0
+    m, e = math.frexp(x)                  # x = m * 2^e, 0.5 <= |m| < 1
+    return math.ldexp(round(m * 256.0), e - 8)   # round(): ties to even on floats
+
+
+def _angle_fp32(p: int, d: int, base: float, denom: float = 64.0) -> float:
+    f = float(np.float32(math.pow(base, -d / denom)))
+    return float(np.float32(float(np.float32(p)) * f))   # exact product, one fp32 rounding
+
+
+def _rope_case(starts, T):
+    """q head h holds a lone 1 at dim h (x1 of pair h); k head h holds a lone
+    1 at dim 64 + h (x2 of pair h); gamma = 1, eps = 0, so every normed
+    nonzero is bf16(sqrt(128))."""
+    B, H = len(starts), 64
+    rows = np.zeros((B * T, 3 * H * 128), dtype=np.float32)
+    for h in range(H):
+        rows[:, h * 128 + h] = 1.0
+        rows[:, (H + h) * 128 + 64 + h] = 1.0
+    rows[:, 2 * H * 128:] = RNG.standard_normal((B * T, H * 128))
+    g = bits(np.ones(128))
+    q, k, _ = oracle.qk_norm_rope(bits(rows), B, T, H, H, g, g, 0.0, starts, 1e6)
+    return val(q), val(k)
+
+
+def _expected(starts, T, angle):
+    n = _bf16_round(math.sqrt(128.0))
+    B, H = len(starts), 64
+    q = np.zeros((B, T, H, 128))
+    k = np.zeros((B, T, H, 128))
+    for b in range(B):
+        for i in range(T):
+            p = starts[b] + i
+            for h in range(H):
+                a = angle(p, h)
+                c, s = math.cos(a), math.sin(a)
+                q[b, i, h, h] = _bf16_round(n * c)
+                q[b, i, h, 64 + h] = _bf16_round(n * s)
+                k[b, i, h, h] = _bf16_round(-n * s)
+                k[b, i, h, 64 + h] = _bf16_round(n * c)
+    return q, k
+
+
+def test_qk_norm_rope_every_pair_fp32_angle():
+    starts, T = [1, 99998, 4097], 2           # positions 1, 2, 99998, 99999, 4097, 4098
+    q, k = _rope_case(starts, T)
+    qe, ke = _expected(starts, T, lambda p, d: _angle_fp32(p, d, 1e6))
+    np.testing.assert_array_equal(q, qe)
+    np.testing.assert_array_equal(k, ke)
+
+    # the pins discriminate: each slip changes some output
+    q128, _ = _expected(starts, T, lambda p, d: _angle_fp32(p, d, 1e6, denom=128.0))
+    assert not np.array_equal(q, q128)
+    q64, _ = _expected(starts, T, lambda p, d: float(p) * math.pow(1e6, -d / 64.0))
+    assert not np.array_equal(q, q64)
+    qrev, _ = _expected(starts, T, lambda p, d: -_angle_fp32(p, d, 1e6))
+    assert not np.array_equal(q, qrev)
+
+
+def test_qk_norm_rope_fp32_angle_differs_from_fp64_at_large_positions():
+    # near position 1e5 the fp32 rounding of the angle (up to ~4e-3 rad) is
+    # larger than a bf16 step of the rotated values for some pairs: the
+    # reading is visible in the outputs, not only in the angles
+    starts, T = [99999], 1
+    q, _ = _rope_case(starts, T)
+    q64, _ = _expected(starts, T, lambda p, d: float(p) * math.pow(1e6, -d / 64.0))
+    diff = np.count_nonzero(q != q64)
+    assert diff > 0
+    angles32 = [_angle_fp32(99999, d, 1e6) for d in range(64)]
+    angles64 = [99999.0 * math.pow(1e6, -d / 64.0) for d in range(64)]
+    assert max(abs(a - b) for a, b in zip(angles32, angles64)) > 1e-3
