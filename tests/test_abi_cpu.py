@@ -267,3 +267,49 @@ def test_python_binding_rejects_cpu_tensors():
     x = torch.zeros(5, 256, dtype=torch.bfloat16)
     with pytest.raises(TypeError, match="ROCm device"):
         w.quantize_act(x)
+
+
+def test_workspace_keeps_keys_apart_from_split_k_partials():
+    """The LM-head argmax keys stay non-zero between its two phases, so they
+    must not share a buffer with the split-K partials that a linear between
+    the phases would add onto (host-side bookkeeping; CPU tensors stand in
+    for device buffers)."""
+    import torch
+    import w8a8_quantized_verification_amd as w
+    ws = w.Workspace()
+    cpu = torch.device("cpu")
+    zeroed = ws.get(4096, cpu, use="zeroed")
+    keys = ws.get(4096, cpu, use="keys")
+    verify = ws.get(4096, cpu, use="verify")
+    ptrs = {zeroed.data_ptr(), keys.data_ptr(), verify.data_ptr()}
+    assert len(ptrs) == 3
+    keys.fill_(7)                                    # keys left behind by phase 1
+    again = ws.get(4096, cpu, use="zeroed")          # a split-K linear in between
+    assert again.data_ptr() == zeroed.data_ptr() and not bool(again.any())
+    assert ws.get(4096, cpu, use="keys").data_ptr() == keys.data_ptr()
+    with pytest.raises(ValueError, match="unknown workspace use"):
+        ws.get(16, cpu, use="partials")
+
+
+def test_python_binding_uses_keys_slot_for_the_argmax_phases():
+    """Every LM-head argmax / acceptance binding takes the keys slot, and the
+    split-K linear the zeroed slot (read from the binding's source)."""
+    import inspect
+    import w8a8_quantized_verification_amd.api as api
+    for fn in (api.lm_head_verify, api.lm_head_argmax, api.lm_head_argmax_tiled_act,
+               api.accept_from_keys, api.lm_head_argmax_w4):
+        src = inspect.getsource(fn)
+        assert 'use="keys"' in src and 'use="zeroed"' not in src, fn.__name__
+    assert 'use="zeroed"' in inspect.getsource(api.linear)
+
+
+def test_hbm_read_probe_validation(lib):
+    sink = 4096
+    # ragged size, NULL sink, NULL buffer with bytes > 0, misalignment, one event alone
+    assert lib.w8a8_hbm_read_probe(16, 24, sink, None, None, None) == INVALID
+    assert lib.w8a8_hbm_read_probe(16, 32, None, None, None, None) == INVALID
+    assert lib.w8a8_hbm_read_probe(None, 32, sink, None, None, None) == INVALID
+    assert lib.w8a8_hbm_read_probe(8, 32, sink, None, None, None) == INVALID
+    assert lib.w8a8_hbm_read_probe(16, 32, 2, None, None, None) == INVALID
+    assert lib.w8a8_hbm_read_probe(16, 32, sink, 1, None, None) == INVALID
+    assert b"both events" in lib.w8a8_last_error()

@@ -544,7 +544,7 @@ def test_lm_head_verify_repeats_leave_workspace_zeroed(B, G, V, K):
         np.testing.assert_array_equal(host(am), am_r)
         np.testing.assert_array_equal(host(al), al_r)
         np.testing.assert_array_equal(host(nt), nt_r)
-        buf = wsp.get(1, xq.device, use="zeroed")
+        buf = wsp.get(1, xq.device, use="keys")
         assert not bool(buf.any()), "workspace not left zero-filled"
         w8.lm_head_argmax(xq, xs, wt, ws, workspace=wsp)                 # the two phases
         am2, al2, nt2 = w8.accept_from_keys(d, workspace=wsp)
@@ -660,7 +660,7 @@ def test_lm_head_argmax_tiled_act(B, G, V, K):
         np.testing.assert_array_equal(host(a), am_r)
         np.testing.assert_array_equal(host(l), al_r)
         np.testing.assert_array_equal(host(n), nt_r)
-    assert not bool(wsp.get(1, x.device, use="zeroed").any())
+    assert not bool(wsp.get(1, x.device, use="keys").any())
 
 
 def test_lm_head_argmax_tiled_act_ties():

@@ -20,8 +20,10 @@ __all__ = [
     "verify_sample_workspace_bytes", "sample_weights", "w4_shape", "quantize_weight_w4",
     "linear_w4", "lm_head_argmax_w4", "residual_rmsnorm_quant", "silu_mul_quant",
     "quantize_act_tiled", "linear_tiled_act", "verify_attention", "qk_norm_rope_append",
-    "pack_v_cache",
+    "pack_v_cache", "hbm_read_probe", "HBM_PROBE_SINK_WORDS",
 ]
+
+HBM_PROBE_SINK_WORDS = 2048   # W8A8_HBM_PROBE_SINK_WORDS
 
 
 def _ptr(t):
@@ -57,20 +59,35 @@ def _out(t, shape, dtype, device, name):
 
 
 class Workspace:
-    """Per-device scratch buffers, two per device: a "zeroed" one (allocated
-    zero-filled) for the calls that need zeros on entry and leave zeros
-    behind — w8a8_linear's split-K partials and lm_head_verify's argmax keys
-    — and a "verify" one for verify_accept's per-chunk results, which it
-    overwrites and leaves non-zero.  Calls that use one Workspace must run
-    in order on one stream (the default use)."""
+    """Per-device scratch buffers, one per device and use:
+
+    * ``"zeroed"`` (allocated zero-filled): w8a8_linear's split-K partials
+      and arrival counters, which every completed call leaves zero again;
+    * ``"keys"`` (allocated zero-filled): the LM-head argmax keys.
+      lm_head_argmax (phase 1) leaves non-zero keys behind until the
+      accept_from_keys that follows it reads and resets them, so they get a
+      buffer of their own: a split-K linear between the two phases would
+      otherwise add its partials onto the keys;
+    * ``"verify"``: per-chunk results of verify_accept, verify_sample and
+      the attention split, overwritten by each call and left non-zero.
+
+    Calls that use one Workspace must run in order on one stream (the
+    default use)."""
+
+    USES = ("zeroed", "keys", "verify")
 
     def __init__(self):
         self._buf = {}
 
     def get(self, nbytes: int, device: torch.device, use: str) -> torch.Tensor | None:
+        if use not in self.USES:
+            raise ValueError(f"unknown workspace use {use!r} (one of {self.USES})")
         if nbytes == 0:
             return None
-        idx = device.index if device.index is not None else torch.cuda.current_device()
+        if device.index is not None:
+            idx = device.index
+        else:
+            idx = torch.cuda.current_device() if device.type == "cuda" else -1
         key = (idx, use)
         b = self._buf.get(key)
         if b is None or b.numel() < nbytes:
@@ -222,7 +239,7 @@ def lm_head_verify(xq, x_scale, wq_tiled, w_scale, draft, *, want_logits=False,
     accept_len = _out(accept_len, (B,), torch.int32, dev, "accept_len")
     next_token = _out(next_token, (B,), torch.int32, dev, "next_token")
     need = int(lib().w8a8_lm_head_verify_workspace_bytes(B, G, V, K))
-    ws = (workspace or _default_ws).get(need, dev, use="zeroed")
+    ws = (workspace or _default_ws).get(need, dev, use="keys")
     check(lib().w8a8_lm_head_verify(_ptr(xq), _ptr(x_scale), _ptr(wq_tiled), _ptr(w_scale), V, K,
                                     _ptr(draft), B, G, _ptr(logits), _ptr(argmax),
                                     _ptr(accept_len), _ptr(next_token), _ptr(ws),
@@ -250,7 +267,7 @@ def lm_head_argmax(xq, x_scale, wq_tiled, w_scale, *, logits=None,
     if logits is not None:
         logits = _out(logits, (M, V), torch.float32, dev, "logits")
     ws = (workspace or _default_ws).get(int(lib().w8a8_lm_head_verify_workspace_bytes(M, 0, V, K)),
-                                        dev, use="zeroed")
+                                        dev, use="keys")
     if events is not None:
         start, stop = events
         if not (start.cuda_event and stop.cuda_event):
@@ -286,7 +303,7 @@ def lm_head_argmax_tiled_act(xq_tiled, x_scale, wq_tiled, w_scale, *, K: int, lo
     if logits is not None:
         logits = _out(logits, (M, V), torch.float32, dev, "logits")
     ws = (workspace or _default_ws).get(int(lib().w8a8_lm_head_verify_workspace_bytes(M, 0, V, K)),
-                                        dev, use="zeroed")
+                                        dev, use="keys")
     check(lib().w8a8_lm_head_argmax_tiled_act(_ptr(xq_tiled), _ptr(x_scale), _ptr(wq_tiled),
                                               _ptr(w_scale), M, V, K, _ptr(logits), _ptr(ws),
                                               0 if ws is None else ws.numel(), _stream(dev)))
@@ -306,7 +323,7 @@ def accept_from_keys(draft, *, want_argmax=True, argmax=None, accept_len=None, n
     accept_len = _out(accept_len, (B,), torch.int32, dev, "accept_len")
     next_token = _out(next_token, (B,), torch.int32, dev, "next_token")
     ws = (workspace or _default_ws).get(int(lib().w8a8_lm_head_verify_workspace_bytes(R, 0, 1, 0)),
-                                        dev, use="zeroed")
+                                        dev, use="keys")
     check(lib().w8a8_accept_from_keys(_ptr(ws), 0 if ws is None else ws.numel(), _ptr(draft), B, G,
                                       _ptr(argmax), _ptr(accept_len), _ptr(next_token),
                                       _stream(dev)))
@@ -454,7 +471,7 @@ def lm_head_argmax_w4(xq, x_scale, wq4, w_scale, *, logits=None,
     if logits is not None:
         logits = _out(logits, (M, V), torch.float32, dev, "logits")
     ws = (workspace or _default_ws).get(int(lib().w8a8_lm_head_verify_workspace_bytes(M, 0, V, K)),
-                                        dev, use="zeroed")
+                                        dev, use="keys")
     check(lib().w8a8_lm_head_argmax_w4(_ptr(xq), _ptr(x_scale), _ptr(wq4), _ptr(w_scale), M, V, K,
                                        _ptr(logits), _ptr(ws), 0 if ws is None else ws.numel(),
                                        _stream(dev)))
@@ -627,3 +644,27 @@ def qk_norm_rope_append(qkv, q_gamma, k_gamma, lengths, k_cache, v_cache, *, T: 
                                          _ptr(lengths), Lmax, _ptr(q_out), _ptr(k_cache),
                                          _ptr(v_cache), _stream(dev)))
     return q_out
+
+
+def hbm_read_probe(buf: torch.Tensor, *, sink=None, events=None) -> torch.Tensor:
+    """Read every byte of the contiguous device tensor ``buf`` once with the
+    library's streaming-read probe (a measurement of the sustained read
+    bandwidth).  ``sink``: int32 ``[HBM_PROBE_SINK_WORDS]`` scratch output.
+    ``events=(start, stop)`` as for :func:`lm_head_argmax` (the kernel's own
+    timestamps).  Returns ``sink``."""
+    if not isinstance(buf, torch.Tensor) or buf.device.type != "cuda":
+        raise TypeError("buf must be a torch.Tensor on a ROCm device; there is no CPU path")
+    if not buf.is_contiguous():
+        raise ValueError("buf must be contiguous")
+    nbytes = buf.numel() * buf.element_size()
+    sink = _out(sink, (HBM_PROBE_SINK_WORDS,), torch.int32, buf.device, "sink")
+    ev0 = ev1 = None
+    if events is not None:
+        start, stop = events
+        if not (start.cuda_event and stop.cuda_event):
+            raise ValueError("record each timing event once before passing it (torch creates "
+                             "the underlying event lazily)")
+        ev0, ev1 = start.cuda_event, stop.cuda_event
+    check(lib().w8a8_hbm_read_probe(_ptr(buf), nbytes, _ptr(sink), ev0, ev1, _stream(buf.device)))
+    return sink
+
