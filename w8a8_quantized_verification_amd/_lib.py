@@ -45,6 +45,7 @@ SIGNATURES = {
                                              _vp]),
     "w8a8_lm_head_argmax_timed": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _sz, _vp,
                                          _vp, _vp]),
+    "w8a8_hbm_read_probe": (_i32, [_vp, _sz, _vp, _vp, _vp, _vp]),
     "w8a8_bf16_linear": (_i32, [_vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp]),
     "w8a8_verify_sample_workspace_bytes": (_sz, [_i64, _i64, _i64]),
     "w8a8_verify_sample": (_i32, [_vp, _i64, _vp, _i64, _i64, _c.c_float, _vp, _vp, _vp, _vp,

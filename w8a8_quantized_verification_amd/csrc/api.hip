@@ -270,6 +270,23 @@ w8a8_status w8a8_lm_head_argmax_timed(const int8_t* xq, const float* x_scale,
                     fn);
 }
 
+w8a8_status w8a8_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* start_event,
+                                void* stop_event, void* stream) {
+  static const char* fn = "w8a8_hbm_read_probe";
+  g_last_error.clear();
+  if (bytes % 16 != 0) return fail(W8A8_ERR_INVALID_ARG, fn, "bytes must be a multiple of 16");
+  if (!sink || (bytes > 0 && !buf)) return fail(W8A8_ERR_INVALID_ARG, fn, "buf or sink is NULL");
+  if (!aligned(buf, 16) || !aligned(sink, 4))
+    return fail(W8A8_ERR_INVALID_ARG, fn, "pointer misaligned (16 bytes for buf, 4 for sink)");
+  if (!start_event != !stop_event)
+    return fail(W8A8_ERR_INVALID_ARG, fn, "pass both events or neither");
+  return hip_status(w8a8_launch_hbm_read_probe(buf, bytes, sink, W8A8_HBM_PROBE_SINK_WORDS,
+                                               reinterpret_cast<hipStream_t>(stream),
+                                               reinterpret_cast<hipEvent_t>(start_event),
+                                               reinterpret_cast<hipEvent_t>(stop_event)),
+                    fn);
+}
+
 w8a8_status w8a8_accept_from_keys(void* workspace, size_t workspace_bytes, const int32_t* draft,
                                   int64_t B, int64_t G, int32_t* argmax, int32_t* accept_len,
                                   int32_t* next_token, void* stream) {
