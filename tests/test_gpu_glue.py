@@ -6,8 +6,13 @@ Bars: the residual sum bit-exact; the normed / SwiGLU bf16 rows within the
 stated tolerance (1e-2 relative / 1e-3 absolute) of the oracle's float64
 computation, and bit-exact on at least 99% of elements (an fp32 kernel can
 differ by one bf16 step next to a rounding boundary); the int8 codes and
-scales bit-exact against the oracle's quantizer applied to the bf16 row the
-kernel produced (the same decision in the same precision)."""
+scales bit-exact against the all-oracle chain (oracle.quantize_act of the
+oracle's own bf16 row) on every case here — the kernels' bf16 rows match the
+oracle's on every element of these inputs, so no code may move; the rows
+with a bf16 difference and the rows whose codes moved are counted and
+printed.  The codes are also checked bit-exact against the oracle's
+quantizer applied to the bf16 row the kernel produced (the same decision in
+the same precision)."""
 import numpy as np
 import pytest
 import torch
@@ -46,6 +51,23 @@ def check_bf16_close(got_bits, want_bits):
     return exact
 
 
+def check_codes_vs_oracle_chain(xq, xsc, got_rows, want_rows, smooth, what):
+    """Codes and scales against oracle.quantize_act(want_rows), the
+    all-oracle chain: identical on every row (the counts of rows with a bf16
+    difference and of rows whose codes moved are printed first)."""
+    q_o, s_o = oracle.quantize_act(want_rows, smooth=smooth)
+    same_row = np.all(got_rows == want_rows, axis=1)
+    q_same = np.all(xq == q_o, axis=1)
+    s_same = xsc.view(np.uint32) == s_o.view(np.uint32)
+    moved = ~(q_same & s_same)
+    assert not np.any(moved & same_row), np.nonzero(moved & same_row)[0][:10]
+    print(f"[gpu] {what}: rows with a bf16 difference {int(np.sum(~same_row))} of "
+          f"{len(same_row)}; rows whose codes or scale moved {int(np.sum(moved))} "
+          f"(codes differing {int(np.sum(xq != q_o))} of {xq.size})", flush=True)
+    np.testing.assert_array_equal(xq, q_o)
+    np.testing.assert_array_equal(xsc.view(np.uint32), s_o.view(np.uint32))
+
+
 @pytest.mark.parametrize("M,D,with_delta,smooth", [(5, 4096, True, False), (5, 4096, False, False),
                                                    (8, 5120, True, True), (288, 4096, True, False),
                                                    (3, 25600, True, False), (1, 16, True, False),
@@ -69,8 +91,10 @@ def test_residual_rmsnorm_quant(M, D, with_delta, smooth):
     if delta is not None:
         np.testing.assert_array_equal(host(h_out), h1)
     n_gpu = host(normed)
-    exact = check_bf16_close(n_gpu, oracle.rmsnorm(h1, gamma, eps))
+    n_oracle = oracle.rmsnorm(h1, gamma, eps)
+    exact = check_bf16_close(n_gpu, n_oracle)
     print(f"[gpu] normed bit-exact fraction {exact:.6f}", flush=True)
+    check_codes_vs_oracle_chain(host(xq), host(xsc), n_gpu, n_oracle, s, "rmsnorm chain")
     q_r, s_r = oracle.quantize_act(n_gpu, smooth=s)
     np.testing.assert_array_equal(host(xq), q_r)
     np.testing.assert_array_equal(host(xsc).view(np.uint32), s_r.view(np.uint32))
@@ -106,8 +130,10 @@ def test_silu_mul_quant(M, F, fused, smooth):
     xq, xsc, act = w8.silu_mul_quant(gd, ud, smooth=None if s is None else dev(s), want_act=True)
     torch.cuda.synchronize()
     a_gpu = host(act)
-    exact = check_bf16_close(a_gpu, oracle.silu_mul(g, u))
+    a_oracle = oracle.silu_mul(g, u)
+    exact = check_bf16_close(a_gpu, a_oracle)
     print(f"[gpu] act bit-exact fraction {exact:.6f}", flush=True)
+    check_codes_vs_oracle_chain(host(xq), host(xsc), a_gpu, a_oracle, s, "swiglu chain")
     q_r, s_r = oracle.quantize_act(a_gpu, smooth=s)
     np.testing.assert_array_equal(host(xq), q_r)
     np.testing.assert_array_equal(host(xsc).view(np.uint32), s_r.view(np.uint32))
