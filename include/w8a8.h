@@ -266,24 +266,25 @@ size_t      w8a8_lm_head_verify_workspace_bytes(int64_t B, int64_t G, int64_t V,
 
 /*
  * Streaming-read probe (measurement): reads `bytes` bytes of `buf` once with
- * 16-byte non-temporal loads in a grid-stride walk (W8A8_HBM_PROBE_SINK_WORDS
- * workgroups of 256 threads, eight loads per thread in flight) and writes one
- * 32-bit fold per workgroup to `sink`.  Its duration gives the read
- * bandwidth this chip sustains for a plain stream, the practical ceiling for
- * a weight stream next to the nominal peak.
+ * 16-byte non-temporal loads, each workgroup of 256 threads one contiguous
+ * 32 KiB chunk (its four waves taking consecutive KiB in turn, eight loads
+ * per lane in flight).  Its duration gives the read bandwidth this chip
+ * sustains for a plain stream, the practical ceiling for a weight stream
+ * next to the nominal peak.
  *
  * Pages: verification time is the weight bytes read over the memory
  * bandwidth ([de] §3 item 4; [ja] §2.3).
  *
  * buf: device buffer, 16-byte aligned; bytes % 16 == 0 (0 reads nothing).
- * sink: device array of W8A8_HBM_PROBE_SINK_WORDS uint32 (4-byte aligned),
- *    overwritten.  start_event / stop_event: both NULL, or two hipEvent_t
- *    handles created with timing enabled that receive the kernel's own start
- *    and end timestamps (as for w8a8_lm_head_argmax_timed).  Errors:
- *    W8A8_ERR_INVALID_ARG for a NULL pointer, misalignment, a ragged size or
- *    one event without the other.
+ * sink: W8A8_HBM_PROBE_SINK_WORDS device uint32 (4-byte aligned) that the
+ *    kernel may overwrite with a fold of the bytes read (the value has no
+ *    use; it keeps the loads from being dropped).  start_event / stop_event:
+ *    both NULL, or two hipEvent_t handles created with timing enabled that
+ *    receive the kernel's own start and end timestamps (as for
+ *    w8a8_lm_head_argmax_timed).  Errors: W8A8_ERR_INVALID_ARG for a NULL
+ *    pointer, misalignment, a ragged size or one event without the other.
  */
-#define W8A8_HBM_PROBE_SINK_WORDS 2048
+#define W8A8_HBM_PROBE_SINK_WORDS 1
 w8a8_status w8a8_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink,
                                 void* start_event, void* stop_event, void* stream);
 

@@ -23,7 +23,7 @@ __all__ = [
     "pack_v_cache", "hbm_read_probe", "HBM_PROBE_SINK_WORDS",
 ]
 
-HBM_PROBE_SINK_WORDS = 2048   # W8A8_HBM_PROBE_SINK_WORDS
+HBM_PROBE_SINK_WORDS = 1      # W8A8_HBM_PROBE_SINK_WORDS
 
 
 def _ptr(t):

@@ -202,10 +202,10 @@ size_t w8a8_lm_head_verify_workspace_bytes(int64_t B, int64_t G, int64_t V, int6
   return w8a8_lm_head_workspace_bytes(B * (G + 1));
 }
 
-static w8a8_status check_lm_head(const char* fn, const int8_t* xq, const float* x_scale,
-                                 const int8_t* wq_tiled, const float* w_scale, int64_t M,
-                                 int64_t V, int64_t K, const float* logits, const void* keys,
-                                 size_t keys_bytes) {
+// The LM-head operands (everything but the key workspace).
+static w8a8_status check_lm_head_operands(const char* fn, const int8_t* xq, const float* x_scale,
+                                          const int8_t* wq_tiled, const float* w_scale, int64_t M,
+                                          int64_t V, int64_t K, const float* logits) {
   if (w8a8_status s = check_rows_k(fn, M, K)) return s;
   if (M == 0) return W8A8_OK;
   if (V < 1 || V > kMaxRows) return fail(W8A8_ERR_INVALID_ARG, fn, "V out of range [1, 2^30]");
@@ -215,6 +215,16 @@ static w8a8_status check_lm_head(const char* fn, const int8_t* xq, const float* 
     return fail(W8A8_ERR_INVALID_ARG, fn, "xq and wq_tiled must be 16-byte aligned");
   if (!aligned(x_scale, 4) || !aligned(w_scale, 4) || !aligned(logits, 4))
     return fail(W8A8_ERR_INVALID_ARG, fn, "pointer misaligned (4 bytes)");
+  return W8A8_OK;
+}
+
+static w8a8_status check_lm_head(const char* fn, const int8_t* xq, const float* x_scale,
+                                 const int8_t* wq_tiled, const float* w_scale, int64_t M,
+                                 int64_t V, int64_t K, const float* logits, const void* keys,
+                                 size_t keys_bytes) {
+  if (w8a8_status s = check_lm_head_operands(fn, xq, x_scale, wq_tiled, w_scale, M, V, K, logits))
+    return s;
+  if (M == 0) return W8A8_OK;
   if (!keys || keys_bytes < w8a8_lm_head_workspace_bytes(M))
     return fail(W8A8_ERR_WORKSPACE, fn, "workspace NULL or smaller than w8a8_lm_head_verify_workspace_bytes()");
   if (!aligned(keys, 256)) return fail(W8A8_ERR_INVALID_ARG, fn, "workspace must be 256-byte aligned");
@@ -280,7 +290,9 @@ w8a8_status w8a8_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, v
     return fail(W8A8_ERR_INVALID_ARG, fn, "pointer misaligned (16 bytes for buf, 4 for sink)");
   if (!start_event != !stop_event)
     return fail(W8A8_ERR_INVALID_ARG, fn, "pass both events or neither");
-  return hip_status(w8a8_launch_hbm_read_probe(buf, bytes, sink, W8A8_HBM_PROBE_SINK_WORDS,
+  if (bytes / 16 / 2048 >= (size_t)INT32_MAX)
+    return fail(W8A8_ERR_INVALID_ARG, fn, "bytes too large for one launch");
+  return hip_status(w8a8_launch_hbm_read_probe(buf, bytes, sink,
                                                reinterpret_cast<hipStream_t>(stream),
                                                reinterpret_cast<hipEvent_t>(start_event),
                                                reinterpret_cast<hipEvent_t>(stop_event)),

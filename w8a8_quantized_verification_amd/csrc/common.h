@@ -154,5 +154,5 @@ hipError_t w8a8_launch_qk_norm_rope_append(const uint16_t* qkv, int64_t B, int64
                                            uint16_t* k_cache, uint16_t* v_cache,
                                            hipStream_t stream);
 
-hipError_t w8a8_launch_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, int blocks,
+hipError_t w8a8_launch_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink,
                                       hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);

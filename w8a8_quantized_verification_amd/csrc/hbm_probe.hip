@@ -8,12 +8,19 @@
 // the weight-streaming GEMM is what a pure read of the same bytes achieves,
 // beside the nominal 8 TB/s.
 //
-// Each thread XORs 16-byte non-temporal loads in a grid-stride walk: at any
-// moment every wave reads inside one sliding window of the buffer, and one
-// wave instruction covers 1 KiB of consecutive bytes.  Eight loads per
-// thread are in flight before any is consumed.  Each workgroup writes one
-// word (the fold of its lanes) so the loads cannot be dropped; those 8 KiB
-// of writes are the probe's only stores.
+// Each workgroup of 4 waves reads one contiguous 32 KiB chunk of the buffer
+// (the last one the ragged rest): its waves take consecutive KiB in turn, so
+// one wave instruction covers 1 KiB of consecutive bytes with 16-byte
+// non-temporal loads, eight of them in flight per lane before any is
+// consumed.  Workgroups go to the 8 XCDs round-robin, so each XCD streams
+// every eighth chunk.  Measured on MI355X over 622 MB, this shape sustained
+// 6.98 TB/s (mean of 20 launches; 7.22 best), against 5.3-5.6 TB/s for a
+// grid-stride walk in which consecutive KiB belong to workgroups on
+// different XCDs, and 6.6-6.9 TB/s for chunks of 128-256 KiB.
+//
+// The XOR fold of everything read is written to sink[0] only when it equals
+// a fixed constant, so the loads cannot be dropped and the probe makes no
+// other memory traffic.
 #include "common.h"
 
 #include <hip/hip_ext.h>
@@ -22,41 +29,39 @@ namespace w8a8 {
 
 constexpr int kProbeThreads = 256;
 constexpr int kProbeUnroll = 8;
+constexpr int64_t kProbeChunkUnits = 2048;   // 32 KiB of 16-byte units per workgroup
 
 __global__ __launch_bounds__(kProbeThreads) void hbm_read_kernel(const v4i* __restrict__ buf,
                                                                   int64_t units,
                                                                   uint32_t* __restrict__ sink) {
-  const int64_t stride = (int64_t)gridDim.x * kProbeThreads;
-  int64_t i = (int64_t)blockIdx.x * kProbeThreads + threadIdx.x;
+  const int64_t beg = (int64_t)blockIdx.x * kProbeChunkUnits;
+  const int64_t end = min(beg + kProbeChunkUnits, units);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  constexpr int kStep = kProbeThreads;   // units per round of the 4 waves (4 KiB)
+  int64_t i = beg + wave * kWave + lane;
   v4i x = v4i{0, 0, 0, 0};
-  for (; i + (kProbeUnroll - 1) * stride < units; i += kProbeUnroll * stride) {
+  for (; i + (kProbeUnroll - 1) * kStep < end; i += kProbeUnroll * kStep) {
     v4i v[kProbeUnroll];
 #pragma unroll
-    for (int u = 0; u < kProbeUnroll; ++u) v[u] = __builtin_nontemporal_load(buf + i + u * stride);
+    for (int u = 0; u < kProbeUnroll; ++u) v[u] = __builtin_nontemporal_load(buf + i + u * kStep);
 #pragma unroll
     for (int u = 0; u < kProbeUnroll; ++u) x ^= v[u];
   }
-  for (; i < units; i += stride) x ^= __builtin_nontemporal_load(buf + i);
-  uint32_t f = (uint32_t)(x[0] ^ x[1] ^ x[2] ^ x[3]);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) f ^= (uint32_t)__shfl_xor((int)f, off, kWave);
-  __shared__ uint32_t part[kProbeThreads / kWave];
-  if ((threadIdx.x & (kWave - 1)) == 0) part[threadIdx.x / kWave] = f;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t s = 0;
-#pragma unroll
-    for (int w = 0; w < kProbeThreads / kWave; ++w) s ^= part[w];
-    sink[blockIdx.x] = s;
-  }
+  for (; i < end; i += kStep) x ^= __builtin_nontemporal_load(buf + i);
+  const uint32_t f = (uint32_t)(x[0] ^ x[1] ^ x[2] ^ x[3]);
+  if (f == 0x9E3779B9u) sink[0] = f;
 }
 
 }  // namespace w8a8
 
-hipError_t w8a8_launch_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, int blocks,
+hipError_t w8a8_launch_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink,
                                       hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   using namespace w8a8;
   const int64_t units = (int64_t)(bytes / 16);
+  if (units == 0) return hipSuccess;
+  const int64_t blocks = (units + kProbeChunkUnits - 1) / kProbeChunkUnits;
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
   const dim3 grid((unsigned)blocks), block(kProbeThreads);
   if (ev0)
     hipExtLaunchKernelGGL(hbm_read_kernel, grid, block, 0, stream, ev0, ev1, 0,
