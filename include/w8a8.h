@@ -337,6 +337,34 @@ w8a8_status w8a8_lm_head_verify(const int8_t* xq, const float* x_scale,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * w8a8_lm_head_verify for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same results, bit for bit, with no workspace argument.
+ * The argmax keys live in a scratch array inside the library, one per GPU
+ * (W8A8_NOALLOC_MAX_ROWS rows of 16 KiB: 4.5 MiB of device memory, held by
+ * each GPU the library runs on until the process ends).  The call allocates
+ * nothing: each call clears the keys its rows use with a small kernel (no
+ * hipMemsetAsync), then runs the LM-head kernel and the acceptance kernel,
+ * which leaves them zero.  The array's device address is looked up on the
+ * first call on each device (make the stream's device current; make that
+ * first call outside graph capture).  Every call on one GPU shares the
+ * array: calls that overlap in time on one GPU (other streams, other
+ * threads) race on it and must be serialized by the caller.
+ *
+ * Arguments and errors as for w8a8_lm_head_verify, without workspace and
+ * workspace_bytes; B*(G+1) > W8A8_NOALLOC_MAX_ROWS returns
+ * W8A8_ERR_UNSUPPORTED (nothing is enqueued).
+ */
+#define W8A8_NOALLOC_MAX_ROWS 288
+w8a8_status w8a8_lm_head_verify_noalloc(const int8_t* xq, const float* x_scale,
+                                        const int8_t* wq_tiled, const float* w_scale,
+                                        int64_t V, int64_t K,
+                                        const int32_t* draft, int64_t B, int64_t G,
+                                        float* logits, int32_t* argmax,
+                                        int32_t* accept_len, int32_t* next_token,
+                                        void* stream);
+
+/*
  * The BF16 glue between linears, fused with the per-token int8
  * quantization of the next linear's input (it replaces that
  * w8a8_quantize_act call).

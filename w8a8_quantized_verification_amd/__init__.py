@@ -12,7 +12,8 @@ from .api import (W8A8Error, Workspace, accept_from_keys, bf16_linear, linear,
                   w4_shape, quantize_weight_w4, linear_w4, lm_head_argmax_w4,
                   residual_rmsnorm_quant, silu_mul_quant, quantize_act_tiled,
                   linear_tiled_act, verify_attention, qk_norm_rope_append, pack_v_cache,
-                  hbm_read_probe, HBM_PROBE_SINK_WORDS)
+                  hbm_read_probe, HBM_PROBE_SINK_WORDS, lm_head_verify_noalloc,
+                  NOALLOC_MAX_ROWS)
 
 __all__ = [
     "W8A8Error", "Workspace", "accept_from_keys", "bf16_linear", "linear", "linear_workspace_bytes",
@@ -22,5 +23,5 @@ __all__ = [
     "sample_weights", "w4_shape", "quantize_weight_w4", "linear_w4", "lm_head_argmax_w4",
     "residual_rmsnorm_quant", "silu_mul_quant", "quantize_act_tiled", "linear_tiled_act",
     "verify_attention", "qk_norm_rope_append", "pack_v_cache", "hbm_read_probe",
-    "HBM_PROBE_SINK_WORDS",
+    "HBM_PROBE_SINK_WORDS", "lm_head_verify_noalloc", "NOALLOC_MAX_ROWS",
 ]

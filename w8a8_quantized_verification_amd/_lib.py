@@ -39,6 +39,8 @@ SIGNATURES = {
     "w8a8_lm_head_verify_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64]),
     "w8a8_lm_head_verify": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _vp,
                                    _vp, _vp, _sz, _vp]),
+    "w8a8_lm_head_verify_noalloc": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _vp, _i64, _i64, _vp,
+                                           _vp, _vp, _vp, _vp]),
     "w8a8_lm_head_argmax": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _sz, _vp]),
     "w8a8_accept_from_keys": (_i32, [_vp, _sz, _vp, _i64, _i64, _vp, _vp, _vp, _vp]),
     "w8a8_lm_head_argmax_tiled_act": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _sz,

@@ -20,8 +20,11 @@ __all__ = [
     "verify_sample_workspace_bytes", "sample_weights", "w4_shape", "quantize_weight_w4",
     "linear_w4", "lm_head_argmax_w4", "residual_rmsnorm_quant", "silu_mul_quant",
     "quantize_act_tiled", "linear_tiled_act", "verify_attention", "qk_norm_rope_append",
-    "pack_v_cache", "hbm_read_probe", "HBM_PROBE_SINK_WORDS",
+    "pack_v_cache", "hbm_read_probe", "HBM_PROBE_SINK_WORDS", "lm_head_verify_noalloc",
+    "NOALLOC_MAX_ROWS",
 ]
+
+NOALLOC_MAX_ROWS = 288        # W8A8_NOALLOC_MAX_ROWS
 
 HBM_PROBE_SINK_WORDS = 1      # W8A8_HBM_PROBE_SINK_WORDS
 
@@ -246,6 +249,39 @@ def lm_head_verify(xq, x_scale, wq_tiled, w_scale, draft, *, want_logits=False,
                                     0 if ws is None else ws.numel(), _stream(dev)))
     return logits, argmax, accept_len, next_token
 
+
+
+def lm_head_verify_noalloc(xq, x_scale, wq_tiled, w_scale, draft, *, logits=None, argmax=None,
+                           accept_len=None, next_token=None):
+    """:func:`lm_head_verify` through the entry point that takes no workspace
+    (the argmax keys live in the library's per-GPU scratch array; at most
+    ``NOALLOC_MAX_ROWS`` verified rows).  Outputs that are not passed are
+    allocated here with torch before the call; pass them all to keep the
+    call allocation-free.  Returns ``(logits or None, argmax or None,
+    accept_len, next_token)``."""
+    _need(xq, "xq", torch.int8, 2)
+    dev = xq.device
+    _need(x_scale, "x_scale", torch.float32, 1, dev)
+    _need(w_scale, "w_scale", torch.float32, 1, dev)
+    _need(draft, "draft", torch.int32, 2, dev)
+    R, K = xq.shape
+    V = w_scale.shape[0]
+    B, G = draft.shape
+    if R != B * (G + 1) or x_scale.shape[0] != R:
+        raise ValueError(f"xq and x_scale must have B*(G+1) = {B * (G + 1)} rows")
+    _need(wq_tiled, "wq_tiled", torch.int8, 4, dev)
+    if tuple(wq_tiled.shape) != tiled_shape(V, K):
+        raise ValueError(f"wq_tiled must have shape {tiled_shape(V, K)}")
+    if logits is not None:
+        logits = _out(logits, (R, V), torch.float32, dev, "logits")
+    if argmax is not None:
+        argmax = _out(argmax, (R,), torch.int32, dev, "argmax")
+    accept_len = _out(accept_len, (B,), torch.int32, dev, "accept_len")
+    next_token = _out(next_token, (B,), torch.int32, dev, "next_token")
+    check(lib().w8a8_lm_head_verify_noalloc(_ptr(xq), _ptr(x_scale), _ptr(wq_tiled), _ptr(w_scale),
+                                            V, K, _ptr(draft), B, G, _ptr(logits), _ptr(argmax),
+                                            _ptr(accept_len), _ptr(next_token), _stream(dev)))
+    return logits, argmax, accept_len, next_token
 
 def lm_head_argmax(xq, x_scale, wq_tiled, w_scale, *, logits=None,
                    workspace: Workspace | None = None, events=None):

@@ -335,6 +335,29 @@ w8a8_status w8a8_lm_head_verify(const int8_t* xq, const float* x_scale, const in
                                                  next_token, st), fn);
 }
 
+w8a8_status w8a8_lm_head_verify_noalloc(const int8_t* xq, const float* x_scale,
+                                        const int8_t* wq_tiled, const float* w_scale, int64_t V,
+                                        int64_t K, const int32_t* draft, int64_t B, int64_t G,
+                                        float* logits, int32_t* argmax, int32_t* accept_len,
+                                        int32_t* next_token, void* stream) {
+  static const char* fn = "w8a8_lm_head_verify_noalloc";
+  g_last_error.clear();
+  if (w8a8_status s = check_accept_keys(fn, draft, B, G, argmax, accept_len, next_token)) return s;
+  if (B == 0) return W8A8_OK;
+  if (B * (G + 1) > W8A8_NOALLOC_MAX_ROWS)
+    return fail(W8A8_ERR_UNSUPPORTED, fn,
+                "B*(G+1) exceeds W8A8_NOALLOC_MAX_ROWS (288 rows of argmax keys in the library's "
+                "scratch array); use w8a8_lm_head_verify with a workspace");
+  if (w8a8_status s = check_lm_head_operands(fn, xq, x_scale, wq_tiled, w_scale, B * (G + 1), V, K,
+                                             logits))
+    return s;
+  return hip_status(w8a8_launch_lm_head_verify_noalloc(xq, x_scale, wq_tiled, w_scale, V, K, draft,
+                                                       B, G, logits, argmax, accept_len,
+                                                       next_token,
+                                                       reinterpret_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 w8a8_status w8a8_bf16_linear(const uint16_t* x_bf16, const uint16_t* w_bf16, int64_t M, int64_t N,
                              int64_t K, uint16_t* y_bf16, float* y_f32, void* stream) {
   static const char* fn = "w8a8_bf16_linear";

@@ -156,3 +156,9 @@ hipError_t w8a8_launch_qk_norm_rope_append(const uint16_t* qkv, int64_t B, int64
 
 hipError_t w8a8_launch_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink,
                                       hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
+hipError_t w8a8_launch_lm_head_verify_noalloc(const int8_t* xq, const float* x_scale,
+                                              const int8_t* wq_tiled, const float* w_scale,
+                                              int64_t V, int64_t K, const int32_t* draft,
+                                              int64_t B, int64_t G, float* logits,
+                                              int32_t* argmax, int32_t* accept_len,
+                                              int32_t* next_token, hipStream_t stream);
