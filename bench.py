@@ -73,6 +73,12 @@ def parse_args():
                    help="summary of a --kernel-trace --stats run of --batched-verify-probe")
     p.add_argument("--attention-probe", action="store_true",
                    help="only the attention scaling runs (for rocprofv3 --kernel-trace)")
+    p.add_argument("--launch-probe", action="store_true",
+                   help="only the launch-overhead runs (M=5 layer linears as a graph, the "
+                        "headline step eager and as a graph) for rocprofv3 --kernel-trace")
+    p.add_argument("--ingest-launch-trace", metavar="TRACE_DIR",
+                   help="per-kernel duration and gap summary of a --kernel-trace run of "
+                        "--launch-probe")
     p.add_argument("--ingest-attention-trace", metavar="TRACE_DIR",
                    help="per-launch-shape summary of a --kernel-trace run of --attention-probe")
     return p.parse_args()
@@ -113,6 +119,31 @@ def read_traffic():
         return None
 
 
+def read_batched_counters():
+    """Per-shape MfmaUtil and HBM traffic over algorithmic bytes of the
+    288-row kernels from the committed rocprofv3 --pmc summary, with
+    ``stale`` set when the summary was taken on another source of the
+    batched kernels than the one built here."""
+    path = os.path.join(ROOT, "profiles", "gemm_w8a8_batched_m288_counters.txt")
+    src = os.path.join(ROOT, "w8a8_quantized_verification_amd", "csrc", "gemm_w8a8_batched.hip")
+    if not os.path.exists(path):
+        return None
+    out, cur, sha = {}, None, None
+    for line in open(path):
+        line = line.rstrip()
+        if line.startswith("[") and "]" in line:
+            cur = line[1:line.index("]")]
+            out[cur] = {}
+        elif line.startswith("kernel_source_sha:"):
+            sha = line.split(":", 1)[1].strip()
+        elif cur and ":" in line and not line.startswith("#"):
+            k, v = (x.strip() for x in line.split(":", 1))
+            if k in ("MfmaUtil", "hbm_over_algorithmic", "duration_us_under_counters"):
+                out[cur][k] = float(v)
+    return {"per_shape": out, "kernel_source_sha": sha, "stale": sha != file_sha(src),
+            "source": "profiles/gemm_w8a8_batched_m288_counters.txt"}
+
+
 def make_weight(N, K, workload, index, device, tiled=True, with_bf16=False):
     """Random-init N(0, 0.02) fp32 weight drawn on the device (seeded by
     workload and index), quantized to int8 per output channel by the library;
@@ -127,9 +158,12 @@ def make_weight(N, K, workload, index, device, tiled=True, with_bf16=False):
     return wq, ws, wb
 
 
-def graph_time(fns, replays=20):
-    """Capture the callables into one HIP graph; return the mean replay time
-    in seconds (one replay runs every callable once, in order)."""
+def graph_time(fns, replays=20, execs=2):
+    """Capture the callables into ``execs`` identical HIP graphs and replay
+    them in turn; return the mean time of one replay in seconds (a replay
+    runs every callable once, in order).  Alternating two graph execs keeps
+    the stream fed: replaying one exec back to back leaves a ~9 us bubble at
+    every replay boundary (kernel trace of --launch-probe)."""
     import torch
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -138,18 +172,21 @@ def graph_time(fns, replays=20):
             f()
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        for f in fns:
-            f()
-    for _ in range(3):
-        g.replay()
+    gs = []
+    for _ in range(execs):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for f in fns:
+                f()
+        gs.append(g)
+    for i in range(3 * execs):
+        gs[i % execs].replay()
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
-    for _ in range(replays):
-        g.replay()
+    for i in range(replays):
+        gs[i % execs].replay()
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / replays / 1e3
@@ -213,15 +250,23 @@ def ingest_pmc(fetch_dir, write_dir, command):
 
 
 def ingest_trace(trace_dir, command, out_path):
-    """Short text summary of a rocprofv3 --kernel-trace --stats csv run."""
+    """Short text summary of a rocprofv3 --kernel-trace --stats csv run: per
+    kernel the average, median, minimum and maximum duration and the call
+    count (the median from the per-dispatch kernel trace)."""
+    import numpy as np
     rows = _csv_rows(trace_dir, "kernel_stats.csv")
+    per = {}
+    for r in _csv_rows(trace_dir, "kernel_trace.csv"):
+        per.setdefault(r["Kernel_Name"], []).append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     lines = ["# rocprofv3 kernel statistics", f"# command: {command}",
-             f"{'avg_us':>10} {'min_us':>10} {'max_us':>10} {'calls':>6}  kernel"]
+             f"{'avg_us':>10} {'median_us':>10} {'min_us':>10} {'max_us':>10} {'calls':>6}  kernel"]
     for r in rows:
         n = r["Name"]
+        med = float(np.median(per[n])) if n in per else float("nan")
         if len(n) > 110:
             n = n[:107] + "..."
-        lines.append(f"{float(r['AverageNs']) / 1e3:10.2f} {float(r['MinNs']) / 1e3:10.2f} "
+        lines.append(f"{float(r['AverageNs']) / 1e3:10.2f} {med:10.2f} {float(r['MinNs']) / 1e3:10.2f} "
                      f"{float(r['MaxNs']) / 1e3:10.2f} {int(r['Calls']):6d}  {n}")
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -391,6 +436,10 @@ def main():
         ingest_trace(args.ingest_batched_trace, args.command,
                      os.path.join(ROOT, "profiles", "lm_head_verify_m288_kernel_trace.txt"))
         return
+    if args.ingest_launch_trace:
+        ingest_launch_trace(args.ingest_launch_trace, args.command,
+                            os.path.join(ROOT, "profiles", "launch_gaps_m5_kernel_trace.txt"))
+        return
     if args.ingest_attention_trace:
         ingest_attention_trace(args.ingest_attention_trace, args.command,
                                os.path.join(ROOT, "profiles", "verify_attention_kernel_trace.txt"))
@@ -483,6 +532,9 @@ def main():
 
     if args.pmc_probe_batched:
         pmc_probe_batched(dev)
+        return
+    if args.launch_probe:
+        launch_probe(dev, step, wsp)
         return
     if args.pmc_probe:
         # fixed short run for counter collection: a plain 1 GiB copy (the
@@ -607,6 +659,7 @@ def main():
         extra["graph_step_separate_calls"] = {"ms_per_step": round(t_sep * 1e3, 5),
                                               "verified_tokens_per_s": round(M / t_sep, 1)}
         extra.update(extra_measurements(dev, copies, x_dev, xq, xsc, wsp))
+        extra["gemm_w8a8_batched_m288_counters"] = read_batched_counters()
         if not args.no_stack:
             extra["qwen3_32b_stack_m8"] = stack32b_measurement(dev, wsp)
         out["extra"] = extra
@@ -691,6 +744,102 @@ def hbm_probe_run(w8, bufs, n):
             "mean_GBs": round(float(nbytes / (us.mean() * 1e-6) / 1e9), 1),
             "best_GBs": round(float(gbs.max()), 1),
             "kernel": "hbm_read_kernel (16-byte non-temporal loads, one contiguous 32 KiB chunk per 256-thread workgroup)"}
+
+
+LAUNCH_PHASES = ("layer linears M=5 (graph: qkv, o, gate_up, down; 2 weight sets)",
+                 "headline step, eager (quantize_act, lm_head_argmax, accept_from_keys)",
+                 "headline step, one HIP graph exec of 2 steps replayed",
+                 "headline step, two HIP graph execs of 2 steps replayed in turn")
+
+
+def launch_probe(dev, step, wsp, reps=20):
+    """Three phases separated by 50 ms of idle time, for a kernel trace:
+    the Qwen3-8B layer's fused linears at M = 5 replayed as one HIP graph
+    (two weight sets, so 8 launches per replay), ``reps`` eager headline
+    steps, and ``reps`` headline steps replayed as a graph of two."""
+    import numpy as np
+    import torch
+
+    import synth
+    import w8a8_quantized_verification_amd as w8
+    M = 5
+    lins = synth.QWEN3_8B_LAYER
+    groups = ((0, 1, 2), (3,), (4, 5), (6,))
+    sets = []
+    for c in range(2):
+        row = []
+        for gi, grp in enumerate(groups):
+            N, K = sum(lins[i].N for i in grp), lins[grp[0]].K
+            w = torch.cat([synth.weights_device(synth.W_LAYER_M5, 9000 + 100 * gi + 10 * c + i,
+                                                lins[i].N, K, dev) for i in grp])
+            wq, ws = w8.quantize_weight(w, tiled=True)
+            del w
+            x = torch.from_numpy(synth.activations_bf16(synth.W_LAYER_M5, M, K, outliers=True)
+                                 .view(np.int16).copy()).view(torch.bfloat16).to(dev)
+            xq, xs = w8.quantize_act(x)
+            row.append((xq, xs, wq, ws, torch.empty(M, N, dtype=torch.bfloat16, device=dev)))
+        sets.append(row)
+    lw = w8.Workspace()
+    fns = [(lambda a=a: w8.linear(a[0], a[1], a[2], a[3], y_bf16=a[4], workspace=lw))
+           for row in sets for a in row]
+    torch.cuda.synchronize()
+    time.sleep(0.05)
+    graph_time(fns, replays=reps)
+    torch.cuda.synchronize()
+    time.sleep(0.05)
+    for i in range(reps):
+        step(i)
+    torch.cuda.synchronize()
+    time.sleep(0.05)
+    graph_time([lambda: step(0), lambda: step(1)], replays=reps // 2, execs=1)
+    torch.cuda.synchronize()
+    time.sleep(0.05)
+    graph_time([lambda: step(0), lambda: step(1)], replays=reps // 2, execs=2)
+    torch.cuda.synchronize()
+    print(json.dumps({"launch_probe": "done", "phases": LAUNCH_PHASES}), flush=True)
+
+
+def ingest_launch_trace(trace_dir, command, out_path):
+    """Per-phase summary of a --kernel-trace run of --launch-probe: for each
+    kernel (name and grid), the median duration and the median gap between
+    the end of the kernel before it and its start; phases are told apart by
+    idle time over 10 ms, warm-up launches (graph capture, first replays)
+    are dropped by taking the last replays only."""
+    import numpy as np
+    rows = _csv_rows(trace_dir, "kernel_trace.csv")
+    ev = sorted(((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"],
+                  int(r.get("Grid_Size_X") or r.get("Grid_Size") or 0)) for r in rows))
+    phases, cur = [], []
+    for e in ev:
+        if cur and e[0] - cur[-1][1] > 10_000_000:
+            phases.append(cur)
+            cur = []
+        cur.append(e)
+    if cur:
+        phases.append(cur)
+    phases = phases[-len(LAUNCH_PHASES):]
+    lines = ["# Kernel durations and launch gaps: rocprofv3 --kernel-trace of bench.py --launch-probe",
+             f"# command: {command}",
+             "# gap = start of a kernel minus end of the kernel before it (same stream)",
+             "# per kernel (name, grid threads): median duration, median gap before it, count"]
+    for title, ph in zip(LAUNCH_PHASES, phases):
+        half = ph[len(ph) // 2:]             # the later half: past capture and warm-up
+        stats = {}
+        for k in range(1, len(half)):
+            s0, e0, name, grid = half[k]
+            key = (name.split("(")[0].replace("void ", ""), grid)
+            stats.setdefault(key, {"dur": [], "gap": []})
+            stats[key]["dur"].append((e0 - s0) / 1e3)
+            stats[key]["gap"].append((s0 - half[k - 1][1]) / 1e3)
+        span = (half[-1][1] - half[0][0]) / 1e3
+        lines.append(f"[{title}] kernels {len(half)}, span {span:.1f} us")
+        for (name, grid), v in stats.items():
+            n = name if len(name) <= 70 else name[:67] + "..."
+            lines.append(f"  {np.median(v['dur']):9.2f} us dur  {np.median(v['gap']):7.2f} us gap "
+                         f"{len(v['dur']):5d}  grid {grid:9d}  {n}")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def rotation_copies(N, K):
