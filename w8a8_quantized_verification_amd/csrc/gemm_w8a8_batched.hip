@@ -401,31 +401,202 @@ __global__ __launch_bounds__(KH * kLdsWaves * kWave) void gemm_w8a8_lds(BatchedA
   batched_epilogue<MB, TN, kArgmax>(g, acc, mt * FA + wr * MB, ng * FB + wc * TN, lane);
 }
 
-// The same pipeline on v_mfma_i32_32x32x32_i8: a workgroup of four waves
-// computes RB blocks of 32 rows x 4*CW blocks of 32 channels; wave w owns
-// channel blocks w*CW .. +CW-1 over all RB row blocks.  The staged
-// fragments are the same 1 KiB (16-row block or 16-channel tile, k step)
-// units; for the 32-wide half h of a step, lane l (r = l % 32, g = l / 32)
-// reads unit 2*b + r/16 of its 32-block b at tile lane (r % 16) + 16 (2h +
-// g), for both operands, so A and B pair the same k.  Lane l gets rows
-// 8 (v / 4) + 4 g + v % 4 of column r in accumulator v.  The launch bound
-// holds every form to 128 registers (at least four workgroups per CU).
-// With the argmax fold's transpose and row maxima inside the stages, the
-// 96-row form (90 registers, 32 KB of LDS) runs five per CU: 288 rows x
-// 151936 channels ~288 us, against ~309 at four per CU and 362-384 at
-// three (the transpose padded, in LDS of its own).
 typedef int v16i __attribute__((ext_vector_type(16)));
 
-template <int RB, int CW, int P, bool kArgmax, bool kRowA = false>
-__global__ __launch_bounds__(kLdsWaves * kWave, 4) void gemm_w8a8_lds32(BatchedArgs g) {
-  constexpr int FA = 2 * RB, FB = 2 * kLdsWaves * CW, F = FA + FB;
-  constexpr int FW = (F + kLdsWaves - 1) / kLdsWaves;
-  constexpr int STAGE = FW * kLdsWaves * 1024;
+// 64-bit argmax keys held as two 32-bit lanes' words.
+__device__ __forceinline__ unsigned long long key_max(unsigned long long a, unsigned long long b) {
+  return b > a ? b : a;
+}
+
+// DPP move of a 64-bit value (both words with the same lane pattern).
+template <int kCtrl>
+__device__ __forceinline__ unsigned long long dpp64(unsigned long long x) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)x, kCtrl, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(x >> 32), kCtrl, 0xF, 0xF, false);
+  return ((unsigned long long)hi << 32) | lo;
+}
+
+// One butterfly level: a lane and its DPP partner (kCtrl) hold keys lo and
+// hi for the same two rows; the lane with `upper` set keeps the row of hi,
+// the other the row of lo, each the larger of its own and the partner's
+// key.  The key to send is selected before the DPP move, so the move runs
+// with every lane active (a DPP read from a lane that is off in EXEC
+// returns 0, and a select of two DPP results can be compiled into exactly
+// such a branch).
+template <int kCtrl>
+__device__ __forceinline__ unsigned long long keep_max(unsigned long long lo, unsigned long long hi,
+                                                       bool upper) {
+  const unsigned long long keep = upper ? hi : lo, send = upper ? lo : hi;
+  return key_max(keep, dpp64<kCtrl>(send));
+}
+constexpr int kDppMirror = 0x140;       // lane j <-> 15 - j in each 16
+constexpr int kDppHalfMirror = 0x141;   // lane j <-> 7 - j in each 8
+constexpr int kDppXor3 = 0x1B;          // quad_perm [3,2,1,0]
+constexpr int kDppXor1 = 0xB1;          // quad_perm [1,0,3,2]
+
+// Epilogue of the 32 x 32 kernels: y32 = (acc * x_scale[m]) * w_scale[n]
+// for wave `wave`'s RB x CW accumulator blocks (rows (mt*RB + i)*32 + 8 (v
+// / 4) + 4 g + v % 4, column (ng*4*CW + wave*CW + j)*32 + l % 32), written
+// as requested (kStores) and folded into the argmax keys (kArgmax).  xs_sh
+// holds the activation scales of the workgroup's RB*32 rows (written to
+// LDS before the k loop, so a lane reads the 16 it needs with four 16-byte
+// loads) and ws_lane[j] the weight scale of the lane's column of block j
+// (registers loaded before the k loop); no global load sits between the
+// epilogue's stores.  `stage_mem` is the workgroup's staging memory (at
+// least lds32_row_key_bytes(RB)), free once every wave is past its last k
+// step.
+//
+// Argmax fold, per row block i: lane l holds, for each of the 16 rows
+// 8 (v / 4) + 4 g + v % 4 of its half-wave, the argmax keys (value, then
+// lower index first; 0 outside M x N) of its CW columns, and keeps their
+// maximum.  The maximum over the half-wave's 32 lanes is found for all 16
+// rows at once by a transposed butterfly: at each of five levels a lane
+// pairs with lane l ^ 16 (permlane16 swap), l ^ 15, l ^ 7, l ^ 3 and l ^ 1
+// (DPP) and keeps the larger key of each pair for half of its remaining
+// rows, so the even lane 2v of each half ends with row v's key and writes
+// it to LDS.  The four waves' keys meet there and wave 0 folds each of the
+// workgroup's rows with one device-scope atomic max.
+constexpr int lds32_row_key_bytes(int RB) { return kLdsWaves * RB * 32 * 8; }
+
+template <int RB, int CW, bool kArgmax, bool kStores>
+__device__ __forceinline__ void lds32_epilogue(const BatchedArgs& g, const v16i (&acc)[RB][CW],
+                                               const float* xs_sh, const float (&ws_lane)[CW],
+                                               int8_t* stage_mem, int mt, int ng, int wave,
+                                               int lane) {
+  const int r32 = lane & 31, hi = lane >> 5;
+  const int c0 = (ng * kLdsWaves + wave) * CW;   // this wave's first 32-channel block
+  unsigned long long* rows = reinterpret_cast<unsigned long long*>(stage_mem);
+  // the row keys go to the stages: every wave must be past its last k step
+  if constexpr (kArgmax) __syncthreads();
+
+#pragma unroll
+  for (int i = 0; i < RB; ++i) {
+    // rows 8 q + 4 g .. +3 of this block for q = 0..3
+    v4f xsq[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      xsq[q] = *reinterpret_cast<const v4f*>(xs_sh + i * 32 + 8 * q + 4 * hi);
+    const int rows_left = g.M - (mt * RB + i) * 32;   // rows of this block below M
+    unsigned long long m[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) m[v] = 0ull;
+#pragma unroll
+    for (int j = 0; j < CW; ++j) {
+      const int n = (c0 + j) * 32 + r32;
+      const bool n_ok = n < g.N;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int rr = 8 * (v >> 2) + (v & 3) + 4 * hi;   // row inside the 32-block
+        const bool ok = rr < rows_left && n_ok;
+        const int32_t a = acc[i][j][v];
+        const float y = (static_cast<float>(a) * xsq[v >> 2][v & 3]) * ws_lane[j];
+        if constexpr (kStores) {
+          if (ok) {
+            const size_t off = (size_t)((mt * RB + i) * 32 + rr) * (size_t)g.N + (size_t)n;
+            if (g.y_f32) g.y_f32[off] = y;
+            if (g.y_bf16) g.y_bf16[off] = f32_to_bf16_rne(y);
+            if (g.acc) g.acc[off] = a;
+          }
+        }
+        if constexpr (kArgmax) {
+          // (no branch: the key is masked to 0 outside M x N)
+          const unsigned long long key = argmax_key(y, n) & (0ull - (unsigned long long)ok);
+          m[v] = key_max(m[v], key);   // blocks in increasing column order
+        }
+      }
+    }
+    if constexpr (kArgmax) {
+      // level 1 (l ^ 16): rows 0..7 stay in lanes with bit 4 clear, 8..15 in the others
+      unsigned long long m1[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)m[k], (uint32_t)m[k + 8], false, false);
+        const auto hw = __builtin_amdgcn_permlane16_swap((uint32_t)(m[k] >> 32),
+                                                         (uint32_t)(m[k + 8] >> 32), false, false);
+        m1[k] = key_max(((unsigned long long)(uint32_t)hw[0] << 32) | (uint32_t)lo[0],
+                        ((unsigned long long)(uint32_t)hw[1] << 32) | (uint32_t)lo[1]);
+      }
+      // levels 2..4 (l ^ 15, l ^ 7, l ^ 3): bit 3, 2, 1 of the lane picks the rows kept
+      unsigned long long m2[4], m3[2];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) m2[k] = keep_max<kDppMirror>(m1[k], m1[k + 4], (lane & 8) != 0);
+#pragma unroll
+      for (int k = 0; k < 2; ++k) m3[k] = keep_max<kDppHalfMirror>(m2[k], m2[k + 2], (lane & 4) != 0);
+      unsigned long long x = keep_max<kDppXor3>(m3[0], m3[1], (lane & 2) != 0);
+      // level 5 (l ^ 1): lanes 2v and 2v + 1 of each half hold row v's key
+      x = key_max(x, dpp64<kDppXor1>(x));
+      if ((lane & 1) == 0) {
+        const int v = (lane >> 1) & 15;
+        const int rr = 8 * (v >> 2) + (v & 3) + 4 * hi;
+        rows[(wave * RB + i) * 32 + rr] = x;
+      }
+    }
+  }
+  if constexpr (kArgmax) {
+    __syncthreads();
+    if (wave == 0) {
+      for (int r = lane; r < RB * 32; r += kWave) {
+        unsigned long long k = rows[r];
+#pragma unroll
+        for (int w = 1; w < kLdsWaves; ++w) k = key_max(k, rows[w * RB * 32 + r]);
+        const int m = mt * RB * 32 + r;
+        if (k != 0ull && m < g.M) {
+          const size_t sub = (size_t)m * g.subkeys + (ng % g.subkeys);
+          __hip_atomic_fetch_max(&g.keys[sub * g.key_stride], k, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    }
+  }
+}
+
+// The pipeline on v_mfma_i32_32x32x32_i8, which does twice the work of the
+// 16 x 16 x 64 instruction for the same two operand KiB: a workgroup of
+// four waves computes RB blocks of 32 rows x 4*CW blocks of 32 channels;
+// wave w owns channel blocks w*CW .. +CW-1 over all RB row blocks.  The
+// operands are the same 1 KiB (16-row block or 16-channel tile, k step)
+// units; for the 32-wide half h of a step, lane l (r = l % 32, g = l / 32)
+// takes unit 2*b + r/16 of its 32-block b at tile lane (r % 16) + 16 (2h +
+// g), for both operands, so A and B pair the same k.  Lane l gets rows
+// 8 (v / 4) + 4 g + v % 4 of column r in accumulator v.
+//
+// A wave's weight fragments feed that wave alone, so only the activation
+// fragments, which all four waves read, go through LDS.  Per k step a wave
+// loads, for each of its blocks, its two 16-byte pieces per lane straight
+// into registers, P - 1 steps ahead, in a ring of P register slots (the
+// loop is unrolled P times so that every slot index is static); the
+// activation fragments of the same step go to LDS stage s % P with
+// direct-to-LDS loads, and one barrier per step publishes them.  Against
+// staging both operands in LDS this takes the weight bytes out of the LDS
+// (their DMA writes and the waves' LDS reads of them) and gives P - 1 steps
+// of lookahead for the same LDS; with CW = 2 each activation fragment read
+// from LDS feeds two MFMAs.
+//
+// Every wave issues the same loads per step, with no wave-dependent branch
+// in the k loop (a branch there makes the compiler drain all loads before
+// the next MFMA): when the FA = 2*RB activation fragments do not split
+// evenly over the four waves (FA % 4 == 2), waves 2w and 2w+1 both copy
+// fragment 4*(FA/4) + w, the same bytes to the same LDS, so each wave
+// issues FA/4 + 1 of them.  Fragments past the last row block or channel
+// tile are fetched from block / tile 0 (in bounds) and their results
+// dropped by the epilogue; the steps past the end are fetched again from
+// the last one.
+template <int RB, int CW, int P, bool kArgmax, bool kStores, bool kRowA = false>
+__global__ __launch_bounds__(kLdsWaves * kWave, CW == 1 ? 4 : 2) void gemm_w8a8_lds32(BatchedArgs g) {
+  constexpr int FA = 2 * RB;                               // activation fragments per step
+  constexpr int FAF = FA / kLdsWaves;                      // whole share per wave
+  constexpr bool kDup = FA % kLdsWaves != 0;               // (FA even: then FA % 4 == 2)
+  constexpr int LA = FAF + (kDup ? 1 : 0);                 // activation loads per wave per step
+  constexpr int LW = LA + 2 * CW;                          // loads per wave per step
+  constexpr int STAGE = FA * 1024;
+  constexpr int D = P - 1;                                 // steps of lookahead
   static_assert(P >= 2, "one stage read while the next one fills");
-  // the stages, also the argmax fold's transpose buffer once the k loop is done
-  constexpr int kTrBytes = kArgmax ? kLdsWaves * 32 * 32 * 8 : 0;
-  constexpr int kStages = P * STAGE >= kTrBytes ? P : (kTrBytes + STAGE - 1) / STAGE;
-  __shared__ __attribute__((aligned(1024))) int8_t stage[kStages][STAGE];
+  constexpr int kTrBytes = kArgmax ? lds32_row_key_bytes(RB) : 0;
+  constexpr int kStageBytes = P * STAGE >= kTrBytes ? P * STAGE : kTrBytes;
+  // (one LDS array: the stages, then the workgroup's row scales; a second
+  // LDS object makes the compiler wait for the direct-to-LDS loads before
+  // every LDS read)
+  __shared__ __attribute__((aligned(1024))) int8_t stage_mem[kStageBytes + RB * 32 * 4];
 
   const int b = blockIdx.x;
   const int xcd = b % kXcds;
@@ -438,42 +609,64 @@ __global__ __launch_bounds__(kLdsWaves * kWave, 4) void gemm_w8a8_lds32(BatchedA
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int steps = g.steps;
   const int mblocks = (g.M + 15) / 16;
+  const int r32 = lane & 31, hi = lane >> 5;
+  const int lane_off = ((r32 & 15) + 16 * hi) << 4;
 
-  const int8_t* src[FW];
+  // the epilogue's scales: the workgroup's row scales into LDS after the
+  // stages (visible after the k loop's first barrier), the lane's column
+  // scales in registers
+  float* xs_sh = reinterpret_cast<float*>(stage_mem + kStageBytes);
+  if (threadIdx.x < RB * 32) {
+    const int m = mt * RB * 32 + threadIdx.x;
+    xs_sh[threadIdx.x] = m < g.M ? g.xs[m] : 0.0f;
+  }
+  float ws_lane[CW];
 #pragma unroll
-  for (int j = 0; j < FW; ++j) {
-    const int f = wave + kLdsWaves * j;
-    if (f >= F) {
-      src[j] = g.xq + (lane << 4);
-    } else if (f < FA) {
-      const int rb = mt * FA + f;
-      if constexpr (kRowA) {
-        // row-major activations (K a multiple of 64): lane l fetches row
-        // 16 rb + l % 16, bytes 16 (l / 16) .. +15 of the step, landing at
-        // l * 16 as in the tiled layout; rows past M repeat row M - 1 (they
-        // only feed accumulator rows the epilogue drops)
-        const int row = min(rb * 16 + (lane & 15), g.M - 1);
-        src[j] = g.xq + (size_t)row * (size_t)g.K + ((lane >> 4) << 4);
-      } else {
-        src[j] = g.xq + ((size_t)(rb < mblocks ? rb : 0) * (size_t)steps << 10) + (lane << 4);
-      }
+  for (int j = 0; j < CW; ++j) {
+    const int n = ((ng * kLdsWaves + wave) * CW + j) * 32 + r32;
+    ws_lane[j] = n < g.N ? g.ws[n] : 0.0f;
+  }
+
+  // activation fragments of every step: wave w copies fragments w, w+4, ...
+  // (FAF of them) and, when FA % 4 == 2, fragment 4 FAF + w / 2
+  const int8_t* src[LA];
+#pragma unroll
+  for (int j = 0; j < LA; ++j) {
+    const int f = j < FAF ? wave + kLdsWaves * j : kLdsWaves * FAF + (wave >> 1);
+    const int rb = mt * FA + f;
+    if constexpr (kRowA) {
+      const int row = min(rb * 16 + (lane & 15), g.M - 1);
+      src[j] = g.xq + (size_t)row * (size_t)g.K + ((lane >> 4) << 4);
     } else {
-      const int t16 = ng * FB + (f - FA);
-      src[j] = g.wq + ((size_t)(t16 < g.tiles16 ? t16 : 0) * (size_t)steps << 10) + (lane << 4);
+      src[j] = g.xq + ((size_t)(rb < mblocks ? rb : 0) * (size_t)steps << 10) + (lane << 4);
     }
   }
-  auto issue = [&](int p, int s) {
+  auto issue_a = [&](int p, int s) {
+    s = min(s, steps - 1);
+    const size_t off = kRowA ? (size_t)s * 64 : ((size_t)s << 10);
+#pragma unroll
+    for (int j = 0; j < LA; ++j) {
+      const int f = j < FAF ? wave + kLdsWaves * j : kLdsWaves * FAF + (wave >> 1);
+      lds_dma16(src[j] + off, stage_mem + p * STAGE + f * 1024);
+    }
+  };
+  // this lane's weight units (tiles past the last are fetched from tile 0;
+  // their columns are dropped by the epilogue)
+  const int8_t* wsrc[CW];
+#pragma unroll
+  for (int j = 0; j < CW; ++j) {
+    const int t16 = ((ng * kLdsWaves + wave) * CW + j) * 2 + (r32 >> 4);
+    wsrc[j] = g.wq + ((size_t)(t16 < g.tiles16 ? t16 : 0) * (size_t)steps << 10) + lane_off;
+  }
+  auto load_b = [&](v4i (&dst)[CW][2], int s) {
     s = min(s, steps - 1);
 #pragma unroll
-    for (int j = 0; j < FW; ++j) {
-      const int f = wave + kLdsWaves * j;
-      const size_t off = (kRowA && f < FA) ? (size_t)s * 64 : ((size_t)s << 10);
-      lds_dma16(src[j] + off, &stage[p][f * 1024]);
+    for (int j = 0; j < CW; ++j) {
+      dst[j][0] = *reinterpret_cast<const v4i*>(wsrc[j] + ((size_t)s << 10));
+      dst[j][1] = *reinterpret_cast<const v4i*>(wsrc[j] + ((size_t)s << 10) + 512);
     }
   };
 
-  const int r32 = lane & 31, hi = lane >> 5;
-  const int lane_off = ((r32 & 15) + 16 * hi) << 4;
   v16i acc[RB][CW];
 #pragma unroll
   for (int i = 0; i < RB; ++i)
@@ -482,123 +675,51 @@ __global__ __launch_bounds__(kLdsWaves * kWave, 4) void gemm_w8a8_lds32(BatchedA
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0;
 
+  v4i bq[P][CW][2];
 #pragma unroll
-  for (int u = 0; u < P - 1; ++u) issue(u, u);
-  for (int s = 0; s < steps; ++s) {
-    wait_vmcnt<(P - 2) * FW>();
-    __builtin_amdgcn_s_barrier();
+  for (int u = 0; u < D; ++u) {
+    issue_a(u, u);
+    load_b(bq[u], u);
+  }
+  // one k step: ring slot u = s % P holds step s's weights, stage u its
+  // activations
+  auto step = [&](int u, int s) {
+    // step s's loads (issued D steps ago) are in; steps s+1 .. s+D-1 may
+    // still be in flight (loads complete in issue order)
+    wait_vmcnt<(D - 1) * LW>();
+    __builtin_amdgcn_s_barrier();   // every wave's activations of step s are in LDS
     compiler_fence();
-    issue((s + P - 1) % P, s + P - 1);
-    const int8_t* st = stage[s % P];
+    issue_a((u + D) % P, s + D);    // the stage step s-1 used (every wave is past it)
+    load_b(bq[(u + D) % P], s + D);
+    const int8_t* st = stage_mem + u * STAGE;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      v4i a[RB], bb[CW];
+      v4i a[RB];
 #pragma unroll
       for (int i = 0; i < RB; ++i)
         a[i] = *reinterpret_cast<const v4i*>(st + (2 * i + (r32 >> 4)) * 1024 + (h << 9) + lane_off);
 #pragma unroll
-      for (int j = 0; j < CW; ++j)
-        bb[j] = *reinterpret_cast<const v4i*>(st + (FA + 2 * (wave * CW + j) + (r32 >> 4)) * 1024 +
-                                              (h << 9) + lane_off);
-#pragma unroll
       for (int i = 0; i < RB; ++i)
 #pragma unroll
         for (int j = 0; j < CW; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], bb[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], bq[u][j][h], acc[i][j], 0, 0, 0);
     }
     compiler_fence();
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this step's LDS reads are done
+  };
+  // whole rounds of P steps with no branch inside (so the ring stays in the
+  // same registers), then the last steps % P
+  int s0 = 0;
+  for (; s0 + P <= steps; s0 += P) {
+#pragma unroll
+    for (int u = 0; u < P; ++u) step(u, s0 + u);
   }
+#pragma unroll
+  for (int u = 0; u < P - 1; ++u)
+    if (s0 + u < steps) step(u, s0 + u);
   wait_vmcnt<0>();
 
-  // argmax fold: each wave transposes its (row, column) keys of one 32 x 32
-  // block at a time through LDS (the stages, free once every wave is past
-  // its last step) so that lane r < 32 reduces row r over the block's 32
-  // columns; the waves' row maxima meet in LDS and wave 0 folds each of the
-  // workgroup's rows with one device-scope atomic max.  Keys order by value
-  // and then by lower index, so their maximum is the row's argmax.
-  // 32 u64 per transposed row, column c of row r stored at c ^ r: the
-  // half-wave's writes of one row and each lane's reads of its own row
-  // across the columns both touch 32 distinct bank pairs, with no padding
-  // (so the transpose fits in the stages of the 96-row form)
-  constexpr int kTrStride = 32;
-  static_assert(!kArgmax || kLdsWaves * 32 * kTrStride * 8 <= kStages * STAGE,
-                "transpose fits the stages");
-  // each wave's RB * 32 row maxima go to the start of its own transpose
-  // region once its last transpose has been read (no LDS beyond the stages)
-  static_assert(RB * 32 <= 32 * kTrStride, "row maxima fit a transpose region");
-  unsigned long long* tr = reinterpret_cast<unsigned long long*>(&stage[0][0]) +
-                           (size_t)wave * 32 * kTrStride;
-  if constexpr (kArgmax) __syncthreads();
-  unsigned long long rk[RB];
-#pragma unroll
-  for (int i = 0; i < RB; ++i) rk[i] = 0ull;
-
-#pragma unroll
-  for (int j = 0; j < CW; ++j) {
-    const int c32 = ng * kLdsWaves * CW + wave * CW + j;   // 32-channel block
-    const int n = c32 * 32 + r32;
-    const bool n_ok = n < g.N;
-    const float wsn = n_ok ? g.ws[n] : 0.0f;
-#pragma unroll
-    for (int i = 0; i < RB; ++i) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int rr = 8 * (v >> 2) + 4 * hi + (v & 3);     // row inside the 32-block
-        const int m = (mt * RB + i) * 32 + rr;
-        unsigned long long key = 0ull;
-        if (m < g.M && n_ok) {
-          const int32_t a = acc[i][j][v];
-          const float y = (static_cast<float>(a) * g.xs[m]) * wsn;
-          const size_t o = (size_t)m * (size_t)g.N + (size_t)n;
-          if (g.y_f32) g.y_f32[o] = y;
-          if (g.y_bf16) g.y_bf16[o] = f32_to_bf16_rne(y);
-          if (g.acc) g.acc[o] = a;
-          key = argmax_key(y, n);
-        }
-        if constexpr (kArgmax) tr[rr * kTrStride + (r32 ^ rr)] = key;
-      }
-      if constexpr (kArgmax) {
-        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS writes landed
-        __builtin_amdgcn_wave_barrier();
-        if (lane < 32) {
-          unsigned long long k = rk[i];
-#pragma unroll 8
-          for (int c = 0; c < 32; ++c) {
-            const unsigned long long o = tr[lane * kTrStride + (c ^ lane)];
-            k = o > k ? o : k;
-          }
-          rk[i] = k;
-        }
-        __builtin_amdgcn_s_waitcnt(0xC07F);
-        __builtin_amdgcn_wave_barrier();
-      }
-    }
-  }
-  if constexpr (kArgmax) {
-    if (lane < 32) {
-#pragma unroll
-      for (int i = 0; i < RB; ++i) tr[i * 32 + lane] = rk[i];
-    }
-    __syncthreads();
-    if (wave == 0) {
-      for (int r = lane; r < RB * 32; r += kWave) {
-        const unsigned long long* rows0 = reinterpret_cast<const unsigned long long*>(&stage[0][0]);
-        unsigned long long k = rows0[r];
-#pragma unroll
-        for (int w = 1; w < kLdsWaves; ++w) {
-          const unsigned long long o = rows0[(size_t)w * 32 * kTrStride + r];
-          k = o > k ? o : k;
-        }
-        const int m = mt * RB * 32 + r;
-        if (k != 0ull && m < g.M) {
-          const size_t sub = (size_t)m * g.subkeys + (ng % g.subkeys);
-          __hip_atomic_fetch_max(&g.keys[sub * g.key_stride], k, __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT);
-        }
-      }
-    }
-  }
+  lds32_epilogue<RB, CW, kArgmax, kStores>(g, acc, xs_sh, ws_lane, stage_mem, mt, ng, wave, lane);
 }
 
 template <int RB, int CW, int P, bool kRowA = false>
@@ -607,10 +728,13 @@ static hipError_t launch_lds32(BatchedArgs g, bool argmax, hipStream_t stream) {
   g.mtiles = (g.M + 32 * RB - 1) / (32 * RB);
   const int64_t ng_padded = ((int64_t)g.ngroups + kXcds - 1) / kXcds * kXcds;
   const dim3 grid((unsigned)(ng_padded * g.mtiles)), block(kLdsWaves * kWave);
-  if (argmax)
-    hipLaunchKernelGGL((gemm_w8a8_lds32<RB, CW, P, true, kRowA>), grid, block, 0, stream, g);
+  const bool stores = g.y_bf16 || g.y_f32 || g.acc;
+  if (argmax && !stores)
+    hipLaunchKernelGGL((gemm_w8a8_lds32<RB, CW, P, true, false, kRowA>), grid, block, 0, stream, g);
+  else if (argmax)
+    hipLaunchKernelGGL((gemm_w8a8_lds32<RB, CW, P, true, true, kRowA>), grid, block, 0, stream, g);
   else
-    hipLaunchKernelGGL((gemm_w8a8_lds32<RB, CW, P, false, kRowA>), grid, block, 0, stream, g);
+    hipLaunchKernelGGL((gemm_w8a8_lds32<RB, CW, P, false, true, kRowA>), grid, block, 0, stream, g);
   return hipGetLastError();
 }
 
@@ -660,31 +784,29 @@ constexpr int64_t kLdsMinWorkgroups = 512;
 constexpr int kLdsSplit = 4, kLdsSplitStages = 3;
 constexpr int64_t kLdsSplitMinWorkgroups = 128;
 
-// The 32 x 32 form (64 rows x 128 channels per workgroup) where its grid
-// fills the chip, measured at 288 rows against the 16 x 16 pipeline:
-// q/k/v fused 4096 -> 6144 (240 workgroups) 22.8 vs 35.5 us, gate 4096 ->
-// 12288 (480) 33.3 vs 39.1 us, gate/up fused 4096 -> 24576 (960) 55-59 vs
-// 67 us; with 160 workgroups (o, down at 4096 channels) it is slower (22.1
-// vs 19.3 us, 50.1 vs 41.6 us), so those keep the k-sliced 16 x 16 form.
-// Stage count and tile by grid width, measured at 288 rows (A/B on one
-// box): wider grids keep more workgroups per CU with fewer stages, which
-// pays more than deeper prefetch (stages beyond these were slower
-// everywhere).  q/k/v 4096 -> 6144 (240 workgroups of 64 x 128): 4 stages,
-// 22.9 us (3: 27.8, 2: 44.1); gate 4096 -> 12288 (480): 3-4 stages, 32.4-33.0
-// us (2: 46.6); gate/up 4096 -> 24576 (960): 2 stages, 55.3 us (3: 58.0);
-// the 4096 -> 151936 LM head: 96 x 128 workgroups (each weight block read
-// once per 96 rows), 2 stages, ~288 us with the argmax folded in (64 x
-// 128, 3 stages: ~447 us).
+// The 32 x 32 kernel where its grid fills the chip (counted in 64-row x
+// 128-channel workgroups), measured at 288 rows against the 16 x 16
+// pipeline: q/k/v fused 4096 -> 6144 (240 workgroups) 22.8 vs 35.5 us,
+// gate 4096 -> 12288 (480) 33.3 vs 39.1 us, gate/up fused 4096 -> 24576
+// (960) 55-59 vs 67 us; with 160 workgroups (o, down at 4096 channels) it
+// is slower (22.1 vs 19.3 us, 50.1 vs 41.6 us), so those keep the k-sliced
+// 16 x 16 form.  Tiles and lookahead by grid width, measured at 288 rows
+// (A/B on one box, weights streamed into registers against the earlier
+// form that staged them in LDS): q/k/v 64 x 128 with 3 steps of lookahead
+// 20.9 us (staged: 22-23), gate the same 30.5-30.9 us (33.6-34.5), gate/up
+// 64 x 256 with 2 steps 51.9-52.2 us (57-60); the 4096 -> 151936 LM head
+// with the argmax folded in, 96 x 256 with 2 steps (each weight block read
+// once per 96 rows, three workgroups per CU): 213-219 us per verify step
+// against 252-265 us for the staged 96 x 128 form.
 constexpr int64_t kLds32MinWorkgroups = 224;
-constexpr int64_t kLds32DeepMinWorkgroups = 512;
-constexpr int64_t kLds32DoubleBufferMinWorkgroups = 768;
-constexpr int64_t kLds32WideMinWorkgroups = 2048;
+constexpr int64_t kLds32WideTileMinWorkgroups = 768;
+constexpr int64_t kLds32TallTileMinWorkgroups = 2048;
 
 static int64_t lds32_workgroups(int64_t M, int64_t N) {
   return ((N + 15) / 16 + 2 * kLdsWaves - 1) / (2 * kLdsWaves) * ((M + 63) / 64);
 }
 
-// the 96-row form's grid
+// the same count for 96-row workgroups
 static int64_t lds32_wide_workgroups(int64_t M, int64_t N) {
   return ((N + 15) / 16 + 2 * kLdsWaves - 1) / (2 * kLdsWaves) * ((M + 95) / 96);
 }
@@ -706,17 +828,13 @@ static int64_t batched_workgroups(const BatchedShape& c, int64_t M, int64_t N) {
 template <bool kRowA>
 static bool launch_lds_path(const BatchedArgs& g, int64_t M, int64_t N, bool argmax,
                             hipStream_t stream, hipError_t* err) {
-  if (lds32_wide_workgroups(M, N) >= kLds32WideMinWorkgroups) {
-    *err = launch_lds32<3, 1, 2, kRowA>(g, argmax, stream);
+  if (lds32_wide_workgroups(M, N) >= kLds32TallTileMinWorkgroups) {
+    *err = launch_lds32<3, 2, 3, kRowA>(g, argmax, stream);
     return true;
   }
   const int64_t wg32 = lds32_workgroups(M, N);
-  if (wg32 >= kLds32DoubleBufferMinWorkgroups) {
-    *err = launch_lds32<2, 1, 2, kRowA>(g, argmax, stream);
-    return true;
-  }
-  if (wg32 >= kLds32DeepMinWorkgroups) {
-    *err = launch_lds32<2, 1, 3, kRowA>(g, argmax, stream);
+  if (wg32 >= kLds32WideTileMinWorkgroups) {
+    *err = launch_lds32<2, 2, 3, kRowA>(g, argmax, stream);
     return true;
   }
   if (wg32 >= kLds32MinWorkgroups) {
