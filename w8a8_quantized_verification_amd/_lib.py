@@ -15,7 +15,9 @@ import re
 import torch  # noqa: F401  (see module docstring)
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libw8a8.so")
+# W8A8_LIBRARY names another build of the same library (the sanitizer test
+# loads a host-instrumented one this way); by default the in-tree build
+LIB_PATH = os.environ.get("W8A8_LIBRARY") or os.path.join(PKG, "libw8a8.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "w8a8.h")
 
 _c = ctypes
