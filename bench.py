@@ -399,7 +399,10 @@ def ingest_pmc_batched(dirs, command):
              "# per shape: medians over 4 dispatches.  FETCH_SIZE/WRITE_SIZE in bytes, calibrated",
              "# by the probe's 1 GiB copy.  MfmaUtil = 100*sum(SQ_VALU_MFMA_BUSY_CYCLES) /",
              "# (max(GRBM_GUI_ACTIVE)*SIMD_NUM).  implied_mfma_pct = 2*M*N*K / duration / 5.0 POPS,",
-             "# with the duration taken from the same dispatches under the counter run"]
+             "# with the duration taken from the same dispatches under the counter run.",
+             "# model_activations_once_per_xcd = (algorithmic + 7*M*K) / algorithmic: the traffic",
+             "# if each of the 8 XCDs (separate L2s) fetches the activations once and the",
+             "# weights are fetched once"]
     for n in BATCHED_SHAPES:
         lin = next(l for l in synth.QWEN3_8B_LAYER if l.name == n)
         alg = linear_bytes(M, lin.N, lin.K)
@@ -414,6 +417,8 @@ def ingest_pmc_batched(dirs, command):
             if "FETCH_SIZE" in e and "WRITE_SIZE" in e:
                 lines.append(f"  algorithmic_bytes: {alg}")
                 lines.append(f"  hbm_over_algorithmic: {(e['FETCH_SIZE'] + e['WRITE_SIZE']) / alg:.3f}")
+                # each of the 8 XCDs fetches the M x K activations into its own L2
+                lines.append(f"  model_activations_once_per_xcd: {(alg + 7 * M * lin.K) / alg:.3f}")
     lines.append(f"kernel_source_sha: {file_sha(BATCHED_SRC)}")
     with open(BATCHED_PMC_FILE, "w") as f:
         f.write("\n".join(lines) + "\n")

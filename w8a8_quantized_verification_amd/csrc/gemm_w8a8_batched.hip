@@ -53,16 +53,32 @@ struct BatchedArgs {
 // Epilogue of one wave's MB x TN accumulator tiles: rows (mb0+i)*16 + 4*grp
 // + r, columns (t0 + t)*16 + col.  y32 = (acc * x_scale[m]) * w_scale[n],
 // written as fp32 / bf16 / int32 as requested, and the fused argmax fold.
+// The lane's scales are all loaded first, in one batch: a load placed
+// after an output store would wait for its own memory round trip (the
+// store may alias it).
 template <int MB, int TN, bool kArgmax>
 __device__ __forceinline__ void batched_epilogue(const BatchedArgs& g, const v4i (&acc)[MB][TN],
                                                  int mb0, int t0, int lane) {
   const int col = lane & 15, grp = lane >> 4;
+  float wsv[TN], xsv[MB][4];
+#pragma unroll
+  for (int t = 0; t < TN; ++t) {
+    const int n = (t0 + t) * 16 + col;
+    wsv[t] = n < g.N ? g.ws[n] : 0.0f;
+  }
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = (mb0 + i) * 16 + 4 * grp + r;
+      xsv[i][r] = m < g.M ? g.xs[m] : 0.0f;
+    }
 #pragma unroll
   for (int t = 0; t < TN; ++t) {
     const int t16 = t0 + t;
     const int n = t16 * 16 + col;
     const bool n_ok = n < g.N;
-    const float wsn = n_ok ? g.ws[n] : 0.0f;
+    const float wsn = wsv[t];
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
 #pragma unroll
@@ -72,7 +88,7 @@ __device__ __forceinline__ void batched_epilogue(const BatchedArgs& g, const v4i
         int idx = INT_MAX;
         if (m < g.M && n_ok) {
           const int32_t a = acc[i][t][r];
-          const float y = (static_cast<float>(a) * g.xs[m]) * wsn;
+          const float y = (static_cast<float>(a) * xsv[i][r]) * wsn;
           const size_t o = (size_t)m * (size_t)g.N + (size_t)n;
           if (g.y_f32) g.y_f32[o] = y;
           if (g.y_bf16) g.y_bf16[o] = f32_to_bf16_rne(y);
