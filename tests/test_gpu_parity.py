@@ -257,7 +257,7 @@ def test_linear_batched_m288(N, K, tiled):
 @pytest.mark.parametrize("M,N,K", [(17, 65, 80), (96, 64, 64), (97, 4099, 1040), (200, 130, 16),
                                    (513, 300, 2048), (97, 4099, 1024), (300, 8200, 2048),
                                    (513, 20000, 64), (200, 131072, 64), (100, 4096, 256),
-                                   (33, 30000, 128)])
+                                   (33, 30000, 128), (288, 24600, 4096), (289, 131080, 1088)])
 def test_linear_batched_ragged(M, N, K):
     """Ragged last tiles in M, N and K (tiled weights, row-major
     activations).  K a multiple of 64 sends wide grids to the LDS-pipelined
@@ -275,18 +275,22 @@ def test_linear_batched_ragged(M, N, K):
                                    (513, 300, 2048), (5, 512, 256), (40, 33, 16), (288, 64, 0),
                                    (200, 20008, 1040), (513, 8200, 144), (288, 24576, 64),
                                    (200, 4000, 4096), (97, 4099, 1024), (288, 6144, 4096),
-                                   (300, 6152, 2048), (65, 16384, 1040), (200, 131072, 64)])
+                                   (300, 6152, 2048), (65, 16384, 1040), (200, 131072, 64),
+                                   (288, 24600, 4096), (288, 131080, 1040)])
 def test_linear_tiled_activations(M, N, K):
     """quantize_act_tiled + linear_tiled_act: the codes read back through
     the tiled layout (padding zero) and every output against the oracle.
     Grids of 224+ workgroups of 64 rows x 128 channels (N >= 6144 here)
-    take the 32 x 32 LDS-pipelined kernel (4 stages below 512 workgroups, 3
-    below 768, 2 above; 96-row workgroups with 2 stages from 2048 of those,
-    N = 131072), with ragged row blocks, channel tiles and k steps; the
-    16 x 16
-    LDS kernel takes 128-511 of its own workgroups with a step count
-    divisible by 4 (q, down and the ragged 4000 / 4099-wide cases) in its
-    k-sliced form; the rest the register-fragment kernel."""
+    take the 32 x 32 kernel with the weights streamed through registers:
+    64 x 128 workgroups with 3 steps of lookahead below 768 such
+    workgroups, 64 x 256 (two channel blocks per wave) from 768 (N = 24576,
+    24600), 96 x 256 from 2048 96-row workgroups (N = 131072, 131080), with
+    ragged row blocks, channel blocks (a wave's second block partly or
+    wholly past N) and k steps (a step count that is not a multiple of the
+    register ring); the 16 x 16 LDS kernel takes 128-511 of its own
+    workgroups with a step count divisible by 4 (q, down and the ragged
+    4000 / 4099-wide cases) in its k-sliced form; the rest the
+    register-fragment kernel."""
     announce(f"linear tiled activations M={M} N={N} K={K}")
     seed = 340 + M + N % 11
     bits = synth.activations_bf16(seed, M, K, outliers=K > 0)
