@@ -842,9 +842,65 @@ def ingest_launch_trace(trace_dir, command, out_path):
             n = name if len(name) <= 70 else name[:67] + "..."
             lines.append(f"  {np.median(v['dur']):9.2f} us dur  {np.median(v['gap']):7.2f} us gap "
                          f"{len(v['dur']):5d}  grid {grid:9d}  {n}")
+    lines += launch_breakdown(phases[0][len(phases[0]) // 2:], phases[1])
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
+
+
+def launch_breakdown(layer, headline):
+    """Per-launch split of the M = 5 layer phase of --launch-probe (graph
+    replays cycling qkv, o, gate_up, down, the widest grid being gate_up)
+    into the gap before the launch, a fixed per-launch cost (ramp to full
+    streaming plus the tail) and the streaming of its bytes: a least-squares
+    line duration = c + bytes / R through the four launches and the
+    headline LM-head GEMM (eager phase) gives c and R."""
+    import numpy as np
+
+    import synth
+    M = 5
+    lins = synth.QWEN3_8B_LAYER
+    shapes = (("qkv", (0, 1, 2)), ("o", (3,)), ("gate_up", (4, 5)), ("down", (6,)))
+    big = max(e[3] for e in layer)
+    per = {n: {"dur": [], "gap": []} for n, _ in shapes}
+    for j in range(3, len(layer) - 1):
+        if layer[j][3] != big:
+            continue
+        for off, (n, _) in zip((-2, -1, 0, 1), shapes):
+            s0, e0 = layer[j + off][0], layer[j + off][1]
+            per[n]["dur"].append((e0 - s0) / 1e3)
+            per[n]["gap"].append((s0 - layer[j + off - 1][1]) / 1e3)
+    head = [(e[1] - e[0]) / 1e3 for e in headline if "skinny" in e[2]]
+    rows = []
+    for n, grp in shapes:
+        N, K = sum(lins[i].N for i in grp), lins[grp[0]].K
+        rows.append((n, linear_bytes(M, N, K), float(np.median(per[n]["dur"])),
+                     float(np.median(per[n]["gap"])), len(per[n]["dur"]), float(np.max(per[n]["gap"]))))
+    lm = synth.QWEN3_8B_LM_HEAD
+    hb = linear_bytes(M, lm.N, lm.K)
+    pts_b = [r[1] for r in rows] + ([hb] if head else [])
+    pts_d = [r[2] for r in rows] + ([float(np.median(head))] if head else [])
+    slope, c = np.polyfit(np.array(pts_b, float), np.array(pts_d, float), 1)
+    rate = 1.0 / slope / 1e6   # TB/s (bytes per us -> TB/s)
+    out = ["[layer linears M=5: per launch, duration = fixed + bytes / R]",
+           f"  least squares over the four launches and the headline LM head "
+           f"({hb / 1e6:.1f} MB, {np.median(head) if head else float('nan'):.2f} us): "
+           f"fixed c = {c:.2f} us per launch, R = {rate:.2f} TB/s",
+           "  (medians over the replays; gap = idle time before the launch, its maximum marks the",
+           "  boundaries between graph replays)",
+           f"  {'launch':8s} {'MB':>8s} {'dur_us':>8s} {'gap_us':>7s} {'gap_max':>7s} {'fixed_us':>8s} "
+           f"{'stream_us':>9s} {'resid_us':>8s} {'n':>4s}"]
+    tot = {"dur": 0.0, "gap": 0.0, "stream": 0.0}
+    for n, b, d, g, cnt, gmax in rows:
+        st = b * slope
+        out.append(f"  {n:8s} {b / 1e6:8.2f} {d:8.2f} {g:7.2f} {gmax:7.2f} {c:8.2f} {st:9.2f} "
+                   f"{d - c - st:8.2f} {cnt:4d}")
+        tot["dur"] += d
+        tot["gap"] += g
+        tot["stream"] += st
+    out.append(f"  layer: {tot['dur']:.2f} us in the four launches + {tot['gap']:.2f} us of gaps; "
+               f"{4 * c:.2f} us of it fixed per-launch cost, {tot['stream']:.2f} us streaming at R")
+    return out
 
 
 def rotation_copies(N, K):
