@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import synth
-from tests.gpu_util import announce, dev, dev_bf16, gpu_available, host
+from tests.gpu_util import DEV, announce, dev, dev_bf16, gpu_available, host
 
 pytestmark = pytest.mark.gpu
 
@@ -312,6 +312,45 @@ def test_linear_tiled_activations(M, N, K):
     np.testing.assert_array_equal(host(acc), acc_r)
     np.testing.assert_array_equal(host(yf).view(np.uint32), y32_r.view(np.uint32))
     np.testing.assert_array_equal(host(yb), y_r)
+
+
+@pytest.mark.parametrize("M,N,K,act,shift", [
+    (288, 4096, 4096, "tiled", 0), (288, 6144, 4096, "tiled", 0), (288, 12288, 4096, "tiled", 0),
+    (288, 24576, 4096, "tiled", 0), (288, 24600, 4096, "tiled", 0), (289, 6152, 1088, "tiled", 0),
+    (288, 131080, 1040, "tiled", 0), (288, 4096, 4096, "rows", 0), (289, 6152, 1088, "rows", 0),
+    (288, 6148, 1024, "tiled", 0), (288, 4096, 1024, "tiled", 1), (289, 6152, 1088, "rows", 1)])
+def test_linear_bf16_only(M, N, K, act, shift):
+    """Only the bf16 output requested, as in a model's layers: with N % 8 == 0
+    and a 16-byte aligned output the 32 x 32 kernels store each 32 x 32 block
+    through the wave's LDS tile as 16-byte row pieces (64 x 128, 64 x 256 and
+    96 x 256 workgroups; ragged rows, channels and k steps; tiled and
+    row-major activations); N % 8 != 0 or an output 2 bytes off alignment
+    (shift = 1) take the element-wise epilogue.  Every output against the
+    oracle, bit for bit, and the 8 bf16 guard elements on either side of the
+    output untouched."""
+    announce(f"linear bf16-only M={M} N={N} K={K} act={act} shift={shift}")
+    seed = 350 + M + N % 13 + K % 7
+    bits = synth.activations_bf16(seed, M, K, outliers=True)
+    w = synth.weights_f32(seed, N, K)
+    xq_r, xs_r = oracle.quantize_act(bits)
+    wq_r, ws_r = oracle.quantize_weight(w)
+    _, y32_r, y_r = oracle.w8a8_linear(xq_r, xs_r, wq_r, ws_r)
+    wt, ws = w8.quantize_weight(dev(w), tiled=True)
+    guard = 8 + shift
+    flat = torch.full((M * N + 2 * guard,), -7.0, dtype=torch.bfloat16, device=DEV)
+    y = flat[guard:guard + M * N].view(M, N)
+    if act == "tiled":
+        xt, xs = w8.quantize_act_tiled(dev_bf16(bits))
+        w8.linear_tiled_act(xt, xs, wt, ws, K=K, want_bf16=False, y_bf16=y)
+    else:
+        xq, xs = w8.quantize_act(dev_bf16(bits))
+        w8.linear(xq, xs, wt, ws, want_bf16=False, y_bf16=y)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(y), y_r)
+    assert_bf16_tolerance(host(y), y32_r)
+    f = host(flat).view(np.uint16)
+    canary = host(torch.full((1,), -7.0, dtype=torch.bfloat16)).view(np.uint16)[0]
+    assert (f[:guard] == canary).all() and (f[guard + M * N:] == canary).all()
 
 
 # --------------------------------------------------------------------------

@@ -566,6 +566,54 @@ __device__ __forceinline__ void lds32_epilogue(const BatchedArgs& g, const v16i 
   }
 }
 
+// The bf16-only epilogue: each 32 x 32 block goes through the wave's own LDS
+// tile (row stride lds32_tile_row halfwords; 80 bytes puts the two half-waves'
+// rows in different banks) and leaves it as 16-byte row pieces, two stores
+// per lane instead of sixteen 2-byte ones.  The block's rows are
+// 8 (v / 4) + 4 g + v % 4 of column l % 32 as in lds32_epilogue; lane l then
+// stores row (64 k + l) / 4, columns 8 ((64 k + l) % 4) .. +7.  Requires
+// N % 8 == 0 and a 16-byte aligned y_bf16 (the kernel checks both and takes
+// lds32_epilogue otherwise).  A wave's LDS writes and reads complete in
+// order, so the tile needs no barrier; the values are those of
+// lds32_epilogue.
+constexpr int lds32_tile_row = 40;
+constexpr int lds32_tile_bytes = 32 * lds32_tile_row * 2;
+
+template <int RB, int CW>
+__device__ __forceinline__ void lds32_store_bf16(const BatchedArgs& g, const v16i (&acc)[RB][CW],
+                                                 const float* xs_sh, const float (&ws_lane)[CW],
+                                                 uint16_t* tile, int mt, int ng, int wave, int lane) {
+  const int r32 = lane & 31, hi = lane >> 5;
+  const int c0 = (ng * kLdsWaves + wave) * CW;
+#pragma unroll
+  for (int i = 0; i < RB; ++i) {
+    v4f xsq[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      xsq[q] = *reinterpret_cast<const v4f*>(xs_sh + i * 32 + 8 * q + 4 * hi);
+    const int rows_left = g.M - (mt * RB + i) * 32;
+    const size_t row0 = (size_t)(mt * RB + i) * 32;
+#pragma unroll
+    for (int j = 0; j < CW; ++j) {
+      const int n0 = (c0 + j) * 32;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int rr = 8 * (v >> 2) + (v & 3) + 4 * hi;
+        const float y = (static_cast<float>(acc[i][j][v]) * xsq[v >> 2][v & 3]) * ws_lane[j];
+        tile[rr * lds32_tile_row + r32] = f32_to_bf16_rne(y);
+      }
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int c = k * kWave + lane, row = c >> 2, n = n0 + 8 * (c & 3);
+        const v4i piece = *reinterpret_cast<const v4i*>(tile + row * lds32_tile_row + 8 * (c & 3));
+        // (N % 8 == 0 and n % 8 == 0: a piece that starts below N ends there)
+        if (row < rows_left && n < g.N)
+          *reinterpret_cast<v4i*>(g.y_bf16 + (row0 + row) * (size_t)g.N + n) = piece;
+      }
+    }
+  }
+}
+
 // The pipeline on v_mfma_i32_32x32x32_i8, which does twice the work of the
 // 16 x 16 x 64 instruction for the same two operand KiB: a workgroup of
 // four waves computes RB blocks of 32 rows x 4*CW blocks of 32 channels;
@@ -597,8 +645,8 @@ __device__ __forceinline__ void lds32_epilogue(const BatchedArgs& g, const v16i 
 // tile are fetched from block / tile 0 (in bounds) and their results
 // dropped by the epilogue; the steps past the end are fetched again from
 // the last one.
-template <int RB, int CW, int P, bool kArgmax, bool kStores, bool kRowA = false>
-__global__ __launch_bounds__(kLdsWaves * kWave, CW == 1 ? 4 : 2) void gemm_w8a8_lds32(BatchedArgs g) {
+template <int RB, int CW, int P, bool kArgmax, bool kStores, bool kRowA = false, bool kRot = false>
+__global__ __launch_bounds__(kLdsWaves * kWave, P <= 4 ? (CW == 1 ? 4 : 2) : 2) void gemm_w8a8_lds32(BatchedArgs g) {
   constexpr int FA = 2 * RB;                               // activation fragments per step
   constexpr int FAF = FA / kLdsWaves;                      // whole share per wave
   constexpr bool kDup = FA % kLdsWaves != 0;               // (FA even: then FA % 4 == 2)
@@ -612,7 +660,11 @@ __global__ __launch_bounds__(kLdsWaves * kWave, CW == 1 ? 4 : 2) void gemm_w8a8_
   // (one LDS array: the stages, then the workgroup's row scales; a second
   // LDS object makes the compiler wait for the direct-to-LDS loads before
   // every LDS read)
-  __shared__ __attribute__((aligned(1024))) int8_t stage_mem[kStageBytes + RB * 32 * 4];
+  // (with stores and no argmax fold, each wave also gets a 32 x 32 bf16
+  // tile after the row scales for the vectorized epilogue)
+  constexpr bool kVecEpi = kStores && !kArgmax;
+  constexpr int kEpiBytes = kVecEpi ? kLdsWaves * lds32_tile_bytes : 0;
+  __shared__ __attribute__((aligned(1024))) int8_t stage_mem[kStageBytes + RB * 32 * 4 + kEpiBytes];
 
   const int b = blockIdx.x;
   const int xcd = b % kXcds;
@@ -657,8 +709,25 @@ __global__ __launch_bounds__(kLdsWaves * kWave, CW == 1 ? 4 : 2) void gemm_w8a8_
       src[j] = g.xq + ((size_t)(rb < mblocks ? rb : 0) * (size_t)steps << 10) + (lane << 4);
     }
   }
+  // k steps in a rotated order (kRot): the workgroups that read one weight
+  // tile (same ng) or one activation tile (same mt) start at different k,
+  // so that one of them misses in L2 while the others hit; the int32 sums do
+  // not depend on the order
+  int kstart = 0;
+  if constexpr (kRot) {
+    const int nq = (g.ngroups + kXcds - 1) / kXcds;
+    kstart = (int)(((int64_t)(mt + g.mtiles * (ng / kXcds)) * steps) / ((int64_t)g.mtiles * nq));
+  }
+  auto kstep = [&](int s) {
+    s = min(s, steps - 1);   // (steps past the end fetch the last one again)
+    if constexpr (kRot) {
+      s += kstart;
+      if (s >= steps) s -= steps;
+    }
+    return s;
+  };
   auto issue_a = [&](int p, int s) {
-    s = min(s, steps - 1);
+    s = kstep(s);
     const size_t off = kRowA ? (size_t)s * 64 : ((size_t)s << 10);
 #pragma unroll
     for (int j = 0; j < LA; ++j) {
@@ -675,7 +744,7 @@ __global__ __launch_bounds__(kLdsWaves * kWave, CW == 1 ? 4 : 2) void gemm_w8a8_
     wsrc[j] = g.wq + ((size_t)(t16 < g.tiles16 ? t16 : 0) * (size_t)steps << 10) + lane_off;
   }
   auto load_b = [&](v4i (&dst)[CW][2], int s) {
-    s = min(s, steps - 1);
+    s = kstep(s);
 #pragma unroll
     for (int j = 0; j < CW; ++j) {
       dst[j][0] = *reinterpret_cast<const v4i*>(wsrc[j] + ((size_t)s << 10));
@@ -735,10 +804,17 @@ __global__ __launch_bounds__(kLdsWaves * kWave, CW == 1 ? 4 : 2) void gemm_w8a8_
     if (s0 + u < steps) step(u, s0 + u);
   wait_vmcnt<0>();
 
+  if constexpr (kVecEpi) {
+    if (g.y_bf16 && !g.y_f32 && !g.acc && g.N % 8 == 0 && (reinterpret_cast<uintptr_t>(g.y_bf16) & 15) == 0) {
+      uint16_t* tile = reinterpret_cast<uint16_t*>(stage_mem + kStageBytes + RB * 32 * 4 + wave * lds32_tile_bytes);
+      lds32_store_bf16<RB, CW>(g, acc, xs_sh, ws_lane, tile, mt, ng, wave, lane);
+      return;
+    }
+  }
   lds32_epilogue<RB, CW, kArgmax, kStores>(g, acc, xs_sh, ws_lane, stage_mem, mt, ng, wave, lane);
 }
 
-template <int RB, int CW, int P, bool kRowA = false>
+template <int RB, int CW, int P, bool kRowA = false, bool kRot = false>
 static hipError_t launch_lds32(BatchedArgs g, bool argmax, hipStream_t stream) {
   g.ngroups = (g.tiles16 + 2 * kLdsWaves * CW - 1) / (2 * kLdsWaves * CW);
   g.mtiles = (g.M + 32 * RB - 1) / (32 * RB);
@@ -746,11 +822,11 @@ static hipError_t launch_lds32(BatchedArgs g, bool argmax, hipStream_t stream) {
   const dim3 grid((unsigned)(ng_padded * g.mtiles)), block(kLdsWaves * kWave);
   const bool stores = g.y_bf16 || g.y_f32 || g.acc;
   if (argmax && !stores)
-    hipLaunchKernelGGL((gemm_w8a8_lds32<RB, CW, P, true, false, kRowA>), grid, block, 0, stream, g);
+    hipLaunchKernelGGL((gemm_w8a8_lds32<RB, CW, P, true, false, kRowA, kRot>), grid, block, 0, stream, g);
   else if (argmax)
-    hipLaunchKernelGGL((gemm_w8a8_lds32<RB, CW, P, true, true, kRowA>), grid, block, 0, stream, g);
+    hipLaunchKernelGGL((gemm_w8a8_lds32<RB, CW, P, true, true, kRowA, kRot>), grid, block, 0, stream, g);
   else
-    hipLaunchKernelGGL((gemm_w8a8_lds32<RB, CW, P, false, true, kRowA>), grid, block, 0, stream, g);
+    hipLaunchKernelGGL((gemm_w8a8_lds32<RB, CW, P, false, true, kRowA, kRot>), grid, block, 0, stream, g);
   return hipGetLastError();
 }
 
@@ -804,9 +880,16 @@ constexpr int64_t kLdsSplitMinWorkgroups = 128;
 // 128-channel workgroups), measured at 288 rows against the 16 x 16
 // pipeline: q/k/v fused 4096 -> 6144 (240 workgroups) 22.8 vs 35.5 us,
 // gate 4096 -> 12288 (480) 33.3 vs 39.1 us, gate/up fused 4096 -> 24576
-// (960) 55-59 vs 67 us; with 160 workgroups (o, down at 4096 channels) it
-// is slower (22.1 vs 19.3 us, 50.1 vs 41.6 us), so those keep the k-sliced
-// 16 x 16 form.  Tiles and lookahead by grid width, measured at 288 rows
+// (960) 55-59 vs 67 us.  With the bf16 outputs stored through the wave's
+// LDS tile (16-byte pieces: the per-workgroup epilogue went from ~3.4 us to
+// well under 1 us), the k order rotated per workgroup and 5 steps of
+// lookahead for the 64 x 128 tile, A/B on one box: o 4096 -> 4096 (160
+// workgroups) 15.3 us against 19.0 for the k-sliced 16 x 16 form, q/k/v
+// 16.0-16.4 (21.1), gate 27.5-28.2 (31.0), gate/up 48.1 (51.6-57).  At 160
+// workgroups every CU holds one workgroup; its loads, not the MFMAs or the
+// barrier, set the step time (without the MFMAs the loop is no faster;
+// deeper lookahead, more waves per workgroup or activations staged through
+// registers instead of direct-to-LDS loads gave no more).  Tiles and lookahead by grid width, measured at 288 rows
 // (A/B on one box, weights streamed into registers against the earlier
 // form that staged them in LDS): q/k/v 64 x 128 with 3 steps of lookahead
 // 20.9 us (staged: 22-23), gate the same 30.5-30.9 us (33.6-34.5), gate/up
@@ -814,7 +897,7 @@ constexpr int64_t kLdsSplitMinWorkgroups = 128;
 // with the argmax folded in, 96 x 256 with 2 steps (each weight block read
 // once per 96 rows, three workgroups per CU): 213-219 us per verify step
 // against 252-265 us for the staged 96 x 128 form.
-constexpr int64_t kLds32MinWorkgroups = 224;
+constexpr int64_t kLds32MinWorkgroups = 160;
 constexpr int64_t kLds32WideTileMinWorkgroups = 768;
 constexpr int64_t kLds32TallTileMinWorkgroups = 2048;
 
@@ -850,11 +933,11 @@ static bool launch_lds_path(const BatchedArgs& g, int64_t M, int64_t N, bool arg
   }
   const int64_t wg32 = lds32_workgroups(M, N);
   if (wg32 >= kLds32WideTileMinWorkgroups) {
-    *err = launch_lds32<2, 2, 3, kRowA>(g, argmax, stream);
+    *err = launch_lds32<2, 2, 3, kRowA, true>(g, argmax, stream);
     return true;
   }
   if (wg32 >= kLds32MinWorkgroups) {
-    *err = launch_lds32<2, 1, 4, kRowA>(g, argmax, stream);
+    *err = launch_lds32<2, 1, 6, kRowA, true>(g, argmax, stream);
     return true;
   }
   if (argmax) return false;   // (the 16 x 16 pipeline has no argmax fold)
