@@ -167,9 +167,12 @@ w8a8_status w8a8_tile_weight(const int8_t* wq, int64_t N, int64_t K,
  * acc      [M][N] int32 output, or NULL.   At least one output is non-NULL.
  * workspace / workspace_bytes: device scratch of at least
  *          w8a8_linear_workspace_bytes(M, N, K) bytes (NULL allowed when that
- *          is 0).  The workspace must be zero-filled before its first use;
- *          every completed call leaves it zero-filled again.  Calls that share
- *          a workspace must not overlap in time.
+ *          is 0), 256-byte aligned.  It holds the int32 partials and arrival
+ *          counters of a reduction split across workgroups: up to 16 rows a
+ *          long or narrow product, above 16 rows (tiled weights, K % 64 == 0)
+ *          a long one on a mid-size grid.  The workspace must be zero-filled
+ *          before its first use; every completed call leaves it zero-filled
+ *          again.  Calls that share a workspace must not overlap in time.
  * Requires 0 <= K <= W8A8_MAX_K, K % 16 == 0; any N (ragged tails are
  * handled); any M (M <= 16 takes the skinny kernel, larger M the batched one).
  */
@@ -200,16 +203,22 @@ w8a8_status w8a8_linear_tiled(const int8_t* xq, const float* x_scale,
  * w8a8_linear_tiled_act is w8a8_linear_tiled (bit-identical outputs) with
  * xq in that layout; loading one contiguous KiB per 16-row block and k step
  * instead of 16 rows x 64 bytes makes the batched product ~30% faster.
- * No workspace.
+ * workspace / workspace_bytes: at least
+ * w8a8_linear_tiled_act_workspace_bytes(M, N, K) bytes (NULL allowed when
+ * that is 0; e.g. 288 x 4096 x 12288 needs ~9.4 MB), under w8a8_linear's
+ * workspace rule (256-byte aligned, zero-filled before first use, left
+ * zero-filled by every completed call, no overlapping calls); one buffer may
+ * serve both.  Errors as for w8a8_linear.
  */
 w8a8_status w8a8_quantize_act_tiled(const uint16_t* x_bf16, const float* smooth,
                                     int64_t M, int64_t K,
                                     int8_t* xq_tiled, float* x_scale, void* stream);
+size_t      w8a8_linear_tiled_act_workspace_bytes(int64_t M, int64_t N, int64_t K);
 w8a8_status w8a8_linear_tiled_act(const int8_t* xq_tiled, const float* x_scale,
                                   const int8_t* wq_tiled, const float* w_scale,
                                   int64_t M, int64_t N, int64_t K,
                                   uint16_t* y_bf16, float* y_f32, int32_t* acc,
-                                  void* stream);
+                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * LM-head argmax and greedy acceptance of a draft block.

@@ -88,6 +88,31 @@ def test_linear_workspace(lib):
     assert lin(lib, N=16, K=25600, work=A16 + 16, wbytes=need) == INVALID  # alignment
 
 
+def test_batched_split_workspace(lib):
+    # above 16 rows, tiled weights: a long reduction on a mid-size grid
+    # (288 x 4096, 192 k steps) is split across workgroups and needs the
+    # workspace; K = 4096 (64 steps), row-major weights and row-major
+    # activations with K % 64 != 0 do not split
+    need = lib.w8a8_linear_tiled_act_workspace_bytes(288, 4096, 12288)
+    assert need >= 288 * 4096 * 4
+    assert lib.w8a8_linear_workspace_bytes(288, 4096, 12288) == need
+    assert lib.w8a8_linear_tiled_act_workspace_bytes(288, 4096, 4096) == 0
+    assert lib.w8a8_linear_tiled_act_workspace_bytes(288, 4096, 8208) > 0
+    assert lib.w8a8_linear_workspace_bytes(288, 4096, 8208) == 0
+    assert lib.w8a8_linear_tiled_act_workspace_bytes(17, 4096, 12288) == 0
+    assert lib.w8a8_linear_tiled_act_workspace_bytes(0, 4096, 12288) == 0
+    f = lib.w8a8_linear_tiled_act
+    args = (A16, A16, A16b, A16, 288, 4096, 12288, A16, None, None)
+    assert f(*args, None, 0, None) == WORKSPACE
+    assert f(*args, A16, need - 1, None) == WORKSPACE
+    assert f(*args, A16 + 16, need, None) == INVALID     # 256-byte alignment
+    assert b"256-byte" in lib.w8a8_last_error()
+    assert f(A16, A16, A16b, A16, 288, 4096, 12288, None, None, None, A16, need, None) == INVALID
+    assert lib.w8a8_linear_tiled(A16, A16, A16b, A16, 288, 4096, 12288, A16, None, None, None, 0,
+                                 None) == WORKSPACE
+    assert f(None, None, None, None, 0, 4096, 12288, None, None, None, None, 0, None) == OK
+
+
 def test_linear_workspace_follows_split_override(lib, monkeypatch):
     monkeypatch.setenv("W8A8_SPLITK", "4")
     assert lib.w8a8_linear_workspace_bytes(5, 1024, 4096) >= 5 * 1024 * 4

@@ -144,6 +144,8 @@ def test_guard_skinny_forced_split_k(split, monkeypatch):
     (289, 12293, 4096, True),    # LDS 32 x 32 (64-row workgroups)
     (289, 4099, 4112, True),     # K not a multiple of 64: register-fragment kernel
     (97, 4099, 4096, False),     # row-major weights
+    (288, 4096, 12288, True),    # LDS 32 x 32, k split across two workgroups (workspace)
+    (280, 4004, 8256, True),     # the same, ragged M, N and an odd step count
 ])
 def test_guard_batched_linear(M, N, K, tiled):
     announce(f"guard batched linear M={M} N={N} K={K} tiled={tiled}")
@@ -153,7 +155,8 @@ def test_guard_batched_linear(M, N, K, tiled):
 
 
 @pytest.mark.parametrize("M,N,K", [(17, 4099, 4096), (289, 4099, 4096), (289, 12293, 4096),
-                                   (289, 1029, 12288), (97, 17, 256)])
+                                   (289, 1029, 12288), (97, 17, 256), (288, 4096, 12288),
+                                   (280, 4004, 8208)])
 def test_guard_tiled_activations(M, N, K):
     announce(f"guard tiled activations M={M} N={N} K={K}")
     x = act(M, K, 7)
@@ -164,10 +167,12 @@ def test_guard_tiled_activations(M, N, K):
     wq, ws = int8_weights(N, K, 200 + M)
     outs = {"y_bf16": Guarded((M, N), torch.bfloat16), "y_f32": Guarded((M, N), torch.float32),
             "acc": Guarded((M, N), torch.int32)}
+    wsp = GuardedWorkspace()
     w8.linear_tiled_act(xt.t, xs.t, wq, ws, K=K, y_bf16=outs["y_bf16"].t, y_f32=outs["y_f32"].t,
-                        acc=outs["acc"].t)
+                        acc=outs["acc"].t, workspace=wsp)
     ref = w8.linear_tiled_act(xt_ref, xs_ref, wq, ws, K=K, want_f32=True, want_acc=True)
     torch.cuda.synchronize()
+    wsp.check()
     assert xt.intact() and xs.intact()
     assert same_bits(xt.t, xt_ref) and same_bits(xs.t, xs_ref)
     for (name, g), r in zip(outs.items(), ref):

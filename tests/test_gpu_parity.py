@@ -318,14 +318,19 @@ def test_linear_tiled_activations(M, N, K):
     (288, 4096, 4096, "tiled", 0), (288, 6144, 4096, "tiled", 0), (288, 12288, 4096, "tiled", 0),
     (288, 24576, 4096, "tiled", 0), (288, 24600, 4096, "tiled", 0), (289, 6152, 1088, "tiled", 0),
     (288, 131080, 1040, "tiled", 0), (288, 4096, 4096, "rows", 0), (289, 6152, 1088, "rows", 0),
-    (288, 6148, 1024, "tiled", 0), (288, 4096, 1024, "tiled", 1), (289, 6152, 1088, "rows", 1)])
+    (288, 6148, 1024, "tiled", 0), (288, 4096, 1024, "tiled", 1), (289, 6152, 1088, "rows", 1),
+    (288, 4096, 12288, "tiled", 0), (288, 4096, 12288, "rows", 0), (280, 4000, 8208, "tiled", 0),
+    (280, 4004, 8208, "tiled", 0), (288, 4096, 8192, "tiled", 1)])
 def test_linear_bf16_only(M, N, K, act, shift):
     """Only the bf16 output requested, as in a model's layers: with N % 8 == 0
     and a 16-byte aligned output the 32 x 32 kernels store each 32 x 32 block
     through the wave's LDS tile as 16-byte row pieces (64 x 128, 64 x 256 and
     96 x 256 workgroups; ragged rows, channels and k steps; tiled and
     row-major activations); N % 8 != 0 or an output 2 bytes off alignment
-    (shift = 1) take the element-wise epilogue.  Every output against the
+    (shift = 1) take the element-wise epilogue.  From 128 k steps on the
+    64 x 128 grids (K = 8192, 8208, 12288 at 4096 channels) the reduction is
+    split across two workgroups (96 x 128 tiles, int32 partials handed over
+    through the workspace) before either epilogue.  Every output against the
     oracle, bit for bit, and the 8 bf16 guard elements on either side of the
     output untouched."""
     announce(f"linear bf16-only M={M} N={N} K={K} act={act} shift={shift}")
@@ -351,6 +356,86 @@ def test_linear_bf16_only(M, N, K, act, shift):
     f = host(flat).view(np.uint16)
     canary = host(torch.full((1,), -7.0, dtype=torch.bfloat16)).view(np.uint16)[0]
     assert (f[:guard] == canary).all() and (f[guard + M * N:] == canary).all()
+
+
+def test_linear_split_workspace_shared():
+    """One zero-filled workspace shared, in turn, by the batched kernel's k
+    split (tiled and row-major activations, two shapes) and the skinny
+    kernel's split-K (8 rows, 25600 -> 5120): each call against the oracle
+    bit for bit, and the workspace zero-filled again after every call (the
+    skinny split adds its partials onto whatever the buffer holds)."""
+    announce("linear split workspace shared")
+    wsp = w8.Workspace()
+    cases = [(288, 4096, 12288, "tiled"), (8, 5120, 25600, "skinny"), (288, 4096, 12288, "rows"),
+             (280, 4004, 8208, "tiled"), (8, 5120, 25600, "skinny"), (288, 4096, 12288, "tiled")]
+    assert w8.linear_tiled_act_workspace_bytes(288, 4096, 12288) > 0
+    assert w8.linear_workspace_bytes(288, 4096, 12288) > 0
+    assert w8.linear_workspace_bytes(8, 5120, 25600) > 0
+    for n, (M, N, K, kind) in enumerate(cases):
+        announce(f"  call {n}: M={M} N={N} K={K} {kind}")
+        seed = 370 + n
+        bits = synth.activations_bf16(seed, M, K, outliers=True)
+        w = synth.weights_f32(seed, N, K)
+        xq_r, xs_r = oracle.quantize_act(bits)
+        wq_r, ws_r = oracle.quantize_weight(w)
+        acc_r, y32_r, y_r = oracle.w8a8_linear(xq_r, xs_r, wq_r, ws_r)
+        wt, ws = w8.quantize_weight(dev(w), tiled=True)
+        if kind == "tiled":
+            xt, xs = w8.quantize_act_tiled(dev_bf16(bits))
+            yb, yf, acc = w8.linear_tiled_act(xt, xs, wt, ws, K=K, want_f32=True, want_acc=True,
+                                              workspace=wsp)
+        else:
+            xq, xs = w8.quantize_act(dev_bf16(bits))
+            yb, yf, acc = w8.linear(xq, xs, wt, ws, want_f32=True, want_acc=True, workspace=wsp)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(acc), acc_r)
+        np.testing.assert_array_equal(host(yf).view(np.uint32), y32_r.view(np.uint32))
+        np.testing.assert_array_equal(host(yb), y_r)
+        buf = wsp.get(1, torch.device(DEV), use="zeroed")
+        assert not bool(buf.any()), f"call {n}: workspace not left zero-filled"
+
+
+def test_linear_split_graph_replays():
+    """The batched k split (288 x 4096 x 12288, tiled activations) captured
+    in a HIP graph and replayed four times, with eager calls of another split
+    shape and output clears between the replays: every replay against the
+    oracle bit for bit (the arrival counters reset by each call, no memset
+    in the graph), the workspace zero-filled after each."""
+    announce("linear split graph replays")
+    M, N, K = 288, 4096, 12288
+    seed = 390
+    bits = synth.activations_bf16(seed, M, K, outliers=True)
+    w = synth.weights_f32(seed, N, K)
+    xq_r, xs_r = oracle.quantize_act(bits)
+    wq_r, ws_r = oracle.quantize_weight(w)
+    _, _, y_r = oracle.w8a8_linear(xq_r, xs_r, wq_r, ws_r)
+    bits2 = synth.activations_bf16(seed + 1, 280, 8208, outliers=True)
+    w2 = synth.weights_f32(seed + 1, 4004, 8208)
+    xq2_r, xs2_r = oracle.quantize_act(bits2)
+    wq2_r, ws2_r = oracle.quantize_weight(w2)
+    _, _, y2_r = oracle.w8a8_linear(xq2_r, xs2_r, wq2_r, ws2_r)
+    wsp = w8.Workspace()
+    xt, xs = w8.quantize_act_tiled(dev_bf16(bits))
+    wt, ws = w8.quantize_weight(dev(w), tiled=True)
+    xt2, xs2 = w8.quantize_act_tiled(dev_bf16(bits2))
+    wt2, ws2 = w8.quantize_weight(dev(w2), tiled=True)
+    y = torch.empty(M, N, dtype=torch.bfloat16, device=DEV)
+    w8.linear_tiled_act(xt, xs, wt, ws, K=K, y_bf16=y, workspace=wsp)   # eager: allocates
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        w8.linear_tiled_act(xt, xs, wt, ws, K=K, y_bf16=y, workspace=wsp)
+    torch.cuda.synchronize()
+    for r in range(4):
+        y.zero_()
+        y2, _, _ = w8.linear_tiled_act(xt2, xs2, wt2, ws2, K=8208, workspace=wsp)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(y2), y2_r)
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(y), y_r)
+        buf = wsp.get(1, torch.device(DEV), use="zeroed")
+        assert not bool(buf.any()), f"replay {r}: workspace not left zero-filled"
 
 
 # --------------------------------------------------------------------------

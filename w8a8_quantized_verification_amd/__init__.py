@@ -11,7 +11,8 @@ from .api import (W8A8Error, Workspace, accept_from_keys, bf16_linear, linear,
                   verify_accept_workspace_bytes, verify_sample, verify_sample_workspace_bytes,
                   w4_shape, quantize_weight_w4, linear_w4, lm_head_argmax_w4,
                   residual_rmsnorm_quant, silu_mul_quant, quantize_act_tiled,
-                  linear_tiled_act, verify_attention, qk_norm_rope_append, pack_v_cache,
+                  linear_tiled_act, linear_tiled_act_workspace_bytes, verify_attention,
+                  qk_norm_rope_append, pack_v_cache,
                   hbm_read_probe, HBM_PROBE_SINK_WORDS, lm_head_verify_noalloc,
                   NOALLOC_MAX_ROWS)
 
@@ -22,6 +23,6 @@ __all__ = [
     "verify_accept_workspace_bytes", "verify_sample", "verify_sample_workspace_bytes",
     "sample_weights", "w4_shape", "quantize_weight_w4", "linear_w4", "lm_head_argmax_w4",
     "residual_rmsnorm_quant", "silu_mul_quant", "quantize_act_tiled", "linear_tiled_act",
-    "verify_attention", "qk_norm_rope_append", "pack_v_cache", "hbm_read_probe",
+    "linear_tiled_act_workspace_bytes", "verify_attention", "qk_norm_rope_append", "pack_v_cache", "hbm_read_probe",
     "HBM_PROBE_SINK_WORDS", "lm_head_verify_noalloc", "NOALLOC_MAX_ROWS",
 ]

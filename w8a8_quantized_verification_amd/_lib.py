@@ -64,7 +64,9 @@ SIGNATURES = {
                                            _vp, _vp, _vp]),
     "w8a8_silu_mul_quant": (_i32, [_vp, _vp, _i64, _vp, _i64, _i64, _vp, _vp, _vp, _vp]),
     "w8a8_quantize_act_tiled": (_i32, [_vp, _vp, _i64, _i64, _vp, _vp, _vp]),
-    "w8a8_linear_tiled_act": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp]),
+    "w8a8_linear_tiled_act_workspace_bytes": (_sz, [_i64, _i64, _i64]),
+    "w8a8_linear_tiled_act": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _sz,
+                                     _vp]),
     "w8a8_verify_attention_workspace_bytes": (_sz, [_i64, _i64, _i64]),
     "w8a8_pack_v_cache": (_i32, [_vp, _i64, _i64, _i64, _i64, _vp, _vp]),
     "w8a8_qk_norm_rope_append": (_i32, [_vp, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _c.c_float,

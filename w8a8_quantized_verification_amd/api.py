@@ -19,7 +19,8 @@ __all__ = [
     "accept_from_keys", "bf16_linear", "Workspace", "verify_sample",
     "verify_sample_workspace_bytes", "sample_weights", "w4_shape", "quantize_weight_w4",
     "linear_w4", "lm_head_argmax_w4", "residual_rmsnorm_quant", "silu_mul_quant",
-    "quantize_act_tiled", "linear_tiled_act", "verify_attention", "qk_norm_rope_append",
+    "quantize_act_tiled", "linear_tiled_act", "linear_tiled_act_workspace_bytes",
+    "verify_attention", "qk_norm_rope_append",
     "pack_v_cache", "hbm_read_probe", "HBM_PROBE_SINK_WORDS", "lm_head_verify_noalloc",
     "NOALLOC_MAX_ROWS",
 ]
@@ -590,11 +591,13 @@ def quantize_act_tiled(x: torch.Tensor, smooth: torch.Tensor | None = None, *, x
 
 def linear_tiled_act(xq_tiled, x_scale, wq_tiled, w_scale, *, K: int | None = None,
                      want_bf16=True, want_f32=False, want_acc=False, y_bf16=None, y_f32=None,
-                     acc=None):
+                     acc=None, workspace: Workspace | None = None):
     """The batched W8A8 linear with tiled activations (from
     :func:`quantize_act_tiled`) and tiled weights; same outputs as
     :func:`linear`.  ``K`` defaults to the padded width of the layout (the
-    result is the same for any K with the same 64-wide step count)."""
+    result is the same for any K with the same 64-wide step count).  Long
+    reductions on mid-size grids split k across workgroups through the
+    ``"zeroed"`` workspace (see :func:`linear_tiled_act_workspace_bytes`)."""
     _need(xq_tiled, "xq_tiled", torch.int8, 4)
     dev = xq_tiled.device
     _need(x_scale, "x_scale", torch.float32, 1, dev)
@@ -611,10 +614,19 @@ def linear_tiled_act(xq_tiled, x_scale, wq_tiled, w_scale, *, K: int | None = No
         y_f32 = _out(y_f32, (M, N), torch.float32, dev, "y_f32")
     if want_acc or acc is not None:
         acc = _out(acc, (M, N), torch.int32, dev, "acc")
+    need = linear_tiled_act_workspace_bytes(M, N, K)
+    ws = (workspace or _default_ws).get(need, dev, use="zeroed")
     check(lib().w8a8_linear_tiled_act(_ptr(xq_tiled), _ptr(x_scale), _ptr(wq_tiled),
                                       _ptr(w_scale), M, N, K, _ptr(y_bf16), _ptr(y_f32),
-                                      _ptr(acc), _stream(dev)))
+                                      _ptr(acc), _ptr(ws), 0 if ws is None else ws.numel(),
+                                      _stream(dev)))
     return y_bf16, y_f32, acc
+
+
+def linear_tiled_act_workspace_bytes(M: int, N: int, K: int) -> int:
+    """Bytes of the ``"zeroed"`` workspace :func:`linear_tiled_act` needs
+    (0 when the reduction is not split across workgroups)."""
+    return int(lib().w8a8_linear_tiled_act_workspace_bytes(M, N, K))
 
 
 def pack_v_cache(v, *, out=None):

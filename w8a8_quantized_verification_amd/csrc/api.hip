@@ -589,10 +589,16 @@ w8a8_status w8a8_quantize_act_tiled(const uint16_t* x_bf16, const float* smooth,
                                               x_scale, reinterpret_cast<hipStream_t>(stream)), fn);
 }
 
+size_t w8a8_linear_tiled_act_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || M > kMaxRows || N > kMaxRows || K < 0 || K > W8A8_MAX_K) return 0;
+  return w8a8_batched_workspace_bytes(M, N, K, true);
+}
+
 w8a8_status w8a8_linear_tiled_act(const int8_t* xq_tiled, const float* x_scale,
                                   const int8_t* wq_tiled, const float* w_scale, int64_t M,
                                   int64_t N, int64_t K, uint16_t* y_bf16, float* y_f32,
-                                  int32_t* acc, void* stream) {
+                                  int32_t* acc, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
   static const char* fn = "w8a8_linear_tiled_act";
   g_last_error.clear();
   if (w8a8_status s = check_rows_k(fn, M, K)) return s;
@@ -606,9 +612,16 @@ w8a8_status w8a8_linear_tiled_act(const int8_t* xq_tiled, const float* x_scale,
   if (!aligned(x_scale, 4) || !aligned(w_scale, 4) || !aligned(y_bf16, 2) || !aligned(y_f32, 4) ||
       !aligned(acc, 4))
     return fail(W8A8_ERR_INVALID_ARG, fn, "scale or output pointer misaligned");
+  const size_t need = w8a8_batched_workspace_bytes(M, N, K, true);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(W8A8_ERR_WORKSPACE, fn,
+                "workspace NULL or smaller than w8a8_linear_tiled_act_workspace_bytes()");
+  if (need > 0 && !aligned(workspace, 256))
+    return fail(W8A8_ERR_INVALID_ARG, fn, "workspace must be 256-byte aligned");
   return hip_status(w8a8_launch_gemm_batched(xq_tiled, x_scale, wq_tiled, w_scale, M, N, K, true,
                                              y_bf16, y_f32, acc, nullptr, 0, 0,
-                                             reinterpret_cast<hipStream_t>(stream), true),
+                                             reinterpret_cast<hipStream_t>(stream), true,
+                                             need > 0 ? workspace : nullptr),
                     fn);
 }
 

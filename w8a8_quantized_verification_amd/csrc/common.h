@@ -76,11 +76,14 @@ hipError_t w8a8_launch_tile_weight(const int8_t* wq, int64_t N, int64_t K, int8_
                                    hipStream_t stream);
 
 size_t w8a8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, bool tiled);
+// workspace of the batched kernel's k split (0: none), and the launcher;
+// `workspace` (zero-filled, left zero) may be null where that size is 0
+size_t w8a8_batched_workspace_bytes(int64_t M, int64_t N, int64_t K, bool a_tiled);
 hipError_t w8a8_launch_gemm_batched(const int8_t* xq, const float* x_scale, const int8_t* wq,
                                     const float* w_scale, int64_t M, int64_t N, int64_t K,
                                     bool tiled, uint16_t* y_bf16, float* y_f32, int32_t* acc,
                                     void* keys, int subkeys, int key_stride, hipStream_t stream,
-                                    bool a_tiled = false);
+                                    bool a_tiled = false, void* workspace = nullptr);
 size_t w8a8_lm_head_workspace_bytes(int64_t M);
 inline int w8a8_argmax_subkeys() { return w8a8::kArgmaxSubkeys; }
 inline int w8a8_argmax_key_stride() { return w8a8::kArgmaxKeyStride; }

@@ -365,7 +365,7 @@ static SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, bool tiled, bool 
 size_t w8a8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, bool tiled) {
   using namespace w8a8;
   if (M <= 0 || N <= 0) return 0;
-  if (M > kSkinnyMaxRows) return 0;  // the batched kernel needs none
+  if (M > kSkinnyMaxRows) return tiled ? w8a8_batched_workspace_bytes(M, N, K, false) : 0;
   const SkinnyPlan p = plan_skinny(M, N, K, tiled);
   if (p.split == 1) return 0;
   const size_t part = (size_t)M * (size_t)N * sizeof(int32_t);
@@ -430,7 +430,7 @@ hipError_t w8a8_launch_gemm(const int8_t* xq, const float* x_scale, const int8_t
   if (M == 0 || N == 0) return hipSuccess;
   if (M > kSkinnyMaxRows)
     return w8a8_launch_gemm_batched(xq, x_scale, wq, w_scale, M, N, K, tiled, y_bf16, y_f32, acc,
-                                    nullptr, 0, 0, stream);
+                                    nullptr, 0, 0, stream, false, workspace);
   const SkinnyPlan p = plan_skinny(M, N, K, tiled);
   GemmArgs g = make_args(p, xq, x_scale, wq, w_scale, M, N, K, y_bf16, y_f32, acc);
   if (p.split > 1) {

@@ -48,6 +48,12 @@ struct BatchedArgs {
   int32_t* acc;
   unsigned long long* keys;  // fused argmax sub-keys (as in the skinny kernel), or null
   int subkeys, key_stride;
+  // k split across workgroups (gemm_w8a8_lds32 with KS > 1): per-wave int32
+  // partials and arrival counters in the caller's workspace (zero between
+  // calls; every call leaves them zero)
+  int32_t* part;
+  uint32_t* count;
+  int part_bytes;
 };
 
 // Epilogue of one wave's MB x TN accumulator tiles: rows (mb0+i)*16 + 4*grp
@@ -566,6 +572,71 @@ __device__ __forceinline__ void lds32_epilogue(const BatchedArgs& g, const v16i 
   }
 }
 
+// Hand-off of a k split across workgroups, per wave (wslot: the wave's
+// (tile, wave) slot).  Each of the KS slices writes its int32 partial tile
+// (16 bytes per lane per 4 accumulators, stores that go through to the
+// device's coherence point), waits until they have completed, and counts its
+// arrival with a device-scope atomic add; the last to arrive reads the other
+// partials (loads from the coherence point, issued after its count
+// returned), adds them, zeroes every partial of the slot and the counter
+// (the workspace is left as it was found) and returns true: it runs the
+// epilogue.  The sums are exact, so which slice is last does not matter.
+// Partial layout: slot-major, then slice, then (block, quarter, lane).
+constexpr int kScDevice = 16;   // cache policy of the buffer accesses: sc1 (device scope)
+
+template <int RB, int CW, int KS>
+__device__ __forceinline__ bool lds32_split_handoff(const BatchedArgs& g, v16i (&acc)[RB][CW],
+                                                    size_t wslot, int ks, int lane) {
+  constexpr int kBlk = RB * CW * 16 * kWave;   // int32 per wave partial
+  const __amdgpu_buffer_rsrc_t part = __builtin_amdgcn_make_buffer_rsrc(g.part, 0, g.part_bytes, 0x00020000);
+  auto offset = [&](int slice, int i, int j, int q) {
+    return (int)((((wslot * KS + slice) * kBlk) + (((i * CW + j) * 4 + q) * kWave + lane) * 4) * 4);
+  };
+#pragma unroll
+  for (int i = 0; i < RB; ++i)
+#pragma unroll
+    for (int j = 0; j < CW; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const v4i v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+        __builtin_amdgcn_raw_buffer_store_b128(v, part, offset(ks, i, j, q), 0, kScDevice);
+      }
+  // the partial has reached the coherence point before the arrival is counted
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  uint32_t old = 0;
+  if (lane == 0) old = __hip_atomic_fetch_add(&g.count[wslot], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  old = __shfl(old, 0, kWave);
+  if (old != (uint32_t)(KS - 1)) return false;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  const v4i zero = {0, 0, 0, 0};
+#pragma unroll
+  for (int o = 1; o < KS; ++o) {
+    const int other = ks + o < KS ? ks + o : ks + o - KS;
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+#pragma unroll
+      for (int j = 0; j < CW; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const v4i t = __builtin_amdgcn_raw_buffer_load_b128(part, offset(other, i, j, q), 0, kScDevice);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] += t[e];
+        }
+  }
+#pragma unroll
+  for (int sl = 0; sl < KS; ++sl)
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+#pragma unroll
+      for (int j = 0; j < CW; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          __builtin_amdgcn_raw_buffer_store_b128(zero, part, offset(sl, i, j, q), 0, kScDevice);
+  if (lane == 0) __hip_atomic_exchange(&g.count[wslot], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return true;
+}
+
 // The bf16-only epilogue: each 32 x 32 block goes through the wave's own LDS
 // tile (row stride lds32_tile_row halfwords; 80 bytes puts the two half-waves'
 // rows in different banks) and leaves it as 16-byte row pieces, two stores
@@ -645,8 +716,10 @@ __device__ __forceinline__ void lds32_store_bf16(const BatchedArgs& g, const v16
 // tile are fetched from block / tile 0 (in bounds) and their results
 // dropped by the epilogue; the steps past the end are fetched again from
 // the last one.
-template <int RB, int CW, int P, bool kArgmax, bool kStores, bool kRowA = false, bool kRot = false>
+template <int RB, int CW, int P, bool kArgmax, bool kStores, bool kRowA = false, bool kRot = false,
+          int KS = 1>
 __global__ __launch_bounds__(kLdsWaves * kWave, P <= 4 ? (CW == 1 ? 4 : 2) : 2) void gemm_w8a8_lds32(BatchedArgs g) {
+  static_assert(KS == 1 || (!kArgmax && kStores), "a k split hands int32 partials over, no argmax fold");
   constexpr int FA = 2 * RB;                               // activation fragments per step
   constexpr int FAF = FA / kLdsWaves;                      // whole share per wave
   constexpr bool kDup = FA % kLdsWaves != 0;               // (FA even: then FA % 4 == 2)
@@ -670,12 +743,15 @@ __global__ __launch_bounds__(kLdsWaves * kWave, P <= 4 ? (CW == 1 ? 4 : 2) : 2) 
   const int xcd = b % kXcds;
   const int slot = b / kXcds;
   const int mt = slot % g.mtiles;
-  const int ng = (slot / g.mtiles) * kXcds + xcd;
+  const int ks = (slot / g.mtiles) % KS;   // k slice (the slices of a tile are KS slots apart)
+  const int ng = (slot / g.mtiles / KS) * kXcds + xcd;
   if (ng >= g.ngroups) return;
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int steps = g.steps;
+  // this workgroup's k steps: [kbase, kbase + steps) of the g.steps
+  const int kbase = (int)(((int64_t)g.steps * ks) / KS);
+  const int steps = (int)(((int64_t)g.steps * (ks + 1)) / KS) - kbase;
   const int mblocks = (g.M + 15) / 16;
   const int r32 = lane & 31, hi = lane >> 5;
   const int lane_off = ((r32 & 15) + 16 * hi) << 4;
@@ -706,7 +782,7 @@ __global__ __launch_bounds__(kLdsWaves * kWave, P <= 4 ? (CW == 1 ? 4 : 2) : 2) 
       const int row = min(rb * 16 + (lane & 15), g.M - 1);
       src[j] = g.xq + (size_t)row * (size_t)g.K + ((lane >> 4) << 4);
     } else {
-      src[j] = g.xq + ((size_t)(rb < mblocks ? rb : 0) * (size_t)steps << 10) + (lane << 4);
+      src[j] = g.xq + ((size_t)(rb < mblocks ? rb : 0) * (size_t)g.steps << 10) + (lane << 4);
     }
   }
   // k steps in a rotated order (kRot): the workgroups that read one weight
@@ -724,7 +800,7 @@ __global__ __launch_bounds__(kLdsWaves * kWave, P <= 4 ? (CW == 1 ? 4 : 2) : 2) 
       s += kstart;
       if (s >= steps) s -= steps;
     }
-    return s;
+    return kbase + s;
   };
   auto issue_a = [&](int p, int s) {
     s = kstep(s);
@@ -741,7 +817,7 @@ __global__ __launch_bounds__(kLdsWaves * kWave, P <= 4 ? (CW == 1 ? 4 : 2) : 2) 
 #pragma unroll
   for (int j = 0; j < CW; ++j) {
     const int t16 = ((ng * kLdsWaves + wave) * CW + j) * 2 + (r32 >> 4);
-    wsrc[j] = g.wq + ((size_t)(t16 < g.tiles16 ? t16 : 0) * (size_t)steps << 10) + lane_off;
+    wsrc[j] = g.wq + ((size_t)(t16 < g.tiles16 ? t16 : 0) * (size_t)g.steps << 10) + lane_off;
   }
   auto load_b = [&](v4i (&dst)[CW][2], int s) {
     s = kstep(s);
@@ -804,6 +880,10 @@ __global__ __launch_bounds__(kLdsWaves * kWave, P <= 4 ? (CW == 1 ? 4 : 2) : 2) 
     if (s0 + u < steps) step(u, s0 + u);
   wait_vmcnt<0>();
 
+  if constexpr (KS > 1) {
+    if (!lds32_split_handoff<RB, CW, KS>(g, acc, ((size_t)ng * g.mtiles + mt) * kLdsWaves + wave, ks, lane))
+      return;   // another slice of this tile finishes it
+  }
   if constexpr (kVecEpi) {
     if (g.y_bf16 && !g.y_f32 && !g.acc && g.N % 8 == 0 && (reinterpret_cast<uintptr_t>(g.y_bf16) & 15) == 0) {
       uint16_t* tile = reinterpret_cast<uint16_t*>(stage_mem + kStageBytes + RB * 32 * 4 + wave * lds32_tile_bytes);
@@ -814,19 +894,24 @@ __global__ __launch_bounds__(kLdsWaves * kWave, P <= 4 ? (CW == 1 ? 4 : 2) : 2) 
   lds32_epilogue<RB, CW, kArgmax, kStores>(g, acc, xs_sh, ws_lane, stage_mem, mt, ng, wave, lane);
 }
 
-template <int RB, int CW, int P, bool kRowA = false, bool kRot = false>
+template <int RB, int CW, int P, bool kRowA = false, bool kRot = false, int KS = 1>
 static hipError_t launch_lds32(BatchedArgs g, bool argmax, hipStream_t stream) {
   g.ngroups = (g.tiles16 + 2 * kLdsWaves * CW - 1) / (2 * kLdsWaves * CW);
   g.mtiles = (g.M + 32 * RB - 1) / (32 * RB);
   const int64_t ng_padded = ((int64_t)g.ngroups + kXcds - 1) / kXcds * kXcds;
-  const dim3 grid((unsigned)(ng_padded * g.mtiles)), block(kLdsWaves * kWave);
-  const bool stores = g.y_bf16 || g.y_f32 || g.acc;
-  if (argmax && !stores)
-    hipLaunchKernelGGL((gemm_w8a8_lds32<RB, CW, P, true, false, kRowA, kRot>), grid, block, 0, stream, g);
-  else if (argmax)
-    hipLaunchKernelGGL((gemm_w8a8_lds32<RB, CW, P, true, true, kRowA, kRot>), grid, block, 0, stream, g);
-  else
-    hipLaunchKernelGGL((gemm_w8a8_lds32<RB, CW, P, false, true, kRowA, kRot>), grid, block, 0, stream, g);
+  const dim3 grid((unsigned)(ng_padded * g.mtiles * KS)), block(kLdsWaves * kWave);
+  if constexpr (KS > 1) {
+    (void)argmax;   // (the dispatcher never splits an argmax fold)
+    hipLaunchKernelGGL((gemm_w8a8_lds32<RB, CW, P, false, true, kRowA, kRot, KS>), grid, block, 0, stream, g);
+  } else {
+    const bool stores = g.y_bf16 || g.y_f32 || g.acc;
+    if (argmax && !stores)
+      hipLaunchKernelGGL((gemm_w8a8_lds32<RB, CW, P, true, false, kRowA, kRot>), grid, block, 0, stream, g);
+    else if (argmax)
+      hipLaunchKernelGGL((gemm_w8a8_lds32<RB, CW, P, true, true, kRowA, kRot>), grid, block, 0, stream, g);
+    else
+      hipLaunchKernelGGL((gemm_w8a8_lds32<RB, CW, P, false, true, kRowA, kRot>), grid, block, 0, stream, g);
+  }
   return hipGetLastError();
 }
 
@@ -910,6 +995,34 @@ static int64_t lds32_wide_workgroups(int64_t M, int64_t N) {
   return ((N + 15) / 16 + 2 * kLdsWaves - 1) / (2 * kLdsWaves) * ((M + 95) / 96);
 }
 
+// k split across two workgroups for long reductions on the 64 x 128 grids
+// (down 12288 -> 4096 at 288 rows: 96 x 128 tiles in 2 slices, 192
+// workgroups, 33-34 us against 39.5-41 unsplit; at K = 4096 the handoff ate
+// the gain: o 15.0-15.3 either way): at least kLds32SplitMinSteps k steps,
+// and every workgroup of the split grid resident at once.
+constexpr int kLds32Split = 2;
+constexpr int64_t kLds32SplitMinSteps = 128;
+constexpr int64_t kLds32SplitMaxWorkgroups = 256;
+
+static bool lds32_split(int64_t M, int64_t N, int64_t steps) {
+  const int64_t wg32 = lds32_workgroups(M, N);
+  return wg32 >= kLds32MinWorkgroups && wg32 < kLds32WideTileMinWorkgroups &&
+         steps >= kLds32SplitMinSteps &&
+         lds32_wide_workgroups(M, N) * kLds32Split <= kLds32SplitMaxWorkgroups;
+}
+
+// workspace of the split: arrival counters (one per wave and tile, padded to
+// 256 bytes), then the partials (per wave and slice, 96 x 32 int32 tiles)
+static int64_t lds32_split_slots(int64_t M, int64_t N) {
+  return lds32_wide_workgroups(M, N) * kLdsWaves;
+}
+static size_t lds32_split_count_bytes(int64_t M, int64_t N) {
+  return ((size_t)lds32_split_slots(M, N) * sizeof(uint32_t) + 255) & ~(size_t)255;
+}
+static size_t lds32_split_part_bytes(int64_t M, int64_t N) {
+  return (size_t)lds32_split_slots(M, N) * kLds32Split * (3 * 1 * 16 * kWave) * sizeof(int32_t);
+}
+
 static int64_t lds_workgroups(int64_t M, int64_t N) {
   const int64_t ngroups = ((N + 15) / 16 + 2 * kLdsShape.tn - 1) / (2 * kLdsShape.tn);
   const int64_t mtiles = (M + 32 * kLdsShape.mb - 1) / (32 * kLdsShape.mb);
@@ -932,6 +1045,10 @@ static bool launch_lds_path(const BatchedArgs& g, int64_t M, int64_t N, bool arg
     return true;
   }
   const int64_t wg32 = lds32_workgroups(M, N);
+  if (!argmax && g.part && lds32_split(M, N, g.steps)) {
+    *err = launch_lds32<3, 1, 6, kRowA, true, kLds32Split>(g, argmax, stream);
+    return true;
+  }
   if (wg32 >= kLds32WideTileMinWorkgroups) {
     *err = launch_lds32<2, 2, 3, kRowA, true>(g, argmax, stream);
     return true;
@@ -976,11 +1093,19 @@ static hipError_t launch_batched(BatchedArgs g, bool tiled, bool argmax, hipStre
 
 }  // namespace w8a8
 
+size_t w8a8_batched_workspace_bytes(int64_t M, int64_t N, int64_t K, bool a_tiled) {
+  using namespace w8a8;
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  if (!a_tiled && K % 64 != 0) return 0;   // (row-major activations: the LDS path needs K % 64 == 0)
+  if (!lds32_split(M, N, (K + 63) / 64)) return 0;
+  return lds32_split_count_bytes(M, N) + lds32_split_part_bytes(M, N);
+}
+
 hipError_t w8a8_launch_gemm_batched(const int8_t* xq, const float* x_scale, const int8_t* wq,
                                     const float* w_scale, int64_t M, int64_t N, int64_t K,
                                     bool tiled, uint16_t* y_bf16, float* y_f32, int32_t* acc,
                                     void* keys, int subkeys, int key_stride, hipStream_t stream,
-                                    bool a_tiled) {
+                                    bool a_tiled, void* workspace) {
   using namespace w8a8;
   if (M == 0 || N == 0) return hipSuccess;
   BatchedArgs g{};
@@ -992,6 +1117,11 @@ hipError_t w8a8_launch_gemm_batched(const int8_t* xq, const float* x_scale, cons
   g.keys = reinterpret_cast<unsigned long long*>(keys);
   g.subkeys = subkeys; g.key_stride = key_stride;
   const bool argmax = keys != nullptr;
+  if (workspace && tiled && w8a8_batched_workspace_bytes(M, N, K, a_tiled) > 0) {
+    g.count = reinterpret_cast<uint32_t*>(workspace);
+    g.part = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(workspace) + lds32_split_count_bytes(M, N));
+    g.part_bytes = (int)lds32_split_part_bytes(M, N);
+  }
   // The LDS-pipelined kernels take tiled activations, or row-major ones
   // when K is a multiple of 64 (each fragment then gathered from 16 rows
   // into the same lane order)
