@@ -349,6 +349,14 @@ def pmc_probe_batched(dev):
     print(json.dumps({"pmc_probe_batched": "done", "shapes": BATCHED_SHAPES}), flush=True)
 
 
+def split_of(kernel_name):
+    """The k split (KS, the last template argument) of a gemm_w8a8_lds32
+    kernel name, else 1."""
+    import re
+    m = re.search(r"gemm_w8a8_lds32<([^>]*)>", kernel_name)
+    return int(m.group(1).split(",")[-1]) if m else 1
+
+
 def ingest_pmc_batched(dirs, command):
     """Per-shape medians of the counters found in the --pmc-probe-batched runs:
     HBM bytes (FETCH_SIZE/WRITE_SIZE, scaled by the 1 GiB copy as for the
@@ -402,7 +410,10 @@ def ingest_pmc_batched(dirs, command):
              "# with the duration taken from the same dispatches under the counter run.",
              "# model_activations_once_per_xcd = (algorithmic + 7*M*K) / algorithmic: the traffic",
              "# if each of the 8 XCDs (separate L2s) fetches the activations once and the",
-             "# weights are fetched once"]
+             "# weights are fetched once; for a kernel that splits k across KS workgroups",
+             "# (last template argument) model_with_split_handoff adds the handoff: each slice",
+             "# writes its int32 partial, the last arriver reads the KS-1 others and zeroes all",
+             "# KS (per wave 96 x 32 int32 per slice, 4 waves per 96 x 128 tile)"]
     for n in BATCHED_SHAPES:
         lin = next(l for l in synth.QWEN3_8B_LAYER if l.name == n)
         alg = linear_bytes(M, lin.N, lin.K)
@@ -419,6 +430,14 @@ def ingest_pmc_batched(dirs, command):
                 lines.append(f"  hbm_over_algorithmic: {(e['FETCH_SIZE'] + e['WRITE_SIZE']) / alg:.3f}")
                 # each of the 8 XCDs fetches the M x K activations into its own L2
                 lines.append(f"  model_activations_once_per_xcd: {(alg + 7 * M * lin.K) / alg:.3f}")
+                ks = split_of(kname[(n, v)])
+                if ks > 1:
+                    slot = 96 * 32 * 4   # bytes of one wave's partial
+                    slots = -(-lin.N // 128) * -(-M // 96) * 4
+                    handoff = slots * slot * (ks + (ks - 1) + ks)
+                    lines.append(f"  split_handoff_bytes: {handoff}")
+                    lines.append(f"  model_with_split_handoff: "
+                                 f"{(alg + 7 * M * lin.K + handoff) / alg:.3f}")
     lines.append(f"kernel_source_sha: {file_sha(BATCHED_SRC)}")
     with open(BATCHED_PMC_FILE, "w") as f:
         f.write("\n".join(lines) + "\n")

@@ -1046,7 +1046,11 @@ static bool launch_lds_path(const BatchedArgs& g, int64_t M, int64_t N, bool arg
   }
   const int64_t wg32 = lds32_workgroups(M, N);
   if (!argmax && g.part && lds32_split(M, N, g.steps)) {
-    *err = launch_lds32<3, 1, 6, kRowA, true, kLds32Split>(g, argmax, stream);
+    // (k order not rotated: with 96-row tiles the rotated starts lie ~8 steps
+    // apart, too far for the L2 to keep the shared weight and activation
+    // steps, and the HBM traffic of 288 x 4096 x 12288 went 1.5 -> 3.5x the
+    // algorithmic bytes for no gain in time)
+    *err = launch_lds32<3, 1, 6, kRowA, false, kLds32Split>(g, argmax, stream);
     return true;
   }
   if (wg32 >= kLds32WideTileMinWorkgroups) {
