@@ -147,7 +147,8 @@ def read_batched_counters():
 def make_weight(N, K, workload, index, device, tiled=True, with_bf16=False):
     """Random-init N(0, 0.02) fp32 weight drawn on the device (seeded by
     workload and index), quantized to int8 per output channel by the library;
-    optionally also its bf16 copy."""
+    optionally also its bf16 copy, row-major (with_bf16=True) or in the tiled
+    bf16 layout (with_bf16="tiled")."""
     import torch
     import synth
     import w8a8_quantized_verification_amd as w8
@@ -155,6 +156,8 @@ def make_weight(N, K, workload, index, device, tiled=True, with_bf16=False):
     wq, ws = w8.quantize_weight(w, tiled=tiled)
     wb = w.to(torch.bfloat16) if with_bf16 else None
     del w
+    if with_bf16 == "tiled":
+        wb = w8.tile_weight_bf16(wb)
     return wq, ws, wb
 
 
@@ -956,12 +959,13 @@ def layer_measurement(dev, wsp, M, workload):
              "TOPS": round(tops, 1), "mfma_frac": round(tops / INT8_PEAK_TOPS, 4)}
         if M <= 16:
             # the in-build bf16 GEMM at the same shape (twice the weight bytes),
-            # over its own rotating bf16 copies
+            # over its own rotating bf16 copies in the tiled bf16 layout
             ncb = rotation_copies(lin.N, 2 * lin.K)
-            wb = [synth.weights_device(workload, 2000 + 200 * li + c, lin.N, lin.K, dev)
-                  .to(torch.bfloat16) for c in range(ncb)]
+            wb = [w8.tile_weight_bf16(synth.weights_device(workload, 2000 + 200 * li + c, lin.N,
+                                                           lin.K, dev).to(torch.bfloat16))
+                  for c in range(ncb)]
             yb16 = torch.empty(M, lin.N, dtype=torch.bfloat16, device=dev)
-            tb = graph_time([(lambda c=c: w8.bf16_linear(x, wb[c], y_bf16=yb16))
+            tb = graph_time([(lambda c=c: w8.bf16_linear(x, wb[c], N=lin.N, y_bf16=yb16))
                              for c in range(ncb)], replays=10) / ncb
             e.update({"bf16_us": round(tb * 1e6, 2),
                       "bf16_GBs": round((2 * lin.N * lin.K + 2 * M * lin.K + 2 * M * lin.N)
@@ -1215,13 +1219,22 @@ def extra_measurements(dev, copies, x_dev, xq, xsc, wsp):
                                  "tiled_GBs": round(b / t_tl / 1e9, 1),
                                  "row_major_us": round(t_rm * 1e6, 2),
                                  "row_major_GBs": round(b / t_rm / 1e9, 1)}
-    # bf16 reference at the LM-head shape (two-times weight traffic)
-    t_bf = ev_time(lambda i: w8.bf16_linear(x_dev[0], rm[i % 2][2], want_bf16=False, y_f32=lg))
+    # bf16 reference at the LM-head shape (two-times weight traffic), on the
+    # tiled bf16 layout (each weight load one KiB, as for the int8 weights)
+    # and, for context, on row-major bf16 weights
+    t_bf_rm = ev_time(lambda i: w8.bf16_linear(x_dev[0], rm[i % 2][2], want_bf16=False, y_f32=lg))
+    bt = [w8.tile_weight_bf16(rm[i][2]) for i in range(2)]
+    t_bf = ev_time(lambda i: w8.bf16_linear(x_dev[0], bt[i % 2], N=V, want_bf16=False, y_f32=lg))
     bb = 2 * V * K + 2 * M * K + 4 * M * V
     res["bf16_reference_lm_head_m5"] = {"us": round(t_bf * 1e6, 2), "GBs": round(bb / t_bf / 1e9, 1),
+                                        "layout": "tiled bf16",
+                                        "row_major_us": round(t_bf_rm * 1e6, 2),
+                                        "row_major_GBs": round(bb / t_bf_rm / 1e9, 1),
                                         "w8a8_tiled_us": round(t_tl * 1e6, 2),
-                                        "time_ratio_bf16_over_w8a8": round(t_bf / t_tl, 3)}
-    del rm
+                                        "w8a8_tiled_GBs": round(b / t_tl / 1e9, 1),
+                                        "time_ratio_bf16_over_w8a8": round(t_bf / t_tl, 3),
+                                        "byte_ratio_bf16_over_w8a8": round(bb / b, 3)}
+    del rm, bt
 
     # stochastic verification at T = 1 on the same LM head: quantize_act ->
     # linear (fp32 logits) -> verify_sample, and verify_sample alone
@@ -1312,11 +1325,11 @@ def stack32b_measurement(dev, wsp, replays=10):
                                                 synth.stack_tensor_index(layer, li),
                                                 lins[li].N, lins[li].K, dev) for li in grp])
             wq, ws = w8.quantize_weight(w, tiled=True)
-            row.append((wq, ws, w.to(torch.bfloat16)))
+            row.append((wq, ws, w8.tile_weight_bf16(w.to(torch.bfloat16))))
             del w
         wts.append(row)
     lm = make_weight(head.N, head.K, synth.W_STACK32B, synth.stack_tensor_index(L, 0), dev,
-                     tiled=True, with_bf16=True)
+                     tiled=True, with_bf16="tiled")
     torch.cuda.synchronize()
     print(f"[bench] 32B stack drawn and quantized on the device "
           f"({time.perf_counter() - t0:.1f} s)", file=sys.stderr, flush=True)
@@ -1378,8 +1391,8 @@ def stack32b_measurement(dev, wsp, replays=10):
     def bf16_step():
         for layer in range(L):
             for j in range(4):
-                w8.bf16_linear(xs[layer][j], wts[layer][j][2], y_bf16=ys[j])
-        w8.bf16_linear(x_lm, lm[2], want_bf16=False, y_f32=logits)
+                w8.bf16_linear(xs[layer][j], wts[layer][j][2], N=ys[j].shape[1], y_bf16=ys[j])
+        w8.bf16_linear(x_lm, lm[2], N=head.N, want_bf16=False, y_f32=logits)
         w8.verify_accept(logits, draft, argmax=am, accept_len=al, next_token=nt, workspace=wsp)
 
     t_w8 = graph_time([w8a8_step], replays=replays)

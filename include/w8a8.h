@@ -608,6 +608,25 @@ w8a8_status w8a8_bf16_linear(const uint16_t* x_bf16, const uint16_t* w_bf16,
                              int64_t M, int64_t N, int64_t K,
                              uint16_t* y_bf16, float* y_f32, void* stream);
 
+/*
+ * The same bf16 reference on tiled weights (the layout that lets every
+ * weight load be one contiguous KiB, as for the W8A8 weights): element
+ * (n, k) of w[N][K] at bf16 offset
+ *   ((n/16 * steps + k/32) * 64 + (n%16 + 16*((k%32)/8))) * 8 + k%8,
+ * steps = ceil(K/32), w8a8_bf16_tiled_weight_bytes(N, K) bytes in all, the
+ * padding (n >= N, k >= K) zero.  w8a8_tile_weight_bf16 writes it from a
+ * row-major w_bf16 (both 16-byte aligned; K % 16 == 0).
+ * w8a8_bf16_linear_tiled: w8a8_bf16_linear's arguments, outputs and
+ * requirements with w_tiled in that layout (the fp32 sums may differ from
+ * w8a8_bf16_linear's in the last bits: another summation order).
+ */
+size_t      w8a8_bf16_tiled_weight_bytes(int64_t N, int64_t K);
+w8a8_status w8a8_tile_weight_bf16(const uint16_t* w_bf16, int64_t N, int64_t K,
+                                  uint16_t* w_tiled, void* stream);
+w8a8_status w8a8_bf16_linear_tiled(const uint16_t* x_bf16, const uint16_t* w_tiled,
+                                   int64_t M, int64_t N, int64_t K,
+                                   uint16_t* y_bf16, float* y_f32, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -279,6 +279,23 @@ def test_bf16_linear_validation(lib):
     assert f(None, None, 0, 512, 256, None, None, None) == OK
 
 
+def test_bf16_tiled_validation(lib):
+    assert lib.w8a8_bf16_tiled_weight_bytes(151936, 4096) == 9496 * 128 * 1024
+    assert lib.w8a8_bf16_tiled_weight_bytes(17, 48) == 2 * 2 * 1024
+    assert lib.w8a8_bf16_tiled_weight_bytes(0, 48) == 0
+    t = lib.w8a8_tile_weight_bf16
+    assert t(A16, 17, 40, A16b, None) == INVALID          # K % 16
+    assert t(A16 + 2, 17, 48, A16b, None) == INVALID      # misaligned
+    assert t(None, 17, 48, A16b, None) == INVALID
+    assert t(None, 0, 48, None, None) == OK
+    f = lib.w8a8_bf16_linear_tiled
+    assert f(A16, A16b, 17, 512, 256, A16, None, None) == UNSUPPORTED
+    assert f(A16, A16b, 5, 512, 250, A16, None, None) == INVALID
+    assert f(A16, A16b, 5, 512, 256, None, None, None) == INVALID
+    assert f(A16 + 2, A16b, 5, 512, 256, A16, None, None) == INVALID
+    assert f(None, None, 0, 512, 256, None, None, None) == OK
+
+
 def test_last_error_is_per_call(lib):
     assert q_act(lib, K=24) == INVALID
     assert lib.w8a8_last_error()

@@ -507,6 +507,44 @@ def test_bf16_reference_linear(M, N, K):
     assert np.all(np.abs(host(yf).astype(np.float64) - ref) <= bound)
 
 
+def untile_bf16(t: np.ndarray, N: int, K: int) -> np.ndarray:
+    """Row-major [N][K] view of a tiled bf16 weight [N/16][K/32][64][8]:
+    lane l of (tile, step) holds channel 16*tile + l%16 and k = 32*step +
+    8*(l//16) .. +7 (the layout stated in include/w8a8.h)."""
+    tiles, steps = t.shape[0], t.shape[1]
+    a = t.reshape(tiles, steps, 4, 16, 8)           # tile, step, k-group, channel, value
+    a = a.transpose(0, 3, 1, 2, 4)                  # tile, channel, step, k-group, value
+    return a.reshape(tiles * 16, steps * 32)
+
+
+@pytest.mark.parametrize("M,N,K", [(5, 512, 256), (5, 4096, 4096), (8, 1000, 5120), (16, 33, 48),
+                                   (5, 40000, 4096), (1, 32784, 1040), (3, 17, 4112)])
+def test_bf16_reference_linear_tiled(M, N, K):
+    """The tiled bf16 layout read back (every value in place, the padding
+    zero) and the product on it against the float64 oracle within the
+    summation-order bound, beside the row-major kernel's.  N >= 32768 takes
+    two tiles per workgroup (32784: an odd tile count, the last
+    workgroup's second tile past N); K = 1040, 4112 end in a half step."""
+    announce(f"bf16 linear tiled M={M} N={N} K={K}")
+    bits = synth.activations_bf16(510, M, K, outliers=True)
+    w = synth.weights_f32(510, N, K)
+    wb = synth.to_bf16_bits(w)
+    ref = oracle.bf16_reference_logits(bits, w)
+    wt = w8.tile_weight_bf16(dev_bf16(wb))
+    full = untile_bf16(host(wt), N, K)
+    np.testing.assert_array_equal(full[:N, :K], wb)
+    assert not full[N:].any() and not full[:, K:].any()
+    yb, yf = w8.bf16_linear(dev_bf16(bits), wt, N=N, want_bf16=True, want_f32=True)
+    _, yf_rm = w8.bf16_linear(dev_bf16(bits), dev_bf16(wb), want_bf16=False, want_f32=True)
+    torch.cuda.synchronize()
+    x64 = np.abs(oracle.bf16_to_f32(bits).astype(np.float64))
+    w64 = np.abs(oracle.bf16_to_f32(wb).astype(np.float64))
+    bound = K * 2.0 ** -23 * (x64 @ w64.T)
+    assert np.all(np.abs(host(yf).astype(np.float64) - ref) <= bound)
+    assert np.all(np.abs(host(yf_rm).astype(np.float64) - ref) <= bound)
+    np.testing.assert_array_equal(host(yb), oracle.f32_to_bf16(host(yf)))
+
+
 # --------------------------------------------------------------------------
 # one verify step end to end (tiny workload)
 # --------------------------------------------------------------------------

@@ -51,6 +51,9 @@ SIGNATURES = {
                                          _vp, _vp]),
     "w8a8_hbm_read_probe": (_i32, [_vp, _sz, _vp, _vp, _vp, _vp]),
     "w8a8_bf16_linear": (_i32, [_vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp]),
+    "w8a8_bf16_tiled_weight_bytes": (_sz, [_i64, _i64]),
+    "w8a8_tile_weight_bf16": (_i32, [_vp, _i64, _i64, _vp, _vp]),
+    "w8a8_bf16_linear_tiled": (_i32, [_vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp]),
     "w8a8_verify_sample_workspace_bytes": (_sz, [_i64, _i64, _i64]),
     "w8a8_verify_sample": (_i32, [_vp, _i64, _vp, _i64, _i64, _c.c_float, _vp, _vp, _vp, _vp,
                                   _vp, _sz, _vp]),

@@ -16,7 +16,8 @@ __all__ = [
     "W8A8Error", "quantize_act", "quantize_weight", "tile_weight", "tiled_shape", "linear",
     "linear_workspace_bytes",
     "verify_accept", "verify_accept_workspace_bytes", "lm_head_verify", "lm_head_argmax",
-    "accept_from_keys", "bf16_linear", "Workspace", "verify_sample",
+    "accept_from_keys", "bf16_linear", "bf16_tiled_shape", "tile_weight_bf16", "Workspace",
+    "verify_sample",
     "verify_sample_workspace_bytes", "sample_weights", "w4_shape", "quantize_weight_w4",
     "linear_w4", "lm_head_argmax_w4", "residual_rmsnorm_quant", "silu_mul_quant",
     "quantize_act_tiled", "linear_tiled_act", "linear_tiled_act_workspace_bytes",
@@ -367,22 +368,48 @@ def accept_from_keys(draft, *, want_argmax=True, argmax=None, accept_len=None, n
     return argmax, accept_len, next_token
 
 
-def bf16_linear(x, w, *, want_bf16=True, want_f32=False, y_bf16=None, y_f32=None):
+def bf16_tiled_shape(N: int, K: int) -> tuple:
+    """Shape of the tiled bf16 weight layout as a bfloat16 tensor:
+    [ceil(N/16), ceil(K/32), 64 lanes, 8 values] (see include/w8a8.h)."""
+    return ((N + 15) // 16, (K + 31) // 32, 64, 8)
+
+
+def tile_weight_bf16(w: torch.Tensor, *, out=None) -> torch.Tensor:
+    """Rearrange a row-major bf16 ``w[N][K]`` into the tiled layout of
+    :func:`bf16_linear` (shape :func:`bf16_tiled_shape`)."""
+    _need(w, "w", torch.bfloat16, 2)
+    N, K = w.shape
+    out = _out(out, bf16_tiled_shape(N, K), torch.bfloat16, w.device, "out")
+    check(lib().w8a8_tile_weight_bf16(_ptr(w), N, K, _ptr(out), _stream(w.device)))
+    return out
+
+
+def bf16_linear(x, w, *, N: int | None = None, want_bf16=True, want_f32=False, y_bf16=None,
+                y_f32=None):
     """The bf16 reference linear ``x[M][K] @ w[N][K]^T`` (M <= 16), fp32
-    accumulation.  Returns ``(y_bf16, y_f32)``."""
+    accumulation.  ``w`` is row-major bf16 ``[N][K]`` or the tiled layout
+    (4-D, from :func:`tile_weight_bf16`; then ``N`` is required).  Returns
+    ``(y_bf16, y_f32)``."""
     _need(x, "x", torch.bfloat16, 2)
     dev = x.device
-    _need(w, "w", torch.bfloat16, 2, dev)
     M, K = x.shape
-    N, K2 = w.shape
-    if K2 != K:
-        raise ValueError("x and w must share K")
+    tiled = isinstance(w, torch.Tensor) and w.dim() == 4
+    _need(w, "w", torch.bfloat16, 4 if tiled else 2, dev)
+    if tiled:
+        if N is None:
+            raise ValueError("N is required with tiled weights")
+        if tuple(w.shape) != bf16_tiled_shape(N, K):
+            raise ValueError(f"tiled w must have shape {bf16_tiled_shape(N, K)} (got {tuple(w.shape)})")
+    else:
+        N, K2 = w.shape
+        if K2 != K:
+            raise ValueError("x and w must share K")
     if want_bf16 or y_bf16 is not None:
         y_bf16 = _out(y_bf16, (M, N), torch.bfloat16, dev, "y_bf16")
     if want_f32 or y_f32 is not None:
         y_f32 = _out(y_f32, (M, N), torch.float32, dev, "y_f32")
-    check(lib().w8a8_bf16_linear(_ptr(x), _ptr(w), M, N, K, _ptr(y_bf16), _ptr(y_f32),
-                                 _stream(dev)))
+    f = lib().w8a8_bf16_linear_tiled if tiled else lib().w8a8_bf16_linear
+    check(f(_ptr(x), _ptr(w), M, N, K, _ptr(y_bf16), _ptr(y_f32), _stream(dev)))
     return y_bf16, y_f32
 
 

@@ -375,6 +375,44 @@ w8a8_status w8a8_bf16_linear(const uint16_t* x_bf16, const uint16_t* w_bf16, int
                                           reinterpret_cast<hipStream_t>(stream)), fn);
 }
 
+size_t w8a8_bf16_tiled_weight_bytes(int64_t N, int64_t K) {
+  if (N <= 0 || N > kMaxRows || K <= 0 || K > (int64_t(1) << 24)) return 0;
+  return w8a8_bf16_tiled_weight_bytes_impl(N, K);
+}
+
+w8a8_status w8a8_tile_weight_bf16(const uint16_t* w_bf16, int64_t N, int64_t K, uint16_t* w_tiled,
+                                  void* stream) {
+  static const char* fn = "w8a8_tile_weight_bf16";
+  g_last_error.clear();
+  if (N < 0 || N > kMaxRows) return fail(W8A8_ERR_INVALID_ARG, fn, "N out of range");
+  if (K < 0 || K > (int64_t(1) << 24) || K % 16 != 0)
+    return fail(W8A8_ERR_INVALID_ARG, fn, "K must be a multiple of 16 in [0, 2^24]");
+  if (N == 0 || K == 0) return W8A8_OK;
+  if (!w_bf16 || !w_tiled) return fail(W8A8_ERR_INVALID_ARG, fn, "w_bf16 or w_tiled is NULL");
+  if (!aligned(w_bf16, 16) || !aligned(w_tiled, 16))
+    return fail(W8A8_ERR_INVALID_ARG, fn, "w_bf16 and w_tiled must be 16-byte aligned");
+  return hip_status(w8a8_launch_tile_bf16(w_bf16, N, K, w_tiled, reinterpret_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+w8a8_status w8a8_bf16_linear_tiled(const uint16_t* x_bf16, const uint16_t* w_tiled, int64_t M,
+                                   int64_t N, int64_t K, uint16_t* y_bf16, float* y_f32,
+                                   void* stream) {
+  static const char* fn = "w8a8_bf16_linear_tiled";
+  g_last_error.clear();
+  if (M < 0 || N < 0 || N > kMaxRows) return fail(W8A8_ERR_INVALID_ARG, fn, "M or N out of range");
+  if (M > 16) return fail(W8A8_ERR_UNSUPPORTED, fn, "the bf16 reference handles M <= 16");
+  if (K < 0 || K > (int64_t(1) << 24) || K % 16 != 0)
+    return fail(W8A8_ERR_INVALID_ARG, fn, "K must be a multiple of 16 in [0, 2^24]");
+  if (M == 0 || N == 0) return W8A8_OK;
+  if (!y_bf16 && !y_f32) return fail(W8A8_ERR_INVALID_ARG, fn, "all outputs are NULL");
+  if (K > 0 && (!x_bf16 || !w_tiled)) return fail(W8A8_ERR_INVALID_ARG, fn, "x_bf16 or w_tiled is NULL");
+  if (!aligned(x_bf16, 16) || !aligned(w_tiled, 16) || !aligned(y_bf16, 2) || !aligned(y_f32, 4))
+    return fail(W8A8_ERR_INVALID_ARG, fn, "pointer misaligned");
+  return hip_status(w8a8_launch_bf16_gemm_tiled(x_bf16, w_tiled, M, N, K, y_bf16, y_f32,
+                                                reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
 
 // ---- stochastic verification (T > 0) ----
 

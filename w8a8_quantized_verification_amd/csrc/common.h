@@ -117,6 +117,12 @@ hipError_t w8a8_launch_accept_keys(unsigned long long* keys, int subkeys, int ke
 
 hipError_t w8a8_launch_bf16_gemm(const uint16_t* x, const uint16_t* w, int64_t M, int64_t N,
                                  int64_t K, uint16_t* y_bf16, float* y_f32, hipStream_t stream);
+size_t w8a8_bf16_tiled_weight_bytes_impl(int64_t N, int64_t K);
+hipError_t w8a8_launch_tile_bf16(const uint16_t* w, int64_t N, int64_t K, uint16_t* out,
+                                 hipStream_t stream);
+hipError_t w8a8_launch_bf16_gemm_tiled(const uint16_t* x, const uint16_t* w_tiled, int64_t M,
+                                       int64_t N, int64_t K, uint16_t* y_bf16, float* y_f32,
+                                       hipStream_t stream);
 
 size_t w8a8_sample_workspace_bytes_impl(int64_t R, int64_t V);
 hipError_t w8a8_launch_sample_weights(const float* logits, int64_t R, int64_t V, float inv_t,
