@@ -67,6 +67,11 @@ def parse_args():
     p.add_argument("--ingest-trace", metavar="TRACE_DIR",
                    help="turn a rocprofv3 --kernel-trace --stats csv run into a summary")
     p.add_argument("--command", default="", help="the command that produced the ingested run")
+    p.add_argument("--layer288-probe", action="store_true",
+                   help="only the fused 288-row Qwen3-8B layer linears, eager (for rocprofv3 "
+                        "--kernel-trace)")
+    p.add_argument("--ingest-layer288-trace", metavar="TRACE_DIR",
+                   help="rocprofv3 --kernel-trace dir of a --layer288-probe run")
     p.add_argument("--batched-verify-probe", action="store_true",
                    help="only the 288-row LM-head verification step (for rocprofv3 --kernel-trace)")
     p.add_argument("--ingest-batched-trace", metavar="TRACE_DIR",
@@ -459,6 +464,10 @@ def main():
         ingest_trace(args.ingest_trace, args.command,
                      os.path.join(ROOT, "profiles", "lm_head_verify_m5_kernel_trace.txt"))
         return
+    if args.ingest_layer288_trace:
+        ingest_layer288_trace(args.ingest_layer288_trace, args.command,
+                              os.path.join(ROOT, "profiles", "batched_layer_m288_kernel_trace.txt"))
+        return
     if args.ingest_batched_trace:
         ingest_trace(args.ingest_batched_trace, args.command,
                      os.path.join(ROOT, "profiles", "lm_head_verify_m288_kernel_trace.txt"))
@@ -492,6 +501,9 @@ def main():
         return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.layer288_probe:
+        layer288_probe(dev)
+        return
 
     M, K, V, G, B = 5, 4096, synth.QWEN3_VOCAB, 4, 1
     # The LM head of the 1000-trial verification workload: fp32 N(0, 0.02)
@@ -1113,6 +1125,85 @@ def w4a8_measurement(dev, x_dev, xq, xsc, wsp):
     res["qwen3_8b_layer_linears_m5"] = {"per_linear": layer,
                                         "sum_us": round(sum(e["us"] for e in layer), 2)}
     return res
+
+
+LAYER288_GROUPS = (("qkv", (0, 1, 2)), ("o", (3,)), ("gate_up", (4, 5)), ("down", (6,)))
+LAYER288_ROUNDS = 12
+
+
+def layer288_probe(dev):
+    """The fused 288-row layer's four launches (tiled activations, bf16 out,
+    the layer's workspace), eager, LAYER288_ROUNDS rounds over rotating weight
+    copies, in the order of LAYER288_GROUPS (for rocprofv3 --kernel-trace)."""
+    import numpy as np
+    import torch
+
+    import synth
+    import w8a8_quantized_verification_amd as w8
+
+    M = 288
+    lins = synth.QWEN3_8B_LAYER
+    wsp = w8.Workspace()
+    shapes = []
+    for gi, (name, grp) in enumerate(LAYER288_GROUPS):
+        N, K = sum(lins[i].N for i in grp), lins[grp[0]].K
+        nc = rotation_copies(N, K)
+        wl = []
+        for c in range(nc):
+            w = torch.cat([synth.weights_device(synth.W_LAYER_M5, 7000 + 100 * gi + 10 * c + i,
+                                                lins[i].N, K, dev) for i in grp])
+            wl.append(w8.quantize_weight(w, tiled=True))
+            del w
+        x = torch.from_numpy(synth.activations_bf16(synth.W_LAYER_M5, M, K, outliers=True)
+                             .view(np.int16).copy()).view(torch.bfloat16).to(dev)
+        xt, xs = w8.quantize_act_tiled(x)
+        y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        shapes.append((wl, xt, xs, y, K))
+    torch.cuda.synchronize()
+    for r in range(LAYER288_ROUNDS):
+        for wl, xt, xs, y, K in shapes:
+            w8.linear_tiled_act(xt, xs, *wl[r % len(wl)], K=K, y_bf16=y, workspace=wsp)
+    torch.cuda.synchronize()
+    print(json.dumps({"layer288_probe": "done", "rounds": LAYER288_ROUNDS}), flush=True)
+
+
+def ingest_layer288_trace(trace_dir, command, out_path):
+    """Per-shape durations of the --layer288-probe launches: the batched
+    kernels' dispatches in start order are the rounds of (qkv, o, gate_up,
+    down); the first round is left out (first touch of the code and data)."""
+    import numpy as np
+
+    import synth
+    rows = sorted((r for r in _csv_rows(trace_dir, "kernel_trace.csv")
+                   if "gemm_w8a8_lds" in r["Kernel_Name"] or "gemm_w8a8_batched" in r["Kernel_Name"]),
+                  key=lambda r: int(r["Start_Timestamp"]))
+    n = len(LAYER288_GROUPS)
+    if len(rows) != n * LAYER288_ROUNDS:
+        raise SystemExit(f"expected {n * LAYER288_ROUNDS} batched dispatches, found {len(rows)}")
+    lins = synth.QWEN3_8B_LAYER
+    lines = ["# rocprofv3 kernel trace of the fused 288-row Qwen3-8B layer (tiled activations,",
+             "# bf16 outputs, weights rotated past the Infinity Cache), one eager launch per shape",
+             f"# and round, rounds 2..{LAYER288_ROUNDS}", f"# command: {command}",
+             f"{'shape':>8} {'N':>6} {'K':>6} {'avg_us':>8} {'median_us':>9} {'min_us':>8} "
+             f"{'max_us':>8} {'TOPS@med':>9} {'wgs':>5}  kernel"]
+    tot, ops_all = 0.0, 0
+    for gi, (name, grp) in enumerate(LAYER288_GROUPS):
+        N, K = sum(lins[i].N for i in grp), lins[grp[0]].K
+        sel = rows[n + gi::n]
+        d = np.array([(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in sel])
+        med = float(np.median(d))
+        ops = 2 * 288 * N * K
+        wgs = int(sel[0]["Grid_Size_X"]) // max(int(sel[0]["Workgroup_Size_X"]), 1)
+        kname = sel[0]["Kernel_Name"].split("(w8a8")[0].replace("void ", "")
+        lines.append(f"{name:>8} {N:6d} {K:6d} {d.mean():8.2f} {med:9.2f} {d.min():8.2f} "
+                     f"{d.max():8.2f} {ops / med / 1e6:9.1f} {wgs:5d}  {kname}")
+        tot += med
+        ops_all += ops
+    lines.append(f"layer (sum of medians): {tot:.2f} us, {ops_all / tot / 1e6:.1f} TOPS "
+                 f"({ops_all / tot / 1e6 / INT8_PEAK_TOPS:.4f} of the int8 MFMA peak)")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def fused_layer_measurement(dev, wsp, M, tiled_act=False):
