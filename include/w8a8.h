@@ -627,90 +627,6 @@ w8a8_status w8a8_bf16_linear_tiled(const uint16_t* x_bf16, const uint16_t* w_til
                                    int64_t M, int64_t N, int64_t K,
                                    uint16_t* y_bf16, float* y_f32, void* stream);
 
-/*
- * Chained verify step: a sequence of steps over the same M token rows
- * (1 <= M <= 16) run by ONE persistent launch.
- *
- * Pages: verification time is the weight bytes over the memory bandwidth
- * ([de] §3 item 4; [ja] §2.3).  A verify pass of a few rows through a whole
- * model is one long weight stream cut into hundreds of linears; launched one
- * by one, each pays a ramp and a tail in which HBM idles.  In a chain the
- * workgroups stay resident and meet at a device-wide barrier between
- * consecutive steps: step i+1 sees every output of steps 0..i, so any
- * dependency between steps is honoured; each workgroup issues the weight
- * loads of its share of the next linear before it waits.  Every output is
- * bit-identical to the separate call's:
- *   W8A8_CHAIN_QUANTIZE  w8a8_quantize_act: in = bf16 x [M][K], smooth =
- *                        optional [K] factors, out = int8 xq [M][K],
- *                        out_f32 = x_scale [M] ([ja] §2.2 items 1-2).
- *   W8A8_CHAIN_LINEAR    w8a8_linear_tiled: in = int8 xq [M][K], in_scale =
- *                        x_scale [M], wq_tiled / w_scale as for
- *                        w8a8_linear_tiled, out = bf16 y [M][N] and/or
- *                        out_f32 = fp32 y [M][N] (at least one) ([ja] §2.2
- *                        item 3).
- *   W8A8_CHAIN_LM_HEAD   w8a8_lm_head_argmax: as LINEAR with N = V, out
- *                        NULL, out_f32 = fp32 logits [M][V] or NULL; the
- *                        row maxima go to the plan's own keys.
- *   W8A8_CHAIN_ACCEPT    w8a8_accept_from_keys on those keys: B, G with
- *                        B * (G + 1) == M, draft [B][G] (NULL if G == 0),
- *                        argmax [M] or NULL, accept_len [B], next_token [B].
- *                        Each LM_HEAD must be followed by an ACCEPT before
- *                        the next LM_HEAD and before the end of the chain.
- * Unused fields of an op are ignored (set them 0 / NULL).  K % 16 == 0 and
- * 16 <= K <= W8A8_MAX_K; 1 <= N <= 2^30; tensors 16-byte aligned, scales
- * 4-byte, bf16 outputs 2-byte.  All pointers are device memory the caller
- * owns and keeps alive while the plan is used.
- *
- * w8a8_chain_plan_bytes(ops, n_ops, M): size of the plan (0 if the ops are
- *    invalid).  w8a8_chain_prepare validates the ops (W8A8_ERR_INVALID_ARG
- *    naming the op; W8A8_ERR_WORKSPACE if plan is NULL, not 256-byte aligned
- *    or plan_bytes is short), writes the step table into `plan` (device
- *    memory the caller owns) and zero-fills its counters, partial sums and
- *    argmax keys; it waits for `stream`, so it is not for graph capture.
- * w8a8_chain_run(plan, stream) enqueues the launch (capturable; no host
- *    synchronization, no allocation).  Its size is the number of workgroups
- *    that fit on the device at once, so the launch must not share the
- *    device with concurrent kernels: should a barrier wait pass one second,
- *    the launch stops, records status 1 in the plan, and its outputs are
- *    invalid.  A completed run leaves the plan ready for the next one.
- *    Runs of one plan must not overlap in time.
- * w8a8_chain_status(plan, status, stream) waits for `stream` and copies the
- *    plan's status word to *status (host): 0 = every run completed; 1 = a
- *    run stopped at a barrier (prepare the plan again before reusing it);
- *    2 = the plan was prepared for a different launch size (another device):
- *    nothing ran.
- */
-#define W8A8_CHAIN_QUANTIZE 1
-#define W8A8_CHAIN_LINEAR   2
-#define W8A8_CHAIN_LM_HEAD  3
-#define W8A8_CHAIN_ACCEPT   4
-#define W8A8_CHAIN_MAX_OPS  65536
-
-typedef struct w8a8_chain_op {
-  int32_t kind;                /* W8A8_CHAIN_* */
-  int32_t reserved;            /* 0 */
-  int64_t N;                   /* LINEAR, LM_HEAD: output channels / vocabulary */
-  int64_t K;                   /* QUANTIZE, LINEAR, LM_HEAD: row length */
-  int64_t B, G;                /* ACCEPT: sequences, drafts per sequence */
-  const void* in;              /* QUANTIZE: bf16 [M][K]; LINEAR, LM_HEAD: int8 [M][K] */
-  const float* in_scale;       /* LINEAR, LM_HEAD: x_scale [M] */
-  const float* smooth;         /* QUANTIZE: smoothing factors [K] or NULL */
-  const int8_t* wq_tiled;      /* LINEAR, LM_HEAD: tiled weight codes */
-  const float* w_scale;        /* LINEAR, LM_HEAD: [N] */
-  void* out;                   /* QUANTIZE: int8 [M][K]; LINEAR: bf16 [M][N] or NULL */
-  float* out_f32;              /* QUANTIZE: x_scale [M]; LINEAR, LM_HEAD: fp32 [M][N] or NULL */
-  const int32_t* draft;        /* ACCEPT */
-  int32_t* argmax;             /* ACCEPT */
-  int32_t* accept_len;         /* ACCEPT */
-  int32_t* next_token;         /* ACCEPT */
-} w8a8_chain_op;
-
-size_t      w8a8_chain_plan_bytes(const w8a8_chain_op* ops, int32_t n_ops, int64_t M);
-w8a8_status w8a8_chain_prepare(const w8a8_chain_op* ops, int32_t n_ops, int64_t M,
-                               void* plan, size_t plan_bytes, void* stream);
-w8a8_status w8a8_chain_run(void* plan, void* stream);
-w8a8_status w8a8_chain_status(const void* plan, int32_t* status, void* stream);
-
 #ifdef __cplusplus
 }
 #endif

@@ -15,8 +15,7 @@ from .api import (W8A8Error, Workspace, accept_from_keys, bf16_linear, bf16_tile
                   linear_tiled_act, linear_tiled_act_workspace_bytes, verify_attention,
                   qk_norm_rope_append, pack_v_cache,
                   hbm_read_probe, HBM_PROBE_SINK_WORDS, lm_head_verify_noalloc,
-                  NOALLOC_MAX_ROWS, chain_quantize, chain_linear, chain_lm_head, chain_accept,
-                  Chain)
+                  NOALLOC_MAX_ROWS)
 
 __all__ = [
     "W8A8Error", "Workspace", "accept_from_keys", "bf16_linear", "bf16_tiled_shape",
@@ -28,5 +27,4 @@ __all__ = [
     "residual_rmsnorm_quant", "silu_mul_quant", "quantize_act_tiled", "linear_tiled_act",
     "linear_tiled_act_workspace_bytes", "verify_attention", "qk_norm_rope_append", "pack_v_cache", "hbm_read_probe",
     "HBM_PROBE_SINK_WORDS", "lm_head_verify_noalloc", "NOALLOC_MAX_ROWS",
-    "chain_quantize", "chain_linear", "chain_lm_head", "chain_accept", "Chain",
 ]

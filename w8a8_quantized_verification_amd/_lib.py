@@ -76,22 +76,7 @@ SIGNATURES = {
                                         _c.c_float, _vp, _i64, _vp, _vp, _vp, _vp]),
     "w8a8_verify_attention": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _vp,
                                      _vp, _sz, _vp]),
-    "w8a8_chain_plan_bytes": (_sz, [_vp, _i32, _i64]),
-    "w8a8_chain_prepare": (_i32, [_vp, _i32, _i64, _vp, _sz, _vp]),
-    "w8a8_chain_run": (_i32, [_vp, _vp]),
-    "w8a8_chain_status": (_i32, [_vp, _vp, _vp]),
 }
-
-# W8A8_CHAIN_* op kinds and the w8a8_chain_op struct (same field order and
-# types as include/w8a8.h)
-CHAIN_QUANTIZE, CHAIN_LINEAR, CHAIN_LM_HEAD, CHAIN_ACCEPT = 1, 2, 3, 4
-
-
-class ChainOp(ctypes.Structure):
-    _fields_ = [("kind", _i32), ("reserved", _i32), ("N", _i64), ("K", _i64), ("B", _i64),
-                ("G", _i64), ("in_", _vp), ("in_scale", _vp), ("smooth", _vp),
-                ("wq_tiled", _vp), ("w_scale", _vp), ("out", _vp), ("out_f32", _vp),
-                ("draft", _vp), ("argmax", _vp), ("accept_len", _vp), ("next_token", _vp)]
 
 _lib = None
 

@@ -10,9 +10,6 @@ from __future__ import annotations
 
 import torch
 
-import ctypes
-
-from . import _lib
 from ._lib import W8A8Error, check, lib
 
 __all__ = [
@@ -26,7 +23,7 @@ __all__ = [
     "quantize_act_tiled", "linear_tiled_act", "linear_tiled_act_workspace_bytes",
     "verify_attention", "qk_norm_rope_append",
     "pack_v_cache", "hbm_read_probe", "HBM_PROBE_SINK_WORDS", "lm_head_verify_noalloc",
-    "NOALLOC_MAX_ROWS", "chain_quantize", "chain_linear", "chain_lm_head", "chain_accept", "Chain",
+    "NOALLOC_MAX_ROWS",
 ]
 
 NOALLOC_MAX_ROWS = 288        # W8A8_NOALLOC_MAX_ROWS
@@ -745,144 +742,4 @@ def hbm_read_probe(buf: torch.Tensor, *, sink=None, events=None) -> torch.Tensor
         ev0, ev1 = start.cuda_event, stop.cuda_event
     check(lib().w8a8_hbm_read_probe(_ptr(buf), nbytes, _ptr(sink), ev0, ev1, _stream(buf.device)))
     return sink
-
-
-# ---------------------------------------------------------------------------
-# Chained verify step (w8a8_chain_*): op descriptions, then one prepared plan
-# that runs them all in one persistent launch.
-# ---------------------------------------------------------------------------
-
-class _ChainStep:
-    """One op of a chain: the ctypes struct and the tensors it points to
-    (kept alive while the plan exists)."""
-
-    def __init__(self, op, tensors, rows):
-        self.op = op
-        self.tensors = tensors
-        self.rows = rows  # M implied by the op's tensors
-
-
-def chain_quantize(x, *, xq, x_scale, smooth=None):
-    """QUANTIZE step: bf16 ``x[M][K]`` -> ``xq`` int8 ``[M][K]`` and
-    ``x_scale`` float32 ``[M]`` (as :func:`quantize_act`)."""
-    _need(x, "x", torch.bfloat16, 2)
-    M, K = x.shape
-    dev = x.device
-    _out(xq, (M, K), torch.int8, dev, "xq")
-    _out(x_scale, (M,), torch.float32, dev, "x_scale")
-    if smooth is not None:
-        _need(smooth, "smooth", torch.float32, 1, dev)
-        if smooth.shape[0] != K:
-            raise ValueError("smooth must have K entries")
-    op = _lib.ChainOp(kind=_lib.CHAIN_QUANTIZE, K=K, in_=_ptr(x), smooth=_ptr(smooth),
-                      out=_ptr(xq), out_f32=_ptr(x_scale))
-    return _ChainStep(op, (x, xq, x_scale, smooth), M)
-
-
-def _chain_weights(xq, x_scale, wq_tiled, w_scale, N):
-    _need(xq, "xq", torch.int8, 2)
-    dev = xq.device
-    M, K = xq.shape
-    _need(x_scale, "x_scale", torch.float32, 1, dev)
-    _need(w_scale, "w_scale", torch.float32, 1, dev)
-    _need(wq_tiled, "wq_tiled", torch.int8, 4, dev)
-    if x_scale.shape[0] != M:
-        raise ValueError("x_scale must have M entries")
-    if w_scale.shape[0] != N or tuple(wq_tiled.shape) != tiled_shape(N, K):
-        raise ValueError(f"wq_tiled must have shape {tiled_shape(N, K)} and w_scale N = {N} entries")
-    return M, K, dev
-
-
-def chain_linear(xq, x_scale, wq_tiled, w_scale, *, y_bf16=None, y_f32=None):
-    """LINEAR step: ``xq[M][K]`` times tiled weights (shape
-    :func:`tiled_shape`), bf16 ``y_bf16`` and/or fp32 ``y_f32`` ``[M][N]``
-    (as :func:`linear` on tiled weights)."""
-    N = w_scale.shape[0] if isinstance(w_scale, torch.Tensor) else 0
-    M, K, dev = _chain_weights(xq, x_scale, wq_tiled, w_scale, N)
-    if y_bf16 is None and y_f32 is None:
-        raise ValueError("chain_linear needs y_bf16 or y_f32")
-    if y_bf16 is not None:
-        _out(y_bf16, (M, N), torch.bfloat16, dev, "y_bf16")
-    if y_f32 is not None:
-        _out(y_f32, (M, N), torch.float32, dev, "y_f32")
-    op = _lib.ChainOp(kind=_lib.CHAIN_LINEAR, N=N, K=K, in_=_ptr(xq), in_scale=_ptr(x_scale),
-                      wq_tiled=_ptr(wq_tiled), w_scale=_ptr(w_scale), out=_ptr(y_bf16),
-                      out_f32=_ptr(y_f32))
-    return _ChainStep(op, (xq, x_scale, wq_tiled, w_scale, y_bf16, y_f32), M)
-
-
-def chain_lm_head(xq, x_scale, wq_tiled, w_scale, *, logits=None):
-    """LM_HEAD step: the LM-head linear with the row argmax folded into the
-    plan's keys (as :func:`lm_head_argmax`); fp32 ``logits[M][V]`` only if
-    passed.  A :func:`chain_accept` must follow."""
-    V = w_scale.shape[0] if isinstance(w_scale, torch.Tensor) else 0
-    M, K, dev = _chain_weights(xq, x_scale, wq_tiled, w_scale, V)
-    if logits is not None:
-        _out(logits, (M, V), torch.float32, dev, "logits")
-    op = _lib.ChainOp(kind=_lib.CHAIN_LM_HEAD, N=V, K=K, in_=_ptr(xq), in_scale=_ptr(x_scale),
-                      wq_tiled=_ptr(wq_tiled), w_scale=_ptr(w_scale), out_f32=_ptr(logits))
-    return _ChainStep(op, (xq, x_scale, wq_tiled, w_scale, logits), M)
-
-
-def chain_accept(draft, *, accept_len, next_token, argmax=None):
-    """ACCEPT step: greedy acceptance of ``draft`` int32 ``[B][G]`` against
-    the argmax of the preceding LM_HEAD step (rows b*(G+1)+i); writes
-    ``accept_len`` and ``next_token`` int32 ``[B]`` and, if passed,
-    ``argmax`` int32 ``[B*(G+1)]``."""
-    _need(draft, "draft", torch.int32, 2)
-    dev = draft.device
-    B, G = draft.shape
-    _out(accept_len, (B,), torch.int32, dev, "accept_len")
-    _out(next_token, (B,), torch.int32, dev, "next_token")
-    if argmax is not None:
-        _out(argmax, (B * (G + 1),), torch.int32, dev, "argmax")
-    op = _lib.ChainOp(kind=_lib.CHAIN_ACCEPT, B=B, G=G, draft=_ptr(draft) if G else None,
-                      argmax=_ptr(argmax), accept_len=_ptr(accept_len),
-                      next_token=_ptr(next_token))
-    return _ChainStep(op, (draft, accept_len, next_token, argmax), B * (G + 1))
-
-
-class Chain:
-    """A prepared chain: the steps run in order by one persistent launch per
-    :meth:`run`, each step seeing every output of the steps before it
-    (w8a8_chain_prepare / w8a8_chain_run).  Preparing waits for the current
-    stream; :meth:`run` only enqueues (capturable in a HIP graph).  The plan
-    (device memory) and the op tensors are held by this object."""
-
-    def __init__(self, steps):
-        steps = list(steps)
-        if not steps:
-            raise ValueError("a chain needs at least one step")
-        rows = {s.rows for s in steps}
-        if len(rows) != 1:
-            raise ValueError(f"every step of a chain works on the same M rows (got {sorted(rows)})")
-        self.M = rows.pop()
-        devs = {t.device for s in steps for t in s.tensors if isinstance(t, torch.Tensor)}
-        if len(devs) != 1:
-            raise ValueError("every tensor of a chain must be on one device")
-        self.device = devs.pop()
-        self._steps = steps
-        self._ops = (_lib.ChainOp * len(steps))(*[s.op for s in steps])
-        n = len(steps)
-        need = lib().w8a8_chain_plan_bytes(ctypes.addressof(self._ops), n, self.M)
-        if need == 0:  # invalid ops: the library names the op in its message
-            raise W8A8Error(1, lib().w8a8_last_error().decode())
-        self.plan = torch.empty(need, dtype=torch.uint8, device=self.device)
-        check(lib().w8a8_chain_prepare(ctypes.addressof(self._ops), n, self.M,
-                                       self.plan.data_ptr(), need, _stream(self.device)))
-
-    def __len__(self):
-        return len(self._steps)
-
-    def run(self):
-        """Enqueue one launch of the whole chain on the current stream."""
-        check(lib().w8a8_chain_run(self.plan.data_ptr(), _stream(self.device)))
-
-    def status(self) -> int:
-        """Wait for the current stream; 0 if every run completed, 1 if a run
-        stopped at a barrier (its outputs are invalid)."""
-        st = ctypes.c_int32(-1)
-        check(lib().w8a8_chain_status(self.plan.data_ptr(), ctypes.addressof(st),
-                                      _stream(self.device)))
-        return int(st.value)
 

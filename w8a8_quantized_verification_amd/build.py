@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libw8a8.so")
 
 SOURCES = ["api.hip", "quantize.hip", "gemm_w8a8.hip", "gemm_w8a8_batched.hip", "argmax_accept.hip",
            "sample_accept.hip", "gemm_w4a8.hip", "glue.hip", "attention.hip", "gemm_bf16.hip",
-           "hbm_probe.hip", "noalloc.hip", "chain.hip"]
+           "hbm_probe.hip", "noalloc.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

@@ -769,109 +769,3 @@ w8a8_status w8a8_qk_norm_rope_append(const uint16_t* qkv, int64_t B, int64_t T, 
 }
 
 }  // extern "C"
-
-
-namespace {
-
-// Validation of a chain: every op's sizes, pointers and alignment, and the
-// LM_HEAD / ACCEPT pairing (the keys an LM head leaves are consumed by an
-// ACCEPT before the next LM head and before the end).
-w8a8_status check_chain(const char* fn, const w8a8_chain_op* ops, int32_t n, int64_t M) {
-  if (!ops) return fail(W8A8_ERR_INVALID_ARG, fn, "ops is NULL");
-  if (n < 1 || n > W8A8_CHAIN_MAX_OPS) return fail(W8A8_ERR_INVALID_ARG, fn, "n_ops out of range [1, 65536]");
-  if (M < 1 || M > 16) return fail(W8A8_ERR_INVALID_ARG, fn, "M must be in [1, 16]");
-  bool keys_pending = false;
-  char msg[192];
-  for (int32_t i = 0; i < n; ++i) {
-    const w8a8_chain_op& o = ops[i];
-    auto bad = [&](const char* what) {
-      snprintf(msg, sizeof msg, "op %d: %s", i, what);
-      return fail(W8A8_ERR_INVALID_ARG, fn, msg);
-    };
-    const bool k_ok = o.K >= 16 && o.K <= W8A8_MAX_K && o.K % 16 == 0;
-    switch (o.kind) {
-      case W8A8_CHAIN_QUANTIZE:
-        if (!k_ok) return bad("K must be a multiple of 16 in [16, 133144]");
-        if (!o.in || !o.out || !o.out_f32) return bad("in, out and out_f32 are required");
-        if (!aligned(o.in, 16) || !aligned(o.out, 16) || !aligned(o.smooth, 16) ||
-            !aligned(o.out_f32, 4))
-          return bad("in, out, smooth must be 16-byte aligned, out_f32 4");
-        break;
-      case W8A8_CHAIN_LINEAR:
-      case W8A8_CHAIN_LM_HEAD:
-        if (!k_ok) return bad("K must be a multiple of 16 in [16, 133144]");
-        if (o.N < 1 || o.N > (int64_t(1) << 30)) return bad("N out of range [1, 2^30]");
-        if ((o.N + 15) / 16 * ((o.K + 63) / 64) * 1024 >= (int64_t(1) << 31)) {
-          snprintf(msg, sizeof msg, "op %d: tiled weights of 2 GiB or more are not supported", i);
-          return fail(W8A8_ERR_UNSUPPORTED, fn, msg);
-        }
-        if (!o.in || !o.in_scale || !o.wq_tiled || !o.w_scale)
-          return bad("in, in_scale, wq_tiled and w_scale are required");
-        if (!aligned(o.in, 16) || !aligned(o.wq_tiled, 16) || !aligned(o.in_scale, 4) ||
-            !aligned(o.w_scale, 4) || !aligned(o.out, 2) || !aligned(o.out_f32, 4))
-          return bad("in, wq_tiled must be 16-byte aligned, scales and out_f32 4, out 2");
-        if (o.kind == W8A8_CHAIN_LINEAR) {
-          if (!o.out && !o.out_f32) return bad("LINEAR needs out or out_f32");
-        } else {
-          if (o.out) return bad("LM_HEAD takes no bf16 out (out_f32 holds the logits)");
-          if (keys_pending) return bad("LM_HEAD before the ACCEPT of the previous LM_HEAD");
-          keys_pending = true;
-        }
-        break;
-      case W8A8_CHAIN_ACCEPT:
-        if (!keys_pending) return bad("ACCEPT without a preceding LM_HEAD");
-        keys_pending = false;
-        if (o.B < 1 || o.G < 0 || o.G > M || o.B * (o.G + 1) != M)
-          return bad("B >= 1, G >= 0 with B * (G + 1) == M required");
-        if ((o.G > 0 && !o.draft) || !o.accept_len || !o.next_token)
-          return bad("draft (G > 0), accept_len and next_token are required");
-        if (!aligned(o.draft, 4) || !aligned(o.argmax, 4) || !aligned(o.accept_len, 4) ||
-            !aligned(o.next_token, 4))
-          return bad("draft, argmax, accept_len, next_token must be 4-byte aligned");
-        break;
-      default:
-        return bad("unknown kind");
-    }
-  }
-  if (keys_pending) return fail(W8A8_ERR_INVALID_ARG, fn, "the last LM_HEAD has no ACCEPT after it");
-  return W8A8_OK;
-}
-
-}  // namespace
-
-extern "C" {
-
-size_t w8a8_chain_plan_bytes(const w8a8_chain_op* ops, int32_t n_ops, int64_t M) {
-  g_last_error.clear();
-  if (check_chain("w8a8_chain_plan_bytes", ops, n_ops, M) != W8A8_OK) return 0;
-  return w8a8_chain_plan_bytes_impl(ops, n_ops, M);
-}
-
-w8a8_status w8a8_chain_prepare(const w8a8_chain_op* ops, int32_t n_ops, int64_t M, void* plan,
-                               size_t plan_bytes, void* stream) {
-  static const char* fn = "w8a8_chain_prepare";
-  g_last_error.clear();
-  if (w8a8_status s = check_chain(fn, ops, n_ops, M)) return s;
-  if (!plan || !aligned(plan, 256) || plan_bytes < w8a8_chain_plan_bytes_impl(ops, n_ops, M))
-    return fail(W8A8_ERR_WORKSPACE, fn,
-                "plan NULL, not 256-byte aligned or smaller than w8a8_chain_plan_bytes()");
-  return hip_status(w8a8_chain_prepare_impl(ops, n_ops, M, plan,
-                                            reinterpret_cast<hipStream_t>(stream)), fn);
-}
-
-w8a8_status w8a8_chain_run(void* plan, void* stream) {
-  static const char* fn = "w8a8_chain_run";
-  g_last_error.clear();
-  if (!plan || !aligned(plan, 256)) return fail(W8A8_ERR_INVALID_ARG, fn, "plan NULL or not 256-byte aligned");
-  return hip_status(w8a8_launch_chain(plan, reinterpret_cast<hipStream_t>(stream)), fn);
-}
-
-w8a8_status w8a8_chain_status(const void* plan, int32_t* status, void* stream) {
-  static const char* fn = "w8a8_chain_status";
-  g_last_error.clear();
-  if (!plan || !aligned(plan, 256) || !status)
-    return fail(W8A8_ERR_INVALID_ARG, fn, "plan NULL or misaligned, or status NULL");
-  return hip_status(w8a8_chain_read_status(plan, status, reinterpret_cast<hipStream_t>(stream)), fn);
-}
-
-}  // extern "C"

@@ -163,14 +163,6 @@ hipError_t w8a8_launch_qk_norm_rope_append(const uint16_t* qkv, int64_t B, int64
                                            uint16_t* k_cache, uint16_t* v_cache,
                                            hipStream_t stream);
 
-// chained verify step (chain.hip); the ops are validated by the C-ABI layer
-struct w8a8_chain_op;
-size_t w8a8_chain_plan_bytes_impl(const w8a8_chain_op* ops, int n_ops, int64_t M);
-hipError_t w8a8_chain_prepare_impl(const w8a8_chain_op* ops, int n_ops, int64_t M, void* plan,
-                                   hipStream_t stream);
-hipError_t w8a8_launch_chain(const void* plan, hipStream_t stream);
-hipError_t w8a8_chain_read_status(const void* plan, int32_t* status, hipStream_t stream);
-
 hipError_t w8a8_launch_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink,
                                       hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t w8a8_launch_lm_head_verify_noalloc(const int8_t* xq, const float* x_scale,
