@@ -113,6 +113,17 @@ def test_batched_split_workspace(lib):
     assert f(None, None, None, None, 0, 4096, 12288, None, None, None, None, 0, None) == OK
 
 
+def test_linear_workspace_split_tail(lib, monkeypatch):
+    # 320 tiles of 128 k steps over 256 CUs: the 64 tiles past the last whole
+    # round are split, so the call needs the split workspace; short tiles
+    # (K = 4096) and outputs narrower than the CUs do not split their tail
+    assert lib.w8a8_linear_workspace_bytes(8, 5120, 8192) >= 8 * 5120 * 4
+    assert lib.w8a8_linear_workspace_bytes(5, 6144, 4096) == 0
+    assert lib.w8a8_linear_workspace_bytes(5, 1024, 8192) == 0
+    monkeypatch.setenv("W8A8_TAIL", "-1")
+    assert lib.w8a8_linear_workspace_bytes(8, 5120, 8192) == 0
+
+
 def test_linear_workspace_follows_split_override(lib, monkeypatch):
     monkeypatch.setenv("W8A8_SPLITK", "4")
     assert lib.w8a8_linear_workspace_bytes(5, 1024, 4096) >= 5 * 1024 * 4

@@ -126,6 +126,19 @@ def test_guard_skinny_linear(M, N, tiled):
     check_linear(xq, xs, wq, ws, M, N, f"skinny M={M} N={N}")
 
 
+@pytest.mark.parametrize("M,N,K", [(8, 5120, 8192), (7, 4100, 6144)])
+@pytest.mark.parametrize("tiled", [True, False])
+def test_guard_skinny_split_tail(M, N, K, tiled):
+    # the tiles past the last whole round over the CUs are split across
+    # workgroups (their partials go through the workspace)
+    announce(f"guard skinny split tail M={M} N={N} K={K} tiled={tiled} "
+             f"workspace {w8.linear_workspace_bytes(M, N, K)} B")
+    assert w8.linear_workspace_bytes(M, N, K) > 0
+    wq, ws = int8_weights(N, K, 7 + N, tiled=tiled)
+    xq, xs = w8.quantize_act(act(M, K, M + 3))
+    check_linear(xq, xs, wq, ws, M, N, f"split tail M={M} N={N}")
+
+
 @pytest.mark.parametrize("split", [2, 4, 8])
 def test_guard_skinny_forced_split_k(split, monkeypatch):
     M, N, K = 5, 4099, 4160          # K not a multiple of 128: ragged k slices too

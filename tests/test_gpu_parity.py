@@ -143,6 +143,9 @@ LINEAR_CASES = [
     (5, 4096, 12288),     # down
     (8, 8192, 5120),      # Qwen3-32B q
     (8, 5120, 25600),     # Qwen3-32B down
+    (8, 5120, 8192),      # Qwen3-32B o: 320 tiles, the 64 past the last round split four ways
+    (8, 10240, 5120),     # Qwen3-32B q/k/v fused: 128 tail tiles split in two
+    (7, 4100, 6144),      # one ragged tail tile split eight ways
     (1, 1000, 4096),      # one token, ragged N
     (16, 777, 1040),      # full 16-row tile, ragged N and a partial 64-wide K step
     (3, 17, 16),          # one 16-byte k group

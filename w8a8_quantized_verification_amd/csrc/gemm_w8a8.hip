@@ -60,7 +60,9 @@ struct GemmArgs {
   int steps;    // ceil(K / 64)
   int tiles16;  // ceil(N / 16): 16-channel tiles in the tiled weight layout
   int split;
-  int tiles;  // number of workgroup column tiles (grid.x)
+  int tiles;  // number of workgroup column tiles
+  int ntail;  // > 0: the last ntail tiles are split tsplit ways, the rest not (1-D grid)
+  int tsplit;
   uint16_t* y_bf16;
   float* y_f32;
   int32_t* acc;
@@ -92,7 +94,28 @@ __global__ __launch_bounds__(WAVES * kWave) void gemm_w8a8_skinny(GemmArgs g) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
   const int col = lane & 15;
   const int grp = lane >> 4;
-  const int tile = blockIdx.x;
+  // (tile, k slice, slices of that tile): grid (tiles, split, mblocks), or
+  // with a split tail a 1-D grid whose first ntail*tsplit workgroups are the
+  // tail tiles' slices (dispatched first, so that their hand-off overlaps
+  // the whole tiles' streaming) and the rest the whole tiles
+  int tile, slice, split;
+  if (g.ntail > 0) {
+    const int nt = g.ntail * g.tsplit;
+    const int id = blockIdx.x;
+    if (id < nt) {
+      tile = g.tiles - g.ntail + id / g.tsplit;
+      slice = id % g.tsplit;
+      split = g.tsplit;
+    } else {
+      tile = id - nt;
+      slice = 0;
+      split = 1;
+    }
+  } else {
+    tile = blockIdx.x;
+    slice = blockIdx.y;
+    split = g.split;
+  }
   const int m_base = blockIdx.z * 16;
   const int n0 = tile * 16 * TN;
   const int K = g.K;
@@ -102,8 +125,8 @@ __global__ __launch_bounds__(WAVES * kWave) void gemm_w8a8_skinny(GemmArgs g) {
   // round-robin (s = g0 + wave + WAVES*j), so the workgroup sweeps adjacent
   // KiB blocks.  Row-major weights: each wave takes a contiguous share
   // (s = sw + j), so each of its loads continues the same 16 rows.
-  const int g0 = (int)(((int64_t)steps * blockIdx.y) / g.split);
-  const int g1 = (int)(((int64_t)steps * (blockIdx.y + 1)) / g.split);
+  const int g0 = (int)(((int64_t)steps * slice) / split);
+  const int g1 = (int)(((int64_t)steps * (slice + 1)) / split);
   int J, sw;
   constexpr int kStride = kTiled ? WAVES : 1;
   if constexpr (kTiled) {
@@ -200,7 +223,7 @@ __global__ __launch_bounds__(WAVES * kWave) void gemm_w8a8_skinny(GemmArgs g) {
   }
 
   // wave 0 holds the workgroup's partial tile: rows 4*grp + r, column col.
-  if (g.split == 1) {
+  if (split == 1) {
     float bv[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     int bi[4] = {INT_MAX, INT_MAX, INT_MAX, INT_MAX};
 #pragma unroll
@@ -269,7 +292,7 @@ __global__ __launch_bounds__(WAVES * kWave) void gemm_w8a8_skinny(GemmArgs g) {
   if (lane == 0)
     old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   old = __shfl(old, 0, kWave);
-  if (old != (uint32_t)(g.split - 1)) return;
+  if (old != (uint32_t)(split - 1)) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 #pragma unroll
   for (int t = 0; t < TN; ++t) {
@@ -293,7 +316,22 @@ __global__ __launch_bounds__(WAVES * kWave) void gemm_w8a8_skinny(GemmArgs g) {
 // owning tn 16-channel tiles.
 struct SkinnyPlan {
   int tiles, split, mblocks, waves, tn;
+  int ntail = 0, tsplit = 1;  // split tail (see plan_skinny)
 };
+
+// Compute units of the current device (cached per device).
+static int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
 
 // k steps of loads issued per wave before their MFMAs.  Measured on the
 // LM head at M = 5 (same box, interleaved builds): 4: 97.8 us, 6: 97.0,
@@ -310,6 +348,7 @@ constexpr int kUnrollArgmax = 10;
 constexpr int64_t kSkinnyMaxRows = 16;  // more token rows go to the batched kernel
 constexpr int kSplitBelowTiles = 32;  // split k across workgroups below this ...
 constexpr int64_t kLongChain = 32;    // ... or above this many k steps per wave
+constexpr int64_t kTailMinSteps = 80; // split tail only for tiles this long (see plan_skinny)
 
 // Tuning overrides (results do not depend on them: int32 sums are exact in
 // any order): W8A8_SPLITK forces the cross-workgroup split, W8A8_WAVES the
@@ -357,6 +396,31 @@ static SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, bool tiled, bool 
   if (fw == 4 || fw == 8 || fw == 16) p.waves = fw;
   const int fs = env_int("W8A8_SPLITK");
   if (!no_split && fs >= 1 && fs <= 64 && fs <= steps) p.split = fs;
+  // Split tail: one CU streams little more than its share of HBM, so when
+  // the tiles do not divide evenly over the CUs, the CUs that get one tile
+  // more set the time (the Qwen3-32B o at M = 8: 320 tiles of 128 KiB over
+  // 256 CUs, 64 of them stream two).  The remainder tiles are then cut into
+  // tsplit k slices, about one per CU, with the atomic hand-off of the
+  // split; their workgroups go first, so that the hand-off overlaps the
+  // whole tiles' streaming.  Measured on MI355X (M = 8, graph-timed): 32B o
+  // 12.68 -> 10.63 us, q/k/v (10240 x 5120) 13.06 -> 12.61, gate/up
+  // (51200 x 5120) 46.1 -> 45.1.  It pays only for long tiles (>= 80 k
+  // steps): at K = 4096 the hand-off costs more than the uneven round
+  // (Qwen3-8B q/k/v at M = 5: 7.48 -> 7.73 us), and it needs whole tiles to
+  // overlap (a 64-tile output split four ways: 4.63 -> 6.35 us).
+  // W8A8_TAIL=-1 turns it off (a tuning override; results are exact either
+  // way).
+  if (!no_split && p.split == 1 && p.mblocks == 1 && steps >= kTailMinSteps &&
+      env_int("W8A8_TAIL") >= 0) {
+    const int cus = cu_count();
+    const int rem = p.tiles > cus ? p.tiles % cus : 0;
+    int ts = 1;
+    while (rem > 0 && ts < 8 && rem * ts * 2 <= cus && ts * 2 <= steps) ts *= 2;
+    if (ts > 1) {
+      p.ntail = rem;
+      p.tsplit = ts;
+    }
+  }
   return p;
 }
 
@@ -367,7 +431,7 @@ size_t w8a8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, bool tiled) {
   if (M <= 0 || N <= 0) return 0;
   if (M > kSkinnyMaxRows) return tiled ? w8a8_batched_workspace_bytes(M, N, K, false) : 0;
   const SkinnyPlan p = plan_skinny(M, N, K, tiled);
-  if (p.split == 1) return 0;
+  if (p.split == 1 && p.ntail == 0) return 0;
   const size_t part = (size_t)M * (size_t)N * sizeof(int32_t);
   const size_t part_aligned = (part + 255) & ~(size_t)255;
   return part_aligned + (size_t)p.tiles * p.mblocks * sizeof(uint32_t);
@@ -379,7 +443,9 @@ static hipError_t launch_plan(const w8a8::SkinnyPlan& p, const w8a8::GemmArgs& g
                               bool argmax, hipStream_t stream, hipEvent_t ev0 = nullptr,
                               hipEvent_t ev1 = nullptr) {
   using namespace w8a8;
-  const dim3 grid((unsigned)p.tiles, (unsigned)p.split, (unsigned)p.mblocks);
+  const dim3 grid = p.ntail > 0
+                        ? dim3((unsigned)(p.ntail * p.tsplit + p.tiles - p.ntail), 1u, (unsigned)p.mblocks)
+                        : dim3((unsigned)p.tiles, (unsigned)p.split, (unsigned)p.mblocks);
 #define W8A8_GEMM(TN, W, TL, AM)                                                              \
   do {                                                                                        \
     if (ev0)                                                                                  \
@@ -418,6 +484,7 @@ static w8a8::GemmArgs make_args(const w8a8::SkinnyPlan& p, const int8_t* xq, con
   g.steps = (int)((K + 63) / 64);
   g.tiles16 = (int)((N + 15) / 16);
   g.split = p.split; g.tiles = p.tiles;
+  g.ntail = p.ntail; g.tsplit = p.tsplit;
   g.y_bf16 = y_bf16; g.y_f32 = y_f32; g.acc = acc;
   return g;
 }
@@ -433,7 +500,7 @@ hipError_t w8a8_launch_gemm(const int8_t* xq, const float* x_scale, const int8_t
                                     nullptr, 0, 0, stream, false, workspace);
   const SkinnyPlan p = plan_skinny(M, N, K, tiled);
   GemmArgs g = make_args(p, xq, x_scale, wq, w_scale, M, N, K, y_bf16, y_f32, acc);
-  if (p.split > 1) {
+  if (p.split > 1 || p.ntail > 0) {
     const size_t part = (size_t)M * (size_t)N * sizeof(int32_t);
     g.part = reinterpret_cast<int32_t*>(workspace);
     g.count = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(workspace) +
