@@ -366,10 +366,13 @@ static int env_int(const char* name) {
 // 17.3 against 17.8-19.1 us with 4 waves; 32B q/k/v at M=8: 13.1 against
 // 13.3 us).  Splitting k across workgroups (its atomic handoff) pays only
 // for outputs too narrow to occupy more than a few dozen CUs and for long
-// reductions over few tiles; once a wave would walk more than 32 k steps,
-// the split goes on until it walks at most 16 (32B down, 5120 x 25600, 400
-// steps: 27.2 us with 4 slices, 31.2 us with 2, 37.2 us without; the 8B
-// down at M=5, 24 steps per wave, is fastest unsplit).
+// reductions over no more tiles than CUs; once a wave would walk more than
+// 32 k steps, the split goes on until it walks at most 16 (the 8B down at
+// M=5, 24 steps per wave, is fastest unsplit).  Outputs with more tiles
+// than CUs split only the tiles past the last whole round (the split tail):
+// the 32B down, 5120 x 25600 with 400 steps per tile, took 37.2 us unsplit
+// before that tail, 31.2 with 2 slices, 27.2-27.8 with 4, and 26.1 with
+// the tail.
 static SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, bool tiled, bool no_split = false) {
   SkinnyPlan p;
   const int64_t tiles16 = (N + 15) / 16;
@@ -389,8 +392,12 @@ static SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, bool tiled, bool 
     p.split *= 2;
   // long reductions over few tiles: more than kLongChain k steps per wave is
   // a chain of dependent round trips that the grid cannot hide, so K is cut
-  // across workgroups until a wave walks at most about half of that
-  if (!no_split && steps / ((int64_t)p.split * p.waves) > kLongChain)
+  // across workgroups until a wave walks at most about half of that.  With
+  // more tiles than CUs the split tail below balances the CUs instead and
+  // the long chains overlap across the grid (32B down, 320 tiles of 400
+  // steps: 26.1 us unsplit with the tail against 27.8 with four slices)
+  if (!no_split && steps / ((int64_t)p.split * p.waves) > kLongChain &&
+      (int64_t)p.tiles * p.mblocks <= cu_count())
     while (p.split < 8 && steps / ((int64_t)p.split * p.waves) > kLongChain / 2) p.split *= 2;
   const int fw = env_int("W8A8_WAVES");
   if (fw == 4 || fw == 8 || fw == 16) p.waves = fw;
