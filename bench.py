@@ -67,6 +67,11 @@ def parse_args():
     p.add_argument("--ingest-trace", metavar="TRACE_DIR",
                    help="turn a rocprofv3 --kernel-trace --stats csv run into a summary")
     p.add_argument("--command", default="", help="the command that produced the ingested run")
+    p.add_argument("--stack32b-probe", action="store_true",
+                   help="run STACK32B_LAYERS layers of the Qwen3-32B stack at M = 8 eagerly, "
+                        "STACK32B_ROUNDS rounds, for rocprofv3 --kernel-trace")
+    p.add_argument("--ingest-stack32b-trace", metavar="TRACE_DIR",
+                   help="summarize a --stack32b-probe kernel trace into profiles/")
     p.add_argument("--layer288-probe", action="store_true",
                    help="only the fused 288-row Qwen3-8B layer linears, eager (for rocprofv3 "
                         "--kernel-trace)")
@@ -468,6 +473,10 @@ def main():
         ingest_layer288_trace(args.ingest_layer288_trace, args.command,
                               os.path.join(ROOT, "profiles", "batched_layer_m288_kernel_trace.txt"))
         return
+    if args.ingest_stack32b_trace:
+        ingest_stack32b_trace(args.ingest_stack32b_trace, args.command,
+                              os.path.join(ROOT, "profiles", "stack32b_m8_kernel_trace.txt"))
+        return
     if args.ingest_batched_trace:
         ingest_trace(args.ingest_batched_trace, args.command,
                      os.path.join(ROOT, "profiles", "lm_head_verify_m288_kernel_trace.txt"))
@@ -503,6 +512,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.layer288_probe:
         layer288_probe(dev)
+        return
+    if args.stack32b_probe:
+        stack32b_probe(dev)
         return
 
     M, K, V, G, B = 5, 4096, synth.QWEN3_VOCAB, 4, 1
@@ -1201,6 +1213,102 @@ def ingest_layer288_trace(trace_dir, command, out_path):
         ops_all += ops
     lines.append(f"layer (sum of medians): {tot:.2f} us, {ops_all / tot / 1e6:.1f} TOPS "
                  f"({ops_all / tot / 1e6 / INT8_PEAK_TOPS:.4f} of the int8 MFMA peak)")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+STACK32B_LAYERS = 8     # 4 GB of int8 weights: past the 256 MB Infinity Cache
+STACK32B_ROUNDS = 6
+STACK32B_GROUPS = (("qkv", (0, 1, 2)), ("o", (3,)), ("gate_up", (4, 5)), ("down", (6,)))
+
+
+def stack32b_probe(dev):
+    """STACK32B_LAYERS layers of the Qwen3-32B stack at M = 8 as the stack
+    measurement runs them (per layer and fused group: quantize_act of the
+    group's input, then the linear; weights drawn on the device), eager,
+    STACK32B_ROUNDS rounds, for rocprofv3 --kernel-trace."""
+    import numpy as np
+    import torch
+
+    import synth
+    import w8a8_quantized_verification_amd as w8
+
+    M = 8
+    lins = synth.QWEN3_32B_LAYER
+    wsp = w8.Workspace()
+    layers = []
+    for layer in range(STACK32B_LAYERS):
+        row = []
+        for j, (name, grp) in enumerate(STACK32B_GROUPS):
+            K = lins[grp[0]].K
+            w = torch.cat([synth.weights_device(synth.W_STACK32B,
+                                                synth.stack_tensor_index(layer, li),
+                                                lins[li].N, K, dev) for li in grp])
+            wq, ws = w8.quantize_weight(w, tiled=True)
+            del w
+            b = synth.activations_bf16(synth.W_STACK32B, M, K, index=10_000 + 4 * layer + j,
+                                       outliers=True, layer=layer)
+            x = torch.from_numpy(b.view(np.int16).copy()).view(torch.bfloat16).to(dev)
+            y = torch.empty(M, ws.shape[0], dtype=torch.bfloat16, device=dev)
+            row.append((x, wq, ws, y))
+        layers.append(row)
+    xq = {k: torch.empty(M, k, dtype=torch.int8, device=dev)
+          for k in {lins[g[0]].K for _, g in STACK32B_GROUPS}}
+    xsc = torch.empty(M, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    for r in range(STACK32B_ROUNDS):
+        for row in layers:
+            for (x, wq, ws, y) in row:
+                k = x.shape[1]
+                w8.quantize_act(x, xq=xq[k], x_scale=xsc)
+                w8.linear(xq[k], xsc, wq, ws, y_bf16=y, workspace=wsp)
+    torch.cuda.synchronize()
+    print(json.dumps({"stack32b_probe": "done", "layers": STACK32B_LAYERS,
+                      "rounds": STACK32B_ROUNDS}), flush=True)
+
+
+def ingest_stack32b_trace(trace_dir, command, out_path):
+    """Per-launch durations of the --stack32b-probe: in start order the
+    rounds of (per layer, per fused group: quantize_act, linear); the first
+    round is left out (first touch of the code and data)."""
+    import numpy as np
+
+    import synth
+    rows = sorted((r for r in _csv_rows(trace_dir, "kernel_trace.csv")
+                   if "quantize_rows_kernel" in r["Kernel_Name"]
+                   or "gemm_w8a8_skinny" in r["Kernel_Name"]),
+                  key=lambda r: int(r["Start_Timestamp"]))
+    n = STACK32B_LAYERS * len(STACK32B_GROUPS) * 2
+    if len(rows) < n * STACK32B_ROUNDS:
+        raise SystemExit(f"expected {n * STACK32B_ROUNDS} dispatches, found {len(rows)}")
+    rows = rows[-n * STACK32B_ROUNDS:]   # the rounds follow the weights' own quantization
+    lins = synth.QWEN3_32B_LAYER
+    lines = ["# rocprofv3 kernel trace of the Qwen3-32B linear stack at M = 8 (tiled int8 weights,",
+             f"# bf16 outputs), {STACK32B_LAYERS} layers x {STACK32B_ROUNDS} eager rounds "
+             f"(rounds 2..{STACK32B_ROUNDS} kept; {STACK32B_LAYERS} layers = 4 GB, past the",
+             "# Infinity Cache); per fused group its quantize_act launch and its linear",
+             f"# command: {command}",
+             f"{'launch':>18} {'N':>6} {'K':>6} {'median_us':>9} {'min_us':>8} {'max_us':>8} "
+             f"{'TB/s@med':>8} {'grid_wgs':>8}  kernel"]
+    per_layer = 0.0
+    for j, (name, grp) in enumerate(STACK32B_GROUPS):
+        N, K = sum(lins[i].N for i in grp), lins[grp[0]].K
+        for part in (0, 1):
+            sel = [rows[rd * n + layer * len(STACK32B_GROUPS) * 2 + 2 * j + part]
+                   for rd in range(1, STACK32B_ROUNDS) for layer in range(STACK32B_LAYERS)]
+            d = np.array([(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in sel])
+            med = float(np.median(d))
+            wgs = int(sel[0]["Grid_Size_X"]) * int(sel[0].get("Grid_Size_Y", 1) or 1) // \
+                max(int(sel[0]["Workgroup_Size_X"]), 1)
+            kname = sel[0]["Kernel_Name"].split("(w8a8")[0].split("(")[0].replace("void ", "")
+            label = f"{name} {'quantize' if part == 0 else 'linear'}"
+            tbs = "" if part == 0 else f"{(N * K + 4 * N + 8 * K + 2 * 8 * N) / med / 1e6:8.2f}"
+            lines.append(f"{label:>18} {N if part else 0:6d} {K:6d} {med:9.2f} {d.min():8.2f} "
+                         f"{d.max():8.2f} {tbs:>8} {wgs:8d}  {kname}")
+            per_layer += med
+    lines.append(f"per layer (sum of medians): {per_layer:.2f} us; x 64 layers = "
+                 f"{per_layer * 64 / 1e3:.3f} ms of kernel time before the LM head")
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
