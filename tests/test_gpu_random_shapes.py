@@ -1,0 +1,142 @@
+"""Seeded random shapes for the W8A8 linear and the LM-head verification,
+GPU against the CPU oracle, bit for bit.
+
+The fixed-shape parity tests pin the workloads' shapes and the edges each
+kernel path was written for; these draw (M, N, K) at random over the whole
+range the dispatch covers (1..16 rows on the skinny kernel, 17..300 rows
+on the batched kernels, ragged N, K any multiple of 16), plus skinny draws
+aimed at its plan boundaries (the split tail past whole rounds over the
+CUs, the k split of narrow long reductions), so that a boundary nobody
+thought of still meets the oracle.  The draws are seeded and printed, so a
+failure names its shape.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.gpu_util import announce, dev, dev_bf16, gpu_available, host
+
+pytestmark = pytest.mark.gpu
+
+if gpu_available():
+    import w8a8_quantized_verification_amd as w8
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not gpu_available():
+        pytest.skip("no ROCm GPU")
+
+
+def _draw_shapes(seed: int, n: int, rows: tuple, max_mnk: float) -> list:
+    """n shapes (M, N, K) with M in rows, N in [1, 40000], K a multiple of 16
+    in [16, 26624], M*N*K <= max_mnk (the oracle's product stays seconds)."""
+    r = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        M = int(r.integers(rows[0], rows[1] + 1))
+        N = int(np.exp(r.uniform(0.0, np.log(40000.0))))
+        K = 16 * int(np.exp(r.uniform(0.0, np.log(26624 / 16))))
+        if M * N * K <= max_mnk:
+            out.append((M, N, K))
+    return out
+
+
+def _plan_edges(seed: int) -> list:
+    """Skinny shapes aimed at the plan boundaries: outputs a few tiles
+    past whole rounds over 256 CUs with long K (the split tail), and narrow
+    outputs with long K (the k split), at random row counts."""
+    r = np.random.default_rng(seed)
+    out = []
+    for _ in range(4):
+        tiles = 256 * int(r.integers(1, 3)) + int(r.integers(1, 256))
+        out.append((int(r.integers(1, 17)), 16 * tiles - int(r.integers(0, 16)),
+                    64 * int(r.integers(80, 129)) + 16 * int(r.integers(0, 4))))
+    for _ in range(3):
+        out.append((int(r.integers(1, 17)), int(r.integers(1, 513)),
+                    16 * int(r.integers(1024, 1665))))
+    return out
+
+
+SKINNY = _draw_shapes(31, 12, (1, 16), 1.5e9) + _plan_edges(33)
+BATCHED = _draw_shapes(32, 10, (17, 300), 3.0e9)
+
+
+def _linear(M, N, K, seed, tiled):
+    bits = synth.activations_bf16(seed, M, K, outliers=True)
+    w = synth.weights_f32(seed, N, K)
+    xq_ref, xs_ref = oracle.quantize_act(bits)
+    wq_ref, ws_ref = oracle.quantize_weight(w)
+    acc_ref, y32_ref, y_ref = oracle.w8a8_linear(xq_ref, xs_ref, wq_ref, ws_ref)
+    xq, xs = w8.quantize_act(dev_bf16(bits))
+    wq, ws = w8.quantize_weight(dev(w), tiled=tiled)
+    yb, yf, acc = w8.linear(xq, xs, wq, ws, want_bf16=True, want_f32=True, want_acc=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(xq), xq_ref)
+    np.testing.assert_array_equal(host(acc), acc_ref)
+    np.testing.assert_array_equal(host(yf).view(np.uint32), y32_ref.view(np.uint32))
+    np.testing.assert_array_equal(host(yb), y_ref)
+
+
+@pytest.mark.parametrize("M,N,K", SKINNY)
+@pytest.mark.parametrize("tiled", [True, False])
+def test_random_skinny_linear(M, N, K, tiled):
+    announce(f"random skinny linear M={M} N={N} K={K} tiled={tiled} "
+             f"workspace {w8.linear_workspace_bytes(M, N, K)} B")
+    _linear(M, N, K, seed=M * 7919 + N * 31 + K, tiled=tiled)
+
+
+@pytest.mark.parametrize("M,N,K", BATCHED)
+def test_random_batched_linear(M, N, K):
+    announce(f"random batched linear M={M} N={N} K={K} "
+             f"workspace {w8.linear_workspace_bytes(M, N, K)} B")
+    _linear(M, N, K, seed=M * 7919 + N * 31 + K, tiled=True)
+
+
+@pytest.mark.parametrize("M,N,K", BATCHED[:5])
+def test_random_batched_tiled_activations(M, N, K):
+    """The batched kernels' tiled-activation path on the same draws."""
+    announce(f"random tiled-activation linear M={M} N={N} K={K}")
+    seed = M * 7919 + N * 31 + K
+    bits = synth.activations_bf16(seed, M, K, outliers=True)
+    w = synth.weights_f32(seed, N, K)
+    xq_ref, xs_ref = oracle.quantize_act(bits)
+    wq_ref, ws_ref = oracle.quantize_weight(w)
+    acc_ref, y32_ref, y_ref = oracle.w8a8_linear(xq_ref, xs_ref, wq_ref, ws_ref)
+    xt, xs = w8.quantize_act_tiled(dev_bf16(bits))
+    wq, ws = w8.quantize_weight(dev(w), tiled=True)
+    yb, yf, acc = w8.linear_tiled_act(xt, xs, wq, ws, K=K, want_bf16=True, want_f32=True,
+                                      want_acc=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(acc), acc_ref)
+    np.testing.assert_array_equal(host(yf).view(np.uint32), y32_ref.view(np.uint32))
+    np.testing.assert_array_equal(host(yb), y_ref)
+
+
+@pytest.mark.parametrize("B,G,V,K", [(1, 4, 77777, 1040), (2, 6, 30011, 2064), (1, 15, 5003, 4160),
+                                     (9, 2, 12007, 528), (24, 11, 3001, 1024)])
+def test_random_lm_head_verify(B, G, V, K):
+    """The fused LM-head verification (skinny up to 16 rows, batched above)
+    at odd vocabularies and K, drafts with spread accepted lengths."""
+    announce(f"random lm_head_verify B={B} G={G} V={V} K={K}")
+    R = B * (G + 1)
+    bits = synth.activations_bf16(V + K, R, K)
+    w = synth.weights_f32(V + K, V, K)
+    xq_ref, xs_ref = oracle.quantize_act(bits)
+    wq_ref, ws_ref = oracle.quantize_weight(w)
+    _, y32_ref, _ = oracle.w8a8_linear(xq_ref, xs_ref, wq_ref, ws_ref)
+    am0 = oracle.argmax_rows(y32_ref).reshape(B, G + 1)
+    draft = synth.draft_ids(V, B, G, V)
+    for b in range(B):
+        p = (3 * b + 1) % (G + 1)
+        draft[b, :p] = am0[b, :p]
+    am_r, al_r, nt_r = oracle.verify_accept(y32_ref, draft)
+    xq, xs = w8.quantize_act(dev_bf16(bits))
+    wt, ws = w8.quantize_weight(dev(w), tiled=True)
+    _, am, al, nt = w8.lm_head_verify(xq, xs, wt, ws, dev(draft))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(am), am_r)
+    np.testing.assert_array_equal(host(al), al_r)
+    np.testing.assert_array_equal(host(nt), nt_r)
