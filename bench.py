@@ -491,7 +491,7 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
 
@@ -1710,7 +1710,7 @@ def library_int8_gemm(dev):
             t = graph_time([(lambda c=c: torch._int_mm(a, ws[c].t())) for c in range(ncp)],
                            replays=10) / ncp
             out[name] = {"us": round(t * 1e6, 2), "TOPS": round(2 * M * N * K / t / 1e12, 1)}
-        except Exception as e:   # the op is missing or unsupported on this build
+        except Exception as e:   # the op is missing or unsupported in the library
             out[name] = {"error": str(e)[:160]}
         del ws
         torch.cuda.empty_cache()

@@ -52,7 +52,7 @@ typedef int32_t w8a8_status;
 
 #define W8A8_OK              0  /* success */
 #define W8A8_ERR_INVALID_ARG 1  /* NULL pointer, bad size, misalignment, K out of range */
-#define W8A8_ERR_UNSUPPORTED 2  /* valid request this build does not handle */
+#define W8A8_ERR_UNSUPPORTED 2  /* valid request the library does not handle */
 #define W8A8_ERR_WORKSPACE   3  /* workspace NULL or smaller than the query says */
 #define W8A8_ERR_HIP         4  /* the HIP runtime reported an error at launch */
 
