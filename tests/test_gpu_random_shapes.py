@@ -1,5 +1,6 @@
-"""Seeded random shapes for the W8A8 linear and the LM-head verification,
-GPU against the CPU oracle, bit for bit.
+"""Seeded random shapes for the W8A8 and W4A8 linears, the LM-head
+verification and the stochastic acceptance, GPU against the CPU oracle, bit
+for bit.
 
 The fixed-shape parity tests pin the workloads' shapes and the edges each
 kernel path was written for; these draw (M, N, K) at random over the whole
@@ -16,6 +17,7 @@ import torch
 
 import oracle
 import synth
+from oracle import sample as S
 from tests.gpu_util import announce, dev, dev_bf16, gpu_available, host
 
 pytestmark = pytest.mark.gpu
@@ -138,5 +140,71 @@ def test_random_lm_head_verify(B, G, V, K):
     _, am, al, nt = w8.lm_head_verify(xq, xs, wt, ws, dev(draft))
     torch.cuda.synchronize()
     np.testing.assert_array_equal(host(am), am_r)
+    np.testing.assert_array_equal(host(al), al_r)
+    np.testing.assert_array_equal(host(nt), nt_r)
+
+
+def _w4_draws(seed: int, n: int) -> list:
+    """W4A8 shapes: M in [1, 48] (skinny and batched), N in [1, 20000], K a
+    multiple of 16 in [16, 16384] (int4 k pairs of 128 padded), M*N*K <= 1e9."""
+    r = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        M = int(r.integers(1, 49))
+        N = int(np.exp(r.uniform(0.0, np.log(20000.0))))
+        K = 16 * int(np.exp(r.uniform(0.0, np.log(16384 / 16))))
+        if M * N * K <= 1.0e9:
+            out.append((M, N, K))
+    return out
+
+
+@pytest.mark.parametrize("M,N,K", _w4_draws(34, 8))
+def test_random_w4_linear(M, N, K):
+    announce(f"random w4 linear M={M} N={N} K={K}")
+    seed = M * 7919 + N * 31 + K + 1
+    bits = synth.activations_bf16(seed, M, K, outliers=True)
+    w = synth.weights_f32(seed, N, K)
+    xq_r, xs_r = oracle.quantize_act(bits)
+    q_r, s_r = oracle.quantize_weight_int4(w)
+    acc_r, y32_r, y_r = oracle.w8a8_linear(xq_r, xs_r, q_r, s_r)
+    xq, xs = w8.quantize_act(dev_bf16(bits))
+    wq4, ws = w8.quantize_weight_w4(dev(w))
+    yb, yf, acc = w8.linear_w4(xq, xs, wq4, ws, want_bf16=True, want_f32=True, want_acc=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(acc), acc_r)
+    np.testing.assert_array_equal(host(yf).view(np.uint32), y32_r.view(np.uint32))
+    np.testing.assert_array_equal(host(yb), y_r)
+
+
+def _sample_draws(seed: int, n: int) -> list:
+    """Stochastic acceptance: B in [1, 8], G in [0, 12], V in [1, 200000],
+    T log-uniform in [0.05, 4]."""
+    r = np.random.default_rng(seed)
+    return [(int(r.integers(1, 9)), int(r.integers(0, 13)),
+             int(np.exp(r.uniform(0.0, np.log(200000.0)))),
+             float(np.float32(np.exp(r.uniform(np.log(0.05), np.log(4.0))))))
+            for _ in range(n)]
+
+
+@pytest.mark.parametrize("B,G,V,t", _sample_draws(35, 8))
+def test_random_verify_sample(B, G, V, t):
+    """Drafts agreeing with the row argmax for a spread of prefix lengths
+    (likely acceptances at low T), the rest random; random words."""
+    announce(f"random verify_sample B={B} G={G} V={V} T={t}")
+    r = np.random.default_rng(B * 1000003 + G * 1009 + V)
+    R = B * (G + 1)
+    y = (r.standard_normal((R, V), dtype=np.float32) * np.float32(2.0)).astype(np.float32)
+    am = oracle.argmax_rows(y).reshape(B, G + 1)
+    d = r.integers(0, V, size=(B, G)).astype(np.int32)
+    for b in range(B):
+        p = (2 * b + 1) % (G + 1)
+        d[b, :p] = am[b, :p]
+    ua = r.integers(0, 1 << 32, size=(B, G), dtype=np.uint64).astype(np.uint32)
+    us = r.integers(0, 1 << 64, size=(B,), dtype=np.uint64)
+    al_r, nt_r = S.verify_sample(y, d, t, ua, us)
+    ua_t = torch.from_numpy(ua.view(np.int32).reshape(B, G).copy()).cuda()
+    us_t = torch.from_numpy(us.view(np.int64).copy()).cuda()
+    al, nt = w8.verify_sample(dev(y), dev(d), t, ua_t, us_t)
+    torch.cuda.synchronize()
     np.testing.assert_array_equal(host(al), al_r)
     np.testing.assert_array_equal(host(nt), nt_r)
