@@ -1,6 +1,7 @@
 """Seeded random shapes for the W8A8 and W4A8 linears, the LM-head
-verification and the stochastic acceptance, GPU against the CPU oracle, bit
-for bit.
+verification, the stochastic acceptance and the fused BF16 glue, GPU
+against the CPU oracle: bit for bit, except the glue's bf16 rows, which
+carry the glue tests' tolerance.
 
 The fixed-shape parity tests pin the workloads' shapes and the edges each
 kernel path was written for; these draw (M, N, K) at random over the whole
@@ -208,3 +209,68 @@ def test_random_verify_sample(B, G, V, t):
     torch.cuda.synchronize()
     np.testing.assert_array_equal(host(al), al_r)
     np.testing.assert_array_equal(host(nt), nt_r)
+
+
+def _glue_draws(seed: int, n: int) -> list:
+    """Glue widths: M in [1, 300], D a multiple of 16 in [16, 32768]
+    (log-uniform), smoothing on about half of them."""
+    r = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        M = int(np.exp(r.uniform(0.0, np.log(300.0))))
+        D = 16 * int(np.exp(r.uniform(0.0, np.log(32768 / 16))))
+        if M * D <= 2_000_000:
+            out.append((M, D, bool(r.integers(0, 2))))
+    return out
+
+
+def _check_glue_codes(xq, xsc, rows_gpu, rows_oracle, smooth):
+    """The codes: bit-exact against the oracle's quantizer on the kernel's own
+    bf16 rows (the same decision in the same precision), and against the
+    all-oracle chain on every row whose bf16 values equal the oracle's; the
+    bf16 rows within 1e-2 relative / 1e-3 absolute, >= 99% bit-identical."""
+    got = oracle.bf16_to_f32(rows_gpu).astype(np.float64)
+    want = oracle.bf16_to_f32(rows_oracle).astype(np.float64)
+    assert np.all(np.abs(got - want) <= 1e-3 + 1e-2 * np.abs(want))
+    assert np.mean(rows_gpu == rows_oracle) >= 0.99
+    q_k, s_k = oracle.quantize_act(rows_gpu, smooth=smooth)
+    np.testing.assert_array_equal(xq, q_k)
+    np.testing.assert_array_equal(xsc.view(np.uint32), s_k.view(np.uint32))
+    same = np.all(rows_gpu == rows_oracle, axis=1)
+    q_o, s_o = oracle.quantize_act(rows_oracle, smooth=smooth)
+    np.testing.assert_array_equal(xq[same], q_o[same])
+    np.testing.assert_array_equal(xsc[same].view(np.uint32), s_o[same].view(np.uint32))
+    print(f"[gpu] glue rows identical to the oracle's: {int(same.sum())} of {len(same)}", flush=True)
+
+
+@pytest.mark.parametrize("M,D,smooth", _glue_draws(36, 6))
+def test_random_residual_rmsnorm_quant(M, D, smooth):
+    announce(f"random residual_rmsnorm_quant M={M} D={D} smooth={smooth}")
+    seed = M * 7919 + D
+    h = oracle.f32_to_bf16(oracle.bf16_to_f32(synth.activations_bf16(seed, M, D))
+                           * np.float32(4.0))
+    delta = synth.activations_bf16(seed + 1, M, D, outliers=True)
+    gamma = oracle.f32_to_bf16(np.random.default_rng(seed).uniform(0.5, 1.5, D).astype(np.float32))
+    s = synth.smoothing_vector(seed, D) if smooth else None
+    eps = 1e-6
+    xq, xsc, normed, h_out = w8.residual_rmsnorm_quant(
+        dev_bf16(h), dev_bf16(gamma), eps, delta=dev_bf16(delta),
+        smooth=None if s is None else dev(s), want_normed=True)
+    torch.cuda.synchronize()
+    h1 = oracle.residual_add(h, delta)
+    np.testing.assert_array_equal(host(h_out), h1)
+    _check_glue_codes(host(xq), host(xsc), host(normed), oracle.rmsnorm(h1, gamma, eps), s)
+
+
+@pytest.mark.parametrize("M,F,smooth", _glue_draws(37, 6))
+def test_random_silu_mul_quant(M, F, smooth):
+    announce(f"random silu_mul_quant M={M} F={F} smooth={smooth}")
+    seed = M * 7919 + F + 2
+    g = oracle.f32_to_bf16(oracle.bf16_to_f32(synth.activations_bf16(seed, M, F))
+                           * np.float32(3.0))
+    u = synth.activations_bf16(seed + 1, M, F)
+    s = synth.smoothing_vector(seed, F) if smooth else None
+    xq, xsc, act = w8.silu_mul_quant(dev_bf16(g), dev_bf16(u),
+                                     smooth=None if s is None else dev(s), want_act=True)
+    torch.cuda.synchronize()
+    _check_glue_codes(host(xq), host(xsc), host(act), oracle.silu_mul(g, u), s)
