@@ -1,7 +1,8 @@
 """Seeded random shapes for the W8A8 and W4A8 linears, the LM-head
-verification, the stochastic acceptance and the fused BF16 glue, GPU
-against the CPU oracle: bit for bit, except the glue's bf16 rows, which
-carry the glue tests' tolerance.
+verification, the stochastic acceptance, the fused BF16 glue and the
+verified block's attention, GPU against the CPU oracle: bit for bit, except
+the glue's bf16 rows and the attention output, which carry the tolerance of
+their own tests (1e-2 relative / 1e-3 absolute).
 
 The fixed-shape parity tests pin the workloads' shapes and the edges each
 kernel path was written for; these draw (M, N, K) at random over the whole
@@ -274,3 +275,38 @@ def test_random_silu_mul_quant(M, F, smooth):
                                      smooth=None if s is None else dev(s), want_act=True)
     torch.cuda.synchronize()
     _check_glue_codes(host(xq), host(xsc), host(act), oracle.silu_mul(g, u), s)
+
+
+def _attention_draws(seed: int, n: int) -> list:
+    """B in [1, 8] sequences of T in [1, 8] verified positions; kv heads in
+    {1, 2, 4, 8} with a query group of at most 64 / T rows; Lmax a multiple
+    of 16 up to 16384; ragged lengths in [T, Lmax]; B*Hq*T*Lmax <= 2e7 (the
+    float64 oracle stays seconds)."""
+    r = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        B, T = int(r.integers(1, 9)), int(r.integers(1, 9))
+        Hkv = int(r.choice([1, 2, 4, 8]))
+        g = int(r.integers(1, 64 // T + 1))
+        Lmax = 16 * int(np.exp(r.uniform(np.log((T + 15) // 16), np.log(1024))))
+        lengths = [int(x) for x in r.integers(T, Lmax + 1, size=B)]
+        if B * Hkv * g * T * Lmax <= 2.0e7:
+            out.append((B, T, Hkv * g, Hkv, Lmax, lengths))
+    return out
+
+
+@pytest.mark.parametrize("B,T,Hq,Hkv,Lmax,lengths", _attention_draws(38, 6))
+def test_random_verify_attention(B, T, Hq, Hkv, Lmax, lengths):
+    announce(f"random verify_attention B={B} T={T} Hq={Hq} Hkv={Hkv} Lmax={Lmax} lengths={lengths}")
+    r = np.random.default_rng(B * 131 + T * 17 + Hq * 7 + Lmax)
+    q, k, v = (synth.to_bf16_bits(r.standard_normal(shape, dtype=np.float32))
+               for shape in ((B, T, Hq, 128), (B, Hkv, Lmax, 128), (B, Hkv, Lmax, 128)))
+    lengths = np.asarray(lengths, dtype=np.int32)
+    want = oracle.verify_attention(q, k, v, lengths)
+    out = w8.verify_attention(dev_bf16(q), dev_bf16(k), w8.pack_v_cache(dev_bf16(v)), dev(lengths))
+    torch.cuda.synchronize()
+    got = host(out)
+    g = oracle.bf16_to_f32(got).astype(np.float64)
+    w = oracle.bf16_to_f32(want).astype(np.float64)
+    assert np.all(np.abs(g - w) <= 1e-3 + 1e-2 * np.abs(w))
+    print(f"[gpu] bit-identical fraction {np.mean(got == want):.4f}", flush=True)
