@@ -1,8 +1,9 @@
 """Seeded random shapes for the W8A8 and W4A8 linears, the LM-head
 verification, the stochastic acceptance, the fused BF16 glue and the
-verified block's attention, GPU against the CPU oracle: bit for bit, except
-the glue's bf16 rows and the attention output, which carry the tolerance of
-their own tests (1e-2 relative / 1e-3 absolute).
+verified block's attention with its q/k norm, rotary embedding and cache
+append, GPU against the CPU oracle: bit for bit, except the glue's bf16 rows
+and the attention outputs, which carry the tolerance of their own tests
+(1e-2 relative / 1e-3 absolute).
 
 The fixed-shape parity tests pin the workloads' shapes and the edges each
 kernel path was written for; these draw (M, N, K) at random over the whole
@@ -310,3 +311,57 @@ def test_random_verify_attention(B, T, Hq, Hkv, Lmax, lengths):
     w = oracle.bf16_to_f32(want).astype(np.float64)
     assert np.all(np.abs(g - w) <= 1e-3 + 1e-2 * np.abs(w))
     print(f"[gpu] bit-identical fraction {np.mean(got == want):.4f}", flush=True)
+
+
+def _append_draws(seed: int, n: int) -> list:
+    """B in [1, 8], T in [1, 8], kv heads in {1, 2, 4, 8} with groups of
+    1-8, Lmax a multiple of 16 up to 131072 (log-uniform), ragged lengths
+    in [T, Lmax], rotary base 1e4 or 1e6; B*Hkv*Lmax <= 5e5."""
+    r = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        B, T = int(r.integers(1, 9)), int(r.integers(1, 9))
+        Hkv = int(r.choice([1, 2, 4, 8]))
+        Hq = Hkv * int(r.integers(1, 9))
+        Lmax = 16 * int(np.exp(r.uniform(0.0, np.log(8192))))
+        lengths = [int(x) for x in r.integers(T, Lmax + 1, size=B)]
+        base = float(r.choice([1.0e4, 1.0e6]))
+        if Lmax >= T and B * Hkv * Lmax <= 5.0e5:
+            out.append((B, T, Hq, Hkv, Lmax, lengths, base))
+    return out
+
+
+@pytest.mark.parametrize("B,T,Hq,Hkv,Lmax,lengths,base", _append_draws(39, 6))
+def test_random_qk_norm_rope_append(B, T, Hq, Hkv, Lmax, lengths, base):
+    announce(f"random qk_norm_rope_append B={B} T={T} Hq={Hq} Hkv={Hkv} Lmax={Lmax} "
+             f"lengths={lengths} base={base:g}")
+    r = np.random.default_rng(B * 131 + T * 17 + Hq * 7 + Lmax + 1)
+
+    def bf(shape, scale=1.0):
+        return synth.to_bf16_bits(r.standard_normal(shape, dtype=np.float32) * np.float32(scale))
+
+    qkv = bf((B * T, (Hq + 2 * Hkv) * 128), 2.0)
+    qg = synth.to_bf16_bits(r.uniform(0.5, 1.5, 128).astype(np.float32))
+    kg = synth.to_bf16_bits(r.uniform(0.5, 1.5, 128).astype(np.float32))
+    kc0, vc0 = bf((B, Hkv, Lmax, 128)), bf((B, Hkv, Lmax, 128))
+    lengths = np.asarray(lengths, dtype=np.int32)
+    kc, vc = dev_bf16(kc0), w8.pack_v_cache(dev_bf16(vc0))
+    q = w8.qk_norm_rope_append(dev_bf16(qkv), dev_bf16(qg), dev_bf16(kg), dev(lengths), kc, vc,
+                               T=T, Hq=Hq, Hkv=Hkv, eps=1e-6, rope_base=base)
+    torch.cuda.synchronize()
+    start = lengths - T
+    q_r, k_r, v_r = oracle.qk_norm_rope(qkv, B, T, Hq, Hkv, qg, kg, 1e-6, start, base)
+    want_k, want_v = kc0.copy(), vc0.copy()
+    for b in range(B):
+        for i in range(T):
+            want_k[b, :, start[b] + i] = k_r[b, i]
+            want_v[b, :, start[b] + i] = v_r[b, i]
+    for got, want in ((host(q), q_r), (host(kc), want_k)):
+        g = oracle.bf16_to_f32(got).astype(np.float64)
+        w = oracle.bf16_to_f32(want).astype(np.float64)
+        assert np.all(np.abs(g - w) <= 1e-3 + 1e-2 * np.abs(w))
+    np.testing.assert_array_equal(host(vc), host(w8.pack_v_cache(dev_bf16(want_v))))
+    touched = np.zeros((B, Hkv, Lmax), dtype=bool)
+    for b in range(B):
+        touched[b, :, start[b]:start[b] + T] = True
+    np.testing.assert_array_equal(host(kc)[~touched], kc0[~touched])
