@@ -13,7 +13,10 @@ Paths covered: the skinny kernel (row-major and tiled weights, with and
 without the split-K handoff), the register-fragment batched kernel, the
 LDS-pipelined 16 x 16 and 32 x 32 kernels (including the 96-row form with
 the argmax fold), tiled activations, the LM-head argmax keys at 5 and 288
-rows, the two-pass verify_accept, the quantizers and the W4A8 kernels."""
+rows, the two-pass verify_accept, the quantizers, the W4A8 kernels, the
+fused glue (residual + RMSNorm + quantize, SwiGLU + quantize), the q/k norm
++ rotary + cache append with both caches guarded, the verified block's
+attention and its workspace, and the stochastic acceptance and its weights."""
 import numpy as np
 import pytest
 import torch
@@ -306,4 +309,95 @@ def test_guard_w4a8(M, N, K):
         assert same_bits(g.t, r), f"{name} differs from the unguarded call"
     assert lg.intact() and same_bits(lg.t, ref_lg)
     assert same_bits(am, ram) and same_bits(al, ral) and same_bits(nt, rnt)
+    wsp.check()
+
+
+@pytest.mark.parametrize("M,D", [(1, 16), (7, 4112), (289, 4096)])
+def test_guard_residual_rmsnorm_quant(M, D):
+    announce(f"guard residual_rmsnorm_quant M={M} D={D}")
+    h, delta = act(M, D, 20), act(M, D, 21)
+    gamma = dev_bf16(synth.activations_bf16(W_GUARD, 1, D, index=22)[0])
+    s = dev(synth.smoothing_vector(W_GUARD, D))
+    g = {"xq": Guarded((M, D), torch.int8), "x_scale": Guarded((M,), torch.float32),
+         "normed": Guarded((M, D), torch.bfloat16), "h_out": Guarded((M, D), torch.bfloat16)}
+    w8.residual_rmsnorm_quant(h, gamma, 1e-6, delta=delta, smooth=s, h_out=g["h_out"].t,
+                              normed=g["normed"].t, xq=g["xq"].t, x_scale=g["x_scale"].t)
+    ref = w8.residual_rmsnorm_quant(h, gamma, 1e-6, delta=delta, smooth=s, want_normed=True)
+    torch.cuda.synchronize()
+    for (name, gd), r in zip(g.items(), ref):
+        assert gd.intact(), f"{name} guard band overwritten"
+        assert same_bits(gd.t, r), f"{name} differs from the unguarded call"
+
+
+@pytest.mark.parametrize("M,F", [(1, 16), (5, 12304), (289, 3088)])
+def test_guard_silu_mul_quant(M, F):
+    announce(f"guard silu_mul_quant M={M} F={F}")
+    gu = act(M, 2 * F, 23)                      # a fused [gate;up] output: column halves
+    gate, up = gu[:, :F], gu[:, F:]
+    g = {"xq": Guarded((M, F), torch.int8), "x_scale": Guarded((M,), torch.float32),
+         "act": Guarded((M, F), torch.bfloat16)}
+    w8.silu_mul_quant(gate, up, act=g["act"].t, xq=g["xq"].t, x_scale=g["x_scale"].t)
+    ref = w8.silu_mul_quant(gate, up, want_act=True)
+    torch.cuda.synchronize()
+    for (name, gd), r in zip(g.items(), ref):
+        assert gd.intact(), f"{name} guard band overwritten"
+        assert same_bits(gd.t, r), f"{name} differs from the unguarded call"
+
+
+def _bf16_normal(shape, index, scale=1.0):
+    z = synth.rng(W_GUARD, 40, index).standard_normal(shape, dtype=np.float32) * np.float32(scale)
+    return dev_bf16(synth.to_bf16_bits(z))
+
+
+@pytest.mark.parametrize("B,T,Hq,Hkv,Lmax,lengths", [(3, 5, 16, 4, 304, [300, 5, 123]),
+                                                     (1, 8, 64, 8, 4096, [4096]),
+                                                     (2, 1, 8, 8, 64, [1, 64])])
+def test_guard_verify_attention_and_append(B, T, Hq, Hkv, Lmax, lengths):
+    """The attention output and workspace, and the q output of the q/k norm +
+    rotary + cache append with both caches inside guard bands (rows past
+    each sequence's block untouched)."""
+    announce(f"guard verify_attention B={B} T={T} Hq={Hq} Hkv={Hkv} Lmax={Lmax}")
+    lengths = dev(np.asarray(lengths, dtype=np.int32))
+    qkv = _bf16_normal((B * T, (Hq + 2 * Hkv) * 128), 1, 2.0)
+    qg, kg = _bf16_normal((128,), 2), _bf16_normal((128,), 3)
+    k0, v0 = _bf16_normal((B, Hkv, Lmax, 128), 4), w8.pack_v_cache(_bf16_normal((B, Hkv, Lmax, 128), 5))
+    kc, vc = Guarded((B, Hkv, Lmax, 128), torch.bfloat16), Guarded((B, Hkv, Lmax, 128), torch.bfloat16)
+    kc.t.copy_(k0)
+    vc.t.copy_(v0)
+    qo = Guarded((B, T, Hq, 128), torch.bfloat16)
+    w8.qk_norm_rope_append(qkv, qg, kg, lengths, kc.t, vc.t, T=T, Hq=Hq, Hkv=Hkv, q_out=qo.t)
+    k1, v1 = k0.clone(), v0.clone()
+    q1 = w8.qk_norm_rope_append(qkv, qg, kg, lengths, k1, v1, T=T, Hq=Hq, Hkv=Hkv)
+    wsp = GuardedWorkspace()
+    out = Guarded((B, T, Hq, 128), torch.bfloat16)
+    w8.verify_attention(qo.t, kc.t, vc.t, lengths, out=out.t, workspace=wsp)
+    ref = w8.verify_attention(q1, k1, v1, lengths)
+    torch.cuda.synchronize()
+    for name, g, r in (("q_out", qo, q1), ("k_cache", kc, k1), ("v_cache", vc, v1), ("out", out, ref)):
+        assert g.intact(), f"{name} guard band overwritten"
+        assert same_bits(g.t, r), f"{name} differs from the unguarded call"
+    wsp.check()
+
+
+@pytest.mark.parametrize("B,G,V,t", [(3, 4, 4099, 1.0), (1, 0, 1, 0.7), (32, 8, 151941, 0.3)])
+def test_guard_verify_sample(B, G, V, t):
+    announce(f"guard verify_sample B={B} G={G} V={V} T={t}")
+    R = B * (G + 1)
+    y = dev(synth.rng(W_GUARD, 41, V).standard_normal((R, V), dtype=np.float32))
+    d = dev(synth.draft_ids(W_GUARD, B, G, V, index=5))
+    r = synth.rng(W_GUARD, 42, V)
+    ua = torch.from_numpy(r.integers(0, 1 << 32, size=(B, G), dtype=np.uint64)
+                          .astype(np.uint32).view(np.int32).copy()).cuda()
+    us = torch.from_numpy(r.integers(0, 1 << 64, size=(B,), dtype=np.uint64).view(np.int64).copy()).cuda()
+    wsp = GuardedWorkspace()
+    al, nt = Guarded((B,), torch.int32), Guarded((B,), torch.int32)
+    w8.verify_sample(y, d, t, ua, us, accept_len=al.t, next_token=nt.t, workspace=wsp)
+    ral, rnt = w8.verify_sample(y, d, t, ua, us)
+    wts = Guarded((R, V), torch.int64)
+    w8.sample_weights(y, t, weights=wts.t, workspace=wsp)
+    rw = w8.sample_weights(y, t)
+    torch.cuda.synchronize()
+    for name, g, ref in (("accept_len", al, ral), ("next_token", nt, rnt), ("weights", wts, rw)):
+        assert g.intact(), f"{name} guard band overwritten"
+        assert same_bits(g.t, ref), f"{name} differs from the unguarded call"
     wsp.check()
