@@ -642,6 +642,85 @@ def test_graph_replay_matches_eager(forced_split):
         del scratch
 
 
+def test_graph_replay_batched_and_stochastic_steps():
+    """The 288-row verify step (quantize_act_tiled; the down-shaped linear
+    12288 -> 4096, whose k is split across two workgroups through the zeroed
+    workspace; the LM-head argmax on tiled activations in its 96 x 256 form;
+    accept_from_keys) and a T = 1 step (the LM-head linear to fp32 logits,
+    then verify_sample's three kernels) captured in one HIP graph: every
+    replay, with eager work and synchronizations between replays, equals the
+    eager result bit for bit, and the zero-on-exit workspaces are zero after
+    each replay."""
+    announce("graph replay of the 288-row and T = 1 steps")
+    gen = torch.Generator(device="cuda:0").manual_seed(612)
+    M, Kd, Nd, K, V, B, G = 288, 12288, 4096, 4096, 100003, 32, 8
+
+    def randn(*shape, scale=1.0):
+        return torch.randn(*shape, device="cuda:0", generator=gen) * scale
+
+    xd = randn(M, Kd).to(torch.bfloat16)
+    x = randn(M, K).to(torch.bfloat16)
+    wq_d, ws_d = w8.quantize_weight(randn(Nd, Kd, scale=0.02), tiled=True)
+    wq_v, ws_v = w8.quantize_weight(randn(V, K, scale=0.02), tiled=True)
+    assert w8.linear_tiled_act_workspace_bytes(M, Nd, Kd) > 0   # the k split is in the graph
+    draft = torch.randint(0, V, (B, G), device="cuda:0", generator=gen, dtype=torch.int32)
+    d5 = draft[:1, :4].contiguous()
+    ua = torch.randint(-(1 << 31), 1 << 31, (1, 4), device="cuda:0", generator=gen, dtype=torch.int64)
+    ua = ua.to(torch.int32)
+    us = torch.randint(-(1 << 62), 1 << 62, (1,), device="cuda:0", generator=gen, dtype=torch.int64)
+    ws = w8.Workspace()
+    xt_d = torch.empty(w8.tiled_shape(M, Kd), dtype=torch.int8, device="cuda:0")
+    xs_d = torch.empty(M, dtype=torch.float32, device="cuda:0")
+    xt = torch.empty(w8.tiled_shape(M, K), dtype=torch.int8, device="cuda:0")
+    xs = torch.empty(M, dtype=torch.float32, device="cuda:0")
+    yd = torch.empty(M, Nd, dtype=torch.bfloat16, device="cuda:0")
+    am = torch.empty(M, dtype=torch.int32, device="cuda:0")
+    al = torch.empty(B, dtype=torch.int32, device="cuda:0")
+    nt = torch.empty(B, dtype=torch.int32, device="cuda:0")
+    xq5 = torch.empty(5, K, dtype=torch.int8, device="cuda:0")
+    xs5 = torch.empty(5, dtype=torch.float32, device="cuda:0")
+    lg5 = torch.empty(5, V, dtype=torch.float32, device="cuda:0")
+    al5 = torch.empty(1, dtype=torch.int32, device="cuda:0")
+    nt5 = torch.empty(1, dtype=torch.int32, device="cuda:0")
+
+    def step():
+        w8.quantize_act_tiled(xd, xq_tiled=xt_d, x_scale=xs_d)
+        w8.linear_tiled_act(xt_d, xs_d, wq_d, ws_d, K=Kd, y_bf16=yd, workspace=ws)
+        w8.quantize_act_tiled(x, xq_tiled=xt, x_scale=xs)
+        w8.lm_head_argmax_tiled_act(xt, xs, wq_v, ws_v, K=K, workspace=ws)
+        w8.accept_from_keys(draft, argmax=am, accept_len=al, next_token=nt, workspace=ws)
+        w8.quantize_act(x[:5], xq=xq5, x_scale=xs5)
+        w8.linear(xq5, xs5, wq_v, ws_v, want_bf16=False, y_f32=lg5, workspace=ws)
+        w8.verify_sample(lg5, d5, 1.0, ua, us, accept_len=al5, next_token=nt5, workspace=ws)
+
+    outs = (xt_d, xs_d, yd, xt, xs, am, al, nt, xq5, xs5, lg5, al5, nt5)
+    step()
+    torch.cuda.synchronize()
+    ref = [host(t) for t in outs]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for r in range(4):
+        for t in outs:
+            t.zero_()
+        scratch = torch.randn(1 << 20, device="cuda:0").sum()  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip((host(t) for t in outs), ref):
+            np.testing.assert_array_equal(a, b, err_msg=f"replay {r}")
+        for use in ("zeroed", "keys"):
+            buf = ws.get(1, torch.device("cuda:0"), use)      # the buffer the step used
+            assert not bool(buf.any()), f"workspace '{use}' not zero after replay {r}"
+        del scratch
+
+
 # --------------------------------------------------------------------------
 # fused LM-head verification
 # --------------------------------------------------------------------------
