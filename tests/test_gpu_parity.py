@@ -642,6 +642,56 @@ def test_graph_replay_matches_eager(forced_split):
         del scratch
 
 
+def test_graph_replay_split_tail():
+    """The skinny kernel's split tail (8 x 8192 -> 5120: 320 tiles on 256
+    CUs, the 64 past the last whole round cut into 4 k slices with the
+    atomic hand-off) and a narrow split-K linear in one HIP graph: each
+    replay equals the eager result and leaves the workspace zero."""
+    announce("graph replay of the split tail")
+    gen = torch.Generator(device="cuda:0").manual_seed(613)
+    M, K, N, N2, K2 = 8, 8192, 5120, 512, 25600
+    assert w8.linear_workspace_bytes(M, N, K) > 0 and w8.linear_workspace_bytes(M, N2, K2) > 0
+    x = (torch.randn(M, K, device="cuda:0", generator=gen)).to(torch.bfloat16)
+    x2 = (torch.randn(M, K2, device="cuda:0", generator=gen)).to(torch.bfloat16)
+    wq, wsc = w8.quantize_weight(torch.randn(N, K, device="cuda:0", generator=gen) * 0.02, tiled=True)
+    wq2, wsc2 = w8.quantize_weight(torch.randn(N2, K2, device="cuda:0", generator=gen) * 0.02,
+                                   tiled=True)
+    xq, xs = w8.quantize_act(x)
+    xq2, xs2 = w8.quantize_act(x2)
+    ws = w8.Workspace()
+    y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda:0")
+    acc = torch.empty(M, N, dtype=torch.int32, device="cuda:0")
+    y2 = torch.empty(M, N2, dtype=torch.bfloat16, device="cuda:0")
+
+    def step():
+        w8.linear(xq, xs, wq, wsc, y_bf16=y, acc=acc, workspace=ws)
+        w8.linear(xq2, xs2, wq2, wsc2, y_bf16=y2, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [host(t) for t in (y, acc, y2)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for r in range(4):
+        for t in (y, acc, y2):
+            t.zero_()
+        scratch = torch.randn(1 << 20, device="cuda:0").sum()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip((host(t) for t in (y, acc, y2)), ref):
+            np.testing.assert_array_equal(a, b, err_msg=f"replay {r}")
+        assert not bool(ws.get(1, torch.device("cuda:0"), "zeroed").any()), f"replay {r}"
+        del scratch
+
+
 def test_graph_replay_batched_and_stochastic_steps():
     """The 288-row verify step (quantize_act_tiled; the down-shaped linear
     12288 -> 4096, whose k is split across two workgroups through the zeroed
