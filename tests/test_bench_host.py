@@ -39,6 +39,19 @@ def test_committed_traffic_matches_the_kernel_source():
     assert 0.95 < t / alg < 1.10
 
 
+def test_committed_batched_counters_match_the_kernel_source():
+    """The 288-row counter summary (MfmaUtil, HBM traffic per shape) was
+    taken on the batched kernels' source in the tree, and each shape's
+    traffic is at least the algorithmic bytes."""
+    c = bench.read_batched_counters()
+    assert c is not None and not c["stale"], \
+        "profiles/gemm_w8a8_batched_m288_counters.txt is stale: retake with --pmc-probe-batched"
+    assert c["per_shape"]
+    for shape, v in c["per_shape"].items():
+        assert 0.0 < v["MfmaUtil"] < 100.0, shape
+        assert v["hbm_over_algorithmic"] >= 0.99, shape
+
+
 def test_traffic_is_dropped_for_another_kernel_source(tmp_path, monkeypatch):
     other = tmp_path / "gemm_w8a8.hip"
     other.write_text("// a different kernel source\n")
