@@ -169,8 +169,9 @@ w8a8_status w8a8_tile_weight(const int8_t* wq, int64_t N, int64_t K,
  *          w8a8_linear_workspace_bytes(M, N, K) bytes (NULL allowed when that
  *          is 0), 256-byte aligned.  It holds the int32 partials and arrival
  *          counters of a reduction split across workgroups: up to 16 rows a
- *          long or narrow product, above 16 rows (tiled weights, K % 64 == 0)
- *          a long one on a mid-size grid.  The workspace must be zero-filled
+ *          long or narrow product, or only the 16-channel tiles past the last
+ *          whole round over the compute units of a long one; above 16 rows
+ *          (tiled weights, K % 64 == 0) a long one on a mid-size grid.  The workspace must be zero-filled
  *          before its first use; every completed call leaves it zero-filled
  *          again.  Calls that share a workspace must not overlap in time.
  * Requires 0 <= K <= W8A8_MAX_K, K % 16 == 0; any N (ragged tails are
