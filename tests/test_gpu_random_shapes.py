@@ -1,4 +1,5 @@
-"""Seeded random shapes for the W8A8 and W4A8 linears, the LM-head
+"""Seeded random shapes for the W8A8 linear (plain and smoothed) and the
+W4A8 linear, the LM-head
 verification, the stochastic acceptance, the fused BF16 glue and the
 verified block's attention with its q/k norm, rotary embedding and cache
 append, GPU against the CPU oracle: bit for bit, except the glue's bf16 rows
@@ -365,3 +366,29 @@ def test_random_qk_norm_rope_append(B, T, Hq, Hkv, Lmax, lengths, base):
     for b in range(B):
         touched[b, :, start[b]:start[b] + T] = True
     np.testing.assert_array_equal(host(kc)[~touched], kc0[~touched])
+
+
+@pytest.mark.parametrize("M,N,K", _draw_shapes(40, 6, (1, 64), 1.5e9))
+def test_random_smoothed_linear(M, N, K):
+    """Online smoothing at random shapes: activations multiplied and weights
+    divided by one positive per-channel vector before quantization, then the
+    linear; codes, scales, int32 sums and outputs bit-exact."""
+    announce(f"random smoothed linear M={M} N={N} K={K}")
+    seed = M * 7919 + N * 31 + K + 3
+    bits = synth.activations_bf16(seed, M, K, outliers=True)
+    w = synth.weights_f32(seed, N, K)
+    s = synth.smoothing_vector(seed, K)
+    xq_r, xs_r = oracle.quantize_act(bits, smooth=s)
+    wq_r, ws_r = oracle.quantize_weight(w, smooth=s)
+    acc_r, y32_r, y_r = oracle.w8a8_linear(xq_r, xs_r, wq_r, ws_r)
+    sd = dev(s)
+    xq, xs = w8.quantize_act(dev_bf16(bits), sd)
+    wq, ws = w8.quantize_weight(dev(w), sd, tiled=True)
+    yb, yf, acc = w8.linear(xq, xs, wq, ws, want_bf16=True, want_f32=True, want_acc=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(xq), xq_r)
+    np.testing.assert_array_equal(host(xs).view(np.uint32), xs_r.view(np.uint32))
+    np.testing.assert_array_equal(host(ws).view(np.uint32), ws_r.view(np.uint32))
+    np.testing.assert_array_equal(host(acc), acc_r)
+    np.testing.assert_array_equal(host(yf).view(np.uint32), y32_r.view(np.uint32))
+    np.testing.assert_array_equal(host(yb), y_r)
