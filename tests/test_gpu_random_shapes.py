@@ -1,10 +1,9 @@
-"""Seeded random shapes for the W8A8 linear (plain and smoothed) and the
-W4A8 linear, the LM-head
-verification, the stochastic acceptance, the fused BF16 glue and the
-verified block's attention with its q/k norm, rotary embedding and cache
-append, GPU against the CPU oracle: bit for bit, except the glue's bf16 rows
-and the attention outputs, which carry the tolerance of their own tests
-(1e-2 relative / 1e-3 absolute).
+"""Seeded random shapes for the W8A8 linear (plain and smoothed), the W4A8
+linear, the LM-head verification, the stochastic acceptance, the fused BF16
+glue and the verified block's attention with its q/k norm, rotary embedding
+and cache append, GPU against the CPU oracle: bit for bit, except the
+glue's bf16 rows and the attention outputs, which carry the tolerance of
+their own tests (1e-2 relative / 1e-3 absolute).
 
 The fixed-shape parity tests pin the workloads' shapes and the edges each
 kernel path was written for; these draw (M, N, K) at random over the whole
