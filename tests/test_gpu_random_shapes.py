@@ -391,3 +391,60 @@ def test_random_smoothed_linear(M, N, K):
     np.testing.assert_array_equal(host(acc), acc_r)
     np.testing.assert_array_equal(host(yf).view(np.uint32), y32_r.view(np.uint32))
     np.testing.assert_array_equal(host(yb), y_r)
+
+
+def _head_draws(seed: int, n: int) -> list:
+    """LM-head verifications: B in [1, 8], G in [0, 10], V in [1, 160000],
+    K a multiple of 16 in [16, 8192]; R*V*K <= 2e9."""
+    r = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        B, G = int(r.integers(1, 9)), int(r.integers(0, 11))
+        V = int(np.exp(r.uniform(0.0, np.log(160000.0))))
+        K = 16 * int(np.exp(r.uniform(0.0, np.log(8192 / 16))))
+        if B * (G + 1) * V * K <= 2.0e9:
+            out.append((B, G, V, K))
+    return out
+
+
+@pytest.mark.parametrize("B,G,V,K", _head_draws(41, 6))
+def test_random_lm_head_argmax_w4(B, G, V, K):
+    """The W4A8 LM head with the argmax folded in, then accept_from_keys."""
+    announce(f"random lm_head_argmax_w4 B={B} G={G} V={V} K={K}")
+    R = B * (G + 1)
+    bits = synth.activations_bf16(V + K + 5, R, K)
+    w = synth.weights_f32(V + K + 5, V, K)
+    xq_r, xs_r = oracle.quantize_act(bits)
+    q_r, s_r = oracle.quantize_weight_int4(w)
+    _, y32_r, _ = oracle.w8a8_linear(xq_r, xs_r, q_r, s_r)
+    am0 = oracle.argmax_rows(y32_r).reshape(B, G + 1)
+    draft = synth.draft_ids(V + K + 5, B, G, V)
+    for b in range(B):
+        p = (3 * b + 2) % (G + 1)
+        draft[b, :p] = am0[b, :p]
+    am_r, al_r, nt_r = oracle.verify_accept(y32_r, draft)
+    xq, xs = w8.quantize_act(dev_bf16(bits))
+    wq4, ws = w8.quantize_weight_w4(dev(w))
+    wsp = w8.Workspace()
+    w8.lm_head_argmax_w4(xq, xs, wq4, ws, workspace=wsp)
+    am, al, nt = w8.accept_from_keys(dev(draft), workspace=wsp)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(am), am_r)
+    np.testing.assert_array_equal(host(al), al_r)
+    np.testing.assert_array_equal(host(nt), nt_r)
+
+
+@pytest.mark.parametrize("R,V,t", [(int(a), int(b), float(np.float32(c))) for a, b, c in zip(
+    np.random.default_rng(42).integers(1, 40, 6),
+    np.exp(np.random.default_rng(43).uniform(0.0, np.log(200000.0), 6)).astype(int) + 1,
+    np.exp(np.random.default_rng(44).uniform(np.log(0.05), np.log(4.0), 6)))])
+def test_random_sample_weights(R, V, t):
+    """The fixed-point softmax numerators of the stochastic acceptance, every
+    weight bit-exact, at random row counts, vocabularies and temperatures."""
+    announce(f"random sample_weights R={R} V={V} T={t}")
+    y = (np.random.default_rng(R * 100003 + V).standard_normal((R, V), dtype=np.float32)
+         * np.float32(3.0)).astype(np.float32)
+    w = host(w8.sample_weights(dev(y), t)).view(np.uint64)
+    inv_t = S.inv_temperature(t)
+    for r in range(R):
+        np.testing.assert_array_equal(w[r], S.fixed_weights(y[r], inv_t))
