@@ -356,10 +356,13 @@ def test_random_qk_norm_rope_append(B, T, Hq, Hkv, Lmax, lengths, base):
         for i in range(T):
             want_k[b, :, start[b] + i] = k_r[b, i]
             want_v[b, :, start[b] + i] = v_r[b, i]
+    fractions = []
     for got, want in ((host(q), q_r), (host(kc), want_k)):
         g = oracle.bf16_to_f32(got).astype(np.float64)
         w = oracle.bf16_to_f32(want).astype(np.float64)
         assert np.all(np.abs(g - w) <= 1e-3 + 1e-2 * np.abs(w))
+        fractions.append(float(np.mean(got == want)))
+    print(f"[gpu] bit-identical q {fractions[0]:.6f} k(all) {fractions[1]:.6f}", flush=True)
     np.testing.assert_array_equal(host(vc), host(w8.pack_v_cache(dev_bf16(want_v))))
     touched = np.zeros((B, Hkv, Lmax), dtype=bool)
     for b in range(B):
