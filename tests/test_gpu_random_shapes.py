@@ -1,9 +1,10 @@
 """Seeded random shapes for the W8A8 linear (plain and smoothed), the W4A8
-linear, the LM-head verification, the stochastic acceptance, the fused BF16
-glue and the verified block's attention with its q/k norm, rotary embedding
-and cache append, GPU against the CPU oracle: bit for bit, except the
-glue's bf16 rows and the attention outputs, which carry the tolerance of
-their own tests (1e-2 relative / 1e-3 absolute).
+linear, the LM-head verification, the two-pass argmax and acceptance on
+planted ties, the stochastic acceptance, the fused BF16 glue and the
+verified block's attention with its q/k norm, rotary embedding and cache
+append, GPU against the CPU oracle: bit for bit, except the glue's bf16
+rows and the attention outputs, which carry the tolerance of their own
+tests (1e-2 relative / 1e-3 absolute).
 
 The fixed-shape parity tests pin the workloads' shapes and the edges each
 kernel path was written for; these draw (M, N, K) at random over the whole
@@ -451,3 +452,34 @@ def test_random_sample_weights(R, V, t):
     inv_t = S.inv_temperature(t)
     for r in range(R):
         np.testing.assert_array_equal(w[r], S.fixed_weights(y[r], inv_t))
+
+
+@pytest.mark.parametrize("B,G,V", [(int(a), int(b), int(c)) for a, b, c in zip(
+    np.random.default_rng(45).integers(1, 9, 6), np.random.default_rng(46).integers(0, 12, 6),
+    np.exp(np.random.default_rng(47).uniform(0.0, np.log(300000.0), 6)).astype(int) + 1)])
+def test_random_verify_accept_ties(B, G, V):
+    """The two-pass argmax and greedy acceptance on fp32 logits, with the
+    row maximum planted at two to four random positions per row (so ties
+    straddle the 4096-logit chunks of the first pass), -0/+0 pairs, and
+    drafts that agree with a spread of prefix lengths: argmax (lowest index
+    on ties), accepted lengths and next tokens exact."""
+    announce(f"random verify_accept ties B={B} G={G} V={V}")
+    r = np.random.default_rng(B * 7 + G * 131 + V)
+    R = B * (G + 1)
+    y = r.standard_normal((R, V), dtype=np.float32)
+    for i in range(R):
+        top = np.float32(10.0 + r.integers(0, 3))
+        y[i, r.integers(0, V, size=int(r.integers(2, 5)))] = top
+        if V > 2:
+            y[i, r.integers(0, V, size=2)] = np.float32([-0.0, 0.0])
+    am0 = oracle.argmax_rows(y).reshape(B, G + 1)
+    d = r.integers(0, V, size=(B, G)).astype(np.int32)
+    for b in range(B):
+        p = (5 * b + 1) % (G + 1)
+        d[b, :p] = am0[b, :p]
+    am_r, al_r, nt_r = oracle.verify_accept(y, d)
+    am, al, nt = w8.verify_accept(dev(y), dev(d))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(am), am_r)
+    np.testing.assert_array_equal(host(al), al_r)
+    np.testing.assert_array_equal(host(nt), nt_r)
